@@ -1,0 +1,125 @@
+/*
+ * qlora.h -- C ABI of the MI355X (gfx950) fused QLoRA linear layer.
+ *
+ * What is computed (sources are the pages' titles and passages):
+ *   A frozen weight W [N,K] is stored in 4 bits and a trainable rank-r LoRA
+ *   pair (A [r,K], B [N,r]) sits on it ("Rev vs unsloth", fused quantized-LoRA
+ *   card; "Unsloth vs The Stack v2", quantized-base card: 4-bit weights stay
+ *   frozen, only the adapters train). With s = lora_alpha / r:
+ *       Y  = X.W^T + s.(X.A^T).B^T
+ *       dX = dY.W + s.(dY.B).A
+ *       dB = s.dY^T.(X.A^T)         dA = s.(dY.B)^T.X        (no dW: W is frozen)
+ *   These are the hand-derived LoRA gradients of the "Unsloth" wiki entry
+ *   (Theory) and of the "Unsloth vs PyTorch" video (0:43-1:24); every product
+ *   is bracketed through the skinny M x r tensors so the N x K matrix B.A is
+ *   never formed (same video, 1:35-2:00). The SwiGLU block of the wiki entry
+ *   (Theory: fused SwiGLU) is g = lin_gate(X), u = lin_up(X),
+ *   h = silu(g)*u, Y = lin_down(h), LoRA on all three projections.
+ *
+ * 4-bit format (the pages say only "4-bit" bitsandbytes checkpoints; this is
+ * the NF4 reading): per row n and 64-column block b, absmax = max |W|,
+ * code = nearest of the 16 NormalFloat-4 levels to W/absmax (fp32 division;
+ * ties to the lower level), two codes per byte with the even column in the
+ * low nibble; dequantized weight What = fp32(L[code] * absmax). A block of
+ * zeros has absmax 0 and code 7 (the exact zero level).
+ *
+ * Conventions for every call:
+ *   - Pointers are device pointers owned by the caller, row-major and
+ *     contiguous, 16-byte aligned. bf16 tensors are passed as uint16_t bit
+ *     patterns. The library allocates no memory; scratch space comes from the
+ *     caller's workspace (size from qlora_workspace_size).
+ *   - Shapes: K % 64 == 0, N % 8 == 0, 1 <= r <= 256, M >= 0 (M == 0 is a
+ *     no-op). Anything else returns QLORA_EINVAL before any launch.
+ *   - Every call enqueues its kernels on `stream` (a hipStream_t, 0 = the
+ *     null stream) and returns without synchronising. Launch failures return
+ *     QLORA_EHIP; qlora_last_error() gives the HIP error text.
+ *   - Calls are re-entrant; concurrent calls must not share output or
+ *     workspace buffers.
+ *   - Matrix products accumulate in fp32. Y, dX, Z, g, u, h are rounded once
+ *     to bf16 (round to nearest even). dA and dB are fp32.
+ */
+#ifndef QLORA_H
+#define QLORA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  QLORA_OK = 0,
+  QLORA_EINVAL = -1,       /* bad shape, null pointer, misalignment */
+  QLORA_EUNSUPPORTED = -2, /* valid request this build does not handle */
+  QLORA_EWORKSPACE = -3,   /* workspace missing or smaller than qlora_workspace_size */
+  QLORA_EHIP = -4          /* a HIP launch failed; see qlora_last_error() */
+} qlora_status;
+
+typedef enum {
+  QLORA_OP_FORWARD = 0,
+  QLORA_OP_BACKWARD = 1,
+  QLORA_OP_MLP_FORWARD = 2,
+  QLORA_OP_MLP_BACKWARD = 3
+} qlora_op;
+
+/* One LoRA-adapted 4-bit projection: out = in . What^T + s . (in . A^T) . B^T. */
+typedef struct {
+  const uint8_t* codes;  /* [N, K/2]  two 4-bit codes per byte, even column in the low nibble */
+  const float* absmax;   /* [N, K/64] fp32 scale of each 64-column block */
+  const uint16_t* A;     /* [r, K]    bf16 LoRA down projection */
+  const uint16_t* B;     /* [N, r]    bf16 LoRA up projection */
+  int64_t K;             /* input features */
+  int64_t N;             /* output features */
+  int64_t r;             /* LoRA rank */
+  float s;               /* lora_alpha / r */
+} qlora_layer;
+
+/* Quantize W [N,K] fp32 to codes [N,K/2] and absmax [N,K/64] (format above).
+ * nonfinite_blocks (device uint32, may be NULL) is set to the number of
+ * blocks holding Inf/NaN; such a block gets absmax = NaN. Setup-time call. */
+int qlora_quantize(const float* W, int64_t N, int64_t K, uint8_t* codes, float* absmax,
+                   uint32_t* nonfinite_blocks, void* stream);
+
+/* What [N,K] fp32 = L[code] * absmax. Exposes the exact operand values for testing. */
+int qlora_dequantize(const uint8_t* codes, const float* absmax, int64_t N, int64_t K, float* W_hat,
+                     void* stream);
+
+/* Workspace bytes needed by `op` (qlora_op) for M tokens. For the MLP ops,
+ * K is the model width and N the intermediate width. */
+size_t qlora_workspace_size(int op, int64_t M, int64_t K, int64_t N, int64_t r);
+
+/* Forward of one projection. X [M,K] bf16 -> Y [M,N] bf16 and Z_save = X.A^T
+ * [M,r] bf16 (kept for the backward). Needs no workspace (ws may be NULL). */
+int qlora_forward(const qlora_layer* L, const uint16_t* X, int64_t M, uint16_t* Y, uint16_t* Z_save,
+                  void* ws, size_t ws_bytes, void* stream);
+
+/* Backward of one projection for upstream dY [M,N]. Writes dX [M,K] bf16
+ * (dX may be NULL to skip it), dA [r,K] fp32 and dB [N,r] fp32.
+ * X and Z_save are the forward's input and saved tensor. */
+int qlora_backward(const qlora_layer* L, const uint16_t* dY, const uint16_t* X, const uint16_t* Z_save,
+                   int64_t M, uint16_t* dX, float* dA, float* dB, void* ws, size_t ws_bytes, void* stream);
+
+/* SwiGLU MLP forward: g = lin_gate(X), u = lin_up(X), h = silu(g)*u,
+ * Y = lin_down(h). gate/up: K = H (model width), N = I; down: K = I, N = H.
+ * Saves g, u, h [M,I] bf16 and Z_save [3][M][r] (gate, up, down) for the
+ * backward. All three layers must share r. Needs no workspace. */
+int swiglu_mlp_forward(const qlora_layer* gate, const qlora_layer* up, const qlora_layer* down,
+                       const uint16_t* X, int64_t M, uint16_t* Y, uint16_t* g_save, uint16_t* u_save,
+                       uint16_t* h_save, uint16_t* Z_save, void* ws, size_t ws_bytes, void* stream);
+
+/* SwiGLU MLP backward for upstream dY [M,H]. dA[i], dB[i] (i = 0 gate,
+ * 1 up, 2 down) receive fp32 [r,K_i] and [N_i,r]; dX [M,H] bf16 may be NULL. */
+int swiglu_mlp_backward(const qlora_layer* gate, const qlora_layer* up, const qlora_layer* down,
+                        const uint16_t* dY, const uint16_t* X, const uint16_t* g_save, const uint16_t* u_save,
+                        const uint16_t* h_save, const uint16_t* Z_save, int64_t M, uint16_t* dX,
+                        float* const dA[3], float* const dB[3], void* ws, size_t ws_bytes, void* stream);
+
+/* Short text for a status code; for QLORA_EHIP, the last HIP error seen by this thread. */
+const char* qlora_status_string(int status);
+const char* qlora_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* QLORA_H */

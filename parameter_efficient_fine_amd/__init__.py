@@ -1,0 +1,16 @@
+"""MI355X (gfx950) fused QLoRA linear layer: 4-bit NF4 frozen weight + rank-r LoRA adapter.
+
+The work runs in libqlora.so (hand-written HIP, C ABI in include/qlora.h);
+this package is its thin Python binding. Importing the package does not load
+the library; the first call does, and fails loudly if it is not built.
+"""
+from .ops import (  # noqa: F401
+    QLoraLayer,
+    backward,
+    dequantize,
+    forward,
+    mlp_backward,
+    mlp_forward,
+    quantize,
+    workspace_size,
+)

@@ -1,0 +1,83 @@
+"""ctypes binding of libqlora.so (the C ABI declared in include/qlora.h).
+
+Argument marshalling only: every step of the layer runs in the HIP kernels
+behind these entry points. Loading fails loudly when the library is missing.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libqlora.so")
+
+QLORA_OK = 0
+QLORA_EINVAL = -1
+QLORA_EUNSUPPORTED = -2
+QLORA_EWORKSPACE = -3
+QLORA_EHIP = -4
+
+OP_FORWARD, OP_BACKWARD, OP_MLP_FORWARD, OP_MLP_BACKWARD = 0, 1, 2, 3
+
+# Every function the header declares (checked by the CPU tests against include/qlora.h).
+EXPORTS = [
+    "qlora_quantize", "qlora_dequantize", "qlora_workspace_size", "qlora_forward", "qlora_backward",
+    "swiglu_mlp_forward", "swiglu_mlp_backward", "qlora_status_string", "qlora_last_error",
+]
+
+
+class QLoraLayerC(ctypes.Structure):
+    _fields_ = [
+        ("codes", ctypes.c_void_p),
+        ("absmax", ctypes.c_void_p),
+        ("A", ctypes.c_void_p),
+        ("B", ctypes.c_void_p),
+        ("K", ctypes.c_int64),
+        ("N", ctypes.c_int64),
+        ("r", ctypes.c_int64),
+        ("s", ctypes.c_float),
+    ]
+
+
+class QLoraError(RuntimeError):
+    def __init__(self, fn: str, status: int, text: str):
+        super().__init__(f"{fn} failed with status {status}: {text}")
+        self.status = status
+
+
+_lib = None
+
+
+def lib():
+    """Load libqlora.so once; raise if it has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} not found: build it with `python -m parameter_efficient_fine_amd.build`")
+    L = ctypes.CDLL(LIB_PATH)
+    vp, i64, sz = ctypes.c_void_p, ctypes.c_int64, ctypes.c_size_t
+    LP = ctypes.POINTER(QLoraLayerC)
+    L.qlora_quantize.argtypes = [vp, i64, i64, vp, vp, vp, vp]
+    L.qlora_dequantize.argtypes = [vp, vp, i64, i64, vp, vp]
+    L.qlora_workspace_size.argtypes = [ctypes.c_int, i64, i64, i64, i64]
+    L.qlora_workspace_size.restype = sz
+    L.qlora_forward.argtypes = [LP, vp, i64, vp, vp, vp, sz, vp]
+    L.qlora_backward.argtypes = [LP, vp, vp, vp, i64, vp, vp, vp, vp, sz, vp]
+    L.swiglu_mlp_forward.argtypes = [LP, LP, LP, vp, i64, vp, vp, vp, vp, vp, vp, sz, vp]
+    L.swiglu_mlp_backward.argtypes = [LP, LP, LP, vp, vp, vp, vp, vp, vp, i64, vp,
+                                      ctypes.POINTER(vp), ctypes.POINTER(vp), vp, sz, vp]
+    L.qlora_status_string.argtypes = [ctypes.c_int]
+    L.qlora_status_string.restype = ctypes.c_char_p
+    L.qlora_last_error.argtypes = []
+    L.qlora_last_error.restype = ctypes.c_char_p
+    for f in ("qlora_quantize", "qlora_dequantize", "qlora_forward", "qlora_backward", "swiglu_mlp_forward",
+              "swiglu_mlp_backward"):
+        getattr(L, f).restype = ctypes.c_int
+    _lib = L
+    return L
+
+
+def check(fn: str, status: int) -> None:
+    if status != QLORA_OK:
+        raise QLoraError(fn, status, lib().qlora_status_string(status).decode())

@@ -1,0 +1,140 @@
+// Device-side building blocks shared by the gfx950 kernels of the fused QLoRA
+// layer: vector types, MFMA wrappers, bf16 packing, the NF4 codebook and the
+// 4-bit -> bf16 dequantizer used inside the GEMM tiles.
+//
+// Method: "Rev vs unsloth", fused quantized-LoRA card (a frozen 4-bit weight
+// and a LoRA adapter evaluated as one layer); "Unsloth vs The Stack v2",
+// quantized-base card (4-bit frozen base). The 4-bit format -- 16 NormalFloat
+// levels, one fp32 absmax per 64 consecutive elements of a weight row, two
+// codes per byte with the even column in the low nibble -- is the plainest
+// reading of the bitsandbytes 4-bit checkpoints the pages load.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace qlora {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+
+constexpr int kBlock = 64;  // weight elements per absmax
+
+// NormalFloat-4 levels (QLoRA paper's printed table) as fp32 bit patterns.
+// Index = 4-bit code. Level 7 is the exact zero.
+constexpr uint32_t kNF4Bits[16] = {
+    0xbf800000u, 0xbf3239b1u, 0xbf066b30u, 0xbeca32a0u, 0xbe91a24du, 0xbe3d353fu, 0xbdba7871u, 0x00000000u,
+    0x3da2faffu, 0x3e24cae3u, 0x3e7c04ddu, 0x3ead033au, 0x3ee1a4b8u, 0x3f1007abu, 0x3f3913b3u, 0x3f800000u};
+
+__host__ __device__ constexpr float nf4_level(int c) { return __builtin_bit_cast(float, kNF4Bits[c]); }
+
+// Decision threshold between level j and j+1: the midpoint, formed in double
+// precision and rounded once to fp32 (evaluated at compile time).
+__host__ __device__ constexpr float nf4_threshold(int j) {
+  return (float)(((double)nf4_level(j) + (double)nf4_level(j + 1)) * 0.5);
+}
+
+// ---------------------------------------------------------------------------
+// bf16 helpers (bit patterns in uint16/uint32; conversion is round-to-nearest-even
+// by v_cvt_pk_bf16_f32)
+
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  f32x2 v = {lo, hi};
+  bf16x2 b = __builtin_convertvector(v, bf16x2);
+  return __builtin_bit_cast(uint32_t, b);
+}
+
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __builtin_bit_cast(float, w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __builtin_bit_cast(float, w & 0xffff0000u); }
+__device__ __forceinline__ float bf16_to_f32(uint16_t h) { return __builtin_bit_cast(float, (uint32_t)h << 16); }
+
+__device__ __forceinline__ uint32_t perm(uint32_t hi, uint32_t lo, uint32_t sel) {
+  return __builtin_amdgcn_perm(hi, lo, sel);
+}
+
+// ---------------------------------------------------------------------------
+// MFMA wrappers (gfx950). Operand layouts, for lane l of a wave64:
+//   32x32x16: A row i = l%32, k = 8*(l/32)+e ; B col j = l%32, k = 8*(l/32)+e
+//             C/D: col j = l%32, row i = 8*(v/4) + 4*(l/32) + v%4 (v = 0..15)
+//   16x16x32: A row i = l%16, k = 8*(l/16)+e ; B col j = l%16, k = 8*(l/16)+e
+//             C/D: col j = l%16, row i = 4*(l/16) + v (v = 0..3)
+
+__device__ __forceinline__ f32x16 mfma32(u32x4 a, u32x4 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b), c, 0,
+                                                 0, 0);
+}
+__device__ __forceinline__ f32x4 mfma16(u32x4 a, u32x4 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b), c, 0,
+                                                 0, 0);
+}
+
+// LDS transposed read (ds_read_b64_tr_b16). Within each 16-lane group, lane s
+// supplies the address of 4 consecutive bf16; lane i receives element i%4 of
+// the chunks supplied by lanes i/4, 4+i/4, 8+i/4, 12+i/4. When lane s points
+// at row (s/4), columns 4*(s%4)..+3 of a row-major tile, lane i ends up with
+// rows 0..3 of column i: the tile is read column-wise.
+__device__ __forceinline__ u32x2 lds_read_tr(const void* p) {
+  s16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p));
+  return __builtin_bit_cast(u32x2, v);
+}
+
+// ---------------------------------------------------------------------------
+// 4-bit -> bf16 dequantization inside the GEMM tiles.
+//
+// For one (row, 64-block) the 16 possible outputs bf16(fp32(L[c] * absmax))
+// are formed once (16 multiplies, 8 packed conversions) and kept as two byte
+// planes (low bytes and high bytes of the 16 bf16 values, 4 dwords each).
+// A code then selects its two bytes with v_perm_b32: the low three bits pick
+// a byte inside an 8-byte half-table, bit 3 picks the half.
+
+struct Nf4Lut {
+  uint32_t lo[4];
+  uint32_t hi[4];
+};
+
+__device__ __forceinline__ Nf4Lut make_lut(float absmax) {
+  uint32_t p[8];
+#pragma unroll
+  for (int q = 0; q < 8; ++q) p[q] = pack_bf16x2(nf4_level(2 * q) * absmax, nf4_level(2 * q + 1) * absmax);
+  Nf4Lut t;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    t.lo[q] = perm(p[2 * q + 1], p[2 * q], 0x06040200u);
+    t.hi[q] = perm(p[2 * q + 1], p[2 * q], 0x07050301u);
+  }
+  return t;
+}
+
+// x holds 8 codes (nibble e of x is the code of element e). Returns the 8
+// bf16 values as 4 dwords in element order: out[q] = elem 2q | elem 2q+1 << 16.
+__device__ __forceinline__ u32x4 dequant8(uint32_t x, const Nf4Lut& t) {
+  const uint32_t xs = x >> 4;
+  const uint32_t s7e = x & 0x07070707u;   // even elements, low 3 bits
+  const uint32_t s7o = xs & 0x07070707u;  // odd elements
+  const uint32_t she = ((x >> 1) & 0x04040404u) | 0x03020100u;  // byte i + 4*bit3
+  const uint32_t sho = ((x >> 5) & 0x04040404u) | 0x03020100u;
+  const uint32_t loe = perm(perm(t.lo[3], t.lo[2], s7e), perm(t.lo[1], t.lo[0], s7e), she);
+  const uint32_t hie = perm(perm(t.hi[3], t.hi[2], s7e), perm(t.hi[1], t.hi[0], s7e), she);
+  const uint32_t loo = perm(perm(t.lo[3], t.lo[2], s7o), perm(t.lo[1], t.lo[0], s7o), sho);
+  const uint32_t hio = perm(perm(t.hi[3], t.hi[2], s7o), perm(t.hi[1], t.hi[0], s7o), sho);
+  const uint32_t e01 = perm(hie, loe, 0x05010400u);  // elem0 | elem2 << 16
+  const uint32_t e23 = perm(hie, loe, 0x07030602u);  // elem4 | elem6 << 16
+  const uint32_t o01 = perm(hio, loo, 0x05010400u);  // elem1 | elem3 << 16
+  const uint32_t o23 = perm(hio, loo, 0x07030602u);  // elem5 | elem7 << 16
+  u32x4 r;
+  r[0] = perm(o01, e01, 0x05040100u);
+  r[1] = perm(o01, e01, 0x07060302u);
+  r[2] = perm(o23, e23, 0x05040100u);
+  r[3] = perm(o23, e23, 0x07060302u);
+  return r;
+}
+
+__device__ __forceinline__ float sigmoid_f(float z) { return 1.0f / (1.0f + expf(-z)); }
+
+}  // namespace qlora

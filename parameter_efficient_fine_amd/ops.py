@@ -1,0 +1,162 @@
+"""Tensor-level entry points over the C ABI (torch provides device memory and the stream).
+
+Each function checks shapes and dtypes, allocates the outputs and workspace
+with torch, and calls one C-ABI entry point on the current HIP stream. No
+arithmetic of the layer happens here.
+"""
+from __future__ import annotations
+
+import ctypes
+from dataclasses import dataclass
+
+import torch
+
+from . import _lib as C
+
+
+def _ptr(t):
+    return ctypes.c_void_p(t.data_ptr()) if t is not None else ctypes.c_void_p(0)
+
+
+def _stream():
+    return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+def _need(t, dtype, shape, name):
+    if t.dtype != dtype or tuple(t.shape) != tuple(shape) or not t.is_contiguous() or not t.is_cuda:
+        raise ValueError(f"{name}: expected contiguous {dtype} {tuple(shape)} on GPU, got {t.dtype} {tuple(t.shape)}")
+
+
+@dataclass
+class QLoraLayer:
+    """A frozen 4-bit weight with its LoRA pair (device tensors)."""
+    codes: torch.Tensor   # uint8 [N, K/2]
+    absmax: torch.Tensor  # float32 [N, K/64]
+    A: torch.Tensor       # bfloat16 [r, K]
+    B: torch.Tensor       # bfloat16 [N, r]
+    s: float
+
+    @property
+    def K(self):
+        return self.A.shape[1]
+
+    @property
+    def N(self):
+        return self.B.shape[0]
+
+    @property
+    def r(self):
+        return self.A.shape[0]
+
+    def c(self) -> C.QLoraLayerC:
+        K, N, r = self.K, self.N, self.r
+        _need(self.codes, torch.uint8, (N, K // 2), "codes")
+        _need(self.absmax, torch.float32, (N, K // 64), "absmax")
+        _need(self.A, torch.bfloat16, (r, K), "A")
+        _need(self.B, torch.bfloat16, (N, r), "B")
+        return C.QLoraLayerC(self.codes.data_ptr(), self.absmax.data_ptr(), self.A.data_ptr(), self.B.data_ptr(),
+                             K, N, r, float(self.s))
+
+
+def quantize(W: torch.Tensor):
+    """fp32 W [N,K] on the GPU -> (codes uint8 [N,K/2], absmax fp32 [N,K/64]). Raises on Inf/NaN."""
+    N, K = W.shape
+    _need(W, torch.float32, (N, K), "W")
+    codes = torch.empty((N, K // 2), dtype=torch.uint8, device=W.device)
+    absmax = torch.empty((N, K // 64), dtype=torch.float32, device=W.device)
+    bad = torch.empty((1,), dtype=torch.int32, device=W.device)
+    C.check("qlora_quantize", C.lib().qlora_quantize(_ptr(W), N, K, _ptr(codes), _ptr(absmax), _ptr(bad), _stream()))
+    if int(bad.item()) != 0:
+        raise ValueError(f"qlora_quantize: {int(bad.item())} block(s) hold non-finite weights")
+    return codes, absmax
+
+
+def dequantize(codes: torch.Tensor, absmax: torch.Tensor) -> torch.Tensor:
+    N, K2 = codes.shape
+    K = 2 * K2
+    _need(codes, torch.uint8, (N, K2), "codes")
+    _need(absmax, torch.float32, (N, K // 64), "absmax")
+    out = torch.empty((N, K), dtype=torch.float32, device=codes.device)
+    C.check("qlora_dequantize", C.lib().qlora_dequantize(_ptr(codes), _ptr(absmax), N, K, _ptr(out), _stream()))
+    return out
+
+
+def workspace_size(op: int, M: int, K: int, N: int, r: int) -> int:
+    return int(C.lib().qlora_workspace_size(op, M, K, N, r))
+
+
+def _workspace(nbytes: int, device) -> torch.Tensor:
+    return torch.empty((max(nbytes, 1),), dtype=torch.uint8, device=device)
+
+
+def forward(L: QLoraLayer, X: torch.Tensor, Y=None, Z=None):
+    """Y [M,N] bf16 and Z = X.A^T [M,r] bf16."""
+    M = X.shape[0]
+    _need(X, torch.bfloat16, (M, L.K), "X")
+    Y = torch.empty((M, L.N), dtype=torch.bfloat16, device=X.device) if Y is None else Y
+    Z = torch.empty((M, L.r), dtype=torch.bfloat16, device=X.device) if Z is None else Z
+    lc = L.c()
+    C.check("qlora_forward", C.lib().qlora_forward(ctypes.byref(lc), _ptr(X), M, _ptr(Y), _ptr(Z), None, 0,
+                                                   _stream()))
+    return Y, Z
+
+
+def backward(L: QLoraLayer, dY, X, Z, need_dX=True, ws=None, out=None):
+    """(dX bf16 [M,K] or None, dA fp32 [r,K], dB fp32 [N,r])."""
+    M = X.shape[0]
+    _need(dY, torch.bfloat16, (M, L.N), "dY")
+    _need(X, torch.bfloat16, (M, L.K), "X")
+    _need(Z, torch.bfloat16, (M, L.r), "Z")
+    dev = X.device
+    if out is None:
+        dX = torch.empty((M, L.K), dtype=torch.bfloat16, device=dev) if need_dX else None
+        dA = torch.empty((L.r, L.K), dtype=torch.float32, device=dev)
+        dB = torch.empty((L.N, L.r), dtype=torch.float32, device=dev)
+    else:
+        dX, dA, dB = out
+    nb = workspace_size(C.OP_BACKWARD, M, L.K, L.N, L.r)
+    ws = _workspace(nb, dev) if ws is None else ws
+    lc = L.c()
+    C.check("qlora_backward", C.lib().qlora_backward(ctypes.byref(lc), _ptr(dY), _ptr(X), _ptr(Z), M, _ptr(dX),
+                                                     _ptr(dA), _ptr(dB), _ptr(ws), ws.numel(), _stream()))
+    return dX, dA, dB
+
+
+def mlp_forward(gate: QLoraLayer, up: QLoraLayer, down: QLoraLayer, X, out=None):
+    """dict(Y, g, u, h, Z) for the SwiGLU block; Z is [3, M, r] (gate, up, down)."""
+    M = X.shape[0]
+    H, I, r = gate.K, gate.N, gate.r
+    _need(X, torch.bfloat16, (M, H), "X")
+    dev = X.device
+    if out is None:
+        out = dict(Y=torch.empty((M, H), dtype=torch.bfloat16, device=dev),
+                   g=torch.empty((M, I), dtype=torch.bfloat16, device=dev),
+                   u=torch.empty((M, I), dtype=torch.bfloat16, device=dev),
+                   h=torch.empty((M, I), dtype=torch.bfloat16, device=dev),
+                   Z=torch.empty((3, M, r), dtype=torch.bfloat16, device=dev))
+    lg, lu, ld = gate.c(), up.c(), down.c()
+    C.check("swiglu_mlp_forward", C.lib().swiglu_mlp_forward(
+        ctypes.byref(lg), ctypes.byref(lu), ctypes.byref(ld), _ptr(X), M, _ptr(out["Y"]), _ptr(out["g"]),
+        _ptr(out["u"]), _ptr(out["h"]), _ptr(out["Z"]), None, 0, _stream()))
+    return out
+
+
+def mlp_backward(gate: QLoraLayer, up: QLoraLayer, down: QLoraLayer, dY, X, saved, need_dX=True, ws=None, out=None):
+    """dict(dX, dA=[gate, up, down] fp32, dB=[...] fp32)."""
+    M = X.shape[0]
+    H, I, r = gate.K, gate.N, gate.r
+    _need(dY, torch.bfloat16, (M, H), "dY")
+    dev = X.device
+    if out is None:
+        out = dict(dX=torch.empty((M, H), dtype=torch.bfloat16, device=dev) if need_dX else None,
+                   dA=[torch.empty((r, L.K), dtype=torch.float32, device=dev) for L in (gate, up, down)],
+                   dB=[torch.empty((L.N, r), dtype=torch.float32, device=dev) for L in (gate, up, down)])
+    nb = workspace_size(C.OP_MLP_BACKWARD, M, H, I, r)
+    ws = _workspace(nb, dev) if ws is None else ws
+    dA = (ctypes.c_void_p * 3)(*[t.data_ptr() for t in out["dA"]])
+    dB = (ctypes.c_void_p * 3)(*[t.data_ptr() for t in out["dB"]])
+    lg, lu, ld = gate.c(), up.c(), down.c()
+    C.check("swiglu_mlp_backward", C.lib().swiglu_mlp_backward(
+        ctypes.byref(lg), ctypes.byref(lu), ctypes.byref(ld), _ptr(dY), _ptr(X), _ptr(saved["g"]), _ptr(saved["u"]),
+        _ptr(saved["h"]), _ptr(saved["Z"]), M, _ptr(out["dX"]), dA, dB, _ptr(ws), ws.numel(), _stream()))
+    return out

@@ -1,0 +1,70 @@
+"""Helpers for the GPU parity tests: device transfer of the seeded inputs and the
+oracle computations the tests compare against."""
+from __future__ import annotations
+
+import numpy as np
+
+from oracle import ref
+from synthetic import bf16_to_f32
+
+TOL = 1e-2  # max|gpu - ref| / max|ref| on bf16 outputs and fp32 gradients (fp32 accumulation)
+
+
+def rel_err(got, want) -> float:
+    got = np.asarray(got, dtype=np.float64)
+    want = np.asarray(want, dtype=np.float64)
+    den = float(np.max(np.abs(want)))
+    return float(np.max(np.abs(got - want))) / (den if den > 0 else 1.0)
+
+
+def dev_bf16(u16):
+    import torch
+    return torch.from_numpy(np.ascontiguousarray(u16).view(np.int16)).view(torch.bfloat16).cuda()
+
+
+def dev_f32(x):
+    import torch
+    return torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32)).cuda()
+
+
+def host(t) -> np.ndarray:
+    """bf16/fp32/uint8 device tensor -> numpy (bf16 widened to fp64)."""
+    import torch
+    t = t.detach().cpu()
+    if t.dtype == torch.bfloat16:
+        return ref.bf16_to_f64(t.view(torch.int16).numpy().view(np.uint16))
+    if t.dtype == torch.float32:
+        return t.numpy().astype(np.float64)
+    return t.numpy()
+
+
+class Prepared:
+    """One projection on both sides: oracle (fp64) and device tensors."""
+
+    def __init__(self, layer: dict, s: float, quantize_on_gpu=True):
+        import parameter_efficient_fine_amd as q
+        self.s = s
+        W = layer["W"]
+        self.codes_ref, self.absmax_ref = ref.quantize(W)
+        self.What = ref.dequantize(self.codes_ref, self.absmax_ref).astype(np.float64)
+        self.A = ref.bf16_to_f64(layer["A"])
+        self.B = ref.bf16_to_f64(layer["B"])
+        if quantize_on_gpu:
+            codes, absmax = q.quantize(dev_f32(W))
+        else:
+            import torch
+            codes = torch.from_numpy(self.codes_ref).cuda()
+            absmax = torch.from_numpy(self.absmax_ref).cuda()
+        self.dev = q.QLoraLayer(codes, absmax, dev_bf16(layer["A"]), dev_bf16(layer["B"]), s)
+
+    def triple(self):
+        return (self.What, self.A, self.B)
+
+
+def sample_rows(M: int, rng, per_block: int = 2, block: int = 256) -> np.ndarray:
+    """Rows spread over every 256-row block (so every tile and every split is hit), plus the ends."""
+    rows = {0, M - 1}
+    for b0 in range(0, M, block):
+        hi = min(M, b0 + block)
+        rows.update(int(x) for x in rng.integers(b0, hi, size=per_block))
+    return np.array(sorted(rows))

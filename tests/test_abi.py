@@ -1,0 +1,109 @@
+"""CPU checks of the C-ABI library: it loads, exports every declared entry point,
+carries the same codebook as the oracle, and rejects bad arguments before any
+GPU work (these calls return before touching HIP, so they run without a GPU)."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+from oracle.codebook import NF4_HEX
+from parameter_efficient_fine_amd import _lib as C
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "qlora.h")
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\*?\s+\*?(\w+)\s*\(", text, flags=re.M)))
+
+
+def test_header_declares_the_binding_exports():
+    assert _declared_functions() == sorted(C.EXPORTS)
+
+
+def test_library_loads_and_exports_every_declared_symbol():
+    lib = C.lib()
+    for name in _declared_functions():
+        assert hasattr(lib, name), name
+
+
+def test_kernel_codebook_matches_oracle_bit_for_bit():
+    src = open(os.path.join(ROOT, "parameter_efficient_fine_amd", "csrc", "common.hpp")).read()
+    block = src[src.index("kNF4Bits[16]"):]
+    block = block[block.index("{") + 1: block.index("}")]
+    words = [int(w, 16) for w in re.findall(r"0x([0-9a-fA-F]+)u", block)]
+    assert words == NF4_HEX
+
+
+def _layer(K=512, N=512, r=16, fake=0x10000):
+    return C.QLoraLayerC(fake, fake, fake, fake, K, N, r, 2.0)
+
+
+@pytest.mark.parametrize("K,N,r", [(500, 512, 16), (512, 12, 16), (512, 512, 0), (512, 512, 257), (0, 512, 8)])
+def test_forward_rejects_bad_shapes(K, N, r):
+    lib = C.lib()
+    L = _layer(K, N, r)
+    st = lib.qlora_forward(ctypes.byref(L), ctypes.c_void_p(0x10000), 4, ctypes.c_void_p(0x10000),
+                           ctypes.c_void_p(0x10000), None, 0, None)
+    assert st == C.QLORA_EINVAL
+
+
+def test_forward_rejects_null_and_misaligned():
+    lib = C.lib()
+    L = _layer()
+    assert lib.qlora_forward(ctypes.byref(L), None, 4, ctypes.c_void_p(0x10000), ctypes.c_void_p(0x10000),
+                             None, 0, None) == C.QLORA_EINVAL
+    assert lib.qlora_forward(ctypes.byref(L), ctypes.c_void_p(0x10002), 4, ctypes.c_void_p(0x10000),
+                             ctypes.c_void_p(0x10000), None, 0, None) == C.QLORA_EINVAL
+    bad = C.QLoraLayerC(0, 0x10000, 0x10000, 0x10000, 512, 512, 16, 2.0)
+    assert lib.qlora_forward(ctypes.byref(bad), ctypes.c_void_p(0x10000), 4, ctypes.c_void_p(0x10000),
+                             ctypes.c_void_p(0x10000), None, 0, None) == C.QLORA_EINVAL
+    assert lib.qlora_forward(None, ctypes.c_void_p(0x10000), 4, ctypes.c_void_p(0x10000),
+                             ctypes.c_void_p(0x10000), None, 0, None) == C.QLORA_EINVAL
+
+
+def test_backward_workspace_checks():
+    lib = C.lib()
+    L = _layer()
+    p = ctypes.c_void_p(0x10000)
+    need = lib.qlora_workspace_size(C.OP_BACKWARD, 64, 512, 512, 16)
+    assert need > 0
+    assert lib.qlora_backward(ctypes.byref(L), p, p, p, 64, p, p, p, None, 0, None) == C.QLORA_EWORKSPACE
+    assert lib.qlora_backward(ctypes.byref(L), p, p, p, 64, p, p, p, p, need - 1, None) == C.QLORA_EWORKSPACE
+    assert lib.qlora_backward(ctypes.byref(L), p, p, p, 64, p, None, p, p, need, None) == C.QLORA_EINVAL
+
+
+def test_mlp_shape_consistency_checks():
+    lib = C.lib()
+    g, u, d = _layer(256, 512), _layer(256, 512), _layer(512, 256)
+    p = ctypes.c_void_p(0x10000)
+    # mismatched down projection (K must equal the intermediate width)
+    bad_d = _layer(256, 256)
+    assert lib.swiglu_mlp_forward(ctypes.byref(g), ctypes.byref(u), ctypes.byref(bad_d), p, 8, p, p, p, p, p,
+                                  None, 0, None) == C.QLORA_EINVAL
+    # ranks must agree
+    u8 = _layer(256, 512, 8)
+    assert lib.swiglu_mlp_forward(ctypes.byref(g), ctypes.byref(u8), ctypes.byref(d), p, 8, p, p, p, p, p,
+                                  None, 0, None) == C.QLORA_EINVAL
+    # M == 0 is a no-op that succeeds without touching the GPU
+    assert lib.swiglu_mlp_forward(ctypes.byref(g), ctypes.byref(u), ctypes.byref(d), p, 0, p, p, p, p, p,
+                                  None, 0, None) == C.QLORA_OK
+
+
+def test_quantize_argument_checks():
+    lib = C.lib()
+    p = ctypes.c_void_p(0x10000)
+    assert lib.qlora_quantize(p, 4, 100, p, p, None, None) == C.QLORA_EINVAL
+    assert lib.qlora_quantize(p, 0, 64, p, p, None, None) == C.QLORA_OK
+    assert lib.qlora_dequantize(p, p, 4, 65, p, None) == C.QLORA_EINVAL
+
+
+def test_status_strings():
+    lib = C.lib()
+    for s in (0, -1, -2, -3):
+        assert len(lib.qlora_status_string(s)) > 0
+    assert np.isscalar(lib.qlora_workspace_size(C.OP_MLP_BACKWARD, 16, 256, 512, 8))

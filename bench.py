@@ -1,0 +1,332 @@
+#!/usr/bin/env python3
+"""Throughput of the fused QLoRA layer (forward + backward) on one MI355X.
+
+python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload attn|tiny|mlp|rsweep|layer] [--rank R]
+
+A step is one forward and one backward of the workload over one batch of
+seeded synthetic inputs already resident in HBM:
+  attn   : one Llama-3-8B attention projection, M=4096 tokens, K=N=4096, r=16 (default)
+  tiny   : M=256, K=N=512, r=8
+  mlp    : SwiGLU block, M=4096, 4096 <-> 14336, LoRA r=16 on gate/up/down
+  rsweep : M=8192, K=N=4096, r from --rank (8, 16, 64, 128)
+  layer  : the 7 projections of a Llama-3.1-8B GQA decoder layer at M=16384
+Prints one JSON line with tokens/s, useful TFLOP/s (4MNK + 6Mr(N+K) per
+projection), the dominant kernel's roofline (live hipEvent durations) and the
+CPU oracle's throughput on a bounded sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 MFMA (published)
+PEAK_HBM_GBS = 8000.0
+WL_INDEX = {"tiny": 0, "attn": 1, "mlp": 2, "rsweep": 3, "layer": 4}
+METRIC = "QLoRA linear fwd+bwd tokens/s and useful TFLOP/s (8B shapes); % MFMA peak"
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default="attn", choices=sorted(WL_INDEX))
+    ap.add_argument("--rank", type=int, default=16)
+    ap.add_argument("--cpu-seconds", type=float, default=10.0, help="target CPU time of the oracle baseline")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    return ap.parse_args()
+
+
+# ---------------------------------------------------------------------------
+# workload set-up (outside the timed region)
+
+def dev_bf16(u16):
+    import torch
+    return torch.from_numpy(np.ascontiguousarray(u16).view(np.int16)).view(torch.bfloat16).cuda()
+
+
+def dev_f32(x):
+    import torch
+    return torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32)).cuda()
+
+
+class Proj:
+    """Device tensors and prebuilt C-ABI arguments of one projection's fwd+bwd."""
+
+    def __init__(self, q, C, layer, s, X, dY):
+        import torch
+        M = X.shape[0]
+        codes, absmax = q.quantize(dev_f32(layer["W"]))
+        self.L = q.QLoraLayer(codes, absmax, dev_bf16(layer["A"]), dev_bf16(layer["B"]), s)
+        self.M, self.K, self.N, self.r = M, self.L.K, self.L.N, self.L.r
+        self.X, self.dY = X, dY
+        dev = X.device
+        self.Y = torch.empty((M, self.N), dtype=torch.bfloat16, device=dev)
+        self.Z = torch.empty((M, self.r), dtype=torch.bfloat16, device=dev)
+        self.dX = torch.empty((M, self.K), dtype=torch.bfloat16, device=dev)
+        self.dA = torch.empty((self.r, self.K), dtype=torch.float32, device=dev)
+        self.dB = torch.empty((self.N, self.r), dtype=torch.float32, device=dev)
+        nb = q.workspace_size(C.OP_BACKWARD, M, self.K, self.N, self.r)
+        self.ws = torch.empty((nb,), dtype=torch.uint8, device=dev)
+        self.lc = self.L.c()
+        p = lambda t: ctypes.c_void_p(t.data_ptr())
+        self.fwd_args = (ctypes.byref(self.lc), p(X), M, p(self.Y), p(self.Z), None, 0)
+        self.bwd_args = (ctypes.byref(self.lc), p(dY), p(X), p(self.Z), M, p(self.dX), p(self.dA), p(self.dB),
+                         p(self.ws), self.ws.numel())
+
+    def run(self, lib, stream):
+        st = lib.qlora_forward(*self.fwd_args, stream)
+        if st:
+            raise RuntimeError(f"qlora_forward: {st}")
+        st = lib.qlora_backward(*self.bwd_args, stream)
+        if st:
+            raise RuntimeError(f"qlora_backward: {st}")
+
+
+class MLP:
+    def __init__(self, q, C, layers, s, X, dY):
+        import torch
+        Ls = []
+        for nm in ("gate", "up", "down"):
+            codes, absmax = q.quantize(dev_f32(layers[nm]["W"]))
+            Ls.append(q.QLoraLayer(codes, absmax, dev_bf16(layers[nm]["A"]), dev_bf16(layers[nm]["B"]), s))
+        self.Ls = Ls
+        M = X.shape[0]
+        H, I, r = Ls[0].K, Ls[0].N, Ls[0].r
+        self.M, self.H, self.I, self.r = M, H, I, r
+        self.X, self.dY = X, dY
+        dev = X.device
+        e = lambda shape, dt=torch.bfloat16: torch.empty(shape, dtype=dt, device=dev)
+        self.saved = dict(Y=e((M, H)), g=e((M, I)), u=e((M, I)), h=e((M, I)), Z=e((3, M, r)))
+        self.dX = e((M, H))
+        self.dA = [e((r, L.K), torch.float32) for L in Ls]
+        self.dB = [e((L.N, r), torch.float32) for L in Ls]
+        self.ws = e((q.workspace_size(C.OP_MLP_BACKWARD, M, H, I, r),), torch.uint8)
+        self.lcs = [L.c() for L in Ls]
+        p = lambda t: ctypes.c_void_p(t.data_ptr())
+        refs = [ctypes.byref(lc) for lc in self.lcs]
+        sv = self.saved
+        self.fwd_args = (*refs, p(X), M, p(sv["Y"]), p(sv["g"]), p(sv["u"]), p(sv["h"]), p(sv["Z"]), None, 0)
+        self._dA = (ctypes.c_void_p * 3)(*[t.data_ptr() for t in self.dA])
+        self._dB = (ctypes.c_void_p * 3)(*[t.data_ptr() for t in self.dB])
+        self.bwd_args = (*refs, p(dY), p(X), p(sv["g"]), p(sv["u"]), p(sv["h"]), p(sv["Z"]), M, p(self.dX),
+                         self._dA, self._dB, p(self.ws), self.ws.numel())
+
+    def run(self, lib, stream):
+        st = lib.swiglu_mlp_forward(*self.fwd_args, stream)
+        if st:
+            raise RuntimeError(f"swiglu_mlp_forward: {st}")
+        st = lib.swiglu_mlp_backward(*self.bwd_args, stream)
+        if st:
+            raise RuntimeError(f"swiglu_mlp_backward: {st}")
+
+
+def build_workload(name: str, rank: int):
+    import torch
+    import parameter_efficient_fine_amd as q
+    from parameter_efficient_fine_amd import _lib as C
+    from synthetic import WORKLOADS, make_workload
+    c = WL_INDEX[name]
+    sub = WORKLOADS[c]["ranks"].index(rank) if name == "rsweep" else 0
+    d = make_workload(c, sub)
+    parts = []
+    if d["kind"] == "linear":
+        parts.append(Proj(q, C, d["layers"]["proj"], d["s"], dev_bf16(d["X"]), dev_bf16(d["dY"])))
+    elif d["kind"] == "mlp":
+        parts.append(MLP(q, C, d["layers"], d["s"], dev_bf16(d["X"]), dev_bf16(d["dY"])))
+    else:
+        Xa, Xo = dev_bf16(d["X_attn"]), dev_bf16(d["X_o"])
+        for nm, X in (("q", Xa), ("k", Xa), ("v", Xa), ("o", Xo)):
+            parts.append(Proj(q, C, d["layers"][nm], d["s"], X, dev_bf16(d["dY_" + nm])))
+        parts.append(MLP(q, C, {k: d["layers"][k] for k in ("gate", "up", "down")}, d["s"], dev_bf16(d["X_mlp"]),
+                         dev_bf16(d["dY_mlp"])))
+    torch.cuda.synchronize()
+    return d, parts
+
+
+def describe(d, name):
+    M, r = d["M"], d["r"]
+    if d["kind"] == "linear":
+        Lr = d["layers"]["proj"]
+        K, N = Lr["W"].shape[1], Lr["W"].shape[0]
+        return dict(workload=f"{name}: one 4-bit NF4 projection, M={M} tokens, K={K}, N={N}, r={r}, alpha={d['alpha']}",
+                    M=M, K=K, N=N, r=r, alpha=d["alpha"], weight_format="nf4, fp32 absmax per 64-block")
+    if d["kind"] == "mlp":
+        return dict(workload=f"{name}: SwiGLU block, M={M}, 4096<->14336, LoRA r={r} on gate/up/down",
+                    M=M, H=4096, I=14336, r=r, alpha=d["alpha"], weight_format="nf4, fp32 absmax per 64-block")
+    return dict(workload=f"{name}: 7 projections of a GQA decoder layer (q,o 4096x4096; k,v 4096->1024; "
+                         f"gate/up/down 4096<->14336), M={M}, r={r}", M=M, r=r, alpha=d["alpha"],
+                weight_format="nf4, fp32 absmax per 64-block")
+
+
+# ---------------------------------------------------------------------------
+# algorithmic work per launch of the fused GEMMs (for the roofline)
+
+def gemm_flops(parts):
+    """{kernel class: algorithmic FLOPs per launch} of the fused dequant GEMMs."""
+    out = {}
+    for p in parts:
+        if isinstance(p, Proj):
+            M, K, N, r = p.M, p.K, p.N, p.r
+            out.setdefault("gemm_fwd", []).append(2 * M * N * K + 2 * M * N * r)   # X.W^T + Z.B^T
+            out.setdefault("gemm_bwd", []).append(2 * M * N * K + 2 * M * K * r)   # dY.W + G.A
+        else:
+            M, H, I, r = p.M, p.H, p.I, p.r
+            out.setdefault("gemm_fwd_gateup", []).append(2 * (2 * M * I * H + 2 * M * I * r))
+            out.setdefault("gemm_fwd", []).append(2 * M * H * I + 2 * M * H * r)
+            out.setdefault("gemm_bwd_swiglu", []).append(2 * M * H * I + 2 * M * I * r)
+            out.setdefault("gemm_bwd", []).append(2 * (2 * M * I * H + 2 * M * H * r))
+    return out
+
+
+# ---------------------------------------------------------------------------
+# CPU oracle baseline (bounded sample of the same workload)
+
+def cpu_baseline(d, target_s: float):
+    from threadpoolctl import threadpool_info, threadpool_limits
+    from oracle import ref
+    cores = len(os.sched_getaffinity(0))
+    with threadpool_limits(limits=cores):
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+        M = d["M"]
+        if d["kind"] == "linear":
+            Lr = d["layers"]["proj"]
+            What = ref.dequantize(*ref.quantize(Lr["W"])).astype(np.float64)
+            A, B = ref.bf16_to_f64(Lr["A"]), ref.bf16_to_f64(Lr["B"])
+            X, dY = ref.bf16_to_f64(d["X"]), ref.bf16_to_f64(d["dY"])
+
+            def run(rows):
+                ref.linear_fwd(X[:rows], What, A, B, d["s"])
+                ref.linear_bwd(dY[:rows], X[:rows], What, A, B, d["s"])
+            what = "linear fwd+bwd"
+        else:
+            names = ("gate", "up", "down")
+            lay = d["layers"]
+            trip = [(ref.dequantize(*ref.quantize(lay[n]["W"])).astype(np.float64), ref.bf16_to_f64(lay[n]["A"]),
+                     ref.bf16_to_f64(lay[n]["B"])) for n in names]
+            xk, dk = ("X", "dY") if d["kind"] == "mlp" else ("X_mlp", "dY_mlp")
+            X, dY = ref.bf16_to_f64(d[xk]), ref.bf16_to_f64(d[dk])
+
+            def run(rows):
+                ref.mlp_bwd(dY[:rows], X[:rows], *trip, d["s"])  # runs the forward inside
+            what = "SwiGLU block fwd+bwd" + (" (MLP part of the layer)" if d["kind"] == "layer" else "")
+        rows = min(64, M)
+        t0 = time.perf_counter()
+        run(rows)
+        dt = time.perf_counter() - t0
+        # scale the sample (rows, then whole repeats) so it takes about target_s
+        rows = int(min(M, max(rows, rows * target_s / max(dt, 1e-3))))
+        reps, done = 0, 0
+        t0 = time.perf_counter()
+        while True:
+            run(rows)
+            reps += 1
+            done += rows
+            dt = time.perf_counter() - t0
+            if dt >= 0.8 * target_s or reps >= 1000:
+                break
+    return dict(value=done / dt, unit="tokens/s", cores=threads, kind="oracle",
+                sample=f"NumPy float64 oracle, {what}, {reps} pass(es) over the first {rows} of {M} tokens "
+                       f"({dt:.1f} s, {threads} BLAS threads on {cores} host cores)")
+
+
+
+# ---------------------------------------------------------------------------
+
+def main():
+    args = parse()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(json.dumps({"error": "this build runs on one GPU only: no sharding or collectives are built; "
+                                   "run with --gpus 1", "n_gpus": args.gpus}), flush=True)
+        sys.exit(2)
+    import torch
+    from parameter_efficient_fine_amd import _lib as C
+    from parameter_efficient_fine_amd.ops import KernelTimer
+    from synthetic import useful_flops
+
+    lib = C.lib()
+    d, parts = build_workload(args.workload, args.rank)
+    c = WL_INDEX[args.workload]
+    sub = d["sub"] if args.workload == "rsweep" else 0
+    flops = useful_flops(c, sub)
+    stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+    def step():
+        for p in parts:
+            p.run(lib, stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
+    ev0.record()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    ev1.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms = ev0.elapsed_time(ev1) / args.steps
+
+    # same steps again with per-launch hipEvents recorded by the library (kernel durations)
+    with KernelTimer(max_launches=args.steps * 64 + 64) as kt:
+        for _ in range(args.steps):
+            step()
+    torch.cuda.synchronize()
+    per_launch_flops = gemm_flops(parts)
+    kernels = {}
+    for name, (n, tot) in kt.result.items():
+        kernels[name] = dict(launches_per_step=n / args.steps, ms_per_step=tot / args.steps, avg_us=1e3 * tot / n)
+    dom = max((k for k in kernels if k in per_launch_flops), key=lambda k: kernels[k]["ms_per_step"])
+    fl = per_launch_flops[dom]
+    avg_flops = float(np.mean(fl))
+    avg_s = kernels[dom]["avg_us"] * 1e-6
+    achieved = avg_flops / avg_s / 1e12
+    roofline = dict(bound="mfma", kernel=dom, achieved=achieved, peak=PEAK_BF16_TFLOPS, unit="TFLOP/s",
+                    frac=achieved / PEAK_BF16_TFLOPS, traffic=None, avg_us=kernels[dom]["avg_us"],
+                    flops_per_launch=avg_flops)
+
+    tokens = d["M"]
+    value = tokens / (ms * 1e-3)
+    tflops = flops / (ms * 1e-3) / 1e12
+    out = {
+        "metric": METRIC,
+        "value": value,
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded N(0,1) activations, 0.02*N(0,1) weights quantized to NF4)",
+        "config": describe(d, args.workload),
+        "useful_tflops": tflops,
+        "mfma_peak_frac": tflops / PEAK_BF16_TFLOPS,
+        "useful_gflop_per_step": flops / 1e9,
+        "wall_s_timed": wall,
+        "roofline": roofline,
+        "kernels": kernels,
+    }
+    if not args.no_cpu:
+        out["cpu_baseline"] = cpu_baseline(d, args.cpu_seconds)
+    else:
+        out["cpu_baseline"] = None
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -115,6 +115,22 @@ int swiglu_mlp_backward(const qlora_layer* gate, const qlora_layer* up, const ql
                         const uint16_t* h_save, const uint16_t* Z_save, int64_t M, uint16_t* dX,
                         float* const dA[3], float* const dB[3], void* ws, size_t ws_bytes, void* stream);
 
+/* Measurement support (off the hot path; not thread-safe).
+ * qlora_profile_begin creates, once, a pool of 2*max_launches hipEvents and
+ * from then on brackets each kernel launch made by this library with an event
+ * pair recorded on that launch's stream. qlora_profile_end waits for those
+ * events, stops recording and writes one entry per kernel class (launch count
+ * and summed event time). It returns QLORA_EUNSUPPORTED if more launches were
+ * made than the pool could hold (those were not timed). No call allocates
+ * anything while recording. */
+typedef struct {
+  char name[32];
+  int64_t launches;
+  double total_ms;
+} qlora_kernel_time;
+int qlora_profile_begin(int max_launches);
+int qlora_profile_end(qlora_kernel_time* out, int max_entries, int* n_entries);
+
 /* Short text for a status code; for QLORA_EHIP, the last HIP error seen by this thread. */
 const char* qlora_status_string(int status);
 const char* qlora_last_error(void);

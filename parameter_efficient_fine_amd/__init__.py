@@ -5,6 +5,7 @@ this package is its thin Python binding. Importing the package does not load
 the library; the first call does, and fails loudly if it is not built.
 """
 from .ops import (  # noqa: F401
+    KernelTimer,
     QLoraLayer,
     backward,
     dequantize,

@@ -22,7 +22,8 @@ OP_FORWARD, OP_BACKWARD, OP_MLP_FORWARD, OP_MLP_BACKWARD = 0, 1, 2, 3
 # Every function the header declares (checked by the CPU tests against include/qlora.h).
 EXPORTS = [
     "qlora_quantize", "qlora_dequantize", "qlora_workspace_size", "qlora_forward", "qlora_backward",
-    "swiglu_mlp_forward", "swiglu_mlp_backward", "qlora_status_string", "qlora_last_error",
+    "swiglu_mlp_forward", "swiglu_mlp_backward", "qlora_profile_begin", "qlora_profile_end",
+    "qlora_status_string", "qlora_last_error",
 ]
 
 
@@ -37,6 +38,10 @@ class QLoraLayerC(ctypes.Structure):
         ("r", ctypes.c_int64),
         ("s", ctypes.c_float),
     ]
+
+
+class KernelTimeC(ctypes.Structure):
+    _fields_ = [("name", ctypes.c_char * 32), ("launches", ctypes.c_int64), ("total_ms", ctypes.c_double)]
 
 
 class QLoraError(RuntimeError):
@@ -67,6 +72,10 @@ def lib():
     L.swiglu_mlp_forward.argtypes = [LP, LP, LP, vp, i64, vp, vp, vp, vp, vp, vp, sz, vp]
     L.swiglu_mlp_backward.argtypes = [LP, LP, LP, vp, vp, vp, vp, vp, vp, i64, vp,
                                       ctypes.POINTER(vp), ctypes.POINTER(vp), vp, sz, vp]
+    L.qlora_profile_begin.argtypes = [ctypes.c_int]
+    L.qlora_profile_begin.restype = ctypes.c_int
+    L.qlora_profile_end.argtypes = [ctypes.POINTER(KernelTimeC), ctypes.c_int, ctypes.POINTER(ctypes.c_int)]
+    L.qlora_profile_end.restype = ctypes.c_int
     L.qlora_status_string.argtypes = [ctypes.c_int]
     L.qlora_status_string.restype = ctypes.c_char_p
     L.qlora_last_error.argtypes = []

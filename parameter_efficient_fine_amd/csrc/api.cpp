@@ -5,6 +5,7 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <vector>
 #include <cstdio>
 #include <cstring>
 
@@ -27,6 +28,38 @@ int hip_fail(hipError_t e, const char* what) {
     hipError_t e_ = (expr);                             \
     if (e_ != hipSuccess) return hip_fail(e_, #expr);   \
   } while (0)
+
+// ---- optional launch timing (measurement support; see qlora_profile_begin)
+struct ProfRec {
+  const char* name;
+  hipEvent_t a, b;
+};
+struct Prof {
+  bool on = false;
+  std::vector<hipEvent_t> pool;
+  std::vector<ProfRec> recs;
+  size_t next = 0;
+  int64_t dropped = 0;
+} g_prof;
+
+template <class F>
+hipError_t timed(const char* name, hipStream_t st, F&& f) {
+  if (!g_prof.on) return f();
+  if (g_prof.next + 2 > g_prof.pool.size()) {
+    ++g_prof.dropped;
+    return f();
+  }
+  hipEvent_t a = g_prof.pool[g_prof.next++], b = g_prof.pool[g_prof.next++];
+  hipError_t e = hipEventRecord(a, st);
+  if (e != hipSuccess) return e;
+  e = f();
+  if (e != hipSuccess) return e;
+  e = hipEventRecord(b, st);
+  if (e == hipSuccess) g_prof.recs.push_back({name, a, b});
+  return e;
+}
+
+#define QL_LAUNCH(name, st, expr) QL_CHECK(timed(name, st, [&]() { return (expr); }))
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
@@ -88,8 +121,8 @@ WSrc wsrc(const qlora_layer* L, const uint16_t* lora_i, const uint16_t* lora_j) 
 int tn_reduce(const uint16_t* P, int r, const uint16_t* Q, int64_t M, int64_t Kd, float s, float* out,
               bool transposed, float* part, hipStream_t st) {
   const int splits = skinny_tn_splits(M, Kd);
-  QL_CHECK(launch_skinny_tn(P, r, Q, M, Kd, part, splits, st));
-  QL_CHECK(launch_reduce_splits(part, splits, r, Kd, s, out, transposed, st));
+  QL_LAUNCH("skinny_tn", st, launch_skinny_tn(P, r, Q, M, Kd, part, splits, st));
+  QL_LAUNCH("reduce_splits", st, launch_reduce_splits(part, splits, r, Kd, s, out, transposed, st));
   return QLORA_OK;
 }
 
@@ -115,7 +148,8 @@ int qlora_quantize(const float* W, int64_t N, int64_t K, uint8_t* codes, float* 
   if (N < 0 || K < 0 || K % 64 != 0) return QLORA_EINVAL;
   if (N * K == 0) return QLORA_OK;
   if (!W || !codes || !absmax || !aligned16(W) || !aligned16(codes)) return QLORA_EINVAL;
-  QL_CHECK(launch_quantize(W, N, K, codes, absmax, nonfinite_blocks, (hipStream_t)stream));
+  hipStream_t st = (hipStream_t)stream;
+  QL_LAUNCH("quantize", st, launch_quantize(W, N, K, codes, absmax, nonfinite_blocks, st));
   return QLORA_OK;
 }
 
@@ -123,7 +157,8 @@ int qlora_dequantize(const uint8_t* codes, const float* absmax, int64_t N, int64
   if (N < 0 || K < 0 || K % 64 != 0) return QLORA_EINVAL;
   if (N * K == 0) return QLORA_OK;
   if (!codes || !absmax || !W_hat || !aligned16(W_hat)) return QLORA_EINVAL;
-  QL_CHECK(launch_dequantize(codes, absmax, N, K, W_hat, (hipStream_t)stream));
+  hipStream_t st = (hipStream_t)stream;
+  QL_LAUNCH("dequantize", st, launch_dequantize(codes, absmax, N, K, W_hat, st));
   return QLORA_OK;
 }
 
@@ -147,8 +182,8 @@ int qlora_forward(const qlora_layer* L, const uint16_t* X, int64_t M, uint16_t* 
   if (!X || !Y || !Z_save || !aligned16(X) || !aligned16(Y) || !aligned16(Z_save)) return QLORA_EINVAL;
   hipStream_t st = (hipStream_t)stream;
   const int r = (int)L->r;
-  QL_CHECK(launch_skinny_nt(X, M, L->K, L->A, r, Z_save, nullptr, 0, nullptr, st));
-  QL_CHECK(launch_gemm_fwd(X, M, L->K, L->N, wsrc(L, L->B, Z_save), Y, st));
+  QL_LAUNCH("skinny_nt", st, launch_skinny_nt(X, M, L->K, L->A, r, Z_save, nullptr, 0, nullptr, st));
+  QL_LAUNCH("gemm_fwd", st, launch_gemm_fwd(X, M, L->K, L->N, wsrc(L, L->B, Z_save), Y, st));
   return QLORA_OK;
 }
 
@@ -172,16 +207,16 @@ int qlora_backward(const qlora_layer* L, const uint16_t* dY, const uint16_t* X, 
   float* part = c.take<float>((size_t)std::max(tn_part_bytes(M, N, r), tn_part_bytes(M, K, r)) / sizeof(float));
   if (!c.ok) return QLORA_EWORKSPACE;
   if (M == 0) {  // empty batch: gradients are zero
-    QL_CHECK(launch_fill_zero_f32(dA, (int64_t)r * K, st));
-    QL_CHECK(launch_fill_zero_f32(dB, (int64_t)N * r, st));
+    QL_LAUNCH("fill_zero_f32", st, launch_fill_zero_f32(dA, (int64_t)r * K, st));
+    QL_LAUNCH("fill_zero_f32", st, launch_fill_zero_f32(dB, (int64_t)N * r, st));
     return QLORA_OK;
   }
-  QL_CHECK(launch_transpose_bf16(L->B, N, r, Bt, st));
-  QL_CHECK(launch_transpose_bf16(L->A, r, K, At, st));
-  QL_CHECK(launch_skinny_nt(dY, M, N, Bt, r, G, nullptr, 0, nullptr, st));
+  QL_LAUNCH("transpose_bf16", st, launch_transpose_bf16(L->B, N, r, Bt, st));
+  QL_LAUNCH("transpose_bf16", st, launch_transpose_bf16(L->A, r, K, At, st));
+  QL_LAUNCH("skinny_nt", st, launch_skinny_nt(dY, M, N, Bt, r, G, nullptr, 0, nullptr, st));
   int rc = tn_reduce(Z_save, r, dY, M, N, L->s, dB, true, part, st);
   if (rc) return rc;
-  if (dX) QL_CHECK(launch_gemm_bwd(dY, wsrc(L, At, G), nullptr, WSrc{}, M, K, N, dX, st));
+  if (dX) QL_LAUNCH("gemm_bwd", st, launch_gemm_bwd(dY, wsrc(L, At, G), nullptr, WSrc{}, M, K, N, dX, st));
   return tn_reduce(G, r, X, M, K, L->s, dA, false, part, st);
 }
 
@@ -209,11 +244,11 @@ int swiglu_mlp_forward(const qlora_layer* gate, const qlora_layer* up, const qlo
   uint16_t* Zg = Z_save;
   uint16_t* Zu = Z_save + (size_t)M * r;
   uint16_t* Zd = Z_save + 2 * (size_t)M * r;
-  QL_CHECK(launch_skinny_nt(X, M, H, gate->A, r, Zg, up->A, r, Zu, st));
-  QL_CHECK(launch_gemm_fwd_gateup(X, M, H, I, wsrc(gate, gate->B, Zg), wsrc(up, up->B, Zu), g_save, u_save, h_save,
+  QL_LAUNCH("skinny_nt", st, launch_skinny_nt(X, M, H, gate->A, r, Zg, up->A, r, Zu, st));
+  QL_LAUNCH("gemm_fwd_gateup", st, launch_gemm_fwd_gateup(X, M, H, I, wsrc(gate, gate->B, Zg), wsrc(up, up->B, Zu), g_save, u_save, h_save,
                                   st));
-  QL_CHECK(launch_skinny_nt(h_save, M, I, down->A, r, Zd, nullptr, 0, nullptr, st));
-  QL_CHECK(launch_gemm_fwd(h_save, M, I, H, wsrc(down, down->B, Zd), Y, st));
+  QL_LAUNCH("skinny_nt", st, launch_skinny_nt(h_save, M, I, down->A, r, Zd, nullptr, 0, nullptr, st));
+  QL_LAUNCH("gemm_fwd", st, launch_gemm_fwd(h_save, M, I, H, wsrc(down, down->B, Zd), Y, st));
   return QLORA_OK;
 }
 
@@ -252,39 +287,79 @@ int swiglu_mlp_backward(const qlora_layer* gate, const qlora_layer* up, const ql
   if (M == 0) {
     const qlora_layer* Ls[3] = {gate, up, down};
     for (int i = 0; i < 3; ++i) {
-      QL_CHECK(launch_fill_zero_f32(dA[i], (int64_t)r * Ls[i]->K, st));
-      QL_CHECK(launch_fill_zero_f32(dB[i], (int64_t)Ls[i]->N * r, st));
+      QL_LAUNCH("fill_zero_f32", st, launch_fill_zero_f32(dA[i], (int64_t)r * Ls[i]->K, st));
+      QL_LAUNCH("fill_zero_f32", st, launch_fill_zero_f32(dB[i], (int64_t)Ls[i]->N * r, st));
     }
     return QLORA_OK;
   }
   const uint16_t* Zg = Z_save;
   const uint16_t* Zu = Z_save + (size_t)M * r;
   const uint16_t* Zd = Z_save + 2 * (size_t)M * r;
-  QL_CHECK(launch_transpose_bf16(down->B, H, r, Btd, st));
-  QL_CHECK(launch_transpose_bf16(gate->B, I, r, Btg, st));
-  QL_CHECK(launch_transpose_bf16(up->B, I, r, Btu, st));
-  QL_CHECK(launch_transpose_bf16(down->A, r, I, Atd, st));
-  QL_CHECK(launch_transpose_bf16(gate->A, r, H, Atg, st));
-  QL_CHECK(launch_transpose_bf16(up->A, r, H, Atu, st));
+  QL_LAUNCH("transpose_bf16", st, launch_transpose_bf16(down->B, H, r, Btd, st));
+  QL_LAUNCH("transpose_bf16", st, launch_transpose_bf16(gate->B, I, r, Btg, st));
+  QL_LAUNCH("transpose_bf16", st, launch_transpose_bf16(up->B, I, r, Btu, st));
+  QL_LAUNCH("transpose_bf16", st, launch_transpose_bf16(down->A, r, I, Atd, st));
+  QL_LAUNCH("transpose_bf16", st, launch_transpose_bf16(gate->A, r, H, Atg, st));
+  QL_LAUNCH("transpose_bf16", st, launch_transpose_bf16(up->A, r, H, Atu, st));
   // down projection: G_d = dY.B_d ; dB_d = s.dY^T.Z_d ; dh -> (dg, du) in the GEMM epilogue ; dA_d = s.G_d^T.h
-  QL_CHECK(launch_skinny_nt(dY, M, H, Btd, r, Gd, nullptr, 0, nullptr, st));
+  QL_LAUNCH("skinny_nt", st, launch_skinny_nt(dY, M, H, Btd, r, Gd, nullptr, 0, nullptr, st));
   int rc = tn_reduce(Zd, r, dY, M, H, down->s, dB[2], true, part, st);
   if (rc) return rc;
-  QL_CHECK(launch_gemm_bwd_swiglu(dY, wsrc(down, Atd, Gd), M, I, H, g_save, u_save, dg, du, st));
+  QL_LAUNCH("gemm_bwd_swiglu", st, launch_gemm_bwd_swiglu(dY, wsrc(down, Atd, Gd), M, I, H, g_save, u_save, dg, du, st));
   rc = tn_reduce(Gd, r, h_save, M, I, down->s, dA[2], false, part, st);
   if (rc) return rc;
   // gate and up: G = d(g|u).B ; dB = s.d(g|u)^T.Z
-  QL_CHECK(launch_skinny_nt(dg, M, I, Btg, r, Gg, nullptr, 0, nullptr, st));
-  QL_CHECK(launch_skinny_nt(du, M, I, Btu, r, Gu, nullptr, 0, nullptr, st));
+  QL_LAUNCH("skinny_nt", st, launch_skinny_nt(dg, M, I, Btg, r, Gg, nullptr, 0, nullptr, st));
+  QL_LAUNCH("skinny_nt", st, launch_skinny_nt(du, M, I, Btu, r, Gu, nullptr, 0, nullptr, st));
   rc = tn_reduce(Zg, r, dg, M, I, gate->s, dB[0], true, part, st);
   if (rc) return rc;
   rc = tn_reduce(Zu, r, du, M, I, up->s, dB[1], true, part, st);
   if (rc) return rc;
   // dX = dg.W_g + du.W_u + s.G_g.A_g + s.G_u.A_u : one GEMM over the concatenated reduction
-  if (dX) QL_CHECK(launch_gemm_bwd(dg, wsrc(gate, Atg, Gg), du, wsrc(up, Atu, Gu), M, H, I, dX, st));
+  if (dX) QL_LAUNCH("gemm_bwd", st, launch_gemm_bwd(dg, wsrc(gate, Atg, Gg), du, wsrc(up, Atu, Gu), M, H, I, dX, st));
   rc = tn_reduce(Gg, r, X, M, H, gate->s, dA[0], false, part, st);
   if (rc) return rc;
   return tn_reduce(Gu, r, X, M, H, up->s, dA[1], false, part, st);
+}
+
+int qlora_profile_begin(int max_launches) {
+  if (max_launches < 1) return QLORA_EINVAL;
+  while ((int)g_prof.pool.size() < 2 * max_launches) {
+    hipEvent_t e;
+    QL_CHECK(hipEventCreate(&e));
+    g_prof.pool.push_back(e);
+  }
+  g_prof.recs.clear();
+  g_prof.recs.reserve((size_t)max_launches);  // no host allocation while recording
+  g_prof.next = 0;
+  g_prof.dropped = 0;
+  g_prof.on = true;
+  return QLORA_OK;
+}
+
+int qlora_profile_end(qlora_kernel_time* out, int max_entries, int* n_entries) {
+  g_prof.on = false;
+  int n = 0;
+  for (const ProfRec& rec : g_prof.recs) {
+    QL_CHECK(hipEventSynchronize(rec.b));
+    float ms = 0.f;
+    QL_CHECK(hipEventElapsedTime(&ms, rec.a, rec.b));
+    int i = 0;
+    for (; i < n; ++i)
+      if (strncmp(out[i].name, rec.name, sizeof(out[i].name)) == 0) break;
+    if (i == n) {
+      if (n >= max_entries) continue;
+      memset(&out[n], 0, sizeof(out[n]));
+      strncpy(out[n].name, rec.name, sizeof(out[n].name) - 1);
+      ++n;
+    }
+    out[i].launches += 1;
+    out[i].total_ms += ms;
+  }
+  if (n_entries) *n_entries = n;
+  g_prof.recs.clear();
+  g_prof.next = 0;
+  return g_prof.dropped ? QLORA_EUNSUPPORTED : QLORA_OK;
 }
 
 }  // extern "C"

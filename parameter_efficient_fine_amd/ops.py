@@ -160,3 +160,25 @@ def mlp_backward(gate: QLoraLayer, up: QLoraLayer, down: QLoraLayer, dY, X, save
         ctypes.byref(lg), ctypes.byref(lu), ctypes.byref(ld), _ptr(dY), _ptr(X), _ptr(saved["g"]), _ptr(saved["u"]),
         _ptr(saved["h"]), _ptr(saved["Z"]), M, _ptr(out["dX"]), dA, dB, _ptr(ws), ws.numel(), _stream()))
     return out
+
+
+class KernelTimer:
+    """Per-kernel-class launch durations from hipEvents the library records around
+    each of its launches (on the launch's stream). Use as a context manager."""
+
+    def __init__(self, max_launches: int = 100_000):
+        self.max_launches = max_launches
+        self.result = {}
+
+    def __enter__(self):
+        C.check("qlora_profile_begin", C.lib().qlora_profile_begin(self.max_launches))
+        return self
+
+    def __exit__(self, *exc):
+        buf = (C.KernelTimeC * 64)()
+        n = ctypes.c_int(0)
+        st = C.lib().qlora_profile_end(buf, 64, ctypes.byref(n))
+        self.result = {buf[i].name.decode(): (int(buf[i].launches), float(buf[i].total_ms)) for i in range(n.value)}
+        if st != C.QLORA_OK and exc[0] is None:
+            C.check("qlora_profile_end", st)
+        return False

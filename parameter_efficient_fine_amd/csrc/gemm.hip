@@ -41,9 +41,13 @@ struct GemmArgs {
   const uint16_t* aux1;  // swiglu backward: saved u
 };
 
+#ifndef QLORA_GEMM_WAVES
+#define QLORA_GEMM_WAVES 8
+#endif
 constexpr int kBI = 256, kBJ = 256, kBR = 64;
 constexpr int kXS = kBR + 8;         // LDS row stride (bf16) of activation and forward weight tiles
-constexpr int kWSB = kBI + 16;       // LDS row stride of the backward weight tile
+constexpr int kWSB = kBI + 32;       // LDS row stride of the backward weight tile: 16 banks mod 64, so
+                                     // each half-wave of a transposed read touches 64 distinct banks
 constexpr int kXElems = kBJ * kXS;
 constexpr int kWElemsF = kBI * kXS;
 constexpr int kWElemsB = kBR * kWSB;
@@ -81,16 +85,23 @@ __device__ __forceinline__ f32x16 lora_frag(const uint16_t* irow, const uint16_t
   return t;
 }
 
-template <int MODE>
-__global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_per_eu(1, 1))) void k_qgemm(GemmArgs p) {
+template <int MODE, int NW>
+__global__ __attribute__((amdgpu_flat_work_group_size(64 * NW, 64 * NW), amdgpu_waves_per_eu(NW / 4, NW / 4)))
+void k_qgemm(GemmArgs p) {
   constexpr bool BW = MODE >= kBwd;
   constexpr int WE = BW ? kWElemsB : kWElemsF;
+  constexpr int T = 64 * NW;          // threads
+  constexpr int WJ = NW / 2;          // waves along j (tokens); 2 waves along i
+  constexpr int TJ = kBJ / WJ;        // j extent of one wave
+  constexpr int FJ = TJ / 32;         // 32x32 fragments along j per wave
+  constexpr int XC = (kBJ * kBR / 8) / T;  // 16-byte activation chunks per thread per step
+  constexpr int WC = 512 / T;         // 16-byte code chunks (32 weights) per thread per step
   extern __shared__ __attribute__((aligned(16))) uint16_t smem[];
   uint16_t* sW = smem;            // [2][WE]
   uint16_t* sX = smem + 2 * WE;   // [2][kXElems]
 
   const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
-  const int wi = wave >> 1, wj = wave & 1;
+  const int wi = wave / WJ, wj = wave % WJ;
   const int64_t M = p.M, K = p.K, N = p.N;
   // i extent: fwd -> N (gate/up: 128 weight rows of each source per tile), bwd -> K
   const int64_t ipt = (MODE == kFwdGateUp) ? 128 : kBI;
@@ -103,118 +114,168 @@ __global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_pe
   const int steps_per_src = (int)((red_len + kBR - 1) / kBR);
   const int nsteps = steps_per_src * (BW ? p.nsrc : 1);
 
-  // ---- per-thread staging registers
-  u32x4 xr[8];
-  u32x4 cr[2];
-  float am;
+  // This thread's weight block (row, 64-block) of the tile: 256 blocks per step,
+  // each split into two 16-byte halves of codes.
+  const int blk = (t * WC) >> 1;       // 0..255
+  const int half0 = (t * WC) & 1;      // first half handled (0 when WC == 2)
 
-  auto load_stage = [&](int step) {
+  // ---- per-thread staging registers (two sets each, used alternately by even and odd steps).
+  // Loads go to clamped, always-valid addresses; out-of-range data is masked
+  // only where it is consumed, so no instruction waits on a load early.
+  u32x4 xa[XC], xb[XC];    // activations two steps ahead
+  u32x4 ca[WC], cb[WC];    // codes: the next step's (being dequantized) and the one after
+  float aa, ab;            // absmax of those blocks
+  uint32_t xoka, xokb;     // bit q: activation chunk q is inside the matrix
+  bool coka, cokb;         // the weight block is inside the matrix
+
+  auto load_x = [&](int step, u32x4 (&xr)[XC], uint32_t& xok) {
     const int src = BW ? step / steps_per_src : 0;
     const int64_t r0 = (int64_t)(step - src * steps_per_src) * kBR;
     const uint16_t* act = (BW && src) ? p.act1 : p.act0;
-    const WSrc& w = (src || (MODE == kFwdGateUp && ((t & 127) >= 64))) ? p.w1 : p.w0;
+    xok = 0;
 #pragma unroll
-    for (int q = 0; q < 8; ++q) {
-      const int c = t + 256 * q;
+    for (int q = 0; q < XC; ++q) {
+      const int c = t + T * q;
       const int row = c >> 3, col = (c & 7) * 8;
       const int64_t m = j0 + row, rc = r0 + col;
-      xr[q] = (m < M && rc < red_len) ? *reinterpret_cast<const u32x4*>(act + m * ld_act + rc) : u32x4{0, 0, 0, 0};
+      xok |= (m < M && rc < red_len) ? (1u << q) : 0u;
+      xr[q] = *reinterpret_cast<const u32x4*>(act + (m < M ? m : M - 1) * ld_act + (rc < red_len ? rc : 0));
     }
+  };
+
+  auto load_codes = [&](int step, u32x4 (&cr)[WC], float& am, bool& cok) {
+    const int src = BW ? step / steps_per_src : 0;
+    const int64_t r0 = (int64_t)(step - src * steps_per_src) * kBR;
+    const WSrc& w = (src || (MODE == kFwdGateUp && ((blk & 127) >= 64))) ? p.w1 : p.w0;
     int64_t n, kb;
     bool ok;
     if (!BW) {
-      n = (MODE == kFwdGateUp) ? i0 + 64 * (t >> 7) + (t & 63) : i0 + t;
+      n = (MODE == kFwdGateUp) ? i0 + 64 * (blk >> 7) + (blk & 63) : i0 + blk;
       kb = r0 / kBlock;
       ok = n < N;
     } else {
-      n = r0 + (t >> 2);
-      kb = i0 / kBlock + (t & 3);
+      n = r0 + (blk >> 2);
+      kb = i0 / kBlock + (blk & 3);
       ok = n < N && kb * kBlock < K;
     }
-    if (ok) {
-      const u32x4* cp = reinterpret_cast<const u32x4*>(w.codes + n * (K / 2) + kb * (kBlock / 2));
-      cr[0] = cp[0];
-      cr[1] = cp[1];
-      am = w.absmax[n * (K / kBlock) + kb];
-    } else {
-      cr[0] = u32x4{0, 0, 0, 0};
-      cr[1] = u32x4{0, 0, 0, 0};
-      am = 0.f;
-    }
+    cok = ok;
+    const int64_t nn = ok ? n : 0, kk = ok ? kb : 0;
+    am = w.absmax[nn * (K / kBlock) + kk];  // first: the LUT needs it before the codes
+    const u32x4* cp = reinterpret_cast<const u32x4*>(w.codes + nn * (K / 2) + kk * (kBlock / 2)) + half0;
+#pragma unroll
+    for (int h = 0; h < WC; ++h) cr[h] = cp[h];
   };
 
-  auto store_stage = [&](int buf) {
-    const Nf4Lut lut = make_lut(am);
-    uint16_t* dstW = sW + buf * WE + (BW ? (t >> 2) * kWSB + (t & 3) * kBlock : t * kXS);
-#pragma unroll
-    for (int q = 0; q < 8; ++q) {
-      const uint32_t codes8 = cr[q >> 2][q & 3];
-      *reinterpret_cast<u32x4*>(dstW + 8 * q) = dequant8(codes8, lut);
-    }
+  auto store_x = [&](int buf, const u32x4 (&xr)[XC], uint32_t xok) {
     uint16_t* dstX = sX + buf * kXElems;
 #pragma unroll
-    for (int q = 0; q < 8; ++q) {
-      const int c = t + 256 * q;
-      *reinterpret_cast<u32x4*>(dstX + (c >> 3) * kXS + (c & 7) * 8) = xr[q];
+    for (int q = 0; q < XC; ++q) {
+      const int c = t + T * q;
+      *reinterpret_cast<u32x4*>(dstX + (c >> 3) * kXS + (c & 7) * 8) =
+          ((xok >> q) & 1u) ? xr[q] : u32x4{0, 0, 0, 0};
     }
   };
 
-  f32x16 acc[4][4];
+  // piece q (8 weights) of codes cr -> bf16 in the weight tile of buffer buf
+  // (a block outside the matrix has a zero LUT, so its codes do not matter)
+  auto dequant_piece = [&](int buf, int q, const u32x4 (&cr)[WC], const Nf4Lut& lut) {
+    uint16_t* dstW = sW + buf * WE + (BW ? (blk >> 2) * kWSB + (blk & 3) * kBlock : blk * kXS) + 32 * half0;
+    *reinterpret_cast<u32x4*>(dstW + 8 * q) = dequant8(cr[q >> 2][q & 3], lut);
+  };
+
+  f32x16 acc[4][FJ];
 #pragma unroll
   for (int a = 0; a < 4; ++a)
 #pragma unroll
-    for (int b = 0; b < 4; ++b) acc[a][b] = f32x16{};
+    for (int b = 0; b < FJ; ++b) acc[a][b] = f32x16{};
 
-  auto compute = [&](int buf) {
+  // MFMAs of one k-substep from LDS buffer buf
+  auto compute_ks = [&](int buf, int ks) {
     const uint16_t* bW = sW + buf * WE;
     const uint16_t* bX = sX + buf * kXElems;
+    u32x4 av[4], bv[FJ];
 #pragma unroll
-    for (int ks = 0; ks < kBR / 16; ++ks) {
-      u32x4 av[4], bv[4];
-#pragma unroll
-      for (int fj = 0; fj < 4; ++fj)
-        bv[fj] = *reinterpret_cast<const u32x4*>(bX + (wj * 128 + 32 * fj + (lane & 31)) * kXS + 16 * ks +
-                                                 8 * (lane >> 5));
-      if (!BW) {
-#pragma unroll
-        for (int fi = 0; fi < 4; ++fi)
-          av[fi] = *reinterpret_cast<const u32x4*>(bW + (wi * 128 + 32 * fi + (lane & 31)) * kXS + 16 * ks +
-                                                   8 * (lane >> 5));
-      } else {
-        const int g = lane >> 4, s = lane & 15;
-        const int rowb = 16 * ks + 8 * (g >> 1) + (s >> 2);
-#pragma unroll
-        for (int fi = 0; fi < 4; ++fi) {
-          const int col = wi * 128 + 32 * fi + 16 * (g & 1) + 4 * (s & 3);
-          const u32x2 lo = lds_read_tr(bW + rowb * kWSB + col);
-          const u32x2 hi = lds_read_tr(bW + (rowb + 4) * kWSB + col);
-          av[fi] = u32x4{lo[0], lo[1], hi[0], hi[1]};
-        }
-      }
+    for (int fj = 0; fj < FJ; ++fj)
+      bv[fj] = *reinterpret_cast<const u32x4*>(bX + (wj * TJ + 32 * fj + (lane & 31)) * kXS + 16 * ks +
+                                               8 * (lane >> 5));
+    if (!BW) {
 #pragma unroll
       for (int fi = 0; fi < 4; ++fi)
+        av[fi] = *reinterpret_cast<const u32x4*>(bW + (wi * 128 + 32 * fi + (lane & 31)) * kXS + 16 * ks +
+                                                 8 * (lane >> 5));
+    } else {
+      const int g = lane >> 4, s = lane & 15;
+      const int rowb = 16 * ks + 8 * (g >> 1) + (s >> 2);
 #pragma unroll
-        for (int fj = 0; fj < 4; ++fj) acc[fi][fj] = mfma32(av[fi], bv[fj], acc[fi][fj]);
+      for (int fi = 0; fi < 4; ++fi) {
+        const int col = wi * 128 + 32 * fi + 16 * (g & 1) + 4 * (s & 3);
+        const u32x2 lo = lds_read_tr(bW + rowb * kWSB + col);
+        const u32x2 hi = lds_read_tr(bW + (rowb + 4) * kWSB + col);
+        av[fi] = u32x4{lo[0], lo[1], hi[0], hi[1]};
+      }
     }
+#pragma unroll
+    for (int fi = 0; fi < 4; ++fi)
+#pragma unroll
+      for (int fj = 0; fj < FJ; ++fj) acc[fi][fj] = mfma32(av[fi], bv[fj], acc[fi][fj]);
   };
 
-  load_stage(0);
-  store_stage(0);
-  __syncthreads();
-  for (int step = 0; step < nsteps; ++step) {
+  // LDS-only workgroup barrier: the register-staged global loads of later
+  // steps stay in flight across it (a full __syncthreads would wait for them).
+  auto lds_barrier = [&]() {
+    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0); vmcnt and expcnt not waited
+    __builtin_amdgcn_s_barrier();
+  };
+
+  // One step: MFMAs of step s from buffer s&1 while the VALU dequantizes step
+  // s+1's codes (loaded a step earlier) into the other buffer; loads for step
+  // s+2 are issued first, and step s+1's activations (loaded a step earlier)
+  // are written to LDS last.
+  auto body = [&](int step, const u32x4 (&xcur)[XC], uint32_t xokcur, u32x4 (&xnext)[XC], uint32_t& xoknext,
+                  const u32x4 (&ccur)[WC], float acur, bool cokcur, u32x4 (&cnext)[WC], float& anext,
+                  bool& coknext) {
     const int cur = step & 1;
-    const bool more = step + 1 < nsteps;
-    if (more) load_stage(step + 1);
-    compute(cur);
-    if (more) store_stage(cur ^ 1);
-    __syncthreads();
+    const int s2 = step + 2 < nsteps ? step + 2 : nsteps - 1;
+    // codes before activations: the next step waits for the codes (in-order
+    // vmcnt) while this step's activation loads may still be in flight
+    load_codes(s2, cnext, anext, coknext);
+    load_x(s2, xnext, xoknext);
+    __builtin_amdgcn_sched_barrier(0);  // keep the loads at the top of the step
+    const Nf4Lut lut = make_lut(cokcur ? acur : 0.f);
+#pragma unroll
+    for (int ks = 0; ks < kBR / 16; ++ks) {
+      compute_ks(cur, ks);
+#pragma unroll
+      for (int q = ks * WC; q < (ks + 1) * WC; ++q) dequant_piece(cur ^ 1, q, ccur, lut);
+    }
+    __builtin_amdgcn_sched_barrier(0);  // the activation stores wait for their loads: keep them last
+    store_x(cur ^ 1, xcur, xokcur);
+    lds_barrier();
+  };
+
+  // Prologue: step 0 staged into buffer 0; step 1's activations and codes in registers.
+  load_codes(0, cb, ab, cokb);
+  load_x(0, xb, xokb);
+  load_codes(nsteps > 1 ? 1 : 0, ca, aa, coka);
+  load_x(nsteps > 1 ? 1 : 0, xa, xoka);
+  {
+    const Nf4Lut lut = make_lut(cokb ? ab : 0.f);
+#pragma unroll
+    for (int q = 0; q < 4 * WC; ++q) dequant_piece(0, q, cb, lut);
+  }
+  store_x(0, xb, xokb);
+  __syncthreads();
+
+  for (int step = 0; step < nsteps; step += 2) {
+    body(step, xa, xoka, xb, xokb, ca, aa, coka, cb, ab, cokb);
+    if (step + 1 < nsteps) body(step + 1, xb, xokb, xa, xoka, cb, ab, cokb, ca, aa, coka);
   }
 
   // ---- epilogue: rank-r term, activation, bf16 stores
   const int jl = lane & 31;
 #pragma unroll
-  for (int fj = 0; fj < 4; ++fj) {
-    const int64_t m = j0 + wj * 128 + 32 * fj + jl;
+  for (int fj = 0; fj < FJ; ++fj) {
+    const int64_t m = j0 + wj * TJ + 32 * fj + jl;
     const bool m_ok = m < M;
     if (MODE == kFwd || MODE == kBwd || MODE == kBwdSwiGLU) {
 #pragma unroll
@@ -284,12 +345,14 @@ __global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_pe
   }
 }
 
+constexpr int kWaves = QLORA_GEMM_WAVES;
+
 template <int MODE>
 static hipError_t launch_qgemm(const GemmArgs& a, hipStream_t st) {
   static bool attr_done = false;  // per process; the attribute is per function
   const size_t lds = gemm_lds_bytes(MODE);
   if (!attr_done) {
-    hipError_t e = hipFuncSetAttribute((const void*)k_qgemm<MODE>, hipFuncAttributeMaxDynamicSharedMemorySize,
+    hipError_t e = hipFuncSetAttribute((const void*)k_qgemm<MODE, kWaves>, hipFuncAttributeMaxDynamicSharedMemorySize,
                                        (int)lds);
     if (e != hipSuccess) return e;
     attr_done = true;
@@ -298,29 +361,8 @@ static hipError_t launch_qgemm(const GemmArgs& a, hipStream_t st) {
   const int64_t iext = MODE >= kBwd ? a.K : a.N;
   const int64_t nI = (iext + ipt - 1) / ipt, nJ = (a.M + kBJ - 1) / kBJ;
   if (nI * nJ == 0) return hipSuccess;
-  k_qgemm<MODE><<<(unsigned)(nI * nJ), 256, lds, st>>>(a);
+  k_qgemm<MODE, kWaves><<<(unsigned)(nI * nJ), 64 * kWaves, lds, st>>>(a);
   return hipGetLastError();
-}
-
-hipError_t launch_gemm_fwd(const uint16_t* X, int64_t M, int64_t K, int64_t N, WSrc w, uint16_t* Y, hipStream_t st) {
-  GemmArgs a{};
-  a.act0 = X;
-  a.w0 = w;
-  a.w1 = w;
-  a.M = M, a.K = K, a.N = N, a.nsrc = 1;
-  a.out0 = Y;
-  return launch_qgemm<kFwd>(a, st);
-}
-
-hipError_t launch_gemm_fwd_gateup(const uint16_t* X, int64_t M, int64_t K, int64_t N, WSrc wg, WSrc wu, uint16_t* g,
-                                  uint16_t* u, uint16_t* h, hipStream_t st) {
-  GemmArgs a{};
-  a.act0 = X;
-  a.w0 = wg;
-  a.w1 = wu;
-  a.M = M, a.K = K, a.N = N, a.nsrc = 2;
-  a.out0 = g, a.out1 = u, a.out2 = h;
-  return launch_qgemm<kFwdGateUp>(a, st);
 }
 
 hipError_t launch_gemm_bwd(const uint16_t* dY0, WSrc w0, const uint16_t* dY1, WSrc w1, int64_t M, int64_t K,

@@ -61,12 +61,17 @@ hipError_t timed(const char* name, hipStream_t st, F&& f) {
 
 #define QL_LAUNCH(name, st, expr) QL_CHECK(timed(name, st, [&]() { return (expr); }))
 
+// Size limits keeping every buffer offset the kernels form within 32 bits.
+constexpr int64_t kMaxDim = int64_t(1) << 23;
+constexpr int64_t kMaxWeight = int64_t(1) << 32;
+
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
 bool layer_ok(const qlora_layer* L) {
   if (!L || !L->codes || !L->absmax || !L->A || !L->B) return false;
   if (L->K <= 0 || L->K % 64 != 0 || L->N <= 0 || L->N % 8 != 0) return false;
   if (L->r < 1 || L->r > 256) return false;
+  if (L->K > kMaxDim || L->N > kMaxDim || L->N * L->K > kMaxWeight) return false;
   if (!aligned16(L->codes) || !aligned16(L->absmax) || !aligned16(L->A) || !aligned16(L->B)) return false;
   return true;
 }
@@ -91,40 +96,129 @@ struct Carve {
   }
 };
 
-size_t tn_part_bytes(int64_t M, int64_t Kd, int64_t r) {
-  return up256((size_t)skinny_tn_splits(M, Kd) * (size_t)r * (size_t)Kd * sizeof(float));
+// The skinny_tn launches behind one reduction with adapter widths (r1, r2):
+// one launch when r1 + r2 fits a launch, else chunks of each part.
+template <class F>
+void tn_chunks(int r1, int r2, F&& f) {
+  if (r1 + r2 <= kTnMaxR) {
+    f(0, r1, r2);
+    return;
+  }
+  for (int c = 0; c < r1; c += kTnMaxR) f(c, std::min(kTnMaxR, r1 - c), 0);
+  for (int c = 0; c < r2; c += kTnMaxR) f(r1 + c, std::min(kTnMaxR, r2 - c), 0);
+}
+
+// Workspace of the skinny_tn launches of a call: the largest fp32 partial
+// buffer (launches run in stream order and reuse it).
+struct BwdLayout {
+  size_t part = 0;
+  void add(int64_t M, int64_t Kd, int r1, int r2 = 0) {
+    tn_chunks(r1, r2, [&](int, int a, int b) {
+      const TnPlan pl = skinny_tn_plan(M, Kd, a + b);
+      part = std::max(part, (size_t)pl.splits * (size_t)(a + b) * (size_t)Kd);
+    });
+  }
+};
+
+BwdLayout bwd_layout(int64_t M, int64_t K, int64_t N, int64_t r) {
+  BwdLayout l;
+  l.add(M, N, (int)r);  // dB
+  l.add(M, K, (int)r);  // dA
+  return l;
 }
 
 size_t bwd_ws(int64_t M, int64_t K, int64_t N, int64_t r) {
-  const size_t part = std::max(tn_part_bytes(M, N, r), tn_part_bytes(M, K, r));
-  return up256(r * N * 2) + up256(K * r * 2) + up256(M * r * 2) + part;
+  const BwdLayout l = bwd_layout(M, K, N, r);
+  return up256(r * N * 2) + up256(K * r * 2) + up256(M * r * 2) + up256(l.part * 4);
+}
+
+BwdLayout mlp_bwd_layout(int64_t M, int64_t H, int64_t I, int64_t r) {
+  BwdLayout l;
+  l.add(M, H, (int)r);            // dB_down
+  l.add(M, I, (int)r);            // dA_down
+  l.add(M, I, (int)r);            // dB_gate
+  l.add(M, I, (int)r);            // dB_up
+  l.add(M, H, (int)r, (int)r);    // dA_gate, dA_up
+  return l;
 }
 
 size_t mlp_bwd_ws(int64_t M, int64_t H, int64_t I, int64_t r) {
-  size_t part = std::max(tn_part_bytes(M, H, r), tn_part_bytes(M, I, r));
-  return 2 * up256((size_t)M * I * 2) + 3 * up256(M * r * 2) + up256(r * H * 2) + 2 * up256(r * I * 2) +
-         up256(I * r * 2) + 2 * up256(H * r * 2) + part;
+  const BwdLayout l = mlp_bwd_layout(M, H, I, r);
+  return 2 * up256((size_t)M * I * 2) + up256(M * r * 2) + up256(M * 2 * r * 2) + up256(r * H * 2) +
+         2 * up256(r * I * 2) + up256(I * r * 2) + 2 * up256(H * r * 2) + up256(l.part * 4);
 }
 
-WSrc wsrc(const qlora_layer* L, const uint16_t* lora_i, const uint16_t* lora_j) {
+WSrc wsrc(const qlora_layer* L, const uint16_t* lora_i, const uint16_t* lora_j, int64_t ldj = 0) {
   WSrc w;
   w.codes = L->codes;
   w.absmax = L->absmax;
   w.lora_i = lora_i;
   w.lora_j = lora_j;
   w.r = (int)L->r;
+  w.ldj = ldj ? ldj : L->r;
   w.s = L->s;
   return w;
 }
 
-// dOut = s * P^T . Q reduced over M (P [M,r], Q [M,Kd]); transposed -> [Kd, r]
-int tn_reduce(const uint16_t* P, int r, const uint16_t* Q, int64_t M, int64_t Kd, float s, float* out,
-              bool transposed, float* part, hipStream_t st) {
-  const int splits = skinny_tn_splits(M, Kd);
-  QL_LAUNCH("skinny_tn", st, launch_skinny_tn(P, r, Q, M, Kd, part, splits, st));
-  QL_LAUNCH("reduce_splits", st, launch_reduce_splits(part, splits, r, Kd, s, out, transposed, st));
-  return QLORA_OK;
+NtArgs nt1(const uint16_t* in, int64_t M, int64_t Kd, const uint16_t* ad, int r, uint16_t* out, int64_t ld) {
+  NtArgs a{};
+  a.in = in;
+  a.M = M;
+  a.Kd = Kd;
+  a.ad1 = ad;
+  a.ad2 = ad;
+  a.r1 = r;
+  a.r2 = 0;
+  a.out1 = out;
+  a.out2 = out;
+  a.ld1 = ld;
+  a.ld2 = ld;
+  return a;
 }
+
+// Issues the skinny_tn + tn_reduce launches of one reduction.
+struct TnCall {
+  float* part;
+  hipStream_t st;
+  // out = s * P^T . Q (P [M, r] with row stride ldp, Q [M, Kd]); transposed -> [Kd, r]
+  int one(const uint16_t* P, int64_t ldp, int r, float s, const uint16_t* Q, int64_t M, int64_t Kd, float* out,
+          bool transposed) {
+    return two(P, ldp, r, s, out, 0, 0.f, nullptr, Q, M, Kd, transposed);
+  }
+  // rows j < r1 of P^T . Q into out1 (scale s1), rows r1 <= j < r1 + r2 into out2 (scale s2)
+  int two(const uint16_t* P, int64_t ldp, int r1, float s1, float* out1, int r2, float s2, float* out2,
+          const uint16_t* Q, int64_t M, int64_t Kd, bool transposed) {
+    int rc = QLORA_OK;
+    tn_chunks(r1, r2, [&](int c0, int a1, int a2) {
+      if (rc) return;
+      // chunk columns [c0, c0 + a1 + a2) of P; a2 > 0 only for the single launch covering both parts
+      const bool in2 = c0 >= r1;
+      TnArgs a{};
+      a.P = P + c0;
+      a.ldp = ldp;
+      a.r1 = a1;
+      a.r2 = a2;
+      a.s1 = in2 ? s2 : s1;
+      a.s2 = s2;
+      const int64_t jo = in2 ? c0 - r1 : c0;  // first output row of the chunk
+      const int64_t ld1 = transposed ? (in2 ? r2 : r1) : Kd;
+      float* o1 = in2 ? out2 : out1;
+      a.out1 = transposed ? o1 + jo : o1 + jo * Kd;
+      a.ldo1 = ld1;
+      a.out2 = out2 ? out2 : out1;
+      a.ldo2 = transposed ? r2 : Kd;
+      a.transposed = transposed ? 1 : 0;
+      a.Q = Q;
+      a.M = M;
+      a.Kd = Kd;
+      a.part = part;
+      hipError_t e = timed("skinny_tn", st, [&]() { return launch_skinny_tn(a, st); });
+      if (e == hipSuccess) e = timed("tn_reduce", st, [&]() { return launch_tn_reduce(a, st); });
+      if (e != hipSuccess) rc = hip_fail(e, "skinny_tn");
+    });
+    return rc;
+  }
+};
 
 }  // namespace
 
@@ -182,7 +276,7 @@ int qlora_forward(const qlora_layer* L, const uint16_t* X, int64_t M, uint16_t* 
   if (!X || !Y || !Z_save || !aligned16(X) || !aligned16(Y) || !aligned16(Z_save)) return QLORA_EINVAL;
   hipStream_t st = (hipStream_t)stream;
   const int r = (int)L->r;
-  QL_LAUNCH("skinny_nt", st, launch_skinny_nt(X, M, L->K, L->A, r, Z_save, nullptr, 0, nullptr, st));
+  QL_LAUNCH("skinny_nt", st, launch_skinny_nt(nt1(X, M, L->K, L->A, r, Z_save, r), st));
   QL_LAUNCH("gemm_fwd", st, launch_gemm_fwd(X, M, L->K, L->N, wsrc(L, L->B, Z_save), Y, st));
   return QLORA_OK;
 }
@@ -190,7 +284,7 @@ int qlora_forward(const qlora_layer* L, const uint16_t* X, int64_t M, uint16_t* 
 int qlora_backward(const qlora_layer* L, const uint16_t* dY, const uint16_t* X, const uint16_t* Z_save, int64_t M,
                    uint16_t* dX, float* dA, float* dB, void* ws, size_t ws_bytes, void* stream) {
   if (!layer_ok(L) || M < 0) return QLORA_EINVAL;
-  if (!dA || !dB) return QLORA_EINVAL;
+  if (!dA || !dB || !aligned16(dA) || !aligned16(dB)) return QLORA_EINVAL;
   const int64_t K = L->K, N = L->N;
   const int r = (int)L->r;
   hipStream_t st = (hipStream_t)stream;
@@ -200,24 +294,30 @@ int qlora_backward(const qlora_layer* L, const uint16_t* dY, const uint16_t* X, 
   }
   const size_t need = bwd_ws(M, K, N, r);
   if (!ws || ws_bytes < need) return QLORA_EWORKSPACE;
+  const BwdLayout lay = bwd_layout(M, K, N, r);
   Carve c{(char*)ws, ws_bytes};
   uint16_t* Bt = c.take<uint16_t>((size_t)r * N);
   uint16_t* At = c.take<uint16_t>((size_t)K * r);
   uint16_t* G = c.take<uint16_t>((size_t)M * r);
-  float* part = c.take<float>((size_t)std::max(tn_part_bytes(M, N, r), tn_part_bytes(M, K, r)) / sizeof(float));
+  float* part = c.take<float>(lay.part);
   if (!c.ok) return QLORA_EWORKSPACE;
   if (M == 0) {  // empty batch: gradients are zero
     QL_LAUNCH("fill_zero_f32", st, launch_fill_zero_f32(dA, (int64_t)r * K, st));
     QL_LAUNCH("fill_zero_f32", st, launch_fill_zero_f32(dB, (int64_t)N * r, st));
     return QLORA_OK;
   }
-  QL_LAUNCH("transpose_bf16", st, launch_transpose_bf16(L->B, N, r, Bt, st));
-  QL_LAUNCH("transpose_bf16", st, launch_transpose_bf16(L->A, r, K, At, st));
-  QL_LAUNCH("skinny_nt", st, launch_skinny_nt(dY, M, N, Bt, r, G, nullptr, 0, nullptr, st));
-  int rc = tn_reduce(Z_save, r, dY, M, N, L->s, dB, true, part, st);
+  PrepJobs pj{};
+  pj.job[0] = {L->B, Bt, N, r};  // B [N, r] -> B^T [r, N]
+  pj.job[1] = {L->A, At, r, K};  // A [r, K] -> A^T [K, r]
+  pj.n = 2;
+  QL_LAUNCH("prep", st, launch_prep(pj, st));
+  // G = dY.B ; dB = s.dY^T.Z (written transposed from Z^T.dY) ; dX ; dA = s.G^T.X
+  QL_LAUNCH("skinny_nt", st, launch_skinny_nt(nt1(dY, M, N, Bt, r, G, r), st));
+  TnCall tn{part, st};
+  int rc = tn.one(Z_save, r, r, L->s, dY, M, N, dB, true);
   if (rc) return rc;
   if (dX) QL_LAUNCH("gemm_bwd", st, launch_gemm_bwd(dY, wsrc(L, At, G), nullptr, WSrc{}, M, K, N, dX, st));
-  return tn_reduce(G, r, X, M, K, L->s, dA, false, part, st);
+  return tn.one(G, r, r, L->s, X, M, K, dA, false);
 }
 
 static bool mlp_shapes_ok(const qlora_layer* g, const qlora_layer* u, const qlora_layer* d) {
@@ -244,10 +344,19 @@ int swiglu_mlp_forward(const qlora_layer* gate, const qlora_layer* up, const qlo
   uint16_t* Zg = Z_save;
   uint16_t* Zu = Z_save + (size_t)M * r;
   uint16_t* Zd = Z_save + 2 * (size_t)M * r;
-  QL_LAUNCH("skinny_nt", st, launch_skinny_nt(X, M, H, gate->A, r, Zg, up->A, r, Zu, st));
+  if (2 * r <= 256) {
+    NtArgs a = nt1(X, M, H, gate->A, r, Zg, r);
+    a.ad2 = up->A;
+    a.r2 = r;
+    a.out2 = Zu;
+    QL_LAUNCH("skinny_nt", st, launch_skinny_nt(a, st));
+  } else {
+    QL_LAUNCH("skinny_nt", st, launch_skinny_nt(nt1(X, M, H, gate->A, r, Zg, r), st));
+    QL_LAUNCH("skinny_nt", st, launch_skinny_nt(nt1(X, M, H, up->A, r, Zu, r), st));
+  }
   QL_LAUNCH("gemm_fwd_gateup", st, launch_gemm_fwd_gateup(X, M, H, I, wsrc(gate, gate->B, Zg), wsrc(up, up->B, Zu), g_save, u_save, h_save,
                                   st));
-  QL_LAUNCH("skinny_nt", st, launch_skinny_nt(h_save, M, I, down->A, r, Zd, nullptr, 0, nullptr, st));
+  QL_LAUNCH("skinny_nt", st, launch_skinny_nt(nt1(h_save, M, I, down->A, r, Zd, r), st));
   QL_LAUNCH("gemm_fwd", st, launch_gemm_fwd(h_save, M, I, H, wsrc(down, down->B, Zd), Y, st));
   return QLORA_OK;
 }
@@ -258,7 +367,7 @@ int swiglu_mlp_backward(const qlora_layer* gate, const qlora_layer* up, const ql
                         void* ws, size_t ws_bytes, void* stream) {
   if (!mlp_shapes_ok(gate, up, down) || M < 0 || !dA || !dB) return QLORA_EINVAL;
   for (int i = 0; i < 3; ++i)
-    if (!dA[i] || !dB[i]) return QLORA_EINVAL;
+    if (!dA[i] || !dB[i] || !aligned16(dA[i]) || !aligned16(dB[i])) return QLORA_EINVAL;
   const int64_t H = gate->K, I = gate->N;
   const int r = (int)gate->r;
   hipStream_t st = (hipStream_t)stream;
@@ -270,19 +379,19 @@ int swiglu_mlp_backward(const qlora_layer* gate, const qlora_layer* up, const ql
   }
   const size_t need = mlp_bwd_ws(M, H, I, r);
   if (!ws || ws_bytes < need) return QLORA_EWORKSPACE;
+  const BwdLayout lay = mlp_bwd_layout(M, H, I, r);
   Carve c{(char*)ws, ws_bytes};
   uint16_t* dg = c.take<uint16_t>((size_t)M * I);
   uint16_t* du = c.take<uint16_t>((size_t)M * I);
   uint16_t* Gd = c.take<uint16_t>((size_t)M * r);
-  uint16_t* Gg = c.take<uint16_t>((size_t)M * r);
-  uint16_t* Gu = c.take<uint16_t>((size_t)M * r);
+  uint16_t* Ggu = c.take<uint16_t>((size_t)M * 2 * r);  // row m: G_gate[m, :] then G_up[m, :]
   uint16_t* Btd = c.take<uint16_t>((size_t)r * H);
   uint16_t* Btg = c.take<uint16_t>((size_t)r * I);
   uint16_t* Btu = c.take<uint16_t>((size_t)r * I);
   uint16_t* Atd = c.take<uint16_t>((size_t)I * r);
   uint16_t* Atg = c.take<uint16_t>((size_t)H * r);
   uint16_t* Atu = c.take<uint16_t>((size_t)H * r);
-  float* part = c.take<float>(std::max(tn_part_bytes(M, H, r), tn_part_bytes(M, I, r)) / sizeof(float));
+  float* part = c.take<float>(lay.part);
   if (!c.ok) return QLORA_EWORKSPACE;
   if (M == 0) {
     const qlora_layer* Ls[3] = {gate, up, down};
@@ -295,31 +404,39 @@ int swiglu_mlp_backward(const qlora_layer* gate, const qlora_layer* up, const ql
   const uint16_t* Zg = Z_save;
   const uint16_t* Zu = Z_save + (size_t)M * r;
   const uint16_t* Zd = Z_save + 2 * (size_t)M * r;
-  QL_LAUNCH("transpose_bf16", st, launch_transpose_bf16(down->B, H, r, Btd, st));
-  QL_LAUNCH("transpose_bf16", st, launch_transpose_bf16(gate->B, I, r, Btg, st));
-  QL_LAUNCH("transpose_bf16", st, launch_transpose_bf16(up->B, I, r, Btu, st));
-  QL_LAUNCH("transpose_bf16", st, launch_transpose_bf16(down->A, r, I, Atd, st));
-  QL_LAUNCH("transpose_bf16", st, launch_transpose_bf16(gate->A, r, H, Atg, st));
-  QL_LAUNCH("transpose_bf16", st, launch_transpose_bf16(up->A, r, H, Atu, st));
+  uint16_t* Gg = Ggu;
+  uint16_t* Gu = Ggu + r;
+  PrepJobs pj{};
+  pj.job[0] = {down->B, Btd, H, r};
+  pj.job[1] = {gate->B, Btg, I, r};
+  pj.job[2] = {up->B, Btu, I, r};
+  pj.job[3] = {down->A, Atd, r, I};
+  pj.job[4] = {gate->A, Atg, r, H};
+  pj.job[5] = {up->A, Atu, r, H};
+  pj.n = 6;
+  QL_LAUNCH("prep", st, launch_prep(pj, st));
+  TnCall tn{part, st};
   // down projection: G_d = dY.B_d ; dB_d = s.dY^T.Z_d ; dh -> (dg, du) in the GEMM epilogue ; dA_d = s.G_d^T.h
-  QL_LAUNCH("skinny_nt", st, launch_skinny_nt(dY, M, H, Btd, r, Gd, nullptr, 0, nullptr, st));
-  int rc = tn_reduce(Zd, r, dY, M, H, down->s, dB[2], true, part, st);
+  QL_LAUNCH("skinny_nt", st, launch_skinny_nt(nt1(dY, M, H, Btd, r, Gd, r), st));
+  int rc = tn.one(Zd, r, r, down->s, dY, M, H, dB[2], true);
   if (rc) return rc;
-  QL_LAUNCH("gemm_bwd_swiglu", st, launch_gemm_bwd_swiglu(dY, wsrc(down, Atd, Gd), M, I, H, g_save, u_save, dg, du, st));
-  rc = tn_reduce(Gd, r, h_save, M, I, down->s, dA[2], false, part, st);
+  QL_LAUNCH("gemm_bwd_swiglu", st,
+            launch_gemm_bwd_swiglu(dY, wsrc(down, Atd, Gd), M, I, H, g_save, u_save, dg, du, st));
+  rc = tn.one(Gd, r, r, down->s, h_save, M, I, dA[2], false);
   if (rc) return rc;
   // gate and up: G = d(g|u).B ; dB = s.d(g|u)^T.Z
-  QL_LAUNCH("skinny_nt", st, launch_skinny_nt(dg, M, I, Btg, r, Gg, nullptr, 0, nullptr, st));
-  QL_LAUNCH("skinny_nt", st, launch_skinny_nt(du, M, I, Btu, r, Gu, nullptr, 0, nullptr, st));
-  rc = tn_reduce(Zg, r, dg, M, I, gate->s, dB[0], true, part, st);
+  QL_LAUNCH("skinny_nt", st, launch_skinny_nt(nt1(dg, M, I, Btg, r, Gg, 2 * r), st));
+  QL_LAUNCH("skinny_nt", st, launch_skinny_nt(nt1(du, M, I, Btu, r, Gu, 2 * r), st));
+  rc = tn.one(Zg, r, r, gate->s, dg, M, I, dB[0], true);
   if (rc) return rc;
-  rc = tn_reduce(Zu, r, du, M, I, up->s, dB[1], true, part, st);
+  rc = tn.one(Zu, r, r, up->s, du, M, I, dB[1], true);
   if (rc) return rc;
   // dX = dg.W_g + du.W_u + s.G_g.A_g + s.G_u.A_u : one GEMM over the concatenated reduction
-  if (dX) QL_LAUNCH("gemm_bwd", st, launch_gemm_bwd(dg, wsrc(gate, Atg, Gg), du, wsrc(up, Atu, Gu), M, H, I, dX, st));
-  rc = tn_reduce(Gg, r, X, M, H, gate->s, dA[0], false, part, st);
-  if (rc) return rc;
-  return tn_reduce(Gu, r, X, M, H, up->s, dA[1], false, part, st);
+  if (dX)
+    QL_LAUNCH("gemm_bwd", st,
+              launch_gemm_bwd(dg, wsrc(gate, Atg, Gg, 2 * r), du, wsrc(up, Atu, Gu, 2 * r), M, H, I, dX, st));
+  // dA_g = s_g.G_g^T.X and dA_u = s_u.G_u^T.X (one pass over X when 2r fits a launch)
+  return tn.two(Ggu, 2 * r, r, gate->s, dA[0], r, up->s, dA[1], X, M, H, false);
 }
 
 int qlora_profile_begin(int max_launches) {

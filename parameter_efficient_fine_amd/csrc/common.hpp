@@ -135,6 +135,29 @@ __device__ __forceinline__ u32x4 dequant8(uint32_t x, const Nf4Lut& t) {
   return r;
 }
 
+// ---------------------------------------------------------------------------
+// Buffer resources: loads and stores through a descriptor with a hardware
+// range check. An offset at or beyond num_records reads zero and drops a
+// store, which replaces data-dependent branches at tile edges.
+
+constexpr int kOff = (int)0x80000000u;  // an offset beyond every buffer's num_records
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, int64_t bytes) {
+  const int n = bytes > 0x7fffffff ? 0x7fffffff : (int)bytes;
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, n, 0x00020000);
+}
+
+// s_waitcnt immediate: wait until at most n vector-memory ops are outstanding
+// (lgkm and exp counters not waited).
+constexpr unsigned waitcnt_vm(int n) { return (unsigned)((n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8)); }
+
+// Workgroup barrier that waits for this wave's LDS operations only, so global
+// loads issued before it stay in flight (a full __syncthreads() would drain them).
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_s_waitcnt(0xC07F);
+  __builtin_amdgcn_s_barrier();
+}
+
 __device__ __forceinline__ float sigmoid_f(float z) { return 1.0f / (1.0f + expf(-z)); }
 
 }  // namespace qlora

@@ -284,7 +284,7 @@ void k_qgemm(GemmArgs p) {
         for (int src = 0; src < (MODE == kBwd ? p.nsrc : 1); ++src) {
           const WSrc& w = src ? p.w1 : p.w0;
           const f32x16 lt = lora_frag(ir < iext ? w.lora_i + ir * w.r : nullptr,
-                                      m_ok ? w.lora_j + m * w.r : nullptr, w.r, lane);
+                                      m_ok ? w.lora_j + m * w.ldj : nullptr, w.r, lane);
 #pragma unroll
           for (int v = 0; v < 16; ++v) acc[fi][fj][v] += w.s * lt[v];
         }
@@ -321,9 +321,9 @@ void k_qgemm(GemmArgs p) {
         const int64_t ir = i0 + wi * 64 + 32 * fi + jl;
         const bool i_ok = ir < N;
         const f32x16 lg = lora_frag(i_ok ? p.w0.lora_i + ir * p.w0.r : nullptr,
-                                    m_ok ? p.w0.lora_j + m * p.w0.r : nullptr, p.w0.r, lane);
+                                    m_ok ? p.w0.lora_j + m * p.w0.ldj : nullptr, p.w0.r, lane);
         const f32x16 lu = lora_frag(i_ok ? p.w1.lora_i + ir * p.w1.r : nullptr,
-                                    m_ok ? p.w1.lora_j + m * p.w1.r : nullptr, p.w1.r, lane);
+                                    m_ok ? p.w1.lora_j + m * p.w1.ldj : nullptr, p.w1.r, lane);
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
           const int64_t ic = i0 + wi * 64 + 32 * fi + 8 * q + 4 * (lane >> 5);

@@ -49,15 +49,8 @@ struct FwdArgs {
 };
 
 // The epilogue is branch-free: loads and stores go through buffer resources
-// whose hardware range check turns an out-of-range lane into a dropped store
-// or a zero load (divergent branches there would push the 256 accumulators
-// out of AGPRs and spill the main loop).
-constexpr int kOff = (int)0x80000000u;  // an offset beyond every buffer's num_records
-
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, int64_t bytes) {
-  const int n = bytes > 0x7fffffff ? 0x7fffffff : (int)bytes;
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, n, 0x00020000);
-}
+// (out-of-range lanes read zero or drop their store); divergent branches there
+// would push the 256 accumulators out of AGPRs and spill the main loop.
 
 // 8 bf16 of row `row` (-1: none) of a [rows, r] bf16 matrix, columns c..c+7 (zero beyond r).
 // ALIGNED (r % 8 == 0): one 16-byte load; otherwise eight 2-byte loads.
@@ -95,10 +88,6 @@ __device__ __forceinline__ void split_scaled(const u32x4 v, float s, u32x4& hi, 
 __device__ __forceinline__ void store4(__amdgpu_buffer_rsrc_t rs, int off, const float (&v)[4]) {
   __builtin_amdgcn_raw_buffer_store_b64(u32x2{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])}, rs, off, 0, 0);
 }
-
-// s_waitcnt immediate: wait until at most n vector-memory ops are outstanding
-// (lgkm and exp counters not waited).
-constexpr unsigned waitcnt_vm(int n) { return (unsigned)((n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8)); }
 
 template <bool GATEUP, int RP, bool ALIGNED>
 __global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_per_eu(1, 1)))

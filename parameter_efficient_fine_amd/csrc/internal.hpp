@@ -11,33 +11,78 @@ hipError_t launch_quantize(const float* W, int64_t N, int64_t K, uint8_t* codes,
 hipError_t launch_dequantize(const uint8_t* codes, const float* absmax, int64_t N, int64_t K, float* W_hat,
                              hipStream_t st);
 
-// out[M, r] (bf16) = in[M, Kd] . ad[r, Kd]^T ; fp32 accumulation.
-// Up to two adapters: rows j < r1 come from ad1 (written to out1, width r1),
-// rows r1 <= j < r1 + r2 from ad2 (written to out2, width r2); ad2 may be null.
-hipError_t launch_skinny_nt(const uint16_t* in, int64_t M, int64_t Kd, const uint16_t* ad1, int r1, uint16_t* out1,
-                            const uint16_t* ad2, int r2, uint16_t* out2, hipStream_t st);
+// Skinny rank-r products ------------------------------------------------------
 
-// part[S, r, Kd] (fp32) = per-split partial of P[M, r]^T . Q[M, Kd]; returns S via *splits.
-int skinny_tn_splits(int64_t M, int64_t Kd);
-hipError_t launch_skinny_tn(const uint16_t* P, int r, const uint16_t* Q, int64_t M, int64_t Kd, float* part,
-                            int splits, hipStream_t st);
-// out = s * sum_S part ; transposed: out[k, j] (ld = r), else out[j, k] (ld = Kd)
-hipError_t launch_reduce_splits(const float* part, int splits, int r, int64_t Kd, float s, float* out, bool transposed,
-                                hipStream_t st);
+// out[M, R] (bf16) = in[M, Kd] . [ad1; ad2]^T with fp32 accumulation: adapter
+// rows j < r1 come from ad1 [r1, Kd] and go to out1 (row stride ld1), rows
+// r1 <= j < r1 + r2 from ad2 [r2, Kd] to out2 (row stride ld2); r2 may be 0.
+struct NtArgs {
+  const uint16_t* in;
+  int64_t M, Kd;
+  const uint16_t* ad1;
+  const uint16_t* ad2;
+  int r1, r2;
+  uint16_t* out1;
+  uint16_t* out2;
+  int64_t ld1, ld2;
+};
+hipError_t launch_skinny_nt(const NtArgs& a, hipStream_t st);
+
+// Reduction over M of P[M, R]^T . Q[M, Kd] (P row stride ldp, R = r1 + r2 <=
+// kTnMaxR): rows j < r1 give s1 * (..) into out1, the others s2 * (..) into
+// out2 (j counted from r1). Element (j, k) goes to out[j * ldo + k], or to
+// out[k * ldo + j] when transposed; fp32. launch_skinny_tn splits the rows
+// over workgroups that write fp32 partials to `part`; launch_tn_reduce (next
+// on the same stream) adds them in split order and writes out1/out2.
+constexpr int kTnMaxR = 128;
+struct TnPlan {
+  int splits;
+  int col_tiles;
+  int64_t rows;  // rows per split (multiple of 64)
+};
+TnPlan skinny_tn_plan(int64_t M, int64_t Kd, int R);
+struct TnArgs {
+  const uint16_t* P;
+  int64_t ldp;
+  int r1, r2;
+  float s1, s2;
+  float* out1;
+  float* out2;
+  int64_t ldo1, ldo2;
+  int transposed;
+  const uint16_t* Q;
+  int64_t M, Kd;
+  float* part;          // [splits, R, Kd]
+  int64_t rows;         // set by the launchers from skinny_tn_plan
+  int splits;
+};
+hipError_t launch_skinny_tn(TnArgs a, hipStream_t st);
+hipError_t launch_tn_reduce(TnArgs a, hipStream_t st);
+
+// One launch before a backward: dst[C, R] = src[R, C]^T for each job (bf16).
+constexpr int kMaxPrepJobs = 6;
+struct TransposeJob {
+  const uint16_t* src;
+  uint16_t* dst;
+  int64_t R, C;
+};
+struct PrepJobs {
+  TransposeJob job[kMaxPrepJobs];
+  int n;
+};
+hipError_t launch_prep(const PrepJobs& jobs, hipStream_t st);
 
 // p[0..n) = 0 (a kernel, so the call stays capturable in a graph)
 hipError_t launch_fill_zero_f32(float* p, int64_t n, hipStream_t st);
-
-// dst[C, R] = src[R, C]^T for bf16 matrices
-hipError_t launch_transpose_bf16(const uint16_t* src, int64_t R, int64_t C, uint16_t* dst, hipStream_t st);
 
 // Fused dequant GEMMs -------------------------------------------------------
 struct WSrc {           // one frozen 4-bit weight [N, K] with its LoRA pair
   const uint8_t* codes;  // [N, K/2]
   const float* absmax;   // [N, K/64]
   const uint16_t* lora_i;  // fwd: B [N, r] ; bwd: A^T [K, r]
-  const uint16_t* lora_j;  // fwd: Z [M, r] ; bwd: G [M, r]
+  const uint16_t* lora_j;  // fwd: Z [M, r] ; bwd: G [M, r] with row stride ldj
   int r;
+  int64_t ldj;
   float s;
 };
 

@@ -3,95 +3,142 @@
 // "Unsloth vs PyTorch" video, 1:35-2:00: the adapters are skinny (rank 8 to
 // 128) against 4096-wide weights, so the products are bracketed to keep every
 // intermediate M x r (or r x K) and never form the N x K matrix B.A.
-//   skinny_nt:  Z = X.A^T  and  G = dY.B          ([M,Kd] x [r,Kd]^T -> [M,r])
+//   skinny_nt:  Z = X.A^T  and  G = dY.B            ([M,Kd] x [r,Kd]^T -> [M,r])
 //   skinny_tn:  dA = s.G^T.X  and  dB^T = s.Z^T.dY  ([M,r]^T x [M,Kd] -> [r,Kd])
-// Both read their big operand exactly once and are HBM-bound.
+// Both read their big operand once and are HBM-bound; MFMA 16x16x32 does the
+// arithmetic, and the kernels are built to keep many loads in flight.
+#include <type_traits>
+
 #include "common.hpp"
 #include "internal.hpp"
 
 namespace qlora {
 
 // ---------------------------------------------------------------------------
-// skinny_nt: 16 rows of `in` per workgroup, 4 waves interleaved over the
-// 32-wide k steps, MFMA 16x16x32, partial sums combined through LDS.
-// RP = adapter rows (r1 + r2) rounded up to 16.
+// skinny_nt: 16 rows of `in` per workgroup. The waves interleave over the
+// 32-wide k steps (wave w takes steps w, w + NW, ...) and issue U steps of
+// loads at once. `in` is read through a buffer resource covering the
+// workgroup's rows: a lane's row and k position form a loop-invariant VGPR
+// offset, the step a scalar offset, and rows past M read zero -- the loop has
+// no per-lane condition (a per-lane select there turns into divergent
+// branches that serialize the loads). The steps a wave owns are done in
+// batches of U, then U/2, .., 1 (binary remainder); a ragged last step
+// (Kd % 32 != 0) is done apart with masks. Per-wave partial sums are combined
+// by a fixed-order tree in LDS. RP = r1 + r2 rounded up to 16.
 
 template <int RP>
-__global__ __launch_bounds__(256) void k_skinny_nt(const uint16_t* __restrict__ in, int64_t M, int64_t Kd,
-                                                   const uint16_t* __restrict__ ad1, int r1,
-                                                   uint16_t* __restrict__ out1, const uint16_t* __restrict__ ad2,
-                                                   int r2, uint16_t* __restrict__ out2) {
-  constexpr int NF = RP / 16;
-  __shared__ float red[4][16][RP + 1];
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+struct NtShape {
+  static constexpr int NF = RP / 16;                  // 16-row adapter fragments
+  static constexpr int NW = RP >= 256 ? 4 : 8;        // waves
+  static constexpr int U = RP <= 32 ? 16 : (RP <= 64 ? 4 : (RP <= 128 ? 2 : 1));  // steps per batch
+};
+
+template <int RP>
+__global__ __attribute__((amdgpu_flat_work_group_size(64 * NtShape<RP>::NW, 64 * NtShape<RP>::NW)))
+void k_skinny_nt(NtArgs p) {
+  constexpr int NF = NtShape<RP>::NF, NW = NtShape<RP>::NW, U = NtShape<RP>::U;
+  __shared__ float red[NW / 2][16][RP + 4];
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int64_t M = p.M, Kd = p.Kd;
   const int64_t m0 = (int64_t)blockIdx.x * 16;
-  const int R = r1 + r2;
-  const int64_t row = m0 + (lane & 15);
-  const bool row_ok = row < M;
-  const int kofs = 8 * (lane >> 4);
-  const int64_t nsteps = (Kd + 31) / 32;  // a ragged last step is masked per lane (Kd % 8 == 0)
+  const int R = p.r1 + p.r2;
+  const int64_t rows_here = (M - m0) < 16 ? (M - m0) : 16;
+  const __amdgpu_buffer_rsrc_t rin = make_rsrc(p.in + m0 * Kd, rows_here * Kd * 2);
+  const int row = lane & 15, kofs = 8 * (lane >> 4);
+  const int voff = (int)((row * Kd + kofs) * 2);
+
+  const uint16_t* adp[NF];  // this lane's adapter row, at its k offset
+#pragma unroll
+  for (int f = 0; f < NF; ++f) {
+    const int j = 16 * f + row;
+    const int jc = j < R ? j : 0;
+    adp[f] = (jc < p.r1 ? p.ad1 + (int64_t)jc * Kd : p.ad2 + (int64_t)(jc - p.r1) * Kd) + kofs;
+  }
 
   f32x4 acc[NF];
 #pragma unroll
   for (int f = 0; f < NF; ++f) acc[f] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  // adapter row pointers for this lane's j within each 16-row fragment
-  const uint16_t* adp[NF];
-  bool ad_ok[NF];
+  // V full steps starting at this wave's step index i0: loads first, then MFMAs
+  auto batch = [&](auto vtag, int64_t i0) {
+    constexpr int V = decltype(vtag)::value;
+    u32x4 a[V], b[V][NF];
 #pragma unroll
-  for (int f = 0; f < NF; ++f) {
-    const int j = 16 * f + (lane & 15);
-    ad_ok[f] = j < R;
-    adp[f] = j < r1 ? ad1 + (int64_t)j * Kd : (j < R ? ad2 + (int64_t)(j - r1) * Kd : ad1);
-  }
-  const uint16_t* inp = in + (row_ok ? row : 0) * Kd;
-
-  constexpr int U = 4;
-  for (int64_t s0 = wave; s0 < nsteps; s0 += 4 * U) {
-    u32x4 a[U];
-    u32x4 b[U][NF];
+    for (int u = 0; u < V; ++u) {
+      const int64_t st = wave + NW * (i0 + u);
+      a[u] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rin, voff, (int)(st * 64), 0));
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int64_t s = s0 + 4 * u;
-      const int64_t k = s * 32 + kofs;
-      const bool ok = s < nsteps && k < Kd;
-      a[u] = (ok && row_ok) ? *reinterpret_cast<const u32x4*>(inp + k) : u32x4{0, 0, 0, 0};
-#pragma unroll
-      for (int f = 0; f < NF; ++f)
-        b[u][f] = (ok && ad_ok[f]) ? *reinterpret_cast<const u32x4*>(adp[f] + k) : u32x4{0, 0, 0, 0};
+      for (int f = 0; f < NF; ++f) b[u][f] = *reinterpret_cast<const u32x4*>(adp[f] + st * 32);
     }
+    __builtin_amdgcn_sched_barrier(0);  // every load of the batch goes out before the first MFMA waits
 #pragma unroll
-    for (int u = 0; u < U; ++u)
+    for (int u = 0; u < V; ++u)
 #pragma unroll
       for (int f = 0; f < NF; ++f) acc[f] = mfma16(a[u], b[u][f], acc[f]);
+  };
+  const int64_t nfull = Kd / 32;  // steps with all 32 columns in range
+  const int64_t cnt = nfull > wave ? (nfull - wave + NW - 1) / NW : 0;
+  int64_t i = 0;
+  for (; i + U <= cnt; i += U) batch(std::integral_constant<int, U>{}, i);
+  if constexpr (U >= 16) if (i + 8 <= cnt) { batch(std::integral_constant<int, 8>{}, i); i += 8; }
+  if constexpr (U >= 8) if (i + 4 <= cnt) { batch(std::integral_constant<int, 4>{}, i); i += 4; }
+  if constexpr (U >= 4) if (i + 2 <= cnt) { batch(std::integral_constant<int, 2>{}, i); i += 2; }
+  if constexpr (U >= 2) if (i + 1 <= cnt) { batch(std::integral_constant<int, 1>{}, i); i += 1; }
+  if (nfull * 32 < Kd && wave == nfull % NW) {  // ragged last step, masked per lane
+    const int64_t k = nfull * 32 + kofs;
+    const bool ok = k < Kd;
+    u32x4 a = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rin, voff, (int)(nfull * 64), 0));
+    if (!ok) a = u32x4{0, 0, 0, 0};
+#pragma unroll
+    for (int f = 0; f < NF; ++f) {
+      u32x4 b = *reinterpret_cast<const u32x4*>(adp[f] + (ok ? nfull * 32 : 0));
+      if (!ok) b = u32x4{0, 0, 0, 0};
+      acc[f] = mfma16(a, b, acc[f]);
+    }
   }
+
+  // fixed-order tree over the waves: (w, w + h) pairs for h = NW/2, NW/4, .., 1
   // C layout: col j = lane%16 (adapter row), row i = 4*(lane/16) + v (token row)
 #pragma unroll
-  for (int f = 0; f < NF; ++f)
+  for (int h = NW / 2; h >= 1; h >>= 1) {
+    if (wave >= h && wave < 2 * h) {
 #pragma unroll
-    for (int v = 0; v < 4; ++v) red[wave][4 * (lane >> 4) + v][16 * f + (lane & 15)] = acc[f][v];
-  __syncthreads();
-  for (int idx = threadIdx.x; idx < 16 * R; idx += 256) {
-    const int i = idx / R, j = idx - i * R;
-    const int64_t m = m0 + i;
-    if (m >= M) continue;
-    const float v = (red[0][i][j] + red[1][i][j]) + (red[2][i][j] + red[3][i][j]);
-    const uint16_t h = __builtin_bit_cast(uint16_t, (__bf16)v);
-    if (j < r1)
-      out1[m * r1 + j] = h;
-    else
-      out2[m * r2 + (j - r1)] = h;
+      for (int f = 0; f < NF; ++f)
+#pragma unroll
+        for (int v = 0; v < 4; ++v) red[wave - h][4 * (lane >> 4) + v][16 * f + row] = acc[f][v];
+    }
+    __syncthreads();
+    if (wave < h) {
+#pragma unroll
+      for (int f = 0; f < NF; ++f)
+#pragma unroll
+        for (int v = 0; v < 4; ++v) acc[f][v] += red[wave][4 * (lane >> 4) + v][16 * f + row];
+    }
+    __syncthreads();
+  }
+  if (wave != 0) return;
+#pragma unroll
+  for (int f = 0; f < NF; ++f) {
+    const int j = 16 * f + row;
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      const int64_t m = m0 + 4 * (lane >> 4) + v;
+      if (m >= M || j >= R) continue;
+      const uint16_t hv = __builtin_bit_cast(uint16_t, (__bf16)acc[f][v]);
+      if (j < p.r1)
+        p.out1[m * p.ld1 + j] = hv;
+      else
+        p.out2[m * p.ld2 + (j - p.r1)] = hv;
+    }
   }
 }
 
-hipError_t launch_skinny_nt(const uint16_t* in, int64_t M, int64_t Kd, const uint16_t* ad1, int r1, uint16_t* out1,
-                            const uint16_t* ad2, int r2, uint16_t* out2, hipStream_t st) {
-  if (M == 0) return hipSuccess;
-  const int R = r1 + (ad2 ? r2 : 0);
-  if (!ad2) r2 = 0;
-  const unsigned grid = (unsigned)((M + 15) / 16);
-#define QL_NT(RPV) \
-  k_skinny_nt<RPV><<<grid, 256, 0, st>>>(in, M, Kd, ad1, r1, out1, ad2, r2, out2)
+hipError_t launch_skinny_nt(const NtArgs& a, hipStream_t st) {
+  if (a.M == 0) return hipSuccess;
+  const int R = a.r1 + a.r2;
+  const unsigned grid = (unsigned)((a.M + 15) / 16);
+#define QL_NT(RPV) k_skinny_nt<RPV><<<grid, 64 * NtShape<RPV>::NW, 0, st>>>(a)
   if (R <= 16)
     QL_NT(16);
   else if (R <= 32)
@@ -109,145 +156,281 @@ hipError_t launch_skinny_nt(const uint16_t* in, int64_t M, int64_t Kd, const uin
 }
 
 // ---------------------------------------------------------------------------
-// skinny_tn: part[s, j, k] = sum over the rows m of split s of P[m, j] * Q[m, k].
-// Workgroup = 256 columns of Q x one split of the rows; 4 waves x 64 columns.
-// Both operands are staged row-major in LDS and read column-wise with
-// ds_read_b64_tr_b16 so that each lane holds 8 consecutive rows (the reduction).
+// skinny_tn: out = s * P[M, R]^T . Q[M, Kd], reduced over the M rows (R <= 128).
+//
+// Workgroup = 128 columns of Q (4 waves x 32) x one split of the rows. Rows
+// go 64 at a time through LDS, where both operands are read column-wise with
+// ds_read_b64_tr_b16 (each lane then holds 8 consecutive rows: the reduction
+// dimension). Two register sets keep the next two 64-row tiles in flight while
+// one is consumed. Each split stores an fp32 partial; k_tn_reduce then adds
+// the partials in split order (deterministic), scales, and writes the result.
 
-constexpr int kTnCols = 256;
-constexpr int kTnRows = 32;  // rows of P/Q per step (one MFMA reduction)
-constexpr int kTnQStride = kTnCols + 16;  // bf16 elements per LDS row (bank spread)
+constexpr int kTnCols = 128;
+constexpr int kTnRows = 64;
+constexpr int kTnQS = kTnCols + 16;  // LDS row stride (bf16): 8 banks between rows
 
-template <int RP>
-__global__ __launch_bounds__(256) void k_skinny_tn(const uint16_t* __restrict__ P, int r,
-                                                   const uint16_t* __restrict__ Q, int64_t M, int64_t Kd,
-                                                   int64_t rows_per_split, float* __restrict__ part) {
-  constexpr int NJ = RP / 16;
-  constexpr int PS = RP + 16;  // P tile row stride (elements)
-  __shared__ __attribute__((aligned(16))) uint16_t sQ[kTnRows * kTnQStride];
-  __shared__ __attribute__((aligned(16))) uint16_t sP[kTnRows * PS];
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, t = threadIdx.x;
-  const int64_t k0 = (int64_t)blockIdx.x * kTnCols;
-  const int split = blockIdx.y;
-  const int64_t mbeg = (int64_t)split * rows_per_split;
-  const int64_t mend = mbeg + rows_per_split < M ? mbeg + rows_per_split : M;
-
-  f32x4 acc[NJ][4];
-#pragma unroll
-  for (int a = 0; a < NJ; ++a)
-#pragma unroll
-    for (int b = 0; b < 4; ++b) acc[a][b] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-  const int g = lane >> 4, s = lane & 15;
-  for (int64_t m0 = mbeg; m0 < mend; m0 += kTnRows) {
-    // stage Q tile [32 rows x 256 cols]: 1024 chunks of 16 B, 4 per thread
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const int c = t + 256 * q;
-      const int rr = c >> 5, cc = (c & 31) * 8;
-      const int64_t m = m0 + rr, k = k0 + cc;
-      u32x4 v = {0, 0, 0, 0};
-      if (m < mend && k < Kd) v = *reinterpret_cast<const u32x4*>(Q + m * Kd + k);
-      *reinterpret_cast<u32x4*>(&sQ[rr * kTnQStride + cc]) = v;
-    }
-    // stage P tile [32 rows x RP cols] (zero beyond r and beyond the split)
-    for (int e = t; e < kTnRows * RP; e += 256) {
-      const int rr = e / RP, j = e - rr * RP;
-      const int64_t m = m0 + rr;
-      sP[rr * PS + j] = (m < mend && j < r) ? P[m * r + j] : (uint16_t)0;
-    }
-    __syncthreads();
-    // operands: lane (group g, index s) -> rows 8g..8g+7, column s of a 16-wide fragment
-    u32x4 pa[NJ], qb[4];
-#pragma unroll
-    for (int a = 0; a < NJ; ++a) {
-      const u32x2 lo = lds_read_tr(&sP[(8 * g + (s >> 2)) * PS + 16 * a + 4 * (s & 3)]);
-      const u32x2 hi = lds_read_tr(&sP[(8 * g + 4 + (s >> 2)) * PS + 16 * a + 4 * (s & 3)]);
-      pa[a] = u32x4{lo[0], lo[1], hi[0], hi[1]};
-    }
-#pragma unroll
-    for (int b = 0; b < 4; ++b) {
-      const int col = 64 * wave + 16 * b + 4 * (s & 3);
-      const u32x2 lo = lds_read_tr(&sQ[(8 * g + (s >> 2)) * kTnQStride + col]);
-      const u32x2 hi = lds_read_tr(&sQ[(8 * g + 4 + (s >> 2)) * kTnQStride + col]);
-      qb[b] = u32x4{lo[0], lo[1], hi[0], hi[1]};
-    }
-#pragma unroll
-    for (int a = 0; a < NJ; ++a)
-#pragma unroll
-      for (int b = 0; b < 4; ++b) acc[a][b] = mfma16(pa[a], qb[b], acc[a][b]);
-    __syncthreads();
-  }
-  // C layout: col (k) = lane%16, row (j) = 4*(lane/16) + v
-  float* dst = part + (int64_t)split * r * Kd;
-#pragma unroll
-  for (int a = 0; a < NJ; ++a)
-#pragma unroll
-    for (int b = 0; b < 4; ++b) {
-      const int64_t k = k0 + 64 * wave + 16 * b + (lane & 15);
-#pragma unroll
-      for (int v = 0; v < 4; ++v) {
-        const int j = 16 * a + 4 * (lane >> 4) + v;
-        if (j < r && k < Kd) dst[(int64_t)j * Kd + k] = acc[a][b][v];
-      }
-    }
-}
-
-int skinny_tn_splits(int64_t M, int64_t Kd) {
-  // enough workgroups to cover the chip, with >= 256 rows per split
-  const int64_t col_tiles = (Kd + kTnCols - 1) / kTnCols;
-  int64_t splits = (1024 + col_tiles - 1) / col_tiles;
-  const int64_t max_by_rows = (M + 255) / 256;
-  if (splits > max_by_rows) splits = max_by_rows;
+TnPlan skinny_tn_plan(int64_t M, int64_t Kd, int R) {
+  TnPlan pl;
+  if (M < 1) M = 1;  // an empty batch launches nothing; size as for one row
+  pl.col_tiles = (int)((Kd + kTnCols - 1) / kTnCols);
+  const int64_t RR = (R + 15) / 16 * 16;
+  int64_t splits = (512 + pl.col_tiles - 1) / pl.col_tiles;  // ~2 workgroups per CU
+  const int64_t by_traffic = M / (8 * RR);                     // partials <= 1/4 of Q's bytes
+  if (splits > by_traffic) splits = by_traffic;
+  if (splits > 64) splits = 64;
   if (splits < 1) splits = 1;
-  if (splits > 256) splits = 256;
-  return (int)splits;
-}
-
-hipError_t launch_skinny_tn(const uint16_t* P, int r, const uint16_t* Q, int64_t M, int64_t Kd, float* part,
-                            int splits, hipStream_t st) {
   int64_t rows = (M + splits - 1) / splits;
   rows = (rows + kTnRows - 1) / kTnRows * kTnRows;
-  dim3 grid((unsigned)((Kd + kTnCols - 1) / kTnCols), (unsigned)splits);
-#define QL_TN(RPV) k_skinny_tn<RPV><<<grid, 256, 0, st>>>(P, r, Q, M, Kd, rows, part)
-  if (r <= 16)
+  pl.rows = rows;
+  pl.splits = (int)((M + rows - 1) / rows);
+  return pl;
+}
+
+template <int RP, bool PV>
+__global__ __launch_bounds__(256) void k_skinny_tn(TnArgs p) {
+  constexpr int NJ = RP / 16;
+  constexpr int PS = RP + 16;                             // P tile row stride (bf16)
+  constexpr int QCH = kTnRows * kTnCols / 8 / 256;        // 16-byte Q chunks per thread
+  constexpr int PTOT = kTnRows * RP / 8;                  // 16-byte P chunks per tile
+  constexpr int PCH = (PTOT + 255) / 256;
+  __shared__ __attribute__((aligned(16))) uint16_t sQ[kTnRows * kTnQS];
+  __shared__ __attribute__((aligned(16))) uint16_t sP[kTnRows * PS];
+  const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+  const int64_t M = p.M, Kd = p.Kd;
+  const int R = p.r1 + p.r2;
+  const int64_t k0 = (int64_t)blockIdx.x * kTnCols;
+  const int64_t mbeg = (int64_t)blockIdx.y * p.rows;
+  const int64_t nrows = (M - mbeg) < p.rows ? (M - mbeg) : p.rows;  // >= 1 by the plan
+  const int ntiles = (int)((nrows + kTnRows - 1) / kTnRows);
+
+  // Loop-invariant per-lane offsets inside a 64-row tile; each tile gets its
+  // own buffer resources (base at the tile's first row, size = the rows left),
+  // so rows past the split read zero and a tile past the end costs nothing.
+  const int qrow = t >> 4, qcol = (t & 15) * 8;  // Q chunk q: row qrow + 16q
+  const bool q_ok = k0 + qcol < Kd;
+  int qoff[QCH];
+#pragma unroll
+  for (int q = 0; q < QCH; ++q) qoff[q] = q_ok ? (int)(((qrow + 16 * q) * Kd + k0 + qcol) * 2) : kOff;
+  // P chunk q of this thread: chunk c = (t + 256 q) mod PTOT (threads past PTOT
+  // duplicate a chunk: same data, same LDS slot)
+  int poff[PCH][4];
+  int pslot[PCH];
+#pragma unroll
+  for (int q = 0; q < PCH; ++q) {
+    const int c = (t + 256 * q) % PTOT;
+    const int prow = c / (RP / 8), pj = (c % (RP / 8)) * 8;
+    pslot[q] = prow * PS + pj;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int j0 = pj + (PV ? 0 : 2 * e);
+      poff[q][e] = j0 < R ? (int)((prow * p.ldp + j0) * 2) : kOff;
+    }
+  }
+  auto load = [&](int tile, u32x4(&qv)[QCH], u32x4(&pv)[PCH]) {
+    const int64_t mt = (int64_t)tile * kTnRows;
+    const int64_t left = nrows - mt > 0 ? nrows - mt : 0;
+    const __amdgpu_buffer_rsrc_t rQ = make_rsrc(p.Q + (mbeg + mt) * Kd, left * Kd * 2);
+    const __amdgpu_buffer_rsrc_t rP = make_rsrc(p.P + (mbeg + mt) * p.ldp, left * p.ldp * 2);
+#pragma unroll
+    for (int q = 0; q < QCH; ++q)
+      qv[q] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rQ, qoff[q], 0, 0));
+#pragma unroll
+    for (int q = 0; q < PCH; ++q) {
+      if (PV) {
+        pv[q] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rP, poff[q][0], 0, 0));
+      } else {  // element-wise (R or the row stride not a multiple of 8)
+        uint32_t w[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int o0 = poff[q][e], o1 = (pslot[q] % PS) + 2 * e + 1 < R ? o0 + 2 : kOff;
+          w[e] = (uint32_t)__builtin_amdgcn_raw_buffer_load_b16(rP, o0, 0, 0) |
+                 ((uint32_t)__builtin_amdgcn_raw_buffer_load_b16(rP, o1, 0, 0) << 16);
+        }
+        pv[q] = u32x4{w[0], w[1], w[2], w[3]};
+      }
+    }
+  };
+  // The issue order of every tile's loads is pinned (sched barriers), so the
+  // loop entry and the back edge present the same outstanding-load sequence
+  // and the compiler's wait counts keep the other tile in flight.
+  auto load_pinned = [&](int tile, u32x4(&qv)[QCH], u32x4(&pv)[PCH]) {
+    __builtin_amdgcn_sched_barrier(0);
+    load(tile, qv, pv);
+    __builtin_amdgcn_sched_barrier(0);
+  };
+  auto stage = [&](const u32x4(&qv)[QCH], const u32x4(&pv)[PCH]) {
+#pragma unroll
+    for (int q = 0; q < QCH; ++q) *reinterpret_cast<u32x4*>(&sQ[(qrow + 16 * q) * kTnQS + qcol]) = qv[q];
+#pragma unroll
+    for (int q = 0; q < PCH; ++q) *reinterpret_cast<u32x4*>(&sP[pslot[q]]) = pv[q];
+  };
+
+  f32x4 acc[NJ][2];
+#pragma unroll
+  for (int a = 0; a < NJ; ++a) acc[a][0] = acc[a][1] = f32x4{0.f, 0.f, 0.f, 0.f};
+  const int g = lane >> 4, sl = lane & 15;
+  auto compute = [&]() {
+#pragma unroll
+    for (int half = 0; half < 2; ++half) {
+      const int rb = 32 * half + 8 * g + (sl >> 2);
+      u32x4 qb[2];
+#pragma unroll
+      for (int b = 0; b < 2; ++b) {
+        const int col = 32 * wave + 16 * b + 4 * (sl & 3);
+        const u32x2 lo = lds_read_tr(&sQ[rb * kTnQS + col]);
+        const u32x2 hi = lds_read_tr(&sQ[(rb + 4) * kTnQS + col]);
+        qb[b] = u32x4{lo[0], lo[1], hi[0], hi[1]};
+      }
+#pragma unroll
+      for (int a = 0; a < NJ; ++a) {
+        const u32x2 lo = lds_read_tr(&sP[rb * PS + 16 * a + 4 * (sl & 3)]);
+        const u32x2 hi = lds_read_tr(&sP[(rb + 4) * PS + 16 * a + 4 * (sl & 3)]);
+        const u32x4 pa = u32x4{lo[0], lo[1], hi[0], hi[1]};
+        acc[a][0] = mfma16(pa, qb[0], acc[a][0]);
+        acc[a][1] = mfma16(pa, qb[1], acc[a][1]);
+      }
+    }
+  };
+
+  // Loads are issued unconditionally (a tile past the end reads nothing), so
+  // the compiler's wait counts stay exact and two tiles stay in flight.
+  u32x4 q0[QCH], p0[PCH], q1[QCH], p1[PCH];
+  load_pinned(0, q0, p0);
+  load_pinned(1, q1, p1);
+  for (int tile = 0; tile < ntiles; tile += 2) {
+    stage(q0, p0);
+    lds_barrier();
+    load_pinned(tile + 2, q0, p0);
+    compute();
+    lds_barrier();
+    if (tile + 1 >= ntiles) break;
+    stage(q1, p1);
+    lds_barrier();
+    load_pinned(tile + 3, q1, p1);
+    compute();
+    lds_barrier();
+  }
+
+  // this split's partial. C layout: col (Q column) = lane%16, row (j) = 4*(lane/16) + v
+  float* dst = p.part + (int64_t)blockIdx.y * R * Kd;
+#pragma unroll
+  for (int a = 0; a < NJ; ++a)
+#pragma unroll
+    for (int b = 0; b < 2; ++b) {
+      const int64_t k = k0 + 32 * wave + 16 * b + sl;
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const int j = 16 * a + 4 * g + v;
+        if (j < R && k < Kd) dst[(int64_t)j * Kd + k] = acc[a][b][v];
+      }
+    }
+
+}
+
+// out = s * (sum of the split partials, added in split order): one float4 of
+// outputs per thread with every split's load in flight at once. A kernel of
+// its own: the launch boundary makes the partials of all workgroups visible
+// (an in-kernel "last workgroup reduces" scheme needs device-scope release
+// fences, which write back the whole L2 of an XCD and cost far more here).
+__global__ __launch_bounds__(64) void k_tn_reduce(TnArgs p) {
+  const int64_t Kd = p.Kd, kq = Kd / 4;
+  const int R = p.r1 + p.r2;
+  const int64_t idx = (int64_t)blockIdx.x * 64 + threadIdx.x;
+  if (idx >= R * kq) return;
+  const int j = (int)(idx / kq);
+  const int64_t k = 4 * (idx - j * kq);
+  const float* src = p.part + (int64_t)j * Kd + k;
+  const int64_t sstride = (int64_t)R * Kd;
+  f32x4 sum = *reinterpret_cast<const f32x4*>(src);
+  int sp = 1;
+  for (; sp + 16 <= p.splits; sp += 16) {
+    f32x4 v[16];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) v[i] = *reinterpret_cast<const f32x4*>(src + (int64_t)(sp + i) * sstride);
+#pragma unroll
+    for (int i = 0; i < 16; ++i) sum += v[i];
+  }
+  for (; sp + 4 <= p.splits; sp += 4) {
+    f32x4 v[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) v[i] = *reinterpret_cast<const f32x4*>(src + (int64_t)(sp + i) * sstride);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) sum += v[i];
+  }
+  for (; sp < p.splits; ++sp) sum += *reinterpret_cast<const f32x4*>(src + (int64_t)sp * sstride);
+  const bool first = j < p.r1;
+  const float s = first ? p.s1 : p.s2;
+  float* out = first ? p.out1 : p.out2;
+  const int64_t jr = first ? j : j - p.r1;
+  const int64_t ldo = first ? p.ldo1 : p.ldo2;
+  sum *= s;
+  if (p.transposed) {
+#pragma unroll
+    for (int c = 0; c < 4; ++c) out[(k + c) * ldo + jr] = sum[c];
+  } else {
+    *reinterpret_cast<f32x4*>(out + jr * ldo + k) = sum;
+  }
+}
+
+hipError_t launch_skinny_tn(TnArgs a, hipStream_t st) {
+  const int R = a.r1 + a.r2;
+  const TnPlan pl = skinny_tn_plan(a.M, a.Kd, R);
+  a.rows = pl.rows;
+  a.splits = pl.splits;
+  const bool pv = (a.ldp % 8 == 0) && (R % 8 == 0) && ((reinterpret_cast<uintptr_t>(a.P) & 15) == 0);
+  dim3 grid((unsigned)pl.col_tiles, (unsigned)pl.splits);
+#define QL_TN(RPV)                                    \
+  do {                                                \
+    if (pv)                                           \
+      k_skinny_tn<RPV, true><<<grid, 256, 0, st>>>(a);  \
+    else                                              \
+      k_skinny_tn<RPV, false><<<grid, 256, 0, st>>>(a); \
+  } while (0)
+  if (R <= 16)
     QL_TN(16);
-  else if (r <= 32)
+  else if (R <= 32)
     QL_TN(32);
-  else if (r <= 64)
+  else if (R <= 64)
     QL_TN(64);
-  else if (r <= 128)
+  else if (R <= kTnMaxR)
     QL_TN(128);
-  else if (r <= 256)
-    QL_TN(256);
   else
     return hipErrorInvalidValue;
 #undef QL_TN
   return hipGetLastError();
 }
 
-// out = s * sum_splits part, summed in split order (deterministic).
-__global__ __launch_bounds__(256) void k_reduce_splits(const float* __restrict__ part, int splits, int r, int64_t Kd,
-                                                       float s, float* __restrict__ out, int transposed) {
+hipError_t launch_tn_reduce(TnArgs a, hipStream_t st) {
+  const int R = a.r1 + a.r2;
+  a.splits = skinny_tn_plan(a.M, a.Kd, R).splits;
+  const int64_t n = (int64_t)R * (a.Kd / 4);
+  if (n == 0) return hipSuccess;
+  k_tn_reduce<<<(unsigned)((n + 63) / 64), 64, 0, st>>>(a);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// Preparation of a backward call, one launch: the adapter transposes (B^T rows
+// for G = dY.B, A^T rows for the rank-r term of dX).
+
+__global__ __launch_bounds__(256) void k_prep(PrepJobs jobs) {
   const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  const int64_t total = (int64_t)r * Kd;
-  if (idx >= total) return;
-  float acc = 0.f;
-  for (int p = 0; p < splits; ++p) acc += part[(int64_t)p * total + idx];
-  acc *= s;
-  if (transposed) {
-    const int64_t j = idx / Kd, k = idx - j * Kd;
-    out[k * r + j] = acc;
-  } else {
-    out[idx] = acc;
+#pragma unroll
+  for (int i = 0; i < kMaxPrepJobs; ++i) {
+    if (i >= jobs.n) break;
+    const TransposeJob& j = jobs.job[i];
+    if (idx < j.R * j.C) {
+      const int64_t c = idx / j.R, rr = idx - c * j.R;
+      j.dst[idx] = j.src[rr * j.C + c];
+    }
   }
 }
 
-hipError_t launch_reduce_splits(const float* part, int splits, int r, int64_t Kd, float s, float* out, bool transposed,
-                                hipStream_t st) {
-  const int64_t total = (int64_t)r * Kd;
-  if (total == 0) return hipSuccess;
-  k_reduce_splits<<<(unsigned)((total + 255) / 256), 256, 0, st>>>(part, splits, r, Kd, s, out, transposed ? 1 : 0);
+hipError_t launch_prep(const PrepJobs& jobs, hipStream_t st) {
+  int64_t work = 0;
+  for (int i = 0; i < jobs.n; ++i) work = work > jobs.job[i].R * jobs.job[i].C ? work : jobs.job[i].R * jobs.job[i].C;
+  if (work == 0) return hipSuccess;
+  k_prep<<<(unsigned)((work + 255) / 256), 256, 0, st>>>(jobs);
   return hipGetLastError();
 }
 
@@ -259,20 +442,6 @@ __global__ __launch_bounds__(256) void k_fill_zero_f32(float* __restrict__ p, in
 hipError_t launch_fill_zero_f32(float* p, int64_t n, hipStream_t st) {
   if (n == 0) return hipSuccess;
   k_fill_zero_f32<<<(unsigned)((n + 255) / 256), 256, 0, st>>>(p, n);
-  return hipGetLastError();
-}
-
-__global__ __launch_bounds__(256) void k_transpose_bf16(const uint16_t* __restrict__ src, int64_t R, int64_t C,
-                                                        uint16_t* __restrict__ dst) {
-  const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (idx >= R * C) return;
-  const int64_t c = idx / R, rr = idx - c * R;
-  dst[idx] = src[rr * C + c];
-}
-
-hipError_t launch_transpose_bf16(const uint16_t* src, int64_t R, int64_t C, uint16_t* dst, hipStream_t st) {
-  if (R * C == 0) return hipSuccess;
-  k_transpose_bf16<<<(unsigned)((R * C + 255) / 256), 256, 0, st>>>(src, R, C, dst);
   return hipGetLastError();
 }
 

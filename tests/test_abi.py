@@ -107,3 +107,24 @@ def test_status_strings():
     for s in (0, -1, -2, -3):
         assert len(lib.qlora_status_string(s)) > 0
     assert np.isscalar(lib.qlora_workspace_size(C.OP_MLP_BACKWARD, 16, 256, 512, 8))
+
+
+@pytest.mark.parametrize("op", [C.OP_BACKWARD, C.OP_MLP_BACKWARD])
+def test_workspace_size_defined_for_every_batch(op):
+    # host-side planning of the row splits must handle every M, including 0
+    lib = C.lib()
+    for M in (0, 1, 63, 64, 65, 4096, 100_000):
+        for K, N in ((64, 8), (4096, 4096), (4096, 14336)):
+            for r in (1, 8, 16, 127, 128, 129, 256):
+                need = lib.qlora_workspace_size(op, M, K, N, r)
+                assert need > 0 and need % 256 == 0
+                # the workspace holds at least the rank-r intermediates it must keep
+                assert need >= 2 * M * r
+
+
+def test_forward_rejects_oversized_weights():
+    lib = C.lib()
+    p = ctypes.c_void_p(0x10000)
+    for K, N in ((1 << 24, 8), (64, (1 << 23) + 8), (1 << 20, 1 << 13)):
+        L = C.QLoraLayerC(0x10000, 0x10000, 0x10000, 0x10000, K, N, 16, 2.0)
+        assert lib.qlora_forward(ctypes.byref(L), p, 4, p, p, None, 0, None) == C.QLORA_EINVAL

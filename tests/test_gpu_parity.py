@@ -124,6 +124,8 @@ def test_linear_tiny_workload_full_oracle():
     (260, 512, 512, 64),
     (129, 320, 512, 128),
     (64, 128, 256, 256),    # largest rank
+    (2000, 1024, 384, 16),  # many row splits in the rank reductions, ragged last split
+    (700, 448, 200, 132),   # rank > 128 (reductions in chunks), rank % 8 != 0
 ])
 def test_linear_ragged_shapes_full_oracle(M, K, N, r):
     _announce(f"linear ragged M={M} K={K} N={N} r={r}")
@@ -214,6 +216,15 @@ def test_mlp_small_full_oracle():
 def test_mlp_ragged_full_oracle():
     _announce("mlp ragged M=130 H=192 I=320 r=8")
     errs = _mlp_case(random_mlp(78, 130, 192, 320, 8))
+    assert max(errs.values()) <= TOL, errs
+
+
+@pytest.mark.parametrize("r", [72, 132, 200])
+def test_mlp_high_rank_full_oracle(r):
+    # 2r > 128: gate/up dA reductions run as separate launches; r = 200 also
+    # splits the forward's paired Z = X.[A_g; A_u]^T (2r > 256)
+    _announce(f"mlp high rank M=200 H=128 I=256 r={r}")
+    errs = _mlp_case(random_mlp(90 + r, 200, 128, 256, r))
     assert max(errs.values()) <= TOL, errs
 
 

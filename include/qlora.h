@@ -28,8 +28,8 @@
  *     contiguous, 16-byte aligned. bf16 tensors are passed as uint16_t bit
  *     patterns. The library allocates no memory; scratch space comes from the
  *     caller's workspace (size from qlora_workspace_size).
- *   - Shapes: K % 64 == 0, N % 8 == 0, 1 <= r <= 256, K and N <= 2^23,
- *     N*K <= 2^32, M >= 0 (M == 0 is a no-op; a backward then writes zero
+ *   - Shapes: K % 64 == 0, N % 8 == 0, 1 <= r <= 256, K and N <= 2^21,
+ *     N*K <= 2^31, M >= 0 (M == 0 is a no-op; a backward then writes zero
  *     gradients). Anything else returns QLORA_EINVAL before any launch.
  *   - Every call enqueues its kernels on `stream` (a hipStream_t, 0 = the
  *     null stream) and returns without synchronising. Launch failures return

@@ -62,8 +62,8 @@ hipError_t timed(const char* name, hipStream_t st, F&& f) {
 #define QL_LAUNCH(name, st, expr) QL_CHECK(timed(name, st, [&]() { return (expr); }))
 
 // Size limits keeping every buffer offset the kernels form within 32 bits.
-constexpr int64_t kMaxDim = int64_t(1) << 23;
-constexpr int64_t kMaxWeight = int64_t(1) << 32;
+constexpr int64_t kMaxDim = int64_t(1) << 21;
+constexpr int64_t kMaxWeight = int64_t(1) << 31;
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 

@@ -158,6 +158,47 @@ __device__ __forceinline__ void lds_barrier() {
   __builtin_amdgcn_s_barrier();
 }
 
+// ---------------------------------------------------------------------------
+// Operand and store helpers of the GEMM tiles
+
+// 8 bf16 of row `row` (-1: none) of a bf16 matrix with row stride ld, columns
+// c..c+7 (zero at and beyond r). ALIGNED (r and ld multiples of 8, base 16-byte
+// aligned): one 16-byte load; otherwise eight 2-byte loads.
+template <bool ALIGNED>
+__device__ __forceinline__ u32x4 rank8(__amdgpu_buffer_rsrc_t rs, int64_t row, int64_t ld, int r, int c) {
+  if (ALIGNED) {
+    const int off = (row >= 0 && c < r) ? (int)((row * ld + c) * 2) : kOff;
+    return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, off, 0, 0));
+  }
+  uint32_t w[4];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const int e0 = c + 2 * q, e1 = e0 + 1;
+    const int o0 = (row >= 0 && e0 < r) ? (int)((row * ld + e0) * 2) : kOff;
+    const int o1 = (row >= 0 && e1 < r) ? (int)((row * ld + e1) * 2) : kOff;
+    const uint32_t lo = __builtin_amdgcn_raw_buffer_load_b16(rs, o0, 0, 0);
+    const uint32_t hi = __builtin_amdgcn_raw_buffer_load_b16(rs, o1, 0, 0);
+    w[q] = lo | (hi << 16);
+  }
+  return u32x4{w[0], w[1], w[2], w[3]};
+}
+
+// s * v (8 bf16) as a sum of two bf16 vectors hi + lo (|s*v - hi - lo| <= 2^-16 |s*v|;
+// lo == 0 when s is a power of two), so that s can ride on an MFMA operand.
+__device__ __forceinline__ void split_scaled(const u32x4 v, float s, u32x4& hi, u32x4& lo) {
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const float a = bf16_lo(v[q]) * s, b = bf16_hi(v[q]) * s;
+    const uint32_t hb = pack_bf16x2(a, b);
+    hi[q] = hb;
+    lo[q] = pack_bf16x2(a - bf16_lo(hb), b - bf16_hi(hb));
+  }
+}
+
+__device__ __forceinline__ void store4(__amdgpu_buffer_rsrc_t rs, int off, const float (&v)[4]) {
+  __builtin_amdgcn_raw_buffer_store_b64(u32x2{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])}, rs, off, 0, 0);
+}
+
 __device__ __forceinline__ float sigmoid_f(float z) { return 1.0f / (1.0f + expf(-z)); }
 
 }  // namespace qlora

@@ -1,0 +1,404 @@
+// Backward fused-dequant GEMM of the QLoRA layer on gfx950:
+//   dX = dY . What + s . G . A                  (G = dY.B from skinny_nt)
+// with two variants: a concatenated reduction over two (dY, W) pairs (the
+// gate and up projections of the SwiGLU block feed one dX), and the SwiGLU
+// backward applied to the down projection's product (dh never stored):
+//   dg = dh * u * sig(g) * (1 + g * (1 - sig(g))),   du = dh * silu(g).
+//
+// "Unsloth" wiki entry, Theory: the hand-derived LoRA backward and the fused
+// SwiGLU block; "Rev vs unsloth", fused quantized-LoRA card: no dequantized
+// weight in HBM; "Unsloth vs PyTorch" video, 1:35-2:00: the rank-r term goes
+// through the skinny G and A, never through the N x K product B.A.
+//
+// Design (one workgroup = 4 waves, 256 output columns x 256 tokens, the
+// reduction over N in steps of 64):
+//   * each wave owns 64 output columns -- one 64-column block of every weight
+//     row -- and all 256 tokens (8 MFMA fragments), 256 fp32 accumulators per
+//     lane in AGPRs;
+//   * the reduction runs over weight rows, so a lane needs 8 consecutive rows
+//     of one column: lane l dequantizes weight row n0 + l of the wave's block
+//     (one NF4 table per lane and step), the wave writes its private 64 x 64
+//     bf16 tile to LDS (XOR-swizzled, conflict-free) and reads it back
+//     column-wise with ds_read_b64_tr_b16. The tile is private to the wave:
+//     no barrier guards it;
+//   * the dY tile (256 tokens x 64) is copied by buffer_load ... lds, double
+//     buffered; codes run a step ahead;
+//   * the compiler must assume a transposed LDS read may touch memory an
+//     LDS copy is still writing, and waits for every copy in flight before
+//     one. So each step starts by waiting for the copies of that step,
+//     reads all of its weight operands from the tile (16 transposed reads),
+//     and only then issues the next step's copies and code loads. During the
+//     16 x 4 MFMAs of the step, the dY fragments of the next substep are read
+//     (plain reads) and the next step's weight rows are dequantized straight
+//     into the other tile buffer.
+// Tile edges use the buffer range check: rows past N and columns past K read
+// zero, tokens past M drop their stores.
+#include <type_traits>
+
+#include "common.hpp"
+#include "internal.hpp"
+
+namespace qlora {
+
+namespace {
+
+constexpr int kTok = 256;                  // tokens per workgroup
+constexpr int kStep = 64;                  // reduction rows per step
+constexpr int kRowB = kStep * 2;           // bytes of one token row of the dY tile
+constexpr int kBufB = kTok * kRowB;        // 32 KB per dY buffer
+constexpr int kWRowB = 128;                // one weight row of a wave's tile (64 columns)
+constexpr int kWBufB = kStep * kWRowB;     // 8 KB per wave and buffer
+constexpr size_t kLds = 2 * (size_t)kBufB + 2 * 4 * (size_t)kWBufB;  // 128 KB: dY x2, weight tiles 4 waves x2
+
+enum BwdMode { kPlain = 0, kConcat = 1, kSwiGLU = 2 };
+
+struct BwdArgs {
+  const uint16_t* dY[2];  // [M, N] per source
+  WSrc w[2];              // lora_i = A^T [K, r], lora_j = G [M, r] (row stride ldj)
+  int64_t M, K, N;        // dX [M, K]; reduction over N per source
+  uint16_t* out0;         // dX | dg
+  uint16_t* out1;         // du
+  const uint16_t* g;      // SwiGLU: saved g, u [M, K]
+  const uint16_t* u;
+};
+
+// Weight tile swizzle: 16-byte chunk q of row j is stored at chunk q ^ wsw(j).
+// Keeps the row writes (8 rows per LDS cycle) and the transposed reads
+// (4 rows x 2 column groups per cycle) on distinct banks.
+__device__ __forceinline__ int wsw(int j) { return (4 * ((j >> 1) & 1)) | (2 * ((j >> 2) & 1)); }
+
+template <int MODE, int RP, bool ALIGNED>
+__global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_per_eu(1, 1)))
+void k_qgemm_bwd(BwdArgs p) {
+  extern __shared__ __attribute__((aligned(16))) uint8_t smem[];  // dY [2], then weight tiles [2][4 waves]
+  constexpr int NSRC = MODE == kConcat ? 2 : 1;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int h = lane >> 5, jl = lane & 31;
+  const int64_t M = p.M, K = p.K, N = p.N;
+  const int64_t nJ = (M + kTok - 1) / kTok;
+  const int64_t it = blockIdx.x / nJ, jt = blockIdx.x - it * nJ;
+  const int64_t i0 = it * 256, j0 = jt * kTok;
+  const int sps = (int)((N + kStep - 1) / kStep);  // steps per source
+  const int nsteps = sps * NSRC;
+  const bool ragged = (N % kStep) != 0;
+  const int64_t rows_here = (M - j0) < kTok ? (M - j0) : kTok;
+  const int64_t kc = i0 + 64 * wave;  // this wave's first output column (a 64-column block)
+  const bool k_ok = kc < K;
+  uint8_t* const wtile = smem + 2 * kBufB + wave * kWBufB;  // buffer b at + b * 4 * kWBufB
+
+  // ---- dY copies (as the forward's activation copies). Lane l of instruction
+  // i fills row 64w + 8i + l/8, physical chunk l%8 = logical chunk
+  // (l%8) ^ ((row>>1)&7). In a ragged last step the chunks past N read nothing.
+  int offY[8], offYl[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int row = 64 * wave + 8 * i + (lane >> 3);
+    const int c = (lane & 7) ^ ((row >> 1) & 7);
+    offY[i] = (int)((int64_t)row * N * 2 + 16 * c);
+    offYl[i] = (int64_t)(sps - 1) * kStep + 8 * c < N ? offY[i] : kOff;
+  }
+  auto dma_y = [&](int step, int buf) {
+    const int src = NSRC > 1 && step >= sps ? 1 : 0;
+    const int sl = step - src * sps;
+    const bool last = ragged && sl == sps - 1;
+    const __amdgpu_buffer_rsrc_t ry = make_rsrc(p.dY[src ? NSRC - 1 : 0] + j0 * N, rows_here * N * 2);
+    uint8_t* base = smem + buf * kBufB + (64 * wave) * kRowB;
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(ry, (__attribute__((address_space(3))) void*)(base + 8 * i * kRowB), 16,
+                                               last ? offYl[i] : offY[i], sl * kRowB, 0, 0);
+  };
+
+  // ---- codes and absmax of weight row n0 + lane, block kc/64 (32 bytes + 4).
+  // Per-lane offsets are loop-invariant; each step gets buffer resources based
+  // at its first weight row and sized to the rows that exist, so rows past N
+  // read zero (zero codes and absmax give an all-zero table) with no per-step
+  // VGPR arithmetic next to loads in flight.
+  const int offC = k_ok ? (int)((int64_t)lane * (K / 2) + kc / 2) : kOff;
+  const int offA = k_ok ? (int)(((int64_t)lane * (K / kBlock) + kc / kBlock) * 4) : kOff;
+  auto load_codes = [&](int step, u32x4 (&cr)[2], float& am) {
+    const int src = NSRC > 1 && step >= sps ? 1 : 0;
+    const int64_t n0 = (int64_t)(step - src * sps) * kStep;
+    const WSrc& w = p.w[src ? NSRC - 1 : 0];
+    const __amdgpu_buffer_rsrc_t rc = make_rsrc(w.codes + n0 * (K / 2), (N - n0) * (K / 2));
+    const __amdgpu_buffer_rsrc_t ra = make_rsrc(w.absmax + n0 * (K / kBlock), (N - n0) * (K / kBlock) * 4);
+    cr[0] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rc, offC, 0, 0));
+    cr[1] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rc, offC, 16, 0));
+    am = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(ra, offA, 0, 0));
+  };
+
+  f32x16 acc[2][8];
+#pragma unroll
+  for (int f = 0; f < 2; ++f)
+#pragma unroll
+    for (int j = 0; j < 8; ++j) acc[f][j] = f32x16{};
+
+  // ---- the rank-r term first, by MFMA: acc += (s.A^T rows) . (G rows)^T
+#pragma unroll
+  for (int src = 0; src < NSRC; ++src) {
+    const WSrc& w = p.w[src];
+    const __amdgpu_buffer_rsrc_t rAt = make_rsrc(w.lora_i, K * (int64_t)w.r * 2);
+    const __amdgpu_buffer_rsrc_t rG = make_rsrc(w.lora_j + j0 * w.ldj, rows_here * w.ldj * 2);
+    const int c0 = 8 * h;
+#pragma unroll
+    for (int rr = 0; rr < RP; rr += 16) {
+      u32x4 ah[2], al[2];
+#pragma unroll
+      for (int f = 0; f < 2; ++f) {
+        const int64_t ir = kc + 32 * f + jl;
+        const u32x4 av = rank8<ALIGNED>(rAt, ir < K ? ir : -1, w.r, w.r, rr + c0);
+        split_scaled(av, w.s, ah[f], al[f]);
+      }
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const int64_t mr = 32 * j + jl;
+        const u32x4 z = rank8<ALIGNED>(rG, mr < rows_here ? mr : -1, w.ldj, w.r, rr + c0);
+#pragma unroll
+        for (int f = 0; f < 2; ++f) {
+          acc[f][j] = mfma32(ah[f], z, acc[f][j]);
+          acc[f][j] = mfma32(al[f], z, acc[f][j]);
+        }
+      }
+    }
+  }
+
+  // ---- operand reads.
+  // B (dY): token 32j + jl, reduction rows 16ks + 8h .. +7 = chunk 2ks + h.
+  int offB[4];
+#pragma unroll
+  for (int ks = 0; ks < 4; ++ks) offB[ks] = jl * kRowB + 16 * ((2 * ks + h) ^ ((jl >> 1) & 7));
+  u32x4 bv[2][8];
+  auto read_b = [&](int buf, int ks, u32x4 (&dst)[8]) {
+    const uint8_t* bx = smem + buf * kBufB + offB[ks];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) dst[j] = *reinterpret_cast<const u32x4*>(bx + 32 * j * kRowB);
+  };
+  // A (weights): fragment f = columns 32f .. 32f+31 of the wave's block, column
+  // 32f + l%32, rows 16ks + 8h .. +7, as two transposed reads (rows +0..3, +4..7).
+  // Within a 16-lane group, lane s points at row (s>>2) (+4), columns 4(s&3)..+3
+  // of a 16-column group; the swizzle only depends on the row mod 8.
+  int offW[2][2];
+  {
+    const int g = lane >> 4, s = lane & 15;
+#pragma unroll
+    for (int f = 0; f < 2; ++f)
+#pragma unroll
+      for (int hi = 0; hi < 2; ++hi) {
+        const int row = 8 * (g >> 1) + (s >> 2) + 4 * hi;
+        const int col = 32 * f + 16 * (g & 1) + 4 * (s & 3);
+        offW[f][hi] = row * kWRowB + 16 * ((col >> 3) ^ wsw(row)) + 2 * (col & 7);
+      }
+  }
+  u32x4 av[4][2];  // the whole step's weight operands
+  auto read_a = [&](int wb, int ks) {
+    const uint8_t* wt = wtile + wb * 4 * kWBufB;
+#pragma unroll
+    for (int f = 0; f < 2; ++f) {
+      const u32x2 lo = lds_read_tr(wt + offW[f][0] + ks * 16 * kWRowB);
+      const u32x2 hi = lds_read_tr(wt + offW[f][1] + ks * 16 * kWRowB);
+      av[ks][f] = u32x4{lo[0], lo[1], hi[0], hi[1]};
+    }
+  };
+  // weight row n0 + lane of the next step: chunk q -> tile buffer wb
+  const int wsl = wsw(lane);
+  auto dequant_write = [&](int wb, const u32x4 (&cr)[2], const Nf4Lut& lut, int q0) {
+    uint8_t* row = wtile + wb * 4 * kWBufB + lane * kWRowB;
+#pragma unroll
+    for (int q = q0; q < q0 + 2; ++q)
+      *reinterpret_cast<u32x4*>(row + 16 * (q ^ wsl)) = dequant8(cr[q >> 2][q & 3], lut);
+  };
+  auto mfmas = [&](const u32x4 (&a)[2], const u32x4 (&b)[8]) {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      acc[0][j] = mfma32(a[0], b[j], acc[0][j]);
+      acc[1][j] = mfma32(a[1], b[j], acc[1][j]);
+    }
+  };
+  // issue order inside a substep: 16 MFMAs, each followed by a slice of the
+  // other work (LDS reads, LDS writes, global loads, VALU)
+  auto interleave = [&](auto nds_read, auto nds_write, auto nvmem, auto nvalu) {
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      if (i < decltype(nds_read)::value) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      if (i < decltype(nds_write)::value) __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);
+      if (i < decltype(nvmem)::value) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x002, decltype(nvalu)::value, 0);
+    }
+  };
+  using I0 = std::integral_constant<int, 0>;
+  using I2 = std::integral_constant<int, 2>;
+  using I4 = std::integral_constant<int, 4>;
+  using I6 = std::integral_constant<int, 6>;
+  using I8 = std::integral_constant<int, 8>;
+
+  // Step s: dY from buffer s&1, weights from tile buffer s&1; the codes of
+  // step s+1 (cc, loaded during step s-1) are dequantized into tile buffer
+  // (s+1)&1; the codes of step s+2 go to cn and the dY copies of step s+1 to
+  // buffer (s+1)&1, both issued after this step's transposed reads.
+  auto body = [&](int s, const u32x4 (&cc)[2], float ac, u32x4 (&cn)[2], float& an) {
+    const int b0 = s & 1, b1 = b0 ^ 1;
+    const int s1 = s + 1 < nsteps ? s + 1 : nsteps - 1;
+    const int s2 = s + 2 < nsteps ? s + 2 : nsteps - 1;
+    __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));  // this wave's dY copies of step s, codes of step s+1
+    __builtin_amdgcn_s_waitcnt(0xC07F);          // this wave's tile writes
+    __builtin_amdgcn_s_barrier();                // every wave's copies landed; buffer b1 is free
+    // operands of substep 0 first, so its MFMAs can start while the rest lands
+    read_b(b0, 0, bv[0]);
+    read_a(b0, 0);
+    read_a(b0, 1);
+    read_a(b0, 2);
+    read_a(b0, 3);
+    __builtin_amdgcn_sched_barrier(0);  // the transposed reads go out before any new copy
+    load_codes(s2, cn, an);
+    dma_y(s1, b1);
+    __builtin_amdgcn_sched_barrier(0);
+    // substep 0 (also the table of step s+1's rows)
+    const Nf4Lut lut = make_lut(ac);
+    read_b(b0, 1, bv[1]);
+    dequant_write(b1, cc, lut, 0);
+    mfmas(av[0], bv[0]);
+    interleave(I8{}, I2{}, I0{}, I6{});
+    __builtin_amdgcn_sched_barrier(0);
+    // substep 1
+    read_b(b0, 2, bv[0]);
+    dequant_write(b1, cc, lut, 2);
+    mfmas(av[1], bv[1]);
+    interleave(I8{}, I2{}, I0{}, I4{});
+    __builtin_amdgcn_sched_barrier(0);
+    // substep 2
+    read_b(b0, 3, bv[1]);
+    dequant_write(b1, cc, lut, 4);
+    mfmas(av[2], bv[0]);
+    interleave(I8{}, I2{}, I0{}, I4{});
+    __builtin_amdgcn_sched_barrier(0);
+    // substep 3
+    dequant_write(b1, cc, lut, 6);
+    mfmas(av[3], bv[1]);
+    interleave(I0{}, I2{}, I0{}, I4{});
+    __builtin_amdgcn_sched_barrier(0);
+  };
+
+  // Prologue: codes of steps 0 and 1, dY of step 0; tile buffer 0 = step 0.
+  u32x4 cA[2], cB[2];
+  float aA, aB;
+  load_codes(0, cA, aA);
+  load_codes(nsteps > 1 ? 1 : 0, cB, aB);
+  dma_y(0, 0);
+  {
+    const Nf4Lut lut0 = make_lut(aA);
+#pragma unroll
+    for (int q = 0; q < 8; q += 2) dequant_write(0, cA, lut0, q);
+  }
+  for (int s = 0; s < nsteps; s += 2) {
+    body(s, cB, aB, cA, aA);
+    if (s + 1 < nsteps) body(s + 1, cA, aA, cB, aB);
+  }
+
+  // ---- epilogue (no control flow): bf16 stores, or the SwiGLU backward
+  const __amdgpu_buffer_rsrc_t rO0 = make_rsrc(p.out0 + j0 * K, rows_here * K * 2);
+  const __amdgpu_buffer_rsrc_t rO1 = make_rsrc(MODE == kSwiGLU ? p.out1 + j0 * K : p.out0,
+                                               MODE == kSwiGLU ? rows_here * K * 2 : 0);
+  const __amdgpu_buffer_rsrc_t rGs = make_rsrc(MODE == kSwiGLU ? p.g + j0 * K : p.out0,
+                                               MODE == kSwiGLU ? rows_here * K * 2 : 0);
+  const __amdgpu_buffer_rsrc_t rUs = make_rsrc(MODE == kSwiGLU ? p.u + j0 * K : p.out0,
+                                               MODE == kSwiGLU ? rows_here * K * 2 : 0);
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const int64_t mr = 32 * j + jl;
+    const bool m_ok = mr < rows_here;
+#pragma unroll
+    for (int f = 0; f < 2; ++f) {
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int64_t ic = kc + 32 * f + 8 * q + 4 * h;
+        const int off = (m_ok && ic < K) ? (int)((mr * K + ic) * 2) : kOff;
+        float v[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) v[e] = acc[f][j][4 * q + e];
+        if (MODE == kSwiGLU) {
+          const u32x2 gw = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(rGs, off, 0, 0));
+          const u32x2 uw = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(rUs, off, 0, 0));
+          const float gv[4] = {bf16_lo(gw[0]), bf16_hi(gw[0]), bf16_lo(gw[1]), bf16_hi(gw[1])};
+          const float uv[4] = {bf16_lo(uw[0]), bf16_hi(uw[0]), bf16_lo(uw[1]), bf16_hi(uw[1])};
+          float dg[4], du[4];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const float sg = sigmoid_f(gv[e]);
+            dg[e] = v[e] * uv[e] * sg * (1.0f + gv[e] * (1.0f - sg));
+            du[e] = v[e] * gv[e] * sg;
+          }
+          store4(rO0, off, dg);
+          store4(rO1, off, du);
+        } else {
+          store4(rO0, off, v);
+        }
+      }
+    }
+  }
+}
+
+template <int MODE, int RP, bool ALIGNED>
+hipError_t launch_rp(const BwdArgs& a, hipStream_t st) {
+  static bool attr_done = false;
+  if (!attr_done) {
+    hipError_t e = hipFuncSetAttribute((const void*)k_qgemm_bwd<MODE, RP, ALIGNED>,
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)kLds);
+    if (e != hipSuccess) return e;
+    attr_done = true;
+  }
+  const int64_t nI = (a.K + 255) / 256, nJ = (a.M + kTok - 1) / kTok;
+  if (nI * nJ == 0) return hipSuccess;
+  k_qgemm_bwd<MODE, RP, ALIGNED><<<(unsigned)(nI * nJ), 256, kLds, st>>>(a);
+  return hipGetLastError();
+}
+
+bool rank_rows_aligned(const WSrc& w) {
+  return w.r % 8 == 0 && w.ldj % 8 == 0 && (reinterpret_cast<uintptr_t>(w.lora_j) & 15) == 0 &&
+         (reinterpret_cast<uintptr_t>(w.lora_i) & 15) == 0;
+}
+
+template <int MODE, int RP>
+hipError_t launch_al(const BwdArgs& a, hipStream_t st) {
+  const bool aligned = rank_rows_aligned(a.w[0]) && rank_rows_aligned(a.w[1]);
+  return aligned ? launch_rp<MODE, RP, true>(a, st) : launch_rp<MODE, RP, false>(a, st);
+}
+
+template <int MODE>
+hipError_t launch(const BwdArgs& a, hipStream_t st) {
+  const int r = a.w[0].r > a.w[1].r ? a.w[0].r : a.w[1].r;
+  if (r <= 16) return launch_al<MODE, 16>(a, st);
+  if (r <= 32) return launch_al<MODE, 32>(a, st);
+  if (r <= 64) return launch_al<MODE, 64>(a, st);
+  if (r <= 128) return launch_al<MODE, 128>(a, st);
+  if (r <= 256) return launch_al<MODE, 256>(a, st);
+  return hipErrorInvalidValue;
+}
+
+}  // namespace
+
+hipError_t launch_gemm_bwd(const uint16_t* dY0, WSrc w0, const uint16_t* dY1, WSrc w1, int64_t M, int64_t K,
+                           int64_t N, uint16_t* dX, hipStream_t st) {
+  BwdArgs a{};
+  a.dY[0] = dY0;
+  a.dY[1] = dY1 ? dY1 : dY0;
+  a.w[0] = w0;
+  a.w[1] = dY1 ? w1 : w0;
+  a.M = M, a.K = K, a.N = N;
+  a.out0 = dX;
+  return dY1 ? launch<kConcat>(a, st) : launch<kPlain>(a, st);
+}
+
+hipError_t launch_gemm_bwd_swiglu(const uint16_t* dY, WSrc w, int64_t M, int64_t K, int64_t N, const uint16_t* g,
+                                  const uint16_t* u, uint16_t* dg, uint16_t* du, hipStream_t st) {
+  BwdArgs a{};
+  a.dY[0] = a.dY[1] = dY;
+  a.w[0] = a.w[1] = w;
+  a.M = M, a.K = K, a.N = N;
+  a.out0 = dg, a.out1 = du;
+  a.g = g, a.u = u;
+  return launch<kSwiGLU>(a, st);
+}
+
+}  // namespace qlora

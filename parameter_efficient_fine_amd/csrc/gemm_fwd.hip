@@ -52,43 +52,6 @@ struct FwdArgs {
 // (out-of-range lanes read zero or drop their store); divergent branches there
 // would push the 256 accumulators out of AGPRs and spill the main loop.
 
-// 8 bf16 of row `row` (-1: none) of a [rows, r] bf16 matrix, columns c..c+7 (zero beyond r).
-// ALIGNED (r % 8 == 0): one 16-byte load; otherwise eight 2-byte loads.
-template <bool ALIGNED>
-__device__ __forceinline__ u32x4 rank8(__amdgpu_buffer_rsrc_t rs, int64_t row, int r, int c) {
-  if (ALIGNED) {
-    const int off = (row >= 0 && c < r) ? (int)((row * r + c) * 2) : kOff;
-    return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, off, 0, 0));
-  }
-  uint32_t w[4];
-#pragma unroll
-  for (int q = 0; q < 4; ++q) {
-    const int e0 = c + 2 * q, e1 = e0 + 1;
-    const int o0 = (row >= 0 && e0 < r) ? (int)((row * r + e0) * 2) : kOff;
-    const int o1 = (row >= 0 && e1 < r) ? (int)((row * r + e1) * 2) : kOff;
-    const uint32_t lo = __builtin_amdgcn_raw_buffer_load_b16(rs, o0, 0, 0);
-    const uint32_t hi = __builtin_amdgcn_raw_buffer_load_b16(rs, o1, 0, 0);
-    w[q] = lo | (hi << 16);
-  }
-  return u32x4{w[0], w[1], w[2], w[3]};
-}
-
-// s * v (8 bf16) as a sum of two bf16 vectors hi + lo (|s*v - hi - lo| <= 2^-16 |s*v|;
-// lo == 0 when s is a power of two), so that s can ride on an MFMA operand.
-__device__ __forceinline__ void split_scaled(const u32x4 v, float s, u32x4& hi, u32x4& lo) {
-#pragma unroll
-  for (int q = 0; q < 4; ++q) {
-    const float a = bf16_lo(v[q]) * s, b = bf16_hi(v[q]) * s;
-    const uint32_t hb = pack_bf16x2(a, b);
-    hi[q] = hb;
-    lo[q] = pack_bf16x2(a - bf16_lo(hb), b - bf16_hi(hb));
-  }
-}
-
-__device__ __forceinline__ void store4(__amdgpu_buffer_rsrc_t rs, int off, const float (&v)[4]) {
-  __builtin_amdgcn_raw_buffer_store_b64(u32x2{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])}, rs, off, 0, 0);
-}
-
 template <bool GATEUP, int RP, bool ALIGNED>
 __global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_per_eu(1, 1)))
 void k_qgemm_fwd(FwdArgs p) {
@@ -168,15 +131,16 @@ void k_qgemm_fwd(FwdArgs p) {
       for (int f = 0; f < 2; ++f) {
         const bool second = GATEUP && f == 1;
         const int64_t ir = nb[f] + jl;
-        const u32x4 bv = rank8<ALIGNED>(second ? rB1 : rB0, ir < N ? ir : -1, second ? p.w1.r : p.w0.r, rr + c0);
+        const int rs = second ? p.w1.r : p.w0.r;
+        const u32x4 bv = rank8<ALIGNED>(second ? rB1 : rB0, ir < N ? ir : -1, rs, rs, rr + c0);
         split_scaled(bv, second ? p.w1.s : p.w0.s, bh[f], bl[f]);
       }
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
         const int64_t mr = 32 * j + jl;
         const int64_t zrow = mr < rows_here ? mr : -1;
-        const u32x4 z0 = rank8<ALIGNED>(rZ0, zrow, p.w0.r, rr + c0);
-        const u32x4 z1 = GATEUP ? rank8<ALIGNED>(rZ1, zrow, p.w1.r, rr + c0) : z0;
+        const u32x4 z0 = rank8<ALIGNED>(rZ0, zrow, p.w0.r, p.w0.r, rr + c0);
+        const u32x4 z1 = GATEUP ? rank8<ALIGNED>(rZ1, zrow, p.w1.r, p.w1.r, rr + c0) : z0;
         acc[0][j] = mfma32(bh[0], z0, acc[0][j]);
         acc[0][j] = mfma32(bl[0], z0, acc[0][j]);
         acc[1][j] = mfma32(bh[1], z1, acc[1][j]);

@@ -125,6 +125,6 @@ def test_workspace_size_defined_for_every_batch(op):
 def test_forward_rejects_oversized_weights():
     lib = C.lib()
     p = ctypes.c_void_p(0x10000)
-    for K, N in ((1 << 24, 8), (64, (1 << 23) + 8), (1 << 20, 1 << 13)):
+    for K, N in ((1 << 22, 8), (64, (1 << 21) + 8), (1 << 20, 1 << 12)):
         L = C.QLoraLayerC(0x10000, 0x10000, 0x10000, 0x10000, K, N, 16, 2.0)
         assert lib.qlora_forward(ctypes.byref(L), p, 4, p, p, None, 0, None) == C.QLORA_EINVAL

@@ -25,12 +25,12 @@
 //     buffered; codes run a step ahead;
 //   * the compiler must assume a transposed LDS read may touch memory an
 //     LDS copy is still writing, and waits for every copy in flight before
-//     one. So each step starts by waiting for the copies of that step,
-//     reads all of its weight operands from the tile (16 transposed reads),
-//     and only then issues the next step's copies and code loads. During the
-//     16 x 4 MFMAs of the step, the dY fragments of the next substep are read
-//     (plain reads) and the next step's weight rows are dequantized straight
-//     into the other tile buffer.
+//     one. So all 16 transposed reads of a step are issued together, during
+//     the previous step's last 16 MFMAs, right after that step's barrier (by
+//     which the copies they would wait for have landed), and the next copies
+//     are issued after them. During the MFMAs, the dY fragments of the next
+//     substep are read (plain reads) and the next step's weight rows are
+//     dequantized straight into the other tile buffer.
 // Tile edges use the buffer range check: rows past N and columns past K read
 // zero, tokens past M drop their stores.
 #include <type_traits>
@@ -229,37 +229,31 @@ void k_qgemm_bwd(BwdArgs p) {
   };
   using I0 = std::integral_constant<int, 0>;
   using I2 = std::integral_constant<int, 2>;
+  using I3 = std::integral_constant<int, 3>;
   using I4 = std::integral_constant<int, 4>;
   using I6 = std::integral_constant<int, 6>;
   using I8 = std::integral_constant<int, 8>;
+  using I12 = std::integral_constant<int, 12>;
 
-  // Step s: dY from buffer s&1, weights from tile buffer s&1; the codes of
-  // step s+1 (cc, loaded during step s-1) are dequantized into tile buffer
-  // (s+1)&1; the codes of step s+2 go to cn and the dY copies of step s+1 to
-  // buffer (s+1)&1, both issued after this step's transposed reads.
+  // Step s: dY from buffer s&1 and weights from tile buffer s&1, both read
+  // ahead (entering the step, av holds all of its weight operands and bv[0]
+  // its first dY fragments). During substeps 0-2 the codes of step s+1 (cc,
+  // loaded during step s-1) are dequantized into tile buffer (s+1)&1 and the
+  // codes of step s+2 are requested. Substep 3 starts with the step's only
+  // barrier (the dY copies of step s+1 landed, every wave is done with dY
+  // buffer s&1); its MFMAs then overlap the reads of step s+1's operands,
+  // after which -- never before a transposed read -- the dY copies of step
+  // s+2 go to buffer s&1.
   auto body = [&](int s, const u32x4 (&cc)[2], float ac, u32x4 (&cn)[2], float& an) {
     const int b0 = s & 1, b1 = b0 ^ 1;
-    const int s1 = s + 1 < nsteps ? s + 1 : nsteps - 1;
     const int s2 = s + 2 < nsteps ? s + 2 : nsteps - 1;
-    __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));  // this wave's dY copies of step s, codes of step s+1
-    __builtin_amdgcn_s_waitcnt(0xC07F);          // this wave's tile writes
-    __builtin_amdgcn_s_barrier();                // every wave's copies landed; buffer b1 is free
-    // operands of substep 0 first, so its MFMAs can start while the rest lands
-    read_b(b0, 0, bv[0]);
-    read_a(b0, 0);
-    read_a(b0, 1);
-    read_a(b0, 2);
-    read_a(b0, 3);
-    __builtin_amdgcn_sched_barrier(0);  // the transposed reads go out before any new copy
+    // substep 0 (also the table of step s+1's rows and the codes of step s+2)
     load_codes(s2, cn, an);
-    dma_y(s1, b1);
-    __builtin_amdgcn_sched_barrier(0);
-    // substep 0 (also the table of step s+1's rows)
     const Nf4Lut lut = make_lut(ac);
     read_b(b0, 1, bv[1]);
     dequant_write(b1, cc, lut, 0);
     mfmas(av[0], bv[0]);
-    interleave(I8{}, I2{}, I0{}, I6{});
+    interleave(I8{}, I2{}, I3{}, I6{});
     __builtin_amdgcn_sched_barrier(0);
     // substep 1
     read_b(b0, 2, bv[0]);
@@ -270,27 +264,46 @@ void k_qgemm_bwd(BwdArgs p) {
     // substep 2
     read_b(b0, 3, bv[1]);
     dequant_write(b1, cc, lut, 4);
-    mfmas(av[2], bv[0]);
-    interleave(I8{}, I2{}, I0{}, I4{});
-    __builtin_amdgcn_sched_barrier(0);
-    // substep 3
     dequant_write(b1, cc, lut, 6);
-    mfmas(av[3], bv[1]);
-    interleave(I0{}, I2{}, I0{}, I4{});
+    mfmas(av[2], bv[0]);
+    interleave(I8{}, I4{}, I0{}, I8{});
     __builtin_amdgcn_sched_barrier(0);
+    __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));  // this wave's dY copies of step s+1 (and codes of s+2)
+    __builtin_amdgcn_s_waitcnt(0xC07F);          // this wave's LDS reads and tile writes
+    __builtin_amdgcn_s_barrier();
+    // substep 3: MFMAs of step s while step s+1's operands are read
+    mfmas(av[3], bv[1]);
+    read_b(b1, 0, bv[0]);
+    read_a(b1, 0);
+    read_a(b1, 1);
+    read_a(b1, 2);
+    read_a(b1, 3);
+    interleave(I12{}, I0{}, I0{}, I0{});
+    __builtin_amdgcn_sched_barrier(0);
+    dma_y(s2, b0);  // after every transposed read of the step
   };
 
-  // Prologue: codes of steps 0 and 1, dY of step 0; tile buffer 0 = step 0.
+  // Prologue: codes of steps 0 and 1; dY of steps 0 and 1; tile buffer 0 = step 0;
+  // the operands of step 0 read.
   u32x4 cA[2], cB[2];
   float aA, aB;
   load_codes(0, cA, aA);
   load_codes(nsteps > 1 ? 1 : 0, cB, aB);
   dma_y(0, 0);
+  dma_y(nsteps > 1 ? 1 : 0, 1);
   {
     const Nf4Lut lut0 = make_lut(aA);
 #pragma unroll
     for (int q = 0; q < 8; q += 2) dequant_write(0, cA, lut0, q);
   }
+  __builtin_amdgcn_s_waitcnt(waitcnt_vm(8));  // dY copies of step 0
+  __builtin_amdgcn_s_waitcnt(0xC07F);
+  __builtin_amdgcn_s_barrier();
+  read_b(0, 0, bv[0]);
+  read_a(0, 0);
+  read_a(0, 1);
+  read_a(0, 2);
+  read_a(0, 3);
   for (int s = 0; s < nsteps; s += 2) {
     body(s, cB, aB, cA, aA);
     if (s + 1 < nsteps) body(s + 1, cA, aA, cB, aB);

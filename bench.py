@@ -43,7 +43,61 @@ def parse():
     ap.add_argument("--rank", type=int, default=16)
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="target CPU time of the oracle baseline")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--cold", action="store_true",
+                    help="also time 10 cache-cold steps (512 MiB written before each, untimed)")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run plain device copies of known size (reference for hardware byte counters)")
     return ap.parse_args()
+
+
+# ---------------------------------------------------------------------------
+# HBM traffic of the dominant kernel, from committed hardware-counter summaries
+
+KERNEL_SOURCES = {  # kernel class -> the sources its code is built from
+    "gemm_bwd": ["gemm_bwd.hip", "common.hpp"],
+    "gemm_fwd": ["gemm_fwd.hip", "common.hpp"],
+}
+
+
+def kernel_source_hash(name):
+    import hashlib
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES.get(name, []):
+        with open(os.path.join(ROOT, "parameter_efficient_fine_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def counted_traffic(name, workload):
+    """HBM bytes per launch of kernel class `name` on `workload` from the summary under
+    profiles/ (FETCH_SIZE + WRITE_SIZE, scaled by the copy-kernel calibration), or None
+    when there is none or the kernel's sources changed since the counters were taken."""
+    path = os.path.join(ROOT, "profiles", f"{name}_{workload}_counters.md")
+    if not os.path.exists(path):
+        return None
+    vals = {}
+    with open(path) as fh:
+        for line in fh:
+            if line.startswith("traffic_bytes_per_launch:") or line.startswith("source_hash:"):
+                k, v = line.split(":", 1)
+                vals[k.strip()] = v.strip().split()[0]
+    if vals.get("source_hash") != kernel_source_hash(name) or "traffic_bytes_per_launch" not in vals:
+        return None
+    return float(vals["traffic_bytes_per_launch"])
+
+
+def copy_calibration(steps):
+    """Plain copies of 256 MiB (device to device): the byte counters of these
+    dispatches, divided by 256 MiB read / written, give the counter scale."""
+    import torch
+    n = 256 << 20
+    src = torch.ones(n // 4, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(steps):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_calibration": True, "bytes_read_per_copy": n, "bytes_written_per_copy": n,
+                      "copies": steps}), flush=True)
 
 
 # ---------------------------------------------------------------------------
@@ -249,6 +303,9 @@ def main():
         print(json.dumps({"error": "this build runs on one GPU only: no sharding or collectives are built; "
                                    "run with --gpus 1", "n_gpus": args.gpus}), flush=True)
         sys.exit(2)
+    if args.copy_calibration:
+        copy_calibration(args.steps)
+        return
     import torch
     from parameter_efficient_fine_amd import _lib as C
     from parameter_efficient_fine_amd.ops import KernelTimer
@@ -268,16 +325,34 @@ def main():
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
-    ev0 = torch.cuda.Event(enable_timing=True)
-    ev1 = torch.cuda.Event(enable_timing=True)
-    ev0.record()
+    # the timed region: K back-to-back steps, one event between consecutive steps
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
+    evs[0].record()
     t0 = time.perf_counter()
-    for _ in range(args.steps):
+    for i in range(args.steps):
         step()
-    ev1.record()
+        evs[i + 1].record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    ms = ev0.elapsed_time(ev1) / args.steps
+    ms = evs[0].elapsed_time(evs[-1]) / args.steps
+    per_step = np.array([evs[i].elapsed_time(evs[i + 1]) for i in range(args.steps)])
+    step_stats = dict(median_ms=float(np.median(per_step)), min_ms=float(per_step.min()),
+                      p90_ms=float(np.percentile(per_step, 90)))
+    if args.cold:
+        # cache-cold steps: 512 MiB written between steps (untimed), so the
+        # step's inputs come from HBM rather than the last-level cache
+        flush = torch.empty(512 << 20, dtype=torch.uint8, device="cuda")
+        cold = []
+        for _ in range(10):
+            flush.fill_(1)
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            step()
+            e1.record()
+            torch.cuda.synchronize()
+            cold.append(e0.elapsed_time(e1))
+        del flush
+        step_stats["cold_median_ms"] = float(np.median(cold))
 
     # same steps again with per-launch hipEvents recorded by the library (kernel durations)
     with KernelTimer(max_launches=args.steps * 64 + 64) as kt:
@@ -294,8 +369,9 @@ def main():
     avg_s = kernels[dom]["avg_us"] * 1e-6
     achieved = avg_flops / avg_s / 1e12
     roofline = dict(bound="mfma", kernel=dom, achieved=achieved, peak=PEAK_BF16_TFLOPS, unit="TFLOP/s",
-                    frac=achieved / PEAK_BF16_TFLOPS, traffic=None, avg_us=kernels[dom]["avg_us"],
-                    flops_per_launch=avg_flops)
+                    frac=achieved / PEAK_BF16_TFLOPS, traffic=counted_traffic(dom, args.workload),
+                    traffic_unit="bytes per launch", avg_us=kernels[dom]["avg_us"], flops_per_launch=avg_flops,
+                    source_hash=kernel_source_hash(dom))
 
     tokens = d["M"]
     value = tokens / (ms * 1e-3)
@@ -318,6 +394,7 @@ def main():
         "mfma_peak_frac": tflops / PEAK_BF16_TFLOPS,
         "useful_gflop_per_step": flops / 1e9,
         "wall_s_timed": wall,
+        "step_time": step_stats,
         "roofline": roofline,
         "kernels": kernels,
     }

@@ -216,13 +216,15 @@ void k_qgemm_bwd(BwdArgs p) {
     }
   };
   // issue order inside a substep: 16 MFMAs, each followed by a slice of the
-  // other work (LDS reads, LDS writes, global loads, VALU)
+  // other work (LDS reads, global loads, VALU). The tile writes take the last
+  // slots: each waits for a whole dequantization chain, and an early slot
+  // would pull that chain in front of the MFMAs instead of between them.
   auto interleave = [&](auto nds_read, auto nds_write, auto nvmem, auto nvalu) {
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
       if (i < decltype(nds_read)::value) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-      if (i < decltype(nds_write)::value) __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);
+      if (i >= 16 - decltype(nds_write)::value) __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);
       if (i < decltype(nvmem)::value) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
       __builtin_amdgcn_sched_group_barrier(0x002, decltype(nvalu)::value, 0);
     }

@@ -56,7 +56,8 @@ template <bool GATEUP, int RP, bool ALIGNED>
 __global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_per_eu(1, 1)))
 void k_qgemm_fwd(FwdArgs p) {
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];  // [kNBuf][256 rows][128 B], swizzled
-  const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+  const int t = threadIdx.x, lane = t & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(t >> 6);  // wave-uniform: LDS bases stay scalar
   const int h = lane >> 5, jl = lane & 31;
   const int64_t M = p.M, K = p.K, N = p.N;
   const int64_t ipt = GATEUP ? 128 : 256;  // output columns per workgroup

@@ -108,15 +108,18 @@ void tn_chunks(int r1, int r2, F&& f) {
   for (int c = 0; c < r2; c += kTnMaxR) f(r1 + c, std::min(kTnMaxR, r2 - c), 0);
 }
 
-// Workspace of the skinny_tn launches of a call: the largest fp32 partial
-// buffer (launches run in stream order and reuse it).
+// fp32 partials of one reduction launch (256-byte multiple, in floats)
+size_t tn_part_floats(int64_t M, int64_t Kd, int R) {
+  const TnPlan pl = skinny_tn_plan(M, Kd, R);
+  return up256((size_t)pl.splits * (size_t)R * (size_t)Kd * sizeof(float)) / sizeof(float);
+}
+
+// Workspace of the reductions of a call: every reduction (chunk) has partials
+// of its own, so independent reductions can share a launch.
 struct BwdLayout {
-  size_t part = 0;
+  size_t part = 0;  // floats
   void add(int64_t M, int64_t Kd, int r1, int r2 = 0) {
-    tn_chunks(r1, r2, [&](int, int a, int b) {
-      const TnPlan pl = skinny_tn_plan(M, Kd, a + b);
-      part = std::max(part, (size_t)pl.splits * (size_t)(a + b) * (size_t)Kd);
-    });
+    tn_chunks(r1, r2, [&](int, int a, int b) { part += tn_part_floats(M, Kd, a + b); });
   }
 };
 
@@ -129,7 +132,7 @@ BwdLayout bwd_layout(int64_t M, int64_t K, int64_t N, int64_t r) {
 
 size_t bwd_ws(int64_t M, int64_t K, int64_t N, int64_t r) {
   const BwdLayout l = bwd_layout(M, K, N, r);
-  return up256(r * N * 2) + up256(K * r * 2) + up256(M * r * 2) + up256(l.part * 4);
+  return up256(r * N * 2) + up256(M * r * 2) + up256(l.part * 4);
 }
 
 BwdLayout mlp_bwd_layout(int64_t M, int64_t H, int64_t I, int64_t r) {
@@ -145,7 +148,7 @@ BwdLayout mlp_bwd_layout(int64_t M, int64_t H, int64_t I, int64_t r) {
 size_t mlp_bwd_ws(int64_t M, int64_t H, int64_t I, int64_t r) {
   const BwdLayout l = mlp_bwd_layout(M, H, I, r);
   return 2 * up256((size_t)M * I * 2) + up256(M * r * 2) + up256(M * 2 * r * 2) + up256(r * H * 2) +
-         2 * up256(r * I * 2) + up256(I * r * 2) + 2 * up256(H * r * 2) + up256(l.part * 4);
+         2 * up256(r * I * 2) + up256(l.part * 4);
 }
 
 WSrc wsrc(const qlora_layer* L, const uint16_t* lora_i, const uint16_t* lora_j, int64_t ldj = 0) {
@@ -176,22 +179,24 @@ NtArgs nt1(const uint16_t* in, int64_t M, int64_t Kd, const uint16_t* ad, int r,
   return a;
 }
 
-// Issues the skinny_tn + tn_reduce launches of one reduction.
+// Collects independent reductions (out = s * P^T . Q) and issues them as one
+// skinny_tn launch and one tn_reduce launch per batch of kTnMaxJobs; each gets
+// its own slice of the partial buffer.
 struct TnCall {
   float* part;
   hipStream_t st;
+  TnJobs jobs{};
+  int rc = QLORA_OK;
   // out = s * P^T . Q (P [M, r] with row stride ldp, Q [M, Kd]); transposed -> [Kd, r]
-  int one(const uint16_t* P, int64_t ldp, int r, float s, const uint16_t* Q, int64_t M, int64_t Kd, float* out,
-          bool transposed) {
-    return two(P, ldp, r, s, out, 0, 0.f, nullptr, Q, M, Kd, transposed);
+  void one(const uint16_t* P, int64_t ldp, int r, float s, const uint16_t* Q, int64_t M, int64_t Kd, float* out,
+           bool transposed) {
+    two(P, ldp, r, s, out, 0, 0.f, nullptr, Q, M, Kd, transposed);
   }
   // rows j < r1 of P^T . Q into out1 (scale s1), rows r1 <= j < r1 + r2 into out2 (scale s2)
-  int two(const uint16_t* P, int64_t ldp, int r1, float s1, float* out1, int r2, float s2, float* out2,
-          const uint16_t* Q, int64_t M, int64_t Kd, bool transposed) {
-    int rc = QLORA_OK;
+  void two(const uint16_t* P, int64_t ldp, int r1, float s1, float* out1, int r2, float s2, float* out2,
+           const uint16_t* Q, int64_t M, int64_t Kd, bool transposed) {
     tn_chunks(r1, r2, [&](int c0, int a1, int a2) {
-      if (rc) return;
-      // chunk columns [c0, c0 + a1 + a2) of P; a2 > 0 only for the single launch covering both parts
+      // chunk columns [c0, c0 + a1 + a2) of P; a2 > 0 only for the single job covering both parts
       const bool in2 = c0 >= r1;
       TnArgs a{};
       a.P = P + c0;
@@ -201,10 +206,9 @@ struct TnCall {
       a.s1 = in2 ? s2 : s1;
       a.s2 = s2;
       const int64_t jo = in2 ? c0 - r1 : c0;  // first output row of the chunk
-      const int64_t ld1 = transposed ? (in2 ? r2 : r1) : Kd;
       float* o1 = in2 ? out2 : out1;
       a.out1 = transposed ? o1 + jo : o1 + jo * Kd;
-      a.ldo1 = ld1;
+      a.ldo1 = transposed ? (in2 ? r2 : r1) : Kd;
       a.out2 = out2 ? out2 : out1;
       a.ldo2 = transposed ? r2 : Kd;
       a.transposed = transposed ? 1 : 0;
@@ -212,10 +216,17 @@ struct TnCall {
       a.M = M;
       a.Kd = Kd;
       a.part = part;
-      hipError_t e = timed("skinny_tn", st, [&]() { return launch_skinny_tn(a, st); });
-      if (e == hipSuccess) e = timed("tn_reduce", st, [&]() { return launch_tn_reduce(a, st); });
-      if (e != hipSuccess) rc = hip_fail(e, "skinny_tn");
+      part += tn_part_floats(M, Kd, a1 + a2);
+      if (jobs.n == kTnMaxJobs) flush();
+      jobs.job[jobs.n++] = a;
     });
+  }
+  int flush() {
+    if (jobs.n == 0 || rc != QLORA_OK) return rc;
+    hipError_t e = timed("skinny_tn", st, [&]() { return launch_skinny_tn(jobs, st); });
+    if (e == hipSuccess) e = timed("tn_reduce", st, [&]() { return launch_tn_reduce(jobs, st); });
+    if (e != hipSuccess) rc = hip_fail(e, "skinny_tn");
+    jobs.n = 0;
     return rc;
   }
 };
@@ -297,7 +308,6 @@ int qlora_backward(const qlora_layer* L, const uint16_t* dY, const uint16_t* X, 
   const BwdLayout lay = bwd_layout(M, K, N, r);
   Carve c{(char*)ws, ws_bytes};
   uint16_t* Bt = c.take<uint16_t>((size_t)r * N);
-  uint16_t* At = c.take<uint16_t>((size_t)K * r);
   uint16_t* G = c.take<uint16_t>((size_t)M * r);
   float* part = c.take<float>(lay.part);
   if (!c.ok) return QLORA_EWORKSPACE;
@@ -308,16 +318,16 @@ int qlora_backward(const qlora_layer* L, const uint16_t* dY, const uint16_t* X, 
   }
   PrepJobs pj{};
   pj.job[0] = {L->B, Bt, N, r};  // B [N, r] -> B^T [r, N]
-  pj.job[1] = {L->A, At, r, K};  // A [r, K] -> A^T [K, r]
-  pj.n = 2;
+  pj.n = 1;
   QL_LAUNCH("prep", st, launch_prep(pj, st));
-  // G = dY.B ; dB = s.dY^T.Z (written transposed from Z^T.dY) ; dX ; dA = s.G^T.X
+  // G = dY.B ; dB = s.dY^T.Z (written transposed from Z^T.dY) and dA = s.G^T.X in one pair of launches ; dX
   QL_LAUNCH("skinny_nt", st, launch_skinny_nt(nt1(dY, M, N, Bt, r, G, r), st));
   TnCall tn{part, st};
-  int rc = tn.one(Z_save, r, r, L->s, dY, M, N, dB, true);
-  if (rc) return rc;
-  if (dX) QL_LAUNCH("gemm_bwd", st, launch_gemm_bwd(dY, wsrc(L, At, G), nullptr, WSrc{}, M, K, N, dX, st));
-  return tn.one(G, r, r, L->s, X, M, K, dA, false);
+  tn.one(Z_save, r, r, L->s, dY, M, N, dB, true);
+  tn.one(G, r, r, L->s, X, M, K, dA, false);
+  if (int rc = tn.flush()) return rc;
+  if (dX) QL_LAUNCH("gemm_bwd", st, launch_gemm_bwd(dY, wsrc(L, L->A, G), nullptr, WSrc{}, M, K, N, dX, st));
+  return QLORA_OK;
 }
 
 static bool mlp_shapes_ok(const qlora_layer* g, const qlora_layer* u, const qlora_layer* d) {
@@ -388,9 +398,6 @@ int swiglu_mlp_backward(const qlora_layer* gate, const qlora_layer* up, const ql
   uint16_t* Btd = c.take<uint16_t>((size_t)r * H);
   uint16_t* Btg = c.take<uint16_t>((size_t)r * I);
   uint16_t* Btu = c.take<uint16_t>((size_t)r * I);
-  uint16_t* Atd = c.take<uint16_t>((size_t)I * r);
-  uint16_t* Atg = c.take<uint16_t>((size_t)H * r);
-  uint16_t* Atu = c.take<uint16_t>((size_t)H * r);
   float* part = c.take<float>(lay.part);
   if (!c.ok) return QLORA_EWORKSPACE;
   if (M == 0) {
@@ -410,33 +417,29 @@ int swiglu_mlp_backward(const qlora_layer* gate, const qlora_layer* up, const ql
   pj.job[0] = {down->B, Btd, H, r};
   pj.job[1] = {gate->B, Btg, I, r};
   pj.job[2] = {up->B, Btu, I, r};
-  pj.job[3] = {down->A, Atd, r, I};
-  pj.job[4] = {gate->A, Atg, r, H};
-  pj.job[5] = {up->A, Atu, r, H};
-  pj.n = 6;
+  pj.n = 3;
   QL_LAUNCH("prep", st, launch_prep(pj, st));
   TnCall tn{part, st};
-  // down projection: G_d = dY.B_d ; dB_d = s.dY^T.Z_d ; dh -> (dg, du) in the GEMM epilogue ; dA_d = s.G_d^T.h
+  // down projection: G_d = dY.B_d ; dB_d = s.dY^T.Z_d and dA_d = s.G_d^T.h ; dh -> (dg, du) in the GEMM epilogue
   QL_LAUNCH("skinny_nt", st, launch_skinny_nt(nt1(dY, M, H, Btd, r, Gd, r), st));
-  int rc = tn.one(Zd, r, r, down->s, dY, M, H, dB[2], true);
-  if (rc) return rc;
+  tn.one(Zd, r, r, down->s, dY, M, H, dB[2], true);
+  tn.one(Gd, r, r, down->s, h_save, M, I, dA[2], false);
+  if (int rc = tn.flush()) return rc;
   QL_LAUNCH("gemm_bwd_swiglu", st,
-            launch_gemm_bwd_swiglu(dY, wsrc(down, Atd, Gd), M, I, H, g_save, u_save, dg, du, st));
-  rc = tn.one(Gd, r, r, down->s, h_save, M, I, dA[2], false);
-  if (rc) return rc;
-  // gate and up: G = d(g|u).B ; dB = s.d(g|u)^T.Z
+            launch_gemm_bwd_swiglu(dY, wsrc(down, down->A, Gd), M, I, H, g_save, u_save, dg, du, st));
+  // gate and up: G = d(g|u).B ; dB = s.d(g|u)^T.Z ; dA_g = s_g.G_g^T.X and dA_u = s_u.G_u^T.X
+  // (one pass over X when 2r fits a launch)
   QL_LAUNCH("skinny_nt", st, launch_skinny_nt(nt1(dg, M, I, Btg, r, Gg, 2 * r), st));
   QL_LAUNCH("skinny_nt", st, launch_skinny_nt(nt1(du, M, I, Btu, r, Gu, 2 * r), st));
-  rc = tn.one(Zg, r, r, gate->s, dg, M, I, dB[0], true);
-  if (rc) return rc;
-  rc = tn.one(Zu, r, r, up->s, du, M, I, dB[1], true);
-  if (rc) return rc;
+  tn.one(Zg, r, r, gate->s, dg, M, I, dB[0], true);
+  tn.one(Zu, r, r, up->s, du, M, I, dB[1], true);
+  tn.two(Ggu, 2 * r, r, gate->s, dA[0], r, up->s, dA[1], X, M, H, false);
+  if (int rc = tn.flush()) return rc;
   // dX = dg.W_g + du.W_u + s.G_g.A_g + s.G_u.A_u : one GEMM over the concatenated reduction
   if (dX)
     QL_LAUNCH("gemm_bwd", st,
-              launch_gemm_bwd(dg, wsrc(gate, Atg, Gg, 2 * r), du, wsrc(up, Atu, Gu, 2 * r), M, H, I, dX, st));
-  // dA_g = s_g.G_g^T.X and dA_u = s_u.G_u^T.X (one pass over X when 2r fits a launch)
-  return tn.two(Ggu, 2 * r, r, gate->s, dA[0], r, up->s, dA[1], X, M, H, false);
+              launch_gemm_bwd(dg, wsrc(gate, gate->A, Gg, 2 * r), du, wsrc(up, up->A, Gu, 2 * r), M, H, I, dX, st));
+  return QLORA_OK;
 }
 
 int qlora_profile_begin(int max_launches) {

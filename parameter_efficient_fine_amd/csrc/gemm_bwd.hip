@@ -54,7 +54,7 @@ enum BwdMode { kPlain = 0, kConcat = 1, kSwiGLU = 2 };
 
 struct BwdArgs {
   const uint16_t* dY[2];  // [M, N] per source
-  WSrc w[2];              // lora_i = A^T [K, r], lora_j = G [M, r] (row stride ldj)
+  WSrc w[2];              // lora_i = A [r, K], lora_j = G [M, r] (row stride ldj)
   int64_t M, K, N;        // dX [M, K]; reduction over N per source
   uint16_t* out0;         // dX | dg
   uint16_t* out1;         // du
@@ -134,11 +134,13 @@ void k_qgemm_bwd(BwdArgs p) {
 #pragma unroll
     for (int j = 0; j < 8; ++j) acc[f][j] = f32x16{};
 
-  // ---- the rank-r term first, by MFMA: acc += (s.A^T rows) . (G rows)^T
+  // ---- the rank-r term first, by MFMA: acc += (s.A^T rows) . (G rows)^T.
+  // A is read in place ([r, K]): a lane's 8 rank entries of column k are
+  // strided by K (eight 2-byte loads, once per kernel).
 #pragma unroll
   for (int src = 0; src < NSRC; ++src) {
     const WSrc& w = p.w[src];
-    const __amdgpu_buffer_rsrc_t rAt = make_rsrc(w.lora_i, K * (int64_t)w.r * 2);
+    const __amdgpu_buffer_rsrc_t rA_ = make_rsrc(w.lora_i, K * (int64_t)w.r * 2);
     const __amdgpu_buffer_rsrc_t rG = make_rsrc(w.lora_j + j0 * w.ldj, rows_here * w.ldj * 2);
     const int c0 = 8 * h;
 #pragma unroll
@@ -147,8 +149,16 @@ void k_qgemm_bwd(BwdArgs p) {
 #pragma unroll
       for (int f = 0; f < 2; ++f) {
         const int64_t ir = kc + 32 * f + jl;
-        const u32x4 av = rank8<ALIGNED>(rAt, ir < K ? ir : -1, w.r, w.r, rr + c0);
-        split_scaled(av, w.s, ah[f], al[f]);
+        uint32_t wv[4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int e0 = rr + c0 + 2 * q, e1 = e0 + 1;
+          const int o0 = (ir < K && e0 < w.r) ? (int)(((int64_t)e0 * K + ir) * 2) : kOff;
+          const int o1 = (ir < K && e1 < w.r) ? (int)(((int64_t)e1 * K + ir) * 2) : kOff;
+          wv[q] = (uint32_t)__builtin_amdgcn_raw_buffer_load_b16(rA_, o0, 0, 0) |
+                  ((uint32_t)__builtin_amdgcn_raw_buffer_load_b16(rA_, o1, 0, 0) << 16);
+        }
+        split_scaled(u32x4{wv[0], wv[1], wv[2], wv[3]}, w.s, ah[f], al[f]);
       }
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
@@ -370,8 +380,7 @@ hipError_t launch_rp(const BwdArgs& a, hipStream_t st) {
 }
 
 bool rank_rows_aligned(const WSrc& w) {
-  return w.r % 8 == 0 && w.ldj % 8 == 0 && (reinterpret_cast<uintptr_t>(w.lora_j) & 15) == 0 &&
-         (reinterpret_cast<uintptr_t>(w.lora_i) & 15) == 0;
+  return w.r % 8 == 0 && w.ldj % 8 == 0 && (reinterpret_cast<uintptr_t>(w.lora_j) & 15) == 0;
 }
 
 template <int MODE, int RP>

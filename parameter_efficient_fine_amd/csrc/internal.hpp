@@ -56,11 +56,18 @@ struct TnArgs {
   int64_t rows;         // set by the launchers from skinny_tn_plan
   int splits;
 };
-hipError_t launch_skinny_tn(TnArgs a, hipStream_t st);
-hipError_t launch_tn_reduce(TnArgs a, hipStream_t st);
+// Up to kTnMaxJobs independent reductions in one launch of each kernel
+// (blockIdx.z selects the job; every job has its own `part`).
+constexpr int kTnMaxJobs = 3;
+struct TnJobs {
+  TnArgs job[kTnMaxJobs];
+  int n;
+};
+hipError_t launch_skinny_tn(TnJobs jobs, hipStream_t st);
+hipError_t launch_tn_reduce(TnJobs jobs, hipStream_t st);
 
 // One launch before a backward: dst[C, R] = src[R, C]^T for each job (bf16).
-constexpr int kMaxPrepJobs = 6;
+constexpr int kMaxPrepJobs = 3;
 struct TransposeJob {
   const uint16_t* src;
   uint16_t* dst;
@@ -79,7 +86,7 @@ hipError_t launch_fill_zero_f32(float* p, int64_t n, hipStream_t st);
 struct WSrc {           // one frozen 4-bit weight [N, K] with its LoRA pair
   const uint8_t* codes;  // [N, K/2]
   const float* absmax;   // [N, K/64]
-  const uint16_t* lora_i;  // fwd: B [N, r] ; bwd: A^T [K, r]
+  const uint16_t* lora_i;  // fwd: B [N, r] ; bwd: A [r, K]
   const uint16_t* lora_j;  // fwd: Z [M, r] ; bwd: G [M, r] with row stride ldj
   int r;
   int64_t ldj;

@@ -187,7 +187,9 @@ TnPlan skinny_tn_plan(int64_t M, int64_t Kd, int R) {
 }
 
 template <int RP, bool PV>
-__global__ __launch_bounds__(256) void k_skinny_tn(TnArgs p) {
+__global__ __launch_bounds__(256) void k_skinny_tn(TnJobs jobs) {
+  const TnArgs& p = jobs.job[blockIdx.z];
+  if ((int64_t)blockIdx.y * p.rows >= p.M || (int64_t)blockIdx.x * kTnCols >= p.Kd) return;  // past this job's grid
   constexpr int NJ = RP / 16;
   constexpr int PS = RP + 16;                             // P tile row stride (bf16)
   constexpr int QCH = kTnRows * kTnCols / 8 / 256;        // 16-byte Q chunks per thread
@@ -332,7 +334,8 @@ __global__ __launch_bounds__(256) void k_skinny_tn(TnArgs p) {
 // its own: the launch boundary makes the partials of all workgroups visible
 // (an in-kernel "last workgroup reduces" scheme needs device-scope release
 // fences, which write back the whole L2 of an XCD and cost far more here).
-__global__ __launch_bounds__(64) void k_tn_reduce(TnArgs p) {
+__global__ __launch_bounds__(64) void k_tn_reduce(TnJobs jobs) {
+  const TnArgs& p = jobs.job[blockIdx.z];
   const int64_t Kd = p.Kd, kq = Kd / 4;
   const int R = p.r1 + p.r2;
   const int64_t idx = (int64_t)blockIdx.x * 64 + threadIdx.x;
@@ -372,27 +375,37 @@ __global__ __launch_bounds__(64) void k_tn_reduce(TnArgs p) {
   }
 }
 
-hipError_t launch_skinny_tn(TnArgs a, hipStream_t st) {
-  const int R = a.r1 + a.r2;
-  const TnPlan pl = skinny_tn_plan(a.M, a.Kd, R);
-  a.rows = pl.rows;
-  a.splits = pl.splits;
-  const bool pv = (a.ldp % 8 == 0) && (R % 8 == 0) && ((reinterpret_cast<uintptr_t>(a.P) & 15) == 0);
-  dim3 grid((unsigned)pl.col_tiles, (unsigned)pl.splits);
-#define QL_TN(RPV)                                    \
-  do {                                                \
-    if (pv)                                           \
-      k_skinny_tn<RPV, true><<<grid, 256, 0, st>>>(a);  \
-    else                                              \
-      k_skinny_tn<RPV, false><<<grid, 256, 0, st>>>(a); \
+hipError_t launch_skinny_tn(TnJobs jobs, hipStream_t st) {
+  if (jobs.n < 1 || jobs.n > kTnMaxJobs) return hipErrorInvalidValue;
+  int rmax = 0;
+  bool pv = true;
+  int64_t gx = 0, gy = 0;
+  for (int i = 0; i < jobs.n; ++i) {
+    TnArgs& a = jobs.job[i];
+    const int R = a.r1 + a.r2;
+    const TnPlan pl = skinny_tn_plan(a.M, a.Kd, R);
+    a.rows = pl.rows;
+    a.splits = pl.splits;
+    rmax = R > rmax ? R : rmax;
+    pv = pv && (a.ldp % 8 == 0) && (R % 8 == 0) && ((reinterpret_cast<uintptr_t>(a.P) & 15) == 0);
+    gx = pl.col_tiles > gx ? pl.col_tiles : gx;
+    gy = pl.splits > gy ? pl.splits : gy;
+  }
+  dim3 grid((unsigned)gx, (unsigned)gy, (unsigned)jobs.n);
+#define QL_TN(RPV)                                         \
+  do {                                                     \
+    if (pv)                                                \
+      k_skinny_tn<RPV, true><<<grid, 256, 0, st>>>(jobs);  \
+    else                                                   \
+      k_skinny_tn<RPV, false><<<grid, 256, 0, st>>>(jobs); \
   } while (0)
-  if (R <= 16)
+  if (rmax <= 16)
     QL_TN(16);
-  else if (R <= 32)
+  else if (rmax <= 32)
     QL_TN(32);
-  else if (R <= 64)
+  else if (rmax <= 64)
     QL_TN(64);
-  else if (R <= kTnMaxR)
+  else if (rmax <= kTnMaxR)
     QL_TN(128);
   else
     return hipErrorInvalidValue;
@@ -400,12 +413,17 @@ hipError_t launch_skinny_tn(TnArgs a, hipStream_t st) {
   return hipGetLastError();
 }
 
-hipError_t launch_tn_reduce(TnArgs a, hipStream_t st) {
-  const int R = a.r1 + a.r2;
-  a.splits = skinny_tn_plan(a.M, a.Kd, R).splits;
-  const int64_t n = (int64_t)R * (a.Kd / 4);
-  if (n == 0) return hipSuccess;
-  k_tn_reduce<<<(unsigned)((n + 63) / 64), 64, 0, st>>>(a);
+hipError_t launch_tn_reduce(TnJobs jobs, hipStream_t st) {
+  if (jobs.n < 1 || jobs.n > kTnMaxJobs) return hipErrorInvalidValue;
+  int64_t nmax = 0;
+  for (int i = 0; i < jobs.n; ++i) {
+    TnArgs& a = jobs.job[i];
+    a.splits = skinny_tn_plan(a.M, a.Kd, a.r1 + a.r2).splits;
+    const int64_t n = (int64_t)(a.r1 + a.r2) * (a.Kd / 4);
+    nmax = n > nmax ? n : nmax;
+  }
+  if (nmax == 0) return hipSuccess;
+  k_tn_reduce<<<dim3((unsigned)((nmax + 63) / 64), 1, (unsigned)jobs.n), 64, 0, st>>>(jobs);
   return hipGetLastError();
 }
 

@@ -252,3 +252,79 @@ def test_decoder_layer_full_size():
     for k, v in _mlp_case(mlp, rows, mask_dy=True).items():
         errs["mlp." + k] = v
     assert max(errs.values()) <= TOL, errs
+
+
+# ---------------------------------------------------------------------------
+# determinism, workspace hygiene, streams
+
+def _bits(t):
+    import torch
+    return t.detach().contiguous().view(torch.int32 if t.dtype == torch.float32 else torch.int16).cpu().numpy()
+
+
+def test_linear_backward_bitwise_deterministic_and_workspace_independent():
+    # the rank-r reductions sum their split partials in a fixed order, so two
+    # runs agree bit for bit; a workspace full of NaN bytes and outputs full of
+    # NaN bytes change nothing (no uninitialised reads)
+    _announce("determinism linear M=2000 K=1024 N=384 r=16")
+    import torch
+    q = _q()
+    d = random_linear(4242, 2000, 1024, 384, 16)
+    P = Prepared(d["layers"]["proj"], d["s"])
+    X, dY = dev_bf16(d["X"]), dev_bf16(d["dY"])
+    runs = []
+    for dirty in (False, True, False):
+        M, K, N, r = 2000, 1024, 384, 16
+        fill = float("nan") if dirty else 0.0
+        Y = torch.full((M, N), fill, dtype=torch.bfloat16, device="cuda")
+        Z = torch.full((M, r), fill, dtype=torch.bfloat16, device="cuda")
+        q.forward(P.dev, X, Y, Z)
+        nb = q.workspace_size(1, M, K, N, r)
+        ws = torch.full((nb,), 255 if dirty else 0, dtype=torch.uint8, device="cuda")
+        out = (torch.full((M, K), fill, dtype=torch.bfloat16, device="cuda"),
+               torch.full((r, K), fill, dtype=torch.float32, device="cuda"),
+               torch.full((N, r), fill, dtype=torch.float32, device="cuda"))
+        dX, dA, dB = q.backward(P.dev, dY, X, Z, ws=ws, out=out)
+        torch.cuda.synchronize()
+        runs.append([_bits(t) for t in (Y, Z, dX, dA, dB)])
+    for other in runs[1:]:
+        for a, b in zip(runs[0], other):
+            assert np.array_equal(a, b)
+
+
+def test_mlp_backward_bitwise_deterministic():
+    _announce("determinism mlp M=300 H=256 I=512 r=16")
+    import torch
+    q = _q()
+    d = random_mlp(4243, 300, 256, 512, 16)
+    Ls = {nm: Prepared(d["layers"][nm], d["s"]) for nm in ("gate", "up", "down")}
+    X, dY = dev_bf16(d["X"]), dev_bf16(d["dY"])
+    runs = []
+    for _ in range(2):
+        f = q.mlp_forward(Ls["gate"].dev, Ls["up"].dev, Ls["down"].dev, X)
+        b = q.mlp_backward(Ls["gate"].dev, Ls["up"].dev, Ls["down"].dev, dY, X, f)
+        torch.cuda.synchronize()
+        runs.append([_bits(t) for t in [f["Y"], b["dX"]] + b["dA"] + b["dB"]])
+    for a, b in zip(*runs):
+        assert np.array_equal(a, b)
+
+
+def test_calls_run_on_the_callers_stream():
+    # every launch goes to the current torch stream: a side stream gives the
+    # same bits as the default one
+    _announce("side stream linear tiny")
+    import torch
+    q = _q()
+    d = make_workload(0)
+    P = Prepared(d["layers"]["proj"], d["s"])
+    X, dY = dev_bf16(d["X"]), dev_bf16(d["dY"])
+    Y0, Z0 = q.forward(P.dev, X)
+    r0 = q.backward(P.dev, dY, X, Z0)
+    torch.cuda.synchronize()
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        Y1, Z1 = q.forward(P.dev, X)
+        r1 = q.backward(P.dev, dY, X, Z1)
+    s.synchronize()
+    for a, b in zip([Y0, Z0, *r0], [Y1, Z1, *r1]):
+        assert np.array_equal(_bits(a), _bits(b))

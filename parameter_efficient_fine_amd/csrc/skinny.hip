@@ -15,38 +15,43 @@
 namespace qlora {
 
 // ---------------------------------------------------------------------------
-// skinny_nt: 16 rows of `in` per workgroup. The waves interleave over the
-// 32-wide k steps (wave w takes steps w, w + NW, ...) and issue U steps of
-// loads at once. `in` is read through a buffer resource covering the
-// workgroup's rows: a lane's row and k position form a loop-invariant VGPR
-// offset, the step a scalar offset, and rows past M read zero -- the loop has
-// no per-lane condition (a per-lane select there turns into divergent
-// branches that serialize the loads). The steps a wave owns are done in
-// batches of U, then U/2, .., 1 (binary remainder); a ragged last step
-// (Kd % 32 != 0) is done apart with masks. Per-wave partial sums are combined
-// by a fixed-order tree in LDS. RP = r1 + r2 rounded up to 16.
+// skinny_nt: 16*RF rows of `in` per workgroup (RF row fragments; RF > 1 when
+// M is large enough to keep one workgroup per CU, so each adapter fragment
+// loaded serves RF fragments of `in`). The waves interleave over the 32-wide
+// k steps (wave w takes steps w, w + NW, ...) and issue U steps of loads at
+// once. `in` is read through a buffer resource covering the workgroup's rows:
+// a lane's row and k position form a loop-invariant VGPR offset, the step a
+// scalar offset, and rows past M read zero -- the loop has no per-lane
+// condition (a per-lane select there turns into divergent branches that
+// serialize the loads). The steps a wave owns are done in batches of U, then
+// U/2, .., 1 (binary remainder); a ragged last step (Kd % 32 != 0) is done
+// apart with masks. Per-wave partial sums are combined by a fixed-order tree
+// in LDS, one row fragment at a time. RP = r1 + r2 rounded up to 16.
 
-template <int RP>
+template <int RP, int RF>
 struct NtShape {
-  static constexpr int NF = RP / 16;                  // 16-row adapter fragments
-  static constexpr int NW = RP >= 256 ? 4 : 8;        // waves
-  static constexpr int U = RP <= 32 ? 16 : (RP <= 64 ? 4 : (RP <= 128 ? 2 : 1));  // steps per batch
+  static constexpr int NF = RP / 16;            // 16-row adapter fragments
+  static constexpr int NW = RP >= 256 ? 4 : 8;  // waves
+  static constexpr int U0 = RP <= 32 ? 16 : (RP <= 64 ? 4 : (RP <= 128 ? 2 : 1));
+  static constexpr int U = U0 / RF > 0 ? U0 / RF : 1;  // steps per batch
 };
 
-template <int RP>
-__global__ __attribute__((amdgpu_flat_work_group_size(64 * NtShape<RP>::NW, 64 * NtShape<RP>::NW)))
+template <int RP, int RF>
+__global__ __attribute__((amdgpu_flat_work_group_size(64 * NtShape<RP, RF>::NW, 64 * NtShape<RP, RF>::NW)))
 void k_skinny_nt(NtArgs p) {
-  constexpr int NF = NtShape<RP>::NF, NW = NtShape<RP>::NW, U = NtShape<RP>::U;
+  constexpr int NF = NtShape<RP, RF>::NF, NW = NtShape<RP, RF>::NW, U = NtShape<RP, RF>::U;
   __shared__ float red[NW / 2][16][RP + 4];
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int64_t M = p.M, Kd = p.Kd;
-  const int64_t m0 = (int64_t)blockIdx.x * 16;
+  const int64_t m0 = (int64_t)blockIdx.x * 16 * RF;
   const int R = p.r1 + p.r2;
-  const int64_t rows_here = (M - m0) < 16 ? (M - m0) : 16;
+  const int64_t rows_here = (M - m0) < 16 * RF ? (M - m0) : 16 * RF;
   const __amdgpu_buffer_rsrc_t rin = make_rsrc(p.in + m0 * Kd, rows_here * Kd * 2);
   const int row = lane & 15, kofs = 8 * (lane >> 4);
-  const int voff = (int)((row * Kd + kofs) * 2);
+  int voff[RF];
+#pragma unroll
+  for (int rf = 0; rf < RF; ++rf) voff[rf] = (int)(((16 * rf + row) * Kd + kofs) * 2);
 
   const uint16_t* adp[NF];  // this lane's adapter row, at its k offset
 #pragma unroll
@@ -56,18 +61,23 @@ void k_skinny_nt(NtArgs p) {
     adp[f] = (jc < p.r1 ? p.ad1 + (int64_t)jc * Kd : p.ad2 + (int64_t)(jc - p.r1) * Kd) + kofs;
   }
 
-  f32x4 acc[NF];
+  f32x4 acc[RF][NF];
 #pragma unroll
-  for (int f = 0; f < NF; ++f) acc[f] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int rf = 0; rf < RF; ++rf)
+#pragma unroll
+    for (int f = 0; f < NF; ++f) acc[rf][f] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   // V full steps starting at this wave's step index i0: loads first, then MFMAs
   auto batch = [&](auto vtag, int64_t i0) {
     constexpr int V = decltype(vtag)::value;
-    u32x4 a[V], b[V][NF];
+    u32x4 a[V][RF], b[V][NF];
 #pragma unroll
     for (int u = 0; u < V; ++u) {
       const int64_t st = wave + NW * (i0 + u);
-      a[u] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rin, voff, (int)(st * 64), 0));
+#pragma unroll
+      for (int rf = 0; rf < RF; ++rf)
+        a[u][rf] =
+            __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rin, voff[rf], (int)(st * 64), 0));
 #pragma unroll
       for (int f = 0; f < NF; ++f) b[u][f] = *reinterpret_cast<const u32x4*>(adp[f] + st * 32);
     }
@@ -75,7 +85,9 @@ void k_skinny_nt(NtArgs p) {
 #pragma unroll
     for (int u = 0; u < V; ++u)
 #pragma unroll
-      for (int f = 0; f < NF; ++f) acc[f] = mfma16(a[u], b[u][f], acc[f]);
+      for (int rf = 0; rf < RF; ++rf)
+#pragma unroll
+        for (int f = 0; f < NF; ++f) acc[rf][f] = mfma16(a[u][rf], b[u][f], acc[rf][f]);
   };
   const int64_t nfull = Kd / 32;  // steps with all 32 columns in range
   const int64_t cnt = nfull > wave ? (nfull - wave + NW - 1) / NW : 0;
@@ -88,71 +100,89 @@ void k_skinny_nt(NtArgs p) {
   if (nfull * 32 < Kd && wave == nfull % NW) {  // ragged last step, masked per lane
     const int64_t k = nfull * 32 + kofs;
     const bool ok = k < Kd;
-    u32x4 a = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rin, voff, (int)(nfull * 64), 0));
-    if (!ok) a = u32x4{0, 0, 0, 0};
+    u32x4 b[NF];
 #pragma unroll
     for (int f = 0; f < NF; ++f) {
-      u32x4 b = *reinterpret_cast<const u32x4*>(adp[f] + (ok ? nfull * 32 : 0));
-      if (!ok) b = u32x4{0, 0, 0, 0};
-      acc[f] = mfma16(a, b, acc[f]);
+      b[f] = *reinterpret_cast<const u32x4*>(adp[f] + (ok ? nfull * 32 : 0));
+      if (!ok) b[f] = u32x4{0, 0, 0, 0};
+    }
+#pragma unroll
+    for (int rf = 0; rf < RF; ++rf) {
+      u32x4 a = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rin, voff[rf], (int)(nfull * 64), 0));
+      if (!ok) a = u32x4{0, 0, 0, 0};
+#pragma unroll
+      for (int f = 0; f < NF; ++f) acc[rf][f] = mfma16(a, b[f], acc[rf][f]);
     }
   }
 
-  // fixed-order tree over the waves: (w, w + h) pairs for h = NW/2, NW/4, .., 1
-  // C layout: col j = lane%16 (adapter row), row i = 4*(lane/16) + v (token row)
+  // per row fragment, a fixed-order tree over the waves: (w, w + h) pairs for
+  // h = NW/2, NW/4, .., 1. C layout: col j = lane%16 (adapter row),
+  // row i = 4*(lane/16) + v (token row)
 #pragma unroll
-  for (int h = NW / 2; h >= 1; h >>= 1) {
-    if (wave >= h && wave < 2 * h) {
+  for (int rf = 0; rf < RF; ++rf) {
 #pragma unroll
-      for (int f = 0; f < NF; ++f)
+    for (int h = NW / 2; h >= 1; h >>= 1) {
+      if (wave >= h && wave < 2 * h) {
 #pragma unroll
-        for (int v = 0; v < 4; ++v) red[wave - h][4 * (lane >> 4) + v][16 * f + row] = acc[f][v];
+        for (int f = 0; f < NF; ++f)
+#pragma unroll
+          for (int v = 0; v < 4; ++v) red[wave - h][4 * (lane >> 4) + v][16 * f + row] = acc[rf][f][v];
+      }
+      __syncthreads();
+      if (wave < h) {
+#pragma unroll
+        for (int f = 0; f < NF; ++f)
+#pragma unroll
+          for (int v = 0; v < 4; ++v) acc[rf][f][v] += red[wave][4 * (lane >> 4) + v][16 * f + row];
+      }
+      __syncthreads();
     }
-    __syncthreads();
-    if (wave < h) {
-#pragma unroll
-      for (int f = 0; f < NF; ++f)
-#pragma unroll
-        for (int v = 0; v < 4; ++v) acc[f][v] += red[wave][4 * (lane >> 4) + v][16 * f + row];
-    }
-    __syncthreads();
   }
   if (wave != 0) return;
 #pragma unroll
-  for (int f = 0; f < NF; ++f) {
-    const int j = 16 * f + row;
+  for (int rf = 0; rf < RF; ++rf)
 #pragma unroll
-    for (int v = 0; v < 4; ++v) {
-      const int64_t m = m0 + 4 * (lane >> 4) + v;
-      if (m >= M || j >= R) continue;
-      const uint16_t hv = __builtin_bit_cast(uint16_t, (__bf16)acc[f][v]);
-      if (j < p.r1)
-        p.out1[m * p.ld1 + j] = hv;
-      else
-        p.out2[m * p.ld2 + (j - p.r1)] = hv;
+    for (int f = 0; f < NF; ++f) {
+      const int j = 16 * f + row;
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const int64_t m = m0 + 16 * rf + 4 * (lane >> 4) + v;
+        if (m >= M || j >= R) continue;
+        const uint16_t hv = __builtin_bit_cast(uint16_t, (__bf16)acc[rf][f][v]);
+        if (j < p.r1)
+          p.out1[m * p.ld1 + j] = hv;
+        else
+          p.out2[m * p.ld2 + (j - p.r1)] = hv;
+      }
     }
-  }
+}
+
+template <int RP>
+hipError_t launch_nt_rf(const NtArgs& a, hipStream_t st) {
+  // row fragments per workgroup: as many as still leave >= 256 workgroups
+  // (at most 2 for RP = 256, whose accumulators would spill at 4)
+  constexpr int kMaxRF = RP >= 256 ? 2 : 4;
+  int rf = 1;
+  while (rf < kMaxRF && (a.M + 32 * rf - 1) / (32 * rf) >= 256) rf *= 2;
+  const unsigned grid = (unsigned)((a.M + 16 * rf - 1) / (16 * rf));
+  if (rf == 1)
+    k_skinny_nt<RP, 1><<<grid, 64 * NtShape<RP, 1>::NW, 0, st>>>(a);
+  else if (rf == 2)
+    k_skinny_nt<RP, 2><<<grid, 64 * NtShape<RP, 2>::NW, 0, st>>>(a);
+  else if constexpr (kMaxRF >= 4)
+    k_skinny_nt<RP, 4><<<grid, 64 * NtShape<RP, 4>::NW, 0, st>>>(a);
+  return hipGetLastError();
 }
 
 hipError_t launch_skinny_nt(const NtArgs& a, hipStream_t st) {
   if (a.M == 0) return hipSuccess;
   const int R = a.r1 + a.r2;
-  const unsigned grid = (unsigned)((a.M + 15) / 16);
-#define QL_NT(RPV) k_skinny_nt<RPV><<<grid, 64 * NtShape<RPV>::NW, 0, st>>>(a)
-  if (R <= 16)
-    QL_NT(16);
-  else if (R <= 32)
-    QL_NT(32);
-  else if (R <= 64)
-    QL_NT(64);
-  else if (R <= 128)
-    QL_NT(128);
-  else if (R <= 256)
-    QL_NT(256);
-  else
-    return hipErrorInvalidValue;
-#undef QL_NT
-  return hipGetLastError();
+  if (R <= 16) return launch_nt_rf<16>(a, st);
+  if (R <= 32) return launch_nt_rf<32>(a, st);
+  if (R <= 64) return launch_nt_rf<64>(a, st);
+  if (R <= 128) return launch_nt_rf<128>(a, st);
+  if (R <= 256) return launch_nt_rf<256>(a, st);
+  return hipErrorInvalidValue;
 }
 
 // ---------------------------------------------------------------------------

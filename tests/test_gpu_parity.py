@@ -126,6 +126,9 @@ def test_linear_tiny_workload_full_oracle():
     (64, 128, 256, 256),    # largest rank
     (2000, 1024, 384, 16),  # many row splits in the rank reductions, ragged last split
     (700, 448, 200, 132),   # rank > 128 (reductions in chunks), rank % 8 != 0
+    (8200, 128, 136, 24),   # two 16-row fragments per rank-product workgroup, ragged last group
+    (16400, 64, 72, 40),    # four fragments per workgroup, ragged last group
+    (8232, 64, 80, 200),    # rank 200 with two fragments per workgroup
 ])
 def test_linear_ragged_shapes_full_oracle(M, K, N, r):
     _announce(f"linear ragged M={M} K={K} N={N} r={r}")
@@ -225,6 +228,13 @@ def test_mlp_high_rank_full_oracle(r):
     # splits the forward's paired Z = X.[A_g; A_u]^T (2r > 256)
     _announce(f"mlp high rank M=200 H=128 I=256 r={r}")
     errs = _mlp_case(random_mlp(90 + r, 200, 128, 256, r))
+    assert max(errs.values()) <= TOL, errs
+
+
+def test_mlp_long_batch_full_oracle():
+    # M large enough that the rank products put several 16-row fragments in a workgroup
+    _announce("mlp long batch M=16400 H=64 I=128 r=16")
+    errs = _mlp_case(random_mlp(79, 16400, 64, 128, 16))
     assert max(errs.values()) <= TOL, errs
 
 

@@ -2,6 +2,7 @@
 """Throughput of the fused QLoRA layer (forward + backward) on one MI355X.
 
 python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload attn|tiny|mlp|rsweep|layer] [--rank R]
+                [--mlp-tile T]
 
 A step is one forward and one backward of the workload over one batch of
 seeded synthetic inputs already resident in HBM:
@@ -10,6 +11,8 @@ seeded synthetic inputs already resident in HBM:
   mlp    : SwiGLU block, M=4096, 4096 <-> 14336, LoRA r=16 on gate/up/down
   rsweep : M=8192, K=N=4096, r from --rank (8, 16, 64, 128)
   layer  : the 7 projections of a Llama-3.1-8B GQA decoder layer at M=16384
+--mlp-tile T runs the SwiGLU block of mlp/layer token-tiled (T tokens at a
+time, g/u/h recomputed in the backward) and reports its activation memory.
 Prints one JSON line with tokens/s, useful TFLOP/s (4MNK + 6Mr(N+K) per
 projection), the dominant kernel's roofline (live hipEvent durations) and the
 CPU oracle's throughput on a bounded sample of the same workload.
@@ -41,6 +44,8 @@ def parse():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="attn", choices=sorted(WL_INDEX))
     ap.add_argument("--rank", type=int, default=16)
+    ap.add_argument("--mlp-tile", type=int, default=0,
+                    help="token-tiled SwiGLU block with this many tokens per tile (0: whole batch)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="target CPU time of the oracle baseline")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--cold", action="store_true",
@@ -55,7 +60,9 @@ def parse():
 
 KERNEL_SOURCES = {  # kernel class -> the sources its code is built from
     "gemm_bwd": ["gemm_bwd.hip", "common.hpp"],
+    "gemm_bwd_swiglu": ["gemm_bwd.hip", "common.hpp"],
     "gemm_fwd": ["gemm_fwd.hip", "common.hpp"],
+    "gemm_fwd_gateup": ["gemm_fwd.hip", "common.hpp"],
 }
 
 
@@ -147,7 +154,7 @@ class Proj:
 
 
 class MLP:
-    def __init__(self, q, C, layers, s, X, dY):
+    def __init__(self, q, C, layers, s, X, dY, tile=0):
         import torch
         Ls = []
         for nm in ("gate", "up", "down"):
@@ -158,24 +165,43 @@ class MLP:
         H, I, r = Ls[0].K, Ls[0].N, Ls[0].r
         self.M, self.H, self.I, self.r = M, H, I, r
         self.X, self.dY = X, dY
+        self.tile = tile
         dev = X.device
         e = lambda shape, dt=torch.bfloat16: torch.empty(shape, dtype=dt, device=dev)
-        self.saved = dict(Y=e((M, H)), g=e((M, I)), u=e((M, I)), h=e((M, I)), Z=e((3, M, r)))
         self.dX = e((M, H))
         self.dA = [e((r, L.K), torch.float32) for L in Ls]
         self.dB = [e((L.N, r), torch.float32) for L in Ls]
-        self.ws = e((q.workspace_size(C.OP_MLP_BACKWARD, M, H, I, r),), torch.uint8)
         self.lcs = [L.c() for L in Ls]
         p = lambda t: ctypes.c_void_p(t.data_ptr())
         refs = [ctypes.byref(lc) for lc in self.lcs]
-        sv = self.saved
-        self.fwd_args = (*refs, p(X), M, p(sv["Y"]), p(sv["g"]), p(sv["u"]), p(sv["h"]), p(sv["Z"]), None, 0)
         self._dA = (ctypes.c_void_p * 3)(*[t.data_ptr() for t in self.dA])
         self._dB = (ctypes.c_void_p * 3)(*[t.data_ptr() for t in self.dB])
-        self.bwd_args = (*refs, p(dY), p(X), p(sv["g"]), p(sv["u"]), p(sv["h"]), p(sv["Z"]), M, p(self.dX),
-                         self._dA, self._dB, p(self.ws), self.ws.numel())
+        if tile:
+            sv = self.saved = dict(Y=e((M, H)), Z=e((3, M, r)))
+            self.ws_f = e((q.mlp_tiled_workspace_size(False, M, H, I, r, tile),), torch.uint8)
+            self.ws = e((q.mlp_tiled_workspace_size(True, M, H, I, r, tile),), torch.uint8)
+            self.fwd_args = (*refs, p(X), M, tile, p(sv["Y"]), p(sv["Z"]), p(self.ws_f), self.ws_f.numel())
+            self.bwd_args = (*refs, p(dY), p(X), p(sv["Z"]), M, tile, p(self.dX), self._dA, self._dB, p(self.ws),
+                             self.ws.numel())
+            # what the block keeps between its forward and backward, plus the larger workspace
+            self.activation_bytes = sv["Z"].numel() * 2 + max(self.ws_f.numel(), self.ws.numel())
+        else:
+            sv = self.saved = dict(Y=e((M, H)), g=e((M, I)), u=e((M, I)), h=e((M, I)), Z=e((3, M, r)))
+            self.ws = e((q.workspace_size(C.OP_MLP_BACKWARD, M, H, I, r),), torch.uint8)
+            self.fwd_args = (*refs, p(X), M, p(sv["Y"]), p(sv["g"]), p(sv["u"]), p(sv["h"]), p(sv["Z"]), None, 0)
+            self.bwd_args = (*refs, p(dY), p(X), p(sv["g"]), p(sv["u"]), p(sv["h"]), p(sv["Z"]), M, p(self.dX),
+                             self._dA, self._dB, p(self.ws), self.ws.numel())
+            self.activation_bytes = sum(sv[k].numel() * 2 for k in ("g", "u", "h", "Z")) + self.ws.numel()
 
     def run(self, lib, stream):
+        if self.tile:
+            st = lib.swiglu_mlp_forward_tiled(*self.fwd_args, stream)
+            if st:
+                raise RuntimeError(f"swiglu_mlp_forward_tiled: {st}")
+            st = lib.swiglu_mlp_backward_tiled(*self.bwd_args, stream)
+            if st:
+                raise RuntimeError(f"swiglu_mlp_backward_tiled: {st}")
+            return
         st = lib.swiglu_mlp_forward(*self.fwd_args, stream)
         if st:
             raise RuntimeError(f"swiglu_mlp_forward: {st}")
@@ -184,7 +210,7 @@ class MLP:
             raise RuntimeError(f"swiglu_mlp_backward: {st}")
 
 
-def build_workload(name: str, rank: int):
+def build_workload(name: str, rank: int, mlp_tile: int = 0):
     import torch
     import parameter_efficient_fine_amd as q
     from parameter_efficient_fine_amd import _lib as C
@@ -196,19 +222,23 @@ def build_workload(name: str, rank: int):
     if d["kind"] == "linear":
         parts.append(Proj(q, C, d["layers"]["proj"], d["s"], dev_bf16(d["X"]), dev_bf16(d["dY"])))
     elif d["kind"] == "mlp":
-        parts.append(MLP(q, C, d["layers"], d["s"], dev_bf16(d["X"]), dev_bf16(d["dY"])))
+        parts.append(MLP(q, C, d["layers"], d["s"], dev_bf16(d["X"]), dev_bf16(d["dY"]), mlp_tile))
     else:
         Xa, Xo = dev_bf16(d["X_attn"]), dev_bf16(d["X_o"])
         for nm, X in (("q", Xa), ("k", Xa), ("v", Xa), ("o", Xo)):
             parts.append(Proj(q, C, d["layers"][nm], d["s"], X, dev_bf16(d["dY_" + nm])))
         parts.append(MLP(q, C, {k: d["layers"][k] for k in ("gate", "up", "down")}, d["s"], dev_bf16(d["X_mlp"]),
-                         dev_bf16(d["dY_mlp"])))
+                         dev_bf16(d["dY_mlp"]), mlp_tile))
     torch.cuda.synchronize()
     return d, parts
 
 
-def describe(d, name):
+def describe(d, name, parts=()):
     M, r = d["M"], d["r"]
+    mlps = [p for p in parts if isinstance(p, MLP)]
+    extra = {}
+    if mlps:  # SwiGLU block memory: what its forward keeps for the backward, plus workspace
+        extra = dict(mlp_tile=mlps[0].tile or None, mlp_activation_bytes=mlps[0].activation_bytes)
     if d["kind"] == "linear":
         Lr = d["layers"]["proj"]
         K, N = Lr["W"].shape[1], Lr["W"].shape[0]
@@ -216,10 +246,10 @@ def describe(d, name):
                     M=M, K=K, N=N, r=r, alpha=d["alpha"], weight_format="nf4, fp32 absmax per 64-block")
     if d["kind"] == "mlp":
         return dict(workload=f"{name}: SwiGLU block, M={M}, 4096<->14336, LoRA r={r} on gate/up/down",
-                    M=M, H=4096, I=14336, r=r, alpha=d["alpha"], weight_format="nf4, fp32 absmax per 64-block")
+                    M=M, H=4096, I=14336, r=r, alpha=d["alpha"], weight_format="nf4, fp32 absmax per 64-block", **extra)
     return dict(workload=f"{name}: 7 projections of a GQA decoder layer (q,o 4096x4096; k,v 4096->1024; "
                          f"gate/up/down 4096<->14336), M={M}, r={r}", M=M, r=r, alpha=d["alpha"],
-                weight_format="nf4, fp32 absmax per 64-block")
+                weight_format="nf4, fp32 absmax per 64-block", **extra)
 
 
 # ---------------------------------------------------------------------------
@@ -234,11 +264,16 @@ def gemm_flops(parts):
             out.setdefault("gemm_fwd", []).append(2 * M * N * K + 2 * M * N * r)   # X.W^T + Z.B^T
             out.setdefault("gemm_bwd", []).append(2 * M * N * K + 2 * M * K * r)   # dY.W + G.A
         else:
-            M, H, I, r = p.M, p.H, p.I, p.r
-            out.setdefault("gemm_fwd_gateup", []).append(2 * (2 * M * I * H + 2 * M * I * r))
-            out.setdefault("gemm_fwd", []).append(2 * M * H * I + 2 * M * H * r)
-            out.setdefault("gemm_bwd_swiglu", []).append(2 * M * H * I + 2 * M * I * r)
-            out.setdefault("gemm_bwd", []).append(2 * (2 * M * I * H + 2 * M * H * r))
+            H, I, r = p.H, p.I, p.r
+            T = p.tile if p.tile else p.M
+            for t0 in range(0, p.M, T):  # one set of launches per token tile
+                M = min(T, p.M - t0)
+                gateup = 2 * (2 * M * I * H + 2 * M * I * r)
+                # a tiled backward recomputes the tile's g, u, h with the same kernel
+                out.setdefault("gemm_fwd_gateup", []).extend([gateup] * (2 if p.tile else 1))
+                out.setdefault("gemm_fwd", []).append(2 * M * H * I + 2 * M * H * r)
+                out.setdefault("gemm_bwd_swiglu", []).append(2 * M * H * I + 2 * M * I * r)
+                out.setdefault("gemm_bwd", []).append(2 * (2 * M * I * H + 2 * M * H * r))
     return out
 
 
@@ -312,7 +347,7 @@ def main():
     from synthetic import useful_flops
 
     lib = C.lib()
-    d, parts = build_workload(args.workload, args.rank)
+    d, parts = build_workload(args.workload, args.rank, args.mlp_tile)
     c = WL_INDEX[args.workload]
     sub = d["sub"] if args.workload == "rsweep" else 0
     flops = useful_flops(c, sub)
@@ -355,7 +390,7 @@ def main():
         step_stats["cold_median_ms"] = float(np.median(cold))
 
     # same steps again with per-launch hipEvents recorded by the library (kernel durations)
-    with KernelTimer(max_launches=args.steps * 64 + 64) as kt:
+    with KernelTimer(max_launches=args.steps * 256 + 64) as kt:
         for _ in range(args.steps):
             step()
     torch.cuda.synchronize()
@@ -389,7 +424,7 @@ def main():
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic (seeded N(0,1) activations, 0.02*N(0,1) weights quantized to NF4)",
-        "config": describe(d, args.workload),
+        "config": describe(d, args.workload, parts),
         "useful_tflops": tflops,
         "mfma_peak_frac": tflops / PEAK_BF16_TFLOPS,
         "useful_gflop_per_step": flops / 1e9,

@@ -116,6 +116,32 @@ int swiglu_mlp_backward(const qlora_layer* gate, const qlora_layer* up, const ql
                         const uint16_t* h_save, const uint16_t* Z_save, int64_t M, uint16_t* dX,
                         float* const dA[3], float* const dB[3], void* ws, size_t ws_bytes, void* stream);
 
+/* Token-tiled SwiGLU block ("Unsloth vs PyTorch" video, 4:25-4:36: tiled
+ * feed-forward layers for long context). The batch is cut into tiles of
+ * `tile` tokens (the last one ragged), and only one tile's intermediates exist
+ * at a time:
+ *   forward  - per tile, g, u, h are formed in the workspace and dropped after
+ *              the tile's Y rows; nothing of size M x I is saved. Z_save
+ *              [3][M][r] (gate, up, down) is written as by swiglu_mlp_forward.
+ *   backward - per tile, g, u, h are recomputed from X and Z_save (the same
+ *              kernels on the same inputs: bitwise the forward's values), then
+ *              the block's backward runs on the tile; dX rows are written per
+ *              tile and dA/dB are summed over the tiles in tile order.
+ * Y, Z_save and dX equal swiglu_mlp_forward/backward's bit for bit (every
+ * token's row is computed the same way); dA and dB differ only by the fp32
+ * summation order across tiles (identical when tile >= M). The workspace
+ * scales with min(tile, M), not M: size from
+ * swiglu_mlp_tiled_workspace_size(backward = 0 or 1, M, H, I, r, tile).
+ * tile >= 1 (a multiple of 256 keeps every GEMM tile full). */
+size_t swiglu_mlp_tiled_workspace_size(int backward, int64_t M, int64_t H, int64_t I, int64_t r, int64_t tile);
+int swiglu_mlp_forward_tiled(const qlora_layer* gate, const qlora_layer* up, const qlora_layer* down,
+                             const uint16_t* X, int64_t M, int64_t tile, uint16_t* Y, uint16_t* Z_save, void* ws,
+                             size_t ws_bytes, void* stream);
+int swiglu_mlp_backward_tiled(const qlora_layer* gate, const qlora_layer* up, const qlora_layer* down,
+                              const uint16_t* dY, const uint16_t* X, const uint16_t* Z_save, int64_t M, int64_t tile,
+                              uint16_t* dX, float* const dA[3], float* const dB[3], void* ws, size_t ws_bytes,
+                              void* stream);
+
 /* Measurement support (off the hot path; not thread-safe).
  * qlora_profile_begin creates, once, a pool of 2*max_launches hipEvents and
  * from then on brackets each kernel launch made by this library with an event

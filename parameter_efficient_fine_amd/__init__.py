@@ -11,7 +11,10 @@ from .ops import (  # noqa: F401
     dequantize,
     forward,
     mlp_backward,
+    mlp_backward_tiled,
     mlp_forward,
+    mlp_forward_tiled,
+    mlp_tiled_workspace_size,
     quantize,
     workspace_size,
 )

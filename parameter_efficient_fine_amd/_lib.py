@@ -22,7 +22,8 @@ OP_FORWARD, OP_BACKWARD, OP_MLP_FORWARD, OP_MLP_BACKWARD = 0, 1, 2, 3
 # Every function the header declares (checked by the CPU tests against include/qlora.h).
 EXPORTS = [
     "qlora_quantize", "qlora_dequantize", "qlora_workspace_size", "qlora_forward", "qlora_backward",
-    "swiglu_mlp_forward", "swiglu_mlp_backward", "qlora_profile_begin", "qlora_profile_end",
+    "swiglu_mlp_forward", "swiglu_mlp_backward", "swiglu_mlp_tiled_workspace_size", "swiglu_mlp_forward_tiled",
+    "swiglu_mlp_backward_tiled", "qlora_profile_begin", "qlora_profile_end",
     "qlora_status_string", "qlora_last_error",
 ]
 
@@ -72,6 +73,11 @@ def lib():
     L.swiglu_mlp_forward.argtypes = [LP, LP, LP, vp, i64, vp, vp, vp, vp, vp, vp, sz, vp]
     L.swiglu_mlp_backward.argtypes = [LP, LP, LP, vp, vp, vp, vp, vp, vp, i64, vp,
                                       ctypes.POINTER(vp), ctypes.POINTER(vp), vp, sz, vp]
+    L.swiglu_mlp_tiled_workspace_size.argtypes = [ctypes.c_int, i64, i64, i64, i64, i64]
+    L.swiglu_mlp_tiled_workspace_size.restype = sz
+    L.swiglu_mlp_forward_tiled.argtypes = [LP, LP, LP, vp, i64, i64, vp, vp, vp, sz, vp]
+    L.swiglu_mlp_backward_tiled.argtypes = [LP, LP, LP, vp, vp, vp, i64, i64, vp, ctypes.POINTER(vp),
+                                            ctypes.POINTER(vp), vp, sz, vp]
     L.qlora_profile_begin.argtypes = [ctypes.c_int]
     L.qlora_profile_begin.restype = ctypes.c_int
     L.qlora_profile_end.argtypes = [ctypes.POINTER(KernelTimeC), ctypes.c_int, ctypes.POINTER(ctypes.c_int)]
@@ -81,7 +87,7 @@ def lib():
     L.qlora_last_error.argtypes = []
     L.qlora_last_error.restype = ctypes.c_char_p
     for f in ("qlora_quantize", "qlora_dequantize", "qlora_forward", "qlora_backward", "swiglu_mlp_forward",
-              "swiglu_mlp_backward"):
+              "swiglu_mlp_backward", "swiglu_mlp_forward_tiled", "swiglu_mlp_backward_tiled"):
         getattr(L, f).restype = ctypes.c_int
     _lib = L
     return L

@@ -1,7 +1,7 @@
 // C ABI of the fused QLoRA layer: argument checks, workspace carving and the
 // kernel sequence of each call on the caller's stream. The math of each step
-// is stated in include/qlora.h; the kernels live in quant.hip, skinny.hip and
-// gemm.hip.
+// is stated in include/qlora.h; the kernels live in quant.hip, skinny.hip,
+// gemm_fwd.hip and gemm_bwd.hip.
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
@@ -151,6 +151,19 @@ size_t mlp_bwd_ws(int64_t M, int64_t H, int64_t I, int64_t r) {
          2 * up256(r * I * 2) + up256(l.part * 4);
 }
 
+// Token-tiled SwiGLU block: per-tile intermediates only (tile T = min(tile, M)).
+size_t mlp_fwd_tiled_ws(int64_t M, int64_t I, int64_t tile) {
+  const int64_t T = std::min(tile, M);
+  return 3 * up256((size_t)T * I * 2);  // g, u, h of one tile
+}
+
+size_t mlp_bwd_tiled_ws(int64_t M, int64_t H, int64_t I, int64_t r, int64_t tile) {
+  const int64_t T = std::min(tile, M);
+  const BwdLayout l = mlp_bwd_layout(T, H, I, r);
+  return 5 * up256((size_t)T * I * 2) + up256(T * r * 2) + up256(T * 2 * r * 2) + up256(r * H * 2) +
+         2 * up256(r * I * 2) + up256(l.part * 4);
+}
+
 WSrc wsrc(const qlora_layer* L, const uint16_t* lora_i, const uint16_t* lora_j, int64_t ldj = 0) {
   WSrc w;
   w.codes = L->codes;
@@ -185,6 +198,7 @@ NtArgs nt1(const uint16_t* in, int64_t M, int64_t Kd, const uint16_t* ad, int r,
 struct TnCall {
   float* part;
   hipStream_t st;
+  int accumulate = 0;  // add to the outputs instead of overwriting them
   TnJobs jobs{};
   int rc = QLORA_OK;
   // out = s * P^T . Q (P [M, r] with row stride ldp, Q [M, Kd]); transposed -> [Kd, r]
@@ -212,6 +226,7 @@ struct TnCall {
       a.out2 = out2 ? out2 : out1;
       a.ldo2 = transposed ? r2 : Kd;
       a.transposed = transposed ? 1 : 0;
+      a.accumulate = accumulate;
       a.Q = Q;
       a.M = M;
       a.Kd = Kd;
@@ -337,6 +352,127 @@ static bool mlp_shapes_ok(const qlora_layer* g, const qlora_layer* u, const qlor
   return true;
 }
 
+}  // extern "C"
+
+namespace {
+
+// Z_g, Z_u = X.A_g^T, X.A_u^T (row stride r each)
+int mlp_zgu(const qlora_layer* gate, const qlora_layer* up, const uint16_t* X, int64_t M, uint16_t* Zg, uint16_t* Zu,
+            hipStream_t st) {
+  const int64_t H = gate->K;
+  const int r = (int)gate->r;
+  if (2 * r <= 256) {
+    NtArgs a = nt1(X, M, H, gate->A, r, Zg, r);
+    a.ad2 = up->A;
+    a.r2 = r;
+    a.out2 = Zu;
+    QL_LAUNCH("skinny_nt", st, launch_skinny_nt(a, st));
+  } else {
+    QL_LAUNCH("skinny_nt", st, launch_skinny_nt(nt1(X, M, H, gate->A, r, Zg, r), st));
+    QL_LAUNCH("skinny_nt", st, launch_skinny_nt(nt1(X, M, H, up->A, r, Zu, r), st));
+  }
+  return QLORA_OK;
+}
+
+// SwiGLU block forward over M tokens: g, u, h, then Z_d and Y.
+int mlp_fwd_body(const qlora_layer* gate, const qlora_layer* up, const qlora_layer* down, const uint16_t* X,
+                 int64_t M, uint16_t* Y, uint16_t* g, uint16_t* u, uint16_t* h, uint16_t* Zg, uint16_t* Zu,
+                 uint16_t* Zd, hipStream_t st) {
+  const int64_t H = gate->K, I = gate->N;
+  const int r = (int)gate->r;
+  if (int rc = mlp_zgu(gate, up, X, M, Zg, Zu, st)) return rc;
+  QL_LAUNCH("gemm_fwd_gateup", st,
+            launch_gemm_fwd_gateup(X, M, H, I, wsrc(gate, gate->B, Zg), wsrc(up, up->B, Zu), g, u, h, st));
+  QL_LAUNCH("skinny_nt", st, launch_skinny_nt(nt1(h, M, I, down->A, r, Zd, r), st));
+  QL_LAUNCH("gemm_fwd", st, launch_gemm_fwd(h, M, I, H, wsrc(down, down->B, Zd), Y, st));
+  return QLORA_OK;
+}
+
+struct MlpBwdWs {
+  uint16_t *dg, *du, *Gd, *Ggu, *Btd, *Btg, *Btu;
+  float* part;
+};
+
+MlpBwdWs carve_mlp_bwd(Carve& c, int64_t M, int64_t H, int64_t I, int64_t r, size_t part_floats) {
+  MlpBwdWs w;
+  w.dg = c.take<uint16_t>((size_t)M * I);
+  w.du = c.take<uint16_t>((size_t)M * I);
+  w.Gd = c.take<uint16_t>((size_t)M * r);
+  w.Ggu = c.take<uint16_t>((size_t)M * 2 * r);  // row m: G_gate[m, :] then G_up[m, :]
+  w.Btd = c.take<uint16_t>((size_t)r * H);
+  w.Btg = c.take<uint16_t>((size_t)r * I);
+  w.Btu = c.take<uint16_t>((size_t)r * I);
+  w.part = c.take<float>(part_floats);
+  return w;
+}
+
+int mlp_zero_grads(const qlora_layer* gate, const qlora_layer* up, const qlora_layer* down, float* const dA[3],
+                   float* const dB[3], hipStream_t st) {
+  const qlora_layer* Ls[3] = {gate, up, down};
+  for (int i = 0; i < 3; ++i) {
+    QL_LAUNCH("fill_zero_f32", st, launch_fill_zero_f32(dA[i], Ls[i]->r * Ls[i]->K, st));
+    QL_LAUNCH("fill_zero_f32", st, launch_fill_zero_f32(dB[i], Ls[i]->N * Ls[i]->r, st));
+  }
+  return QLORA_OK;
+}
+
+int mlp_prep(const qlora_layer* gate, const qlora_layer* up, const qlora_layer* down, const MlpBwdWs& w,
+             hipStream_t st) {
+  const int64_t H = gate->K, I = gate->N, r = gate->r;
+  PrepJobs pj{};
+  pj.job[0] = {down->B, w.Btd, H, r};
+  pj.job[1] = {gate->B, w.Btg, I, r};
+  pj.job[2] = {up->B, w.Btu, I, r};
+  pj.n = 3;
+  QL_LAUNCH("prep", st, launch_prep(pj, st));
+  return QLORA_OK;
+}
+
+// SwiGLU block backward over M tokens, after mlp_prep. accumulate = 1 adds
+// the adapter gradients to dA/dB (later tiles of a batch).
+int mlp_bwd_body(const qlora_layer* gate, const qlora_layer* up, const qlora_layer* down, const uint16_t* dY,
+                 const uint16_t* X, const uint16_t* g, const uint16_t* u, const uint16_t* h, const uint16_t* Zg,
+                 const uint16_t* Zu, const uint16_t* Zd, int64_t M, uint16_t* dX, float* const dA[3],
+                 float* const dB[3], const MlpBwdWs& w, int accumulate, hipStream_t st) {
+  const int64_t H = gate->K, I = gate->N;
+  const int r = (int)gate->r;
+  uint16_t* Gg = w.Ggu;
+  uint16_t* Gu = w.Ggu + r;
+  TnCall tn{w.part, st, accumulate};
+  // down projection: G_d = dY.B_d ; dB_d = s.dY^T.Z_d and dA_d = s.G_d^T.h ; dh -> (dg, du) in the GEMM epilogue
+  QL_LAUNCH("skinny_nt", st, launch_skinny_nt(nt1(dY, M, H, w.Btd, r, w.Gd, r), st));
+  tn.one(Zd, r, r, down->s, dY, M, H, dB[2], true);
+  tn.one(w.Gd, r, r, down->s, h, M, I, dA[2], false);
+  if (int rc = tn.flush()) return rc;
+  QL_LAUNCH("gemm_bwd_swiglu", st,
+            launch_gemm_bwd_swiglu(dY, wsrc(down, down->A, w.Gd), M, I, H, g, u, w.dg, w.du, st));
+  // gate and up: G = d(g|u).B ; dB = s.d(g|u)^T.Z ; dA_g = s_g.G_g^T.X and dA_u = s_u.G_u^T.X
+  // (one pass over X when 2r fits a launch)
+  QL_LAUNCH("skinny_nt", st, launch_skinny_nt(nt1(w.dg, M, I, w.Btg, r, Gg, 2 * r), st));
+  QL_LAUNCH("skinny_nt", st, launch_skinny_nt(nt1(w.du, M, I, w.Btu, r, Gu, 2 * r), st));
+  tn.one(Zg, r, r, gate->s, w.dg, M, I, dB[0], true);
+  tn.one(Zu, r, r, up->s, w.du, M, I, dB[1], true);
+  tn.two(w.Ggu, 2 * r, r, gate->s, dA[0], r, up->s, dA[1], X, M, H, false);
+  if (int rc = tn.flush()) return rc;
+  // dX = dg.W_g + du.W_u + s.G_g.A_g + s.G_u.A_u : one GEMM over the concatenated reduction
+  if (dX)
+    QL_LAUNCH("gemm_bwd", st,
+              launch_gemm_bwd(w.dg, wsrc(gate, gate->A, Gg, 2 * r), w.du, wsrc(up, up->A, Gu, 2 * r), M, H, I, dX,
+                              st));
+  return QLORA_OK;
+}
+
+bool mlp_grads_ok(float* const dA[3], float* const dB[3]) {
+  if (!dA || !dB) return false;
+  for (int i = 0; i < 3; ++i)
+    if (!dA[i] || !dB[i] || !aligned16(dA[i]) || !aligned16(dB[i])) return false;
+  return true;
+}
+
+}  // namespace
+
+extern "C" {
+
 int swiglu_mlp_forward(const qlora_layer* gate, const qlora_layer* up, const qlora_layer* down, const uint16_t* X,
                        int64_t M, uint16_t* Y, uint16_t* g_save, uint16_t* u_save, uint16_t* h_save,
                        uint16_t* Z_save, void* ws, size_t ws_bytes, void* stream) {
@@ -348,38 +484,17 @@ int swiglu_mlp_forward(const qlora_layer* gate, const qlora_layer* up, const qlo
   if (!aligned16(X) || !aligned16(Y) || !aligned16(g_save) || !aligned16(u_save) || !aligned16(h_save) ||
       !aligned16(Z_save))
     return QLORA_EINVAL;
-  hipStream_t st = (hipStream_t)stream;
-  const int64_t H = gate->K, I = gate->N;
-  const int r = (int)gate->r;
-  uint16_t* Zg = Z_save;
-  uint16_t* Zu = Z_save + (size_t)M * r;
-  uint16_t* Zd = Z_save + 2 * (size_t)M * r;
-  if (2 * r <= 256) {
-    NtArgs a = nt1(X, M, H, gate->A, r, Zg, r);
-    a.ad2 = up->A;
-    a.r2 = r;
-    a.out2 = Zu;
-    QL_LAUNCH("skinny_nt", st, launch_skinny_nt(a, st));
-  } else {
-    QL_LAUNCH("skinny_nt", st, launch_skinny_nt(nt1(X, M, H, gate->A, r, Zg, r), st));
-    QL_LAUNCH("skinny_nt", st, launch_skinny_nt(nt1(X, M, H, up->A, r, Zu, r), st));
-  }
-  QL_LAUNCH("gemm_fwd_gateup", st, launch_gemm_fwd_gateup(X, M, H, I, wsrc(gate, gate->B, Zg), wsrc(up, up->B, Zu), g_save, u_save, h_save,
-                                  st));
-  QL_LAUNCH("skinny_nt", st, launch_skinny_nt(nt1(h_save, M, I, down->A, r, Zd, r), st));
-  QL_LAUNCH("gemm_fwd", st, launch_gemm_fwd(h_save, M, I, H, wsrc(down, down->B, Zd), Y, st));
-  return QLORA_OK;
+  const size_t Mr = (size_t)M * gate->r;
+  return mlp_fwd_body(gate, up, down, X, M, Y, g_save, u_save, h_save, Z_save, Z_save + Mr, Z_save + 2 * Mr,
+                      (hipStream_t)stream);
 }
 
 int swiglu_mlp_backward(const qlora_layer* gate, const qlora_layer* up, const qlora_layer* down, const uint16_t* dY,
                         const uint16_t* X, const uint16_t* g_save, const uint16_t* u_save, const uint16_t* h_save,
                         const uint16_t* Z_save, int64_t M, uint16_t* dX, float* const dA[3], float* const dB[3],
                         void* ws, size_t ws_bytes, void* stream) {
-  if (!mlp_shapes_ok(gate, up, down) || M < 0 || !dA || !dB) return QLORA_EINVAL;
-  for (int i = 0; i < 3; ++i)
-    if (!dA[i] || !dB[i] || !aligned16(dA[i]) || !aligned16(dB[i])) return QLORA_EINVAL;
-  const int64_t H = gate->K, I = gate->N;
-  const int r = (int)gate->r;
+  if (!mlp_shapes_ok(gate, up, down) || M < 0 || !mlp_grads_ok(dA, dB)) return QLORA_EINVAL;
+  const int64_t H = gate->K, I = gate->N, r = gate->r;
   hipStream_t st = (hipStream_t)stream;
   if (M > 0) {
     if (!dY || !X || !g_save || !u_save || !h_save || !Z_save) return QLORA_EINVAL;
@@ -387,58 +502,80 @@ int swiglu_mlp_backward(const qlora_layer* gate, const qlora_layer* up, const ql
         !aligned16(Z_save) || (dX && !aligned16(dX)))
       return QLORA_EINVAL;
   }
-  const size_t need = mlp_bwd_ws(M, H, I, r);
-  if (!ws || ws_bytes < need) return QLORA_EWORKSPACE;
-  const BwdLayout lay = mlp_bwd_layout(M, H, I, r);
+  if (!ws || ws_bytes < mlp_bwd_ws(M, H, I, r)) return QLORA_EWORKSPACE;
   Carve c{(char*)ws, ws_bytes};
-  uint16_t* dg = c.take<uint16_t>((size_t)M * I);
-  uint16_t* du = c.take<uint16_t>((size_t)M * I);
-  uint16_t* Gd = c.take<uint16_t>((size_t)M * r);
-  uint16_t* Ggu = c.take<uint16_t>((size_t)M * 2 * r);  // row m: G_gate[m, :] then G_up[m, :]
-  uint16_t* Btd = c.take<uint16_t>((size_t)r * H);
-  uint16_t* Btg = c.take<uint16_t>((size_t)r * I);
-  uint16_t* Btu = c.take<uint16_t>((size_t)r * I);
-  float* part = c.take<float>(lay.part);
+  const MlpBwdWs w = carve_mlp_bwd(c, M, H, I, r, mlp_bwd_layout(M, H, I, r).part);
   if (!c.ok) return QLORA_EWORKSPACE;
-  if (M == 0) {
-    const qlora_layer* Ls[3] = {gate, up, down};
-    for (int i = 0; i < 3; ++i) {
-      QL_LAUNCH("fill_zero_f32", st, launch_fill_zero_f32(dA[i], (int64_t)r * Ls[i]->K, st));
-      QL_LAUNCH("fill_zero_f32", st, launch_fill_zero_f32(dB[i], (int64_t)Ls[i]->N * r, st));
-    }
-    return QLORA_OK;
+  if (M == 0) return mlp_zero_grads(gate, up, down, dA, dB, st);
+  if (int rc = mlp_prep(gate, up, down, w, st)) return rc;
+  const size_t Mr = (size_t)M * r;
+  return mlp_bwd_body(gate, up, down, dY, X, g_save, u_save, h_save, Z_save, Z_save + Mr, Z_save + 2 * Mr, M, dX,
+                      dA, dB, w, 0, st);
+}
+
+size_t swiglu_mlp_tiled_workspace_size(int backward, int64_t M, int64_t H, int64_t I, int64_t r, int64_t tile) {
+  if (M < 0 || H < 0 || I < 0 || r < 1 || tile < 1) return 0;
+  return backward ? mlp_bwd_tiled_ws(M, H, I, r, tile) : mlp_fwd_tiled_ws(M, I, tile);
+}
+
+int swiglu_mlp_forward_tiled(const qlora_layer* gate, const qlora_layer* up, const qlora_layer* down,
+                             const uint16_t* X, int64_t M, int64_t tile, uint16_t* Y, uint16_t* Z_save, void* ws,
+                             size_t ws_bytes, void* stream) {
+  if (!mlp_shapes_ok(gate, up, down) || M < 0 || tile < 1) return QLORA_EINVAL;
+  if (M == 0) return QLORA_OK;
+  if (!X || !Y || !Z_save || !aligned16(X) || !aligned16(Y) || !aligned16(Z_save)) return QLORA_EINVAL;
+  const int64_t H = gate->K, I = gate->N, r = gate->r;
+  const int64_t T = std::min(tile, M);
+  if (!ws || ws_bytes < mlp_fwd_tiled_ws(M, I, tile)) return QLORA_EWORKSPACE;
+  Carve c{(char*)ws, ws_bytes};
+  uint16_t* g = c.take<uint16_t>((size_t)T * I);
+  uint16_t* u = c.take<uint16_t>((size_t)T * I);
+  uint16_t* h = c.take<uint16_t>((size_t)T * I);
+  if (!c.ok) return QLORA_EWORKSPACE;
+  hipStream_t st = (hipStream_t)stream;
+  const size_t Mr = (size_t)M * r;
+  for (int64_t t0 = 0; t0 < M; t0 += T) {
+    const int64_t Mt = std::min(T, M - t0);
+    uint16_t* Zt = Z_save + (size_t)t0 * r;
+    if (int rc = mlp_fwd_body(gate, up, down, X + t0 * H, Mt, Y + t0 * H, g, u, h, Zt, Zt + Mr, Zt + 2 * Mr, st))
+      return rc;
   }
-  const uint16_t* Zg = Z_save;
-  const uint16_t* Zu = Z_save + (size_t)M * r;
-  const uint16_t* Zd = Z_save + 2 * (size_t)M * r;
-  uint16_t* Gg = Ggu;
-  uint16_t* Gu = Ggu + r;
-  PrepJobs pj{};
-  pj.job[0] = {down->B, Btd, H, r};
-  pj.job[1] = {gate->B, Btg, I, r};
-  pj.job[2] = {up->B, Btu, I, r};
-  pj.n = 3;
-  QL_LAUNCH("prep", st, launch_prep(pj, st));
-  TnCall tn{part, st};
-  // down projection: G_d = dY.B_d ; dB_d = s.dY^T.Z_d and dA_d = s.G_d^T.h ; dh -> (dg, du) in the GEMM epilogue
-  QL_LAUNCH("skinny_nt", st, launch_skinny_nt(nt1(dY, M, H, Btd, r, Gd, r), st));
-  tn.one(Zd, r, r, down->s, dY, M, H, dB[2], true);
-  tn.one(Gd, r, r, down->s, h_save, M, I, dA[2], false);
-  if (int rc = tn.flush()) return rc;
-  QL_LAUNCH("gemm_bwd_swiglu", st,
-            launch_gemm_bwd_swiglu(dY, wsrc(down, down->A, Gd), M, I, H, g_save, u_save, dg, du, st));
-  // gate and up: G = d(g|u).B ; dB = s.d(g|u)^T.Z ; dA_g = s_g.G_g^T.X and dA_u = s_u.G_u^T.X
-  // (one pass over X when 2r fits a launch)
-  QL_LAUNCH("skinny_nt", st, launch_skinny_nt(nt1(dg, M, I, Btg, r, Gg, 2 * r), st));
-  QL_LAUNCH("skinny_nt", st, launch_skinny_nt(nt1(du, M, I, Btu, r, Gu, 2 * r), st));
-  tn.one(Zg, r, r, gate->s, dg, M, I, dB[0], true);
-  tn.one(Zu, r, r, up->s, du, M, I, dB[1], true);
-  tn.two(Ggu, 2 * r, r, gate->s, dA[0], r, up->s, dA[1], X, M, H, false);
-  if (int rc = tn.flush()) return rc;
-  // dX = dg.W_g + du.W_u + s.G_g.A_g + s.G_u.A_u : one GEMM over the concatenated reduction
-  if (dX)
-    QL_LAUNCH("gemm_bwd", st,
-              launch_gemm_bwd(dg, wsrc(gate, gate->A, Gg, 2 * r), du, wsrc(up, up->A, Gu, 2 * r), M, H, I, dX, st));
+  return QLORA_OK;
+}
+
+int swiglu_mlp_backward_tiled(const qlora_layer* gate, const qlora_layer* up, const qlora_layer* down,
+                              const uint16_t* dY, const uint16_t* X, const uint16_t* Z_save, int64_t M, int64_t tile,
+                              uint16_t* dX, float* const dA[3], float* const dB[3], void* ws, size_t ws_bytes,
+                              void* stream) {
+  if (!mlp_shapes_ok(gate, up, down) || M < 0 || tile < 1 || !mlp_grads_ok(dA, dB)) return QLORA_EINVAL;
+  const int64_t H = gate->K, I = gate->N, r = gate->r;
+  hipStream_t st = (hipStream_t)stream;
+  if (M > 0) {
+    if (!dY || !X || !Z_save || !aligned16(dY) || !aligned16(X) || !aligned16(Z_save) || (dX && !aligned16(dX)))
+      return QLORA_EINVAL;
+  }
+  const int64_t T = std::min(tile, M);
+  if (!ws || ws_bytes < mlp_bwd_tiled_ws(M, H, I, r, tile)) return QLORA_EWORKSPACE;
+  Carve c{(char*)ws, ws_bytes};
+  uint16_t* g = c.take<uint16_t>((size_t)T * I);
+  uint16_t* u = c.take<uint16_t>((size_t)T * I);
+  uint16_t* h = c.take<uint16_t>((size_t)T * I);
+  const MlpBwdWs w = carve_mlp_bwd(c, T, H, I, r, mlp_bwd_layout(T, H, I, r).part);
+  if (!c.ok) return QLORA_EWORKSPACE;
+  if (M == 0) return mlp_zero_grads(gate, up, down, dA, dB, st);
+  if (int rc = mlp_prep(gate, up, down, w, st)) return rc;
+  const size_t Mr = (size_t)M * r;
+  for (int64_t t0 = 0; t0 < M; t0 += T) {
+    const int64_t Mt = std::min(T, M - t0);
+    const uint16_t* Xt = X + t0 * H;
+    const uint16_t* Zt = Z_save + (size_t)t0 * r;
+    // recompute the tile's g, u, h (bitwise what the forward produced: same kernels, same inputs)
+    QL_LAUNCH("gemm_fwd_gateup", st,
+              launch_gemm_fwd_gateup(Xt, Mt, H, I, wsrc(gate, gate->B, Zt), wsrc(up, up->B, Zt + Mr), g, u, h, st));
+    if (int rc = mlp_bwd_body(gate, up, down, dY + t0 * H, Xt, g, u, h, Zt, Zt + Mr, Zt + 2 * Mr, Mt,
+                              dX ? dX + t0 * H : nullptr, dA, dB, w, t0 > 0 ? 1 : 0, st))
+      return rc;
+  }
   return QLORA_OK;
 }
 

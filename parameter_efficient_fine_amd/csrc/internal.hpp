@@ -50,6 +50,7 @@ struct TnArgs {
   float* out2;
   int64_t ldo1, ldo2;
   int transposed;
+  int accumulate;       // 1: add the result to what out1/out2 hold (sums over batch tiles)
   const uint16_t* Q;
   int64_t M, Kd;
   float* part;          // [splits, R, Kd]

@@ -193,7 +193,8 @@ hipError_t launch_skinny_nt(const NtArgs& a, hipStream_t st) {
 // ds_read_b64_tr_b16 (each lane then holds 8 consecutive rows: the reduction
 // dimension). Two register sets keep the next two 64-row tiles in flight while
 // one is consumed. Each split stores an fp32 partial; k_tn_reduce then adds
-// the partials in split order (deterministic), scales, and writes the result.
+// the partials in split order (deterministic), scales, and writes the result
+// (or adds it to the output, when a batch is reduced tile by tile).
 
 constexpr int kTnCols = 128;
 constexpr int kTnRows = 64;
@@ -399,9 +400,13 @@ __global__ __launch_bounds__(64) void k_tn_reduce(TnJobs jobs) {
   sum *= s;
   if (p.transposed) {
 #pragma unroll
-    for (int c = 0; c < 4; ++c) out[(k + c) * ldo + jr] = sum[c];
+    for (int c = 0; c < 4; ++c) {
+      float* o = out + (k + c) * ldo + jr;
+      *o = p.accumulate ? *o + sum[c] : sum[c];
+    }
   } else {
-    *reinterpret_cast<f32x4*>(out + jr * ldo + k) = sum;
+    f32x4* o = reinterpret_cast<f32x4*>(out + jr * ldo + k);
+    *o = p.accumulate ? *o + sum : sum;
   }
 }
 

@@ -162,6 +162,52 @@ def mlp_backward(gate: QLoraLayer, up: QLoraLayer, down: QLoraLayer, dY, X, save
     return out
 
 
+def mlp_tiled_workspace_size(backward: bool, M: int, H: int, I: int, r: int, tile: int) -> int:
+    return int(C.lib().swiglu_mlp_tiled_workspace_size(1 if backward else 0, M, H, I, r, tile))
+
+
+def mlp_forward_tiled(gate: QLoraLayer, up: QLoraLayer, down: QLoraLayer, X, tile: int, ws=None, out=None):
+    """dict(Y, Z) for the SwiGLU block computed `tile` tokens at a time (no g, u, h kept)."""
+    M = X.shape[0]
+    H, I, r = gate.K, gate.N, gate.r
+    _need(X, torch.bfloat16, (M, H), "X")
+    dev = X.device
+    if out is None:
+        out = dict(Y=torch.empty((M, H), dtype=torch.bfloat16, device=dev),
+                   Z=torch.empty((3, M, r), dtype=torch.bfloat16, device=dev))
+    nb = mlp_tiled_workspace_size(False, M, H, I, r, tile)
+    ws = _workspace(nb, dev) if ws is None else ws
+    lg, lu, ld = gate.c(), up.c(), down.c()
+    C.check("swiglu_mlp_forward_tiled", C.lib().swiglu_mlp_forward_tiled(
+        ctypes.byref(lg), ctypes.byref(lu), ctypes.byref(ld), _ptr(X), M, tile, _ptr(out["Y"]), _ptr(out["Z"]),
+        _ptr(ws), ws.numel(), _stream()))
+    return out
+
+
+def mlp_backward_tiled(gate: QLoraLayer, up: QLoraLayer, down: QLoraLayer, dY, X, Z, tile: int, need_dX=True,
+                       ws=None, out=None):
+    """dict(dX, dA, dB) of the SwiGLU block, `tile` tokens at a time (g, u, h recomputed per tile)."""
+    M = X.shape[0]
+    H, I, r = gate.K, gate.N, gate.r
+    _need(dY, torch.bfloat16, (M, H), "dY")
+    _need(X, torch.bfloat16, (M, H), "X")
+    _need(Z, torch.bfloat16, (3, M, r), "Z")
+    dev = X.device
+    if out is None:
+        out = dict(dX=torch.empty((M, H), dtype=torch.bfloat16, device=dev) if need_dX else None,
+                   dA=[torch.empty((r, L.K), dtype=torch.float32, device=dev) for L in (gate, up, down)],
+                   dB=[torch.empty((L.N, r), dtype=torch.float32, device=dev) for L in (gate, up, down)])
+    nb = mlp_tiled_workspace_size(True, M, H, I, r, tile)
+    ws = _workspace(nb, dev) if ws is None else ws
+    dA = (ctypes.c_void_p * 3)(*[t.data_ptr() for t in out["dA"]])
+    dB = (ctypes.c_void_p * 3)(*[t.data_ptr() for t in out["dB"]])
+    lg, lu, ld = gate.c(), up.c(), down.c()
+    C.check("swiglu_mlp_backward_tiled", C.lib().swiglu_mlp_backward_tiled(
+        ctypes.byref(lg), ctypes.byref(lu), ctypes.byref(ld), _ptr(dY), _ptr(X), _ptr(Z), M, tile, _ptr(out["dX"]),
+        dA, dB, _ptr(ws), ws.numel(), _stream()))
+    return out
+
+
 class KernelTimer:
     """Per-kernel-class launch durations from hipEvents the library records around
     each of its launches (on the launch's stream). Use as a context manager."""

@@ -128,3 +128,52 @@ def test_forward_rejects_oversized_weights():
     for K, N in ((1 << 22, 8), (64, (1 << 21) + 8), (1 << 20, 1 << 12)):
         L = C.QLoraLayerC(0x10000, 0x10000, 0x10000, 0x10000, K, N, 16, 2.0)
         assert lib.qlora_forward(ctypes.byref(L), p, 4, p, p, None, 0, None) == C.QLORA_EINVAL
+
+
+def test_tiled_mlp_workspace_scales_with_the_tile_not_the_batch():
+    lib = C.lib()
+    H, I = 4096, 14336
+    for r in (1, 16, 129, 256):
+        for bwd in (0, 1):
+            per_tile = lib.swiglu_mlp_tiled_workspace_size(bwd, 4096, H, I, r, 4096)
+            assert per_tile > 0 and per_tile % 256 == 0
+            # a longer batch with the same tile needs no more workspace
+            assert lib.swiglu_mlp_tiled_workspace_size(bwd, 1 << 20, H, I, r, 4096) == per_tile
+            # a tile longer than the batch is sized by the batch
+            assert lib.swiglu_mlp_tiled_workspace_size(bwd, 4096, H, I, r, 1 << 20) == per_tile
+            assert lib.swiglu_mlp_tiled_workspace_size(bwd, 0, H, I, r, 4096) >= 0
+        # the tiled backward's workspace holds g, u, h, dg, du of one tile; the whole-batch
+        # backward holds dg, du of the batch (g, u, h are saved by its forward)
+        assert lib.swiglu_mlp_tiled_workspace_size(1, 4096, H, I, r, 4096) >= 5 * 4096 * I * 2
+    assert lib.swiglu_mlp_tiled_workspace_size(1, 4096, H, I, 16, 0) == 0  # tile < 1 is invalid
+
+
+def test_tiled_mlp_argument_checks():
+    lib = C.lib()
+    g, u, d = _layer(256, 512), _layer(256, 512), _layer(512, 256)
+    p = ctypes.c_void_p(0x10000)
+    G = [ctypes.byref(x) for x in (g, u, d)]
+    grads = (ctypes.c_void_p * 3)(0x10000, 0x10000, 0x10000)
+    need_f = lib.swiglu_mlp_tiled_workspace_size(0, 64, 256, 512, 16, 32)
+    need_b = lib.swiglu_mlp_tiled_workspace_size(1, 64, 256, 512, 16, 32)
+    assert need_f > 0 and need_b > need_f
+    # tile must be >= 1
+    assert lib.swiglu_mlp_forward_tiled(*G, p, 64, 0, p, p, p, need_f, None) == C.QLORA_EINVAL
+    assert lib.swiglu_mlp_backward_tiled(*G, p, p, p, 64, 0, p, grads, grads, p, need_b, None) == C.QLORA_EINVAL
+    # workspace missing or short
+    assert lib.swiglu_mlp_forward_tiled(*G, p, 64, 32, p, p, None, 0, None) == C.QLORA_EWORKSPACE
+    assert lib.swiglu_mlp_forward_tiled(*G, p, 64, 32, p, p, p, need_f - 1, None) == C.QLORA_EWORKSPACE
+    assert lib.swiglu_mlp_backward_tiled(*G, p, p, p, 64, 32, p, grads, grads, p, need_b - 1,
+                                         None) == C.QLORA_EWORKSPACE
+    # null or misaligned tensors
+    assert lib.swiglu_mlp_forward_tiled(*G, None, 64, 32, p, p, p, need_f, None) == C.QLORA_EINVAL
+    assert lib.swiglu_mlp_backward_tiled(*G, p, ctypes.c_void_p(0x10002), p, 64, 32, p, grads, grads, p, need_b,
+                                         None) == C.QLORA_EINVAL
+    bad = (ctypes.c_void_p * 3)(0x10000, 0, 0x10000)
+    assert lib.swiglu_mlp_backward_tiled(*G, p, p, p, 64, 32, p, bad, grads, p, need_b, None) == C.QLORA_EINVAL
+    # mismatched shapes as for the whole-batch call
+    bad_d = _layer(256, 256)
+    assert lib.swiglu_mlp_forward_tiled(ctypes.byref(g), ctypes.byref(u), ctypes.byref(bad_d), p, 64, 32, p, p, p,
+                                        need_f, None) == C.QLORA_EINVAL
+    # an empty batch's forward is a no-op that touches no GPU
+    assert lib.swiglu_mlp_forward_tiled(*G, p, 0, 32, p, p, None, 0, None) == C.QLORA_OK

@@ -11,6 +11,7 @@ seeded synthetic inputs already resident in HBM:
   mlp    : SwiGLU block, M=4096, 4096 <-> 14336, LoRA r=16 on gate/up/down
   rsweep : M=8192, K=N=4096, r from --rank (8, 16, 64, 128)
   layer  : the 7 projections of a Llama-3.1-8B GQA decoder layer at M=16384
+  normrope: the layer's two RMSNorms (H=4096) and q/k RoPE (32+8 heads of 128), M=16384
 --mlp-tile T runs the SwiGLU block of mlp/layer token-tiled (T tokens at a
 time, g/u/h recomputed in the backward) and reports its activation memory.
 Prints one JSON line with tokens/s, useful TFLOP/s (4MNK + 6Mr(N+K) per
@@ -33,7 +34,10 @@ sys.path.insert(0, ROOT)
 
 PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 MFMA (published)
 PEAK_HBM_GBS = 8000.0
-WL_INDEX = {"tiny": 0, "attn": 1, "mlp": 2, "rsweep": 3, "layer": 4}
+WL_INDEX = {"tiny": 0, "attn": 1, "mlp": 2, "rsweep": 3, "layer": 4, "normrope": None}
+# the steps around the projections of one decoder layer at M=16384: two
+# RMSNorms of the 4096-wide residual stream and RoPE of q (32 heads) and k (8)
+NORMROPE = dict(M=16384, H=4096, hq=32, hk=8, d=128, eps=1e-5, base=500000.0)
 METRIC = "QLoRA linear fwd+bwd tokens/s and useful TFLOP/s (8B shapes); % MFMA peak"
 
 
@@ -63,6 +67,10 @@ KERNEL_SOURCES = {  # kernel class -> the sources its code is built from
     "gemm_bwd_swiglu": ["gemm_bwd.hip", "common.hpp"],
     "gemm_fwd": ["gemm_fwd.hip", "common.hpp"],
     "gemm_fwd_gateup": ["gemm_fwd.hip", "common.hpp"],
+    "rmsnorm_fwd": ["normrope.hip", "common.hpp"],
+    "rmsnorm_bwd": ["normrope.hip", "common.hpp"],
+    "rope_fwd": ["normrope.hip", "common.hpp"],
+    "rope_bwd": ["normrope.hip", "common.hpp"],
 }
 
 
@@ -210,12 +218,57 @@ class MLP:
             raise RuntimeError(f"swiglu_mlp_backward: {st}")
 
 
+class NormRope:
+    """RMSNorm fwd+bwd twice and RoPE fwd+bwd of q, k: the steps around one layer's projections."""
+
+    def __init__(self, q, cfg):
+        import torch
+        from synthetic import random_norm_rope
+        d = random_norm_rope(5000, cfg["M"], cfg["H"], cfg["hq"], cfg["hk"], cfg["d"])
+        self.d, self.cfg = d, cfg
+        M, H = cfg["M"], cfg["H"]
+        self.x, self.w, self.dy = dev_bf16(d["x"]), dev_bf16(d["w"]), dev_bf16(d["dy"])
+        self.qh, self.kh, self.dq, self.dk = (dev_bf16(d[k]) for k in ("q", "k", "dq", "dk"))
+        self.pos = torch.from_numpy(d["pos"]).cuda()
+        self.y = torch.empty_like(self.x)
+        self.dx = torch.empty_like(self.x)
+        self.rstd = torch.empty((M,), dtype=torch.float32, device="cuda")
+        p = lambda t: ctypes.c_void_p(t.data_ptr())
+        hq, hk, hd = cfg["hq"], cfg["hk"], cfg["d"]
+        self.f_args = (p(self.x), p(self.w), M, H, cfg["eps"], p(self.y), p(self.rstd))
+        self.b_args = (p(self.dy), p(self.x), p(self.w), p(self.rstd), M, H, p(self.dx))
+        self.rf_args = (p(self.qh), p(self.kh), p(self.pos), M, hq, hk, hd, cfg["base"])
+        self.rb_args = (p(self.dq), p(self.dk), p(self.pos), M, hq, hk, hd, cfg["base"])
+
+    def run(self, lib, stream):
+        for _ in range(2):  # input norm and post-attention norm
+            if lib.qlora_rmsnorm_forward(*self.f_args, stream):
+                raise RuntimeError("qlora_rmsnorm_forward")
+        if lib.qlora_rope_forward(*self.rf_args, stream) or lib.qlora_rope_backward(*self.rb_args, stream):
+            raise RuntimeError("qlora_rope")
+        for _ in range(2):
+            if lib.qlora_rmsnorm_backward(*self.b_args, stream):
+                raise RuntimeError("qlora_rmsnorm_backward")
+
+    def bytes_per_launch(self):
+        c = self.cfg
+        M, H, heads = c["M"], c["H"], c["hq"] + c["hk"]
+        rope = 2 * M * heads * c["d"] * 2 + M * 4  # read and write every head element, positions
+        return {"rmsnorm_fwd": 2 * M * H * 2 + H * 2 + M * 4, "rmsnorm_bwd": 3 * M * H * 2 + H * 2 + M * 4,
+                "rope_fwd": rope, "rope_bwd": rope}
+
+
 def build_workload(name: str, rank: int, mlp_tile: int = 0):
     import torch
     import parameter_efficient_fine_amd as q
     from parameter_efficient_fine_amd import _lib as C
     from synthetic import WORKLOADS, make_workload
     c = WL_INDEX[name]
+    if name == "normrope":
+        parts = [NormRope(q, NORMROPE)]
+        d = dict(NORMROPE, kind="normrope", _data=parts[0].d)
+        torch.cuda.synchronize()
+        return d, parts
     sub = WORKLOADS[c]["ranks"].index(rank) if name == "rsweep" else 0
     d = make_workload(c, sub)
     parts = []
@@ -234,6 +287,10 @@ def build_workload(name: str, rank: int, mlp_tile: int = 0):
 
 
 def describe(d, name, parts=()):
+    if d["kind"] == "normrope":
+        return dict(workload=f"{name}: two RMSNorms (H={d['H']}, eps={d['eps']}) and RoPE of q ({d['hq']} heads) and "
+                             f"k ({d['hk']} heads) of {d['d']}, base {d['base']:g}, fwd+bwd, M={d['M']} tokens in "
+                             f"packed sequences", **{k: d[k] for k in ("M", "H", "hq", "hk", "d")})
     M, r = d["M"], d["r"]
     mlps = [p for p in parts if isinstance(p, MLP)]
     extra = {}
@@ -259,6 +316,8 @@ def gemm_flops(parts):
     """{kernel class: algorithmic FLOPs per launch} of the fused dequant GEMMs."""
     out = {}
     for p in parts:
+        if isinstance(p, NormRope):
+            continue
         if isinstance(p, Proj):
             M, K, N, r = p.M, p.K, p.N, p.r
             out.setdefault("gemm_fwd", []).append(2 * M * N * K + 2 * M * N * r)   # X.W^T + Z.B^T
@@ -297,6 +356,21 @@ def cpu_baseline(d, target_s: float):
                 ref.linear_fwd(X[:rows], What, A, B, d["s"])
                 ref.linear_bwd(dY[:rows], X[:rows], What, A, B, d["s"])
             what = "linear fwd+bwd"
+        elif d["kind"] == "normrope":
+            from oracle import normrope as nr
+            nd = d["_data"]
+            X, Wn, DY = ref.bf16_to_f64(nd["x"]), ref.bf16_to_f64(nd["w"]), ref.bf16_to_f64(nd["dy"])
+            Q, Kh = ref.bf16_to_f64(nd["q"]), ref.bf16_to_f64(nd["k"])
+            DQ, DK = ref.bf16_to_f64(nd["dq"]), ref.bf16_to_f64(nd["dk"])
+
+            def run(rows):
+                for _ in range(2):
+                    nr.rmsnorm_fwd(X[:rows], Wn, d["eps"])
+                for v, f in ((Q, nr.rope), (Kh, nr.rope), (DQ, nr.rope_bwd), (DK, nr.rope_bwd)):
+                    f(v[:rows], nd["pos"][:rows], d["d"], d["base"])
+                for _ in range(2):
+                    nr.rmsnorm_bwd(DY[:rows], X[:rows], Wn, d["eps"])
+            what = "two RMSNorms and q/k RoPE, fwd+bwd"
         else:
             names = ("gate", "up", "down")
             lay = d["layers"]
@@ -350,7 +424,7 @@ def main():
     d, parts = build_workload(args.workload, args.rank, args.mlp_tile)
     c = WL_INDEX[args.workload]
     sub = d["sub"] if args.workload == "rsweep" else 0
-    flops = useful_flops(c, sub)
+    flops = useful_flops(c, sub) if c is not None else None
     stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
 
     def step():
@@ -398,19 +472,29 @@ def main():
     kernels = {}
     for name, (n, tot) in kt.result.items():
         kernels[name] = dict(launches_per_step=n / args.steps, ms_per_step=tot / args.steps, avg_us=1e3 * tot / n)
-    dom = max((k for k in kernels if k in per_launch_flops), key=lambda k: kernels[k]["ms_per_step"])
-    fl = per_launch_flops[dom]
-    avg_flops = float(np.mean(fl))
-    avg_s = kernels[dom]["avg_us"] * 1e-6
-    achieved = avg_flops / avg_s / 1e12
-    roofline = dict(bound="mfma", kernel=dom, achieved=achieved, peak=PEAK_BF16_TFLOPS, unit="TFLOP/s",
-                    frac=achieved / PEAK_BF16_TFLOPS, traffic=counted_traffic(dom, args.workload),
-                    traffic_unit="bytes per launch", avg_us=kernels[dom]["avg_us"], flops_per_launch=avg_flops,
-                    source_hash=kernel_source_hash(dom))
+    if flops is None:  # HBM-bound steps: algorithmic bytes of the dominant kernel
+        per_launch_bytes = parts[0].bytes_per_launch()
+        dom = max((k for k in kernels if k in per_launch_bytes), key=lambda k: kernels[k]["ms_per_step"])
+        avg_s = kernels[dom]["avg_us"] * 1e-6
+        achieved = per_launch_bytes[dom] / avg_s / 1e9
+        roofline = dict(bound="hbm", kernel=dom, achieved=achieved, peak=PEAK_HBM_GBS, unit="GB/s",
+                        frac=achieved / PEAK_HBM_GBS, traffic=counted_traffic(dom, args.workload),
+                        traffic_unit="bytes per launch", avg_us=kernels[dom]["avg_us"],
+                        bytes_per_launch=per_launch_bytes[dom], source_hash=kernel_source_hash(dom))
+    else:
+        dom = max((k for k in kernels if k in per_launch_flops), key=lambda k: kernels[k]["ms_per_step"])
+        fl = per_launch_flops[dom]
+        avg_flops = float(np.mean(fl))
+        avg_s = kernels[dom]["avg_us"] * 1e-6
+        achieved = avg_flops / avg_s / 1e12
+        roofline = dict(bound="mfma", kernel=dom, achieved=achieved, peak=PEAK_BF16_TFLOPS, unit="TFLOP/s",
+                        frac=achieved / PEAK_BF16_TFLOPS, traffic=counted_traffic(dom, args.workload),
+                        traffic_unit="bytes per launch", avg_us=kernels[dom]["avg_us"], flops_per_launch=avg_flops,
+                        source_hash=kernel_source_hash(dom))
 
     tokens = d["M"]
     value = tokens / (ms * 1e-3)
-    tflops = flops / (ms * 1e-3) / 1e12
+    tflops = flops / (ms * 1e-3) / 1e12 if flops is not None else None
     out = {
         "metric": METRIC,
         "value": value,
@@ -423,11 +507,13 @@ def main():
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "bf16",
-        "data": "synthetic (seeded N(0,1) activations, 0.02*N(0,1) weights quantized to NF4)",
+        "data": ("synthetic (seeded N(0,1) activations and gradients, norm weight 1+0.1*N(0,1), packed-sequence "
+                 "positions)" if flops is None else
+                 "synthetic (seeded N(0,1) activations, 0.02*N(0,1) weights quantized to NF4)"),
         "config": describe(d, args.workload, parts),
         "useful_tflops": tflops,
-        "mfma_peak_frac": tflops / PEAK_BF16_TFLOPS,
-        "useful_gflop_per_step": flops / 1e9,
+        "mfma_peak_frac": tflops / PEAK_BF16_TFLOPS if tflops is not None else None,
+        "useful_gflop_per_step": flops / 1e9 if flops is not None else None,
         "wall_s_timed": wall,
         "step_time": step_stats,
         "roofline": roofline,

@@ -142,6 +142,35 @@ int swiglu_mlp_backward_tiled(const qlora_layer* gate, const qlora_layer* up, co
                               uint16_t* dX, float* const dA[3], float* const dB[3], void* ws, size_t ws_bytes,
                               void* stream);
 
+/* RMSNorm before the projections ("Unsloth" wiki entry, Theory: fused RMSNorm
+ * kernel; no formula on the pages, the Llama definition is taken): per row of
+ * x [M,H] bf16, rstd = 1/sqrt(mean(x^2) + eps) (fp32, saved [M]) and
+ * y = bf16(w * (x * rstd)) with the frozen bf16 weight w [H]. H % 8 == 0,
+ * eps >= 0. One pass over x. */
+int qlora_rmsnorm_forward(const uint16_t* x, const uint16_t* w, int64_t M, int64_t H, float eps, uint16_t* y,
+                          float* rstd, void* stream);
+
+/* Backward of the RMSNorm for upstream dy [M,H]: dx = rstd * (g - n * mean(g * n))
+ * with g = w * dy and n = x * rstd (rstd from the forward). w is frozen with the
+ * base model, so no weight gradient is formed. dx may not alias dy or x. */
+int qlora_rmsnorm_backward(const uint16_t* dy, const uint16_t* x, const uint16_t* w, const float* rstd, int64_t M,
+                           int64_t H, uint16_t* dx, void* stream);
+
+/* Rotary position embeddings after the q and k projections ("Unsloth" wiki
+ * entry, Theory: fused RoPE kernel; "Unsloth vs PyTorch" video, 2:11-2:22),
+ * in place on q [M, hq*d] and k [M, hk*d] bf16 (hq or hk may be 0; q or k is
+ * then ignored). Token m has position pos[m] (int32, device) and each head
+ * vector is rotated pairwise, element i with element i + d/2 ("rotate half"):
+ *   a = pos * base^(-2i/d),  v[i] <- v[i] cos a - v[i+d/2] sin a,
+ *                            v[i+d/2] <- v[i+d/2] cos a + v[i] sin a.
+ * The angles and their cos/sin are formed in fp64, the rotation in fp32,
+ * one bf16 rounding. 16 <= d <= 1024, d % 16 == 0, base > 1.
+ * qlora_rope_backward applies the inverse rotation to the gradients dq, dk. */
+int qlora_rope_forward(uint16_t* q, uint16_t* k, const int32_t* pos, int64_t M, int hq, int hk, int d, float base,
+                       void* stream);
+int qlora_rope_backward(uint16_t* dq, uint16_t* dk, const int32_t* pos, int64_t M, int hq, int hk, int d, float base,
+                        void* stream);
+
 /* Measurement support (off the hot path; not thread-safe).
  * qlora_profile_begin creates, once, a pool of 2*max_launches hipEvents and
  * from then on brackets each kernel launch made by this library with an event

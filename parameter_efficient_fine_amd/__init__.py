@@ -16,5 +16,9 @@ from .ops import (  # noqa: F401
     mlp_forward_tiled,
     mlp_tiled_workspace_size,
     quantize,
+    rmsnorm_backward,
+    rmsnorm_forward,
+    rope_backward,
+    rope_forward,
     workspace_size,
 )

@@ -23,7 +23,8 @@ OP_FORWARD, OP_BACKWARD, OP_MLP_FORWARD, OP_MLP_BACKWARD = 0, 1, 2, 3
 EXPORTS = [
     "qlora_quantize", "qlora_dequantize", "qlora_workspace_size", "qlora_forward", "qlora_backward",
     "swiglu_mlp_forward", "swiglu_mlp_backward", "swiglu_mlp_tiled_workspace_size", "swiglu_mlp_forward_tiled",
-    "swiglu_mlp_backward_tiled", "qlora_profile_begin", "qlora_profile_end",
+    "swiglu_mlp_backward_tiled", "qlora_rmsnorm_forward", "qlora_rmsnorm_backward", "qlora_rope_forward",
+    "qlora_rope_backward", "qlora_profile_begin", "qlora_profile_end",
     "qlora_status_string", "qlora_last_error",
 ]
 
@@ -78,6 +79,11 @@ def lib():
     L.swiglu_mlp_forward_tiled.argtypes = [LP, LP, LP, vp, i64, i64, vp, vp, vp, sz, vp]
     L.swiglu_mlp_backward_tiled.argtypes = [LP, LP, LP, vp, vp, vp, i64, i64, vp, ctypes.POINTER(vp),
                                             ctypes.POINTER(vp), vp, sz, vp]
+    ci, cf = ctypes.c_int, ctypes.c_float
+    L.qlora_rmsnorm_forward.argtypes = [vp, vp, i64, i64, cf, vp, vp, vp]
+    L.qlora_rmsnorm_backward.argtypes = [vp, vp, vp, vp, i64, i64, vp, vp]
+    L.qlora_rope_forward.argtypes = [vp, vp, vp, i64, ci, ci, ci, cf, vp]
+    L.qlora_rope_backward.argtypes = [vp, vp, vp, i64, ci, ci, ci, cf, vp]
     L.qlora_profile_begin.argtypes = [ctypes.c_int]
     L.qlora_profile_begin.restype = ctypes.c_int
     L.qlora_profile_end.argtypes = [ctypes.POINTER(KernelTimeC), ctypes.c_int, ctypes.POINTER(ctypes.c_int)]
@@ -87,7 +93,8 @@ def lib():
     L.qlora_last_error.argtypes = []
     L.qlora_last_error.restype = ctypes.c_char_p
     for f in ("qlora_quantize", "qlora_dequantize", "qlora_forward", "qlora_backward", "swiglu_mlp_forward",
-              "swiglu_mlp_backward", "swiglu_mlp_forward_tiled", "swiglu_mlp_backward_tiled"):
+              "swiglu_mlp_backward", "swiglu_mlp_forward_tiled", "swiglu_mlp_backward_tiled", "qlora_rmsnorm_forward",
+              "qlora_rmsnorm_backward", "qlora_rope_forward", "qlora_rope_backward"):
         getattr(L, f).restype = ctypes.c_int
     _lib = L
     return L

@@ -13,7 +13,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 OUT = os.path.join(HERE, "libqlora.so")
 OBJDIR = os.path.join(HERE, "_build")
-SOURCES = ["quant.hip", "skinny.hip", "gemm_fwd.hip", "gemm_bwd.hip", "api.cpp"]
+SOURCES = ["quant.hip", "skinny.hip", "gemm_fwd.hip", "gemm_bwd.hip", "normrope.hip", "api.cpp"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 # No fast-math: the quantizer needs IEEE division and fp32 denormals. Packed
 # fp32 VALU ops are disabled (the compiler would otherwise emit them by itself).

@@ -579,6 +579,50 @@ int swiglu_mlp_backward_tiled(const qlora_layer* gate, const qlora_layer* up, co
   return QLORA_OK;
 }
 
+int qlora_rmsnorm_forward(const uint16_t* x, const uint16_t* w, int64_t M, int64_t H, float eps, uint16_t* y,
+                          float* rstd, void* stream) {
+  if (M < 0 || H <= 0 || H % 8 != 0 || H > kMaxDim || !(eps >= 0.f)) return QLORA_EINVAL;
+  if (M == 0) return QLORA_OK;
+  if (!x || !w || !y || !rstd || !aligned16(x) || !aligned16(w) || !aligned16(y) || !aligned16(rstd))
+    return QLORA_EINVAL;
+  hipStream_t st = (hipStream_t)stream;
+  QL_LAUNCH("rmsnorm_fwd", st, launch_rmsnorm_fwd(x, w, M, H, eps, y, rstd, st));
+  return QLORA_OK;
+}
+
+int qlora_rmsnorm_backward(const uint16_t* dy, const uint16_t* x, const uint16_t* w, const float* rstd, int64_t M,
+                           int64_t H, uint16_t* dx, void* stream) {
+  if (M < 0 || H <= 0 || H % 8 != 0 || H > kMaxDim) return QLORA_EINVAL;
+  if (M == 0) return QLORA_OK;
+  if (!dy || !x || !w || !rstd || !dx || !aligned16(dy) || !aligned16(x) || !aligned16(w) || !aligned16(rstd) ||
+      !aligned16(dx))
+    return QLORA_EINVAL;
+  hipStream_t st = (hipStream_t)stream;
+  QL_LAUNCH("rmsnorm_bwd", st, launch_rmsnorm_bwd(dy, x, w, rstd, M, H, dx, st));
+  return QLORA_OK;
+}
+
+static int rope_call(uint16_t* q, uint16_t* k, const int32_t* pos, int64_t M, int hq, int hk, int d, float base,
+                     bool inverse, void* stream) {
+  if (M < 0 || hq < 0 || hk < 0 || d < 16 || d > 1024 || d % 16 != 0 || !(base > 1.f)) return QLORA_EINVAL;
+  if ((int64_t)(hq > hk ? hq : hk) * d > kMaxDim) return QLORA_EINVAL;
+  if (M == 0 || hq + hk == 0) return QLORA_OK;
+  if (!pos || (hq && (!q || !aligned16(q))) || (hk && (!k || !aligned16(k)))) return QLORA_EINVAL;
+  hipStream_t st = (hipStream_t)stream;
+  QL_LAUNCH(inverse ? "rope_bwd" : "rope_fwd", st, launch_rope(q, k, pos, M, hq, hk, d, (double)base, inverse, st));
+  return QLORA_OK;
+}
+
+int qlora_rope_forward(uint16_t* q, uint16_t* k, const int32_t* pos, int64_t M, int hq, int hk, int d, float base,
+                       void* stream) {
+  return rope_call(q, k, pos, M, hq, hk, d, base, false, stream);
+}
+
+int qlora_rope_backward(uint16_t* dq, uint16_t* dk, const int32_t* pos, int64_t M, int hq, int hk, int d, float base,
+                        void* stream) {
+  return rope_call(dq, dk, pos, M, hq, hk, d, base, true, stream);
+}
+
 int qlora_profile_begin(int max_launches) {
   if (max_launches < 1) return QLORA_EINVAL;
   while ((int)g_prof.pool.size() < 2 * max_launches) {

@@ -108,4 +108,14 @@ hipError_t launch_gemm_bwd(const uint16_t* dY0, WSrc w0, const uint16_t* dY1, WS
 hipError_t launch_gemm_bwd_swiglu(const uint16_t* dY, WSrc w, int64_t M, int64_t K, int64_t N, const uint16_t* g,
                                   const uint16_t* u, uint16_t* dg, uint16_t* du, hipStream_t st);
 
+// RMSNorm rows of x [M,H] with frozen weight w [H]: y bf16, rstd fp32 [M];
+// backward: dx only.
+hipError_t launch_rmsnorm_fwd(const uint16_t* x, const uint16_t* w, int64_t M, int64_t H, float eps, uint16_t* y,
+                              float* rstd, hipStream_t st);
+hipError_t launch_rmsnorm_bwd(const uint16_t* dy, const uint16_t* x, const uint16_t* w, const float* rstd, int64_t M,
+                              int64_t H, uint16_t* dx, hipStream_t st);
+// In-place RoPE of q [M, hq*d] and k [M, hk*d] by pos [M]; inverse rotates back.
+hipError_t launch_rope(uint16_t* q, uint16_t* k, const int32_t* pos, int64_t M, int hq, int hk, int d, double base,
+                       bool inverse, hipStream_t st);
+
 }  // namespace qlora

@@ -208,6 +208,54 @@ def mlp_backward_tiled(gate: QLoraLayer, up: QLoraLayer, down: QLoraLayer, dY, X
     return out
 
 
+def rmsnorm_forward(x, w, eps: float, y=None, rstd=None):
+    """(y bf16 [M,H], rstd fp32 [M]) = RMSNorm of x [M,H] with the frozen weight w [H] (bf16)."""
+    M, H = x.shape
+    _need(x, torch.bfloat16, (M, H), "x")
+    _need(w, torch.bfloat16, (H,), "w")
+    y = torch.empty_like(x) if y is None else y
+    rstd = torch.empty((M,), dtype=torch.float32, device=x.device) if rstd is None else rstd
+    C.check("qlora_rmsnorm_forward", C.lib().qlora_rmsnorm_forward(_ptr(x), _ptr(w), M, H, float(eps), _ptr(y),
+                                                                   _ptr(rstd), _stream()))
+    return y, rstd
+
+
+def rmsnorm_backward(dy, x, w, rstd, dx=None):
+    """dx bf16 [M,H] of the RMSNorm (no weight gradient: w is frozen)."""
+    M, H = x.shape
+    _need(dy, torch.bfloat16, (M, H), "dy")
+    _need(x, torch.bfloat16, (M, H), "x")
+    _need(w, torch.bfloat16, (H,), "w")
+    _need(rstd, torch.float32, (M,), "rstd")
+    dx = torch.empty_like(x) if dx is None else dx
+    C.check("qlora_rmsnorm_backward", C.lib().qlora_rmsnorm_backward(_ptr(dy), _ptr(x), _ptr(w), _ptr(rstd), M, H,
+                                                                     _ptr(dx), _stream()))
+    return dx
+
+
+def _rope(fn, q, k, pos, d: int, base: float):
+    M = pos.shape[0]
+    _need(pos, torch.int32, (M,), "pos")
+    hq = 0 if q is None else q.shape[1] // d
+    hk = 0 if k is None else k.shape[1] // d
+    if q is not None:
+        _need(q, torch.bfloat16, (M, hq * d), "q")
+    if k is not None:
+        _need(k, torch.bfloat16, (M, hk * d), "k")
+    C.check(fn, getattr(C.lib(), fn)(_ptr(q), _ptr(k), _ptr(pos), M, hq, hk, d, float(base), _stream()))
+    return q, k
+
+
+def rope_forward(q, k, pos, d: int, base: float):
+    """Rotate q [M, hq*d] and k [M, hk*d] (bf16, in place) by positions pos [M] (int32)."""
+    return _rope("qlora_rope_forward", q, k, pos, d, base)
+
+
+def rope_backward(dq, dk, pos, d: int, base: float):
+    """Gradients through rope_forward (the inverse rotation, in place)."""
+    return _rope("qlora_rope_backward", dq, dk, pos, d, base)
+
+
 class KernelTimer:
     """Per-kernel-class launch durations from hipEvents the library records around
     each of its launches (on the launch's stream). Use as a context manager."""

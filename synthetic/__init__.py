@@ -148,3 +148,29 @@ def useful_flops(c: int, sub: int = 0, M: int | None = None) -> float:
     projs, r = projections(c, sub)
     M = WORKLOADS[c]["M"] if M is None else M
     return float(sum(4 * M * N * K + 6 * M * r * (N + K) for _, K, N in projs))
+
+
+# ---------------------------------------------------------------------------
+# inputs of the steps around the projections (RMSNorm, RoPE)
+
+def packed_positions(rng, M: int, max_len: int) -> np.ndarray:
+    """Positions of M tokens packed from sequences of random length (1..max_len),
+    each counting from 0: int32 [M]."""
+    pos = np.empty(M, dtype=np.int32)
+    m = 0
+    while m < M:
+        n = int(min(M - m, rng.integers(1, max_len + 1)))
+        pos[m:m + n] = np.arange(n, dtype=np.int32)
+        m += n
+    return pos
+
+
+def random_norm_rope(seed: int, M: int, H: int, hq: int, hk: int, d: int, max_len: int = 16384):
+    """x, dy [M,H] = N(0,1); norm weight w [H] = 1 + 0.1 N(0,1); q [M,hq*d], k [M,hk*d],
+    dq, dk = N(0,1); positions of packed sequences up to max_len. All bf16 bits but pos."""
+    rng = np.random.default_rng(seed)
+    return dict(x=bf16_bits(_normal(rng, (M, H))), dy=bf16_bits(_normal(rng, (M, H))),
+                w=bf16_bits(1.0 + 0.1 * _normal(rng, (H,))),
+                q=bf16_bits(_normal(rng, (M, hq * d))), k=bf16_bits(_normal(rng, (M, hk * d))),
+                dq=bf16_bits(_normal(rng, (M, hq * d))), dk=bf16_bits(_normal(rng, (M, hk * d))),
+                pos=packed_positions(rng, M, max_len), M=M, H=H, hq=hq, hk=hk, d=d)

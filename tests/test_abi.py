@@ -177,3 +177,24 @@ def test_tiled_mlp_argument_checks():
                                         need_f, None) == C.QLORA_EINVAL
     # an empty batch's forward is a no-op that touches no GPU
     assert lib.swiglu_mlp_forward_tiled(*G, p, 0, 32, p, p, None, 0, None) == C.QLORA_OK
+
+
+def test_norm_and_rope_argument_checks():
+    lib = C.lib()
+    p = ctypes.c_void_p(0x10000)
+    # RMSNorm: H % 8, H > 0, eps >= 0, alignment; an empty batch is a no-op
+    assert lib.qlora_rmsnorm_forward(p, p, 4, 12, 1e-5, p, p, None) == C.QLORA_EINVAL
+    assert lib.qlora_rmsnorm_forward(p, p, 4, 0, 1e-5, p, p, None) == C.QLORA_EINVAL
+    assert lib.qlora_rmsnorm_forward(p, p, 4, 64, -1.0, p, p, None) == C.QLORA_EINVAL
+    assert lib.qlora_rmsnorm_forward(ctypes.c_void_p(0x10002), p, 4, 64, 1e-5, p, p, None) == C.QLORA_EINVAL
+    assert lib.qlora_rmsnorm_forward(p, p, 0, 64, 1e-5, p, p, None) == C.QLORA_OK
+    assert lib.qlora_rmsnorm_backward(p, p, p, None, 4, 64, p, None) == C.QLORA_EINVAL
+    assert lib.qlora_rmsnorm_backward(p, p, p, p, 0, 64, p, None) == C.QLORA_OK
+    # RoPE: head size a multiple of 16 in [16, 1024], base > 1, positions given
+    for d in (8, 24, 2048):
+        assert lib.qlora_rope_forward(p, p, p, 4, 2, 1, d, 10000.0, None) == C.QLORA_EINVAL
+    assert lib.qlora_rope_forward(p, p, p, 4, 2, 1, 64, 1.0, None) == C.QLORA_EINVAL
+    assert lib.qlora_rope_forward(p, p, None, 4, 2, 1, 64, 10000.0, None) == C.QLORA_EINVAL
+    assert lib.qlora_rope_backward(p, None, p, 4, 2, 1, 64, 10000.0, None) == C.QLORA_EINVAL  # k heads need k
+    assert lib.qlora_rope_forward(p, None, p, 0, 2, 1, 64, 10000.0, None) == C.QLORA_OK
+    assert lib.qlora_rope_forward(None, None, p, 4, 0, 0, 64, 10000.0, None) == C.QLORA_OK

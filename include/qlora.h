@@ -29,7 +29,7 @@
  *     patterns. The library allocates no memory; scratch space comes from the
  *     caller's workspace (size from qlora_workspace_size).
  *   - Shapes: K % 64 == 0, N % 8 == 0, 1 <= r <= 256, K and N <= 2^21,
- *     N*K <= 2^31, M >= 0 (M == 0 is a no-op; a backward then writes zero
+ *     N*K <= 2^31 (2^30 for the 8-bit formats), M >= 0 (M == 0 is a no-op; a backward then writes zero
  *     gradients). Anything else returns QLORA_EINVAL before any launch.
  *   - Every call enqueues its kernels on `stream` (a hipStream_t, 0 = the
  *     null stream) and returns without synchronising. Launch failures return
@@ -57,6 +57,21 @@ typedef enum {
   QLORA_EHIP = -4          /* a HIP launch failed; see qlora_last_error() */
 } qlora_status;
 
+/* Formats of the frozen weight ("Rev vs unsloth", fused quantized-LoRA card:
+ * int4, int8 and fp8 base weights; "Unsloth vs The Stack v2": 4-bit and
+ * 8-bit). All keep one fp32 per 64-element block of a weight row (the
+ * `absmax` array):
+ *   QLORA_FMT_NF4   codes [N, K/2], 4-bit NormalFloat levels (below); the block
+ *                   value is its absmax.
+ *   QLORA_FMT_INT8  codes [N, K], two's-complement q in [-127, 127]; the block
+ *                   value is s = absmax / 127, q = rint(W / s) (half to even).
+ *   QLORA_FMT_FP8   codes [N, K], OCP E4M3 bytes (bias 7, max 448); the block
+ *                   value is s = absmax / 448, code = nearest E4M3 value to
+ *                   W / s (ties to the even code), saturating at 448.
+ * A block of zeros stores 0 and zero codes (NF4: code 7). The dequantized
+ * weight is fp32(v * block value) for the code's exact value v. */
+typedef enum { QLORA_FMT_NF4 = 0, QLORA_FMT_INT8 = 1, QLORA_FMT_FP8 = 2 } qlora_format;
+
 typedef enum {
   QLORA_OP_FORWARD = 0,
   QLORA_OP_BACKWARD = 1,
@@ -64,26 +79,29 @@ typedef enum {
   QLORA_OP_MLP_BACKWARD = 3
 } qlora_op;
 
-/* One LoRA-adapted 4-bit projection: out = in . What^T + s . (in . A^T) . B^T. */
+/* One LoRA-adapted quantized projection: out = in . What^T + s . (in . A^T) . B^T. */
 typedef struct {
-  const uint8_t* codes;  /* [N, K/2]  two 4-bit codes per byte, even column in the low nibble */
-  const float* absmax;   /* [N, K/64] fp32 scale of each 64-column block */
+  const uint8_t* codes;  /* NF4: [N, K/2], two 4-bit codes per byte, even column in the low nibble;
+                            INT8, FP8: [N, K] */
+  const float* absmax;   /* [N, K/64] fp32 value of each 64-column block (see qlora_format) */
   const uint16_t* A;     /* [r, K]    bf16 LoRA down projection */
   const uint16_t* B;     /* [N, r]    bf16 LoRA up projection */
   int64_t K;             /* input features */
   int64_t N;             /* output features */
   int64_t r;             /* LoRA rank */
   float s;               /* lora_alpha / r */
+  int32_t format;        /* qlora_format of codes/absmax */
 } qlora_layer;
 
-/* Quantize W [N,K] fp32 to codes [N,K/2] and absmax [N,K/64] (format above).
+/* Quantize W [N,K] fp32 to codes and absmax [N,K/64] in `format` (qlora_format).
  * nonfinite_blocks (device uint32, may be NULL) is set to the number of
  * blocks holding Inf/NaN; such a block gets absmax = NaN. Setup-time call. */
-int qlora_quantize(const float* W, int64_t N, int64_t K, uint8_t* codes, float* absmax,
+int qlora_quantize(int format, const float* W, int64_t N, int64_t K, uint8_t* codes, float* absmax,
                    uint32_t* nonfinite_blocks, void* stream);
 
-/* What [N,K] fp32 = L[code] * absmax. Exposes the exact operand values for testing. */
-int qlora_dequantize(const uint8_t* codes, const float* absmax, int64_t N, int64_t K, float* W_hat,
+/* What [N,K] fp32 = fp32(v(code) * absmax), decoded as the GEMMs decode it.
+ * Exposes the exact operand values for testing. */
+int qlora_dequantize(int format, const uint8_t* codes, const float* absmax, int64_t N, int64_t K, float* W_hat,
                      void* stream);
 
 /* Workspace bytes needed by `op` (qlora_op) for M tokens. For the MLP ops,

@@ -18,6 +18,7 @@ QLORA_EWORKSPACE = -3
 QLORA_EHIP = -4
 
 OP_FORWARD, OP_BACKWARD, OP_MLP_FORWARD, OP_MLP_BACKWARD = 0, 1, 2, 3
+FMT_NF4, FMT_INT8, FMT_FP8 = 0, 1, 2
 
 # Every function the header declares (checked by the CPU tests against include/qlora.h).
 EXPORTS = [
@@ -39,6 +40,7 @@ class QLoraLayerC(ctypes.Structure):
         ("N", ctypes.c_int64),
         ("r", ctypes.c_int64),
         ("s", ctypes.c_float),
+        ("format", ctypes.c_int32),
     ]
 
 
@@ -65,8 +67,8 @@ def lib():
     L = ctypes.CDLL(LIB_PATH)
     vp, i64, sz = ctypes.c_void_p, ctypes.c_int64, ctypes.c_size_t
     LP = ctypes.POINTER(QLoraLayerC)
-    L.qlora_quantize.argtypes = [vp, i64, i64, vp, vp, vp, vp]
-    L.qlora_dequantize.argtypes = [vp, vp, i64, i64, vp, vp]
+    L.qlora_quantize.argtypes = [ctypes.c_int, vp, i64, i64, vp, vp, vp, vp]
+    L.qlora_dequantize.argtypes = [ctypes.c_int, vp, vp, i64, i64, vp, vp]
     L.qlora_workspace_size.argtypes = [ctypes.c_int, i64, i64, i64, i64]
     L.qlora_workspace_size.restype = sz
     L.qlora_forward.argtypes = [LP, vp, i64, vp, vp, vp, sz, vp]

@@ -13,7 +13,11 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 OUT = os.path.join(HERE, "libqlora.so")
 OBJDIR = os.path.join(HERE, "_build")
-SOURCES = ["quant.hip", "skinny.hip", "gemm_fwd.hip", "gemm_bwd.hip", "normrope.hip", "api.cpp"]
+# (source, object, extra flags): the fused GEMMs are built once per weight
+# format (QL_WFMT 0 NF4, 1 INT8, 2 FP8), each into its own namespace
+SOURCES = [("quant.hip", "quant.o", []), ("skinny.hip", "skinny.o", []), ("normrope.hip", "normrope.o", []),
+           ("api.cpp", "api.o", [])] + [
+    (f"{g}.hip", f"{g}_f{fmt}.o", [f"-DQL_WFMT={fmt}"]) for g in ("gemm_bwd", "gemm_fwd") for fmt in (0, 1, 2)]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 # No fast-math: the quantizer needs IEEE division and fp32 denormals. Packed
 # fp32 VALU ops are disabled (the compiler would otherwise emit them by itself).
@@ -21,9 +25,10 @@ FLAGS = ["-O3", "-std=c++17", "-fPIC", "--offload-arch=gfx950", "-Wall", "-Wno-u
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
 
 
-def _compile(src: str) -> str:
-    obj = os.path.join(OBJDIR, os.path.splitext(src)[0] + ".o")
-    cmd = [HIPCC, *FLAGS, "-c", "-x", "hip", os.path.join(CSRC, src), "-o", obj]
+def _compile(entry) -> str:
+    src, objname, extra = entry
+    obj = os.path.join(OBJDIR, objname)
+    cmd = [HIPCC, *FLAGS, *extra, "-c", "-x", "hip", os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"hipcc failed for {src}:\n{r.stdout}\n{r.stderr}")
@@ -36,7 +41,7 @@ def _compile(src: str) -> str:
 
 def build(verbose: bool = True) -> str:
     os.makedirs(OBJDIR, exist_ok=True)
-    with ThreadPoolExecutor(max_workers=len(SOURCES)) as ex:
+    with ThreadPoolExecutor(max_workers=min(len(SOURCES), os.cpu_count() or 4)) as ex:
         objs = list(ex.map(_compile, SOURCES))
     tmp = OUT + ".tmp"
     cmd = [HIPCC, "-shared", "-fPIC", "--offload-arch=gfx950", *objs, "-o", tmp]

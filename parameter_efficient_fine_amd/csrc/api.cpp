@@ -71,7 +71,10 @@ bool layer_ok(const qlora_layer* L) {
   if (!L || !L->codes || !L->absmax || !L->A || !L->B) return false;
   if (L->K <= 0 || L->K % 64 != 0 || L->N <= 0 || L->N % 8 != 0) return false;
   if (L->r < 1 || L->r > 256) return false;
-  if (L->K > kMaxDim || L->N > kMaxDim || L->N * L->K > kMaxWeight) return false;
+  if (L->format < QLORA_FMT_NF4 || L->format > QLORA_FMT_FP8) return false;
+  // code bytes of the weight stay below 2^30 for every format
+  if (L->K > kMaxDim || L->N > kMaxDim || L->N * L->K > (L->format == QLORA_FMT_NF4 ? kMaxWeight : kMaxWeight / 2))
+    return false;
   if (!aligned16(L->codes) || !aligned16(L->absmax) || !aligned16(L->A) || !aligned16(L->B)) return false;
   return true;
 }
@@ -173,6 +176,7 @@ WSrc wsrc(const qlora_layer* L, const uint16_t* lora_i, const uint16_t* lora_j, 
   w.r = (int)L->r;
   w.ldj = ldj ? ldj : L->r;
   w.s = L->s;
+  w.fmt = L->format;
   return w;
 }
 
@@ -263,22 +267,26 @@ const char* qlora_status_string(int status) {
 
 const char* qlora_last_error(void) { return g_err; }
 
-int qlora_quantize(const float* W, int64_t N, int64_t K, uint8_t* codes, float* absmax, uint32_t* nonfinite_blocks,
-                   void* stream) {
+int qlora_quantize(int format, const float* W, int64_t N, int64_t K, uint8_t* codes, float* absmax,
+                   uint32_t* nonfinite_blocks, void* stream) {
+  if (format < QLORA_FMT_NF4 || format > QLORA_FMT_FP8) return QLORA_EINVAL;
   if (N < 0 || K < 0 || K % 64 != 0) return QLORA_EINVAL;
   if (N * K == 0) return QLORA_OK;
   if (!W || !codes || !absmax || !aligned16(W) || !aligned16(codes)) return QLORA_EINVAL;
   hipStream_t st = (hipStream_t)stream;
-  QL_LAUNCH("quantize", st, launch_quantize(W, N, K, codes, absmax, nonfinite_blocks, st));
+  QL_LAUNCH("quantize", st, launch_quantize(format, W, N, K, codes, absmax, nonfinite_blocks, st));
   return QLORA_OK;
 }
 
-int qlora_dequantize(const uint8_t* codes, const float* absmax, int64_t N, int64_t K, float* W_hat, void* stream) {
+int qlora_dequantize(int format, const uint8_t* codes, const float* absmax, int64_t N, int64_t K, float* W_hat,
+                     void* stream) {
+  if (format < QLORA_FMT_NF4 || format > QLORA_FMT_FP8) return QLORA_EINVAL;
   if (N < 0 || K < 0 || K % 64 != 0) return QLORA_EINVAL;
   if (N * K == 0) return QLORA_OK;
-  if (!codes || !absmax || !W_hat || !aligned16(W_hat)) return QLORA_EINVAL;
+  if (!codes || !absmax || !W_hat || !aligned16(W_hat) || (format != QLORA_FMT_NF4 && !aligned16(codes)))
+    return QLORA_EINVAL;
   hipStream_t st = (hipStream_t)stream;
-  QL_LAUNCH("dequantize", st, launch_dequantize(codes, absmax, N, K, W_hat, st));
+  QL_LAUNCH("dequantize", st, launch_dequantize(format, codes, absmax, N, K, W_hat, st));
   return QLORA_OK;
 }
 
@@ -349,6 +357,7 @@ static bool mlp_shapes_ok(const qlora_layer* g, const qlora_layer* u, const qlor
   if (!layer_ok(g) || !layer_ok(u) || !layer_ok(d)) return false;
   if (g->K != u->K || g->N != u->N || d->K != g->N || d->N != g->K) return false;
   if (g->r != u->r || g->r != d->r) return false;
+  if (g->format != u->format || g->format != d->format) return false;
   return true;
 }
 

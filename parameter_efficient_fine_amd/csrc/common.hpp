@@ -136,6 +136,98 @@ __device__ __forceinline__ u32x4 dequant8(uint32_t x, const Nf4Lut& t) {
 }
 
 // ---------------------------------------------------------------------------
+// Weight formats. Every format stores one fp32 per 64-element block of a
+// weight row ("absmax" array): NF4 its absmax (levels span [-1, 1]), INT8 and
+// FP8 their scale s (absmax / 127, absmax / 448). The dequantized weight is
+// fp32(v * that value) for the code's exact value v, then bf16 for the MFMA.
+
+enum WFmt { kNF4 = 0, kInt8 = 1, kFp8 = 2 };
+
+// bytes of codes per weight element x 2 (NF4: 1, 8-bit: 2)
+template <int F>
+constexpr int kCodeHalfBytes = F == kNF4 ? 1 : 2;
+
+// Per (row, block) state formed once from the block's fp32 value.
+template <int F>
+struct WPrep;
+template <>
+struct WPrep<kNF4> {
+  Nf4Lut lut;
+};
+template <>
+struct WPrep<kInt8> {
+  float s, o;  // scale and -128 * scale
+};
+template <>
+struct WPrep<kFp8> {
+  float s;
+};
+
+template <int F>
+__device__ __forceinline__ WPrep<F> wprep(float a) {
+  if constexpr (F == kNF4) {
+    return WPrep<kNF4>{make_lut(a)};
+  } else if constexpr (F == kInt8) {
+    return WPrep<kInt8>{a, -128.0f * a};
+  } else {
+    return WPrep<kFp8>{a};
+  }
+}
+
+// Elements 8c .. 8c+7 of a run of codes held in 16-byte registers (NF4: 8
+// codes per dword, element e in nibble e; 8-bit: 4 codes per dword, element e
+// in byte e) -> 8 bf16 in element order, out[q] = elem 2q | elem 2q+1 << 16.
+template <int F, int NV>
+__device__ __forceinline__ u32x4 wdeq8(const u32x4 (&cw)[NV], int c, const WPrep<F>& p) {
+  if constexpr (F == kNF4) {
+    return dequant8(cw[c >> 2][c & 3], p.lut);
+  } else if constexpr (F == kInt8) {
+    // byte b ^ 0x80 = q + 128 as an unsigned byte; fma(q + 128, s, -128 s)
+    // rounds the exact q * s once, i.e. equals fp32(q * s)
+    float v[8];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int d = 2 * c + h;
+      const uint32_t x = cw[d >> 2][d & 3] ^ 0x80808080u;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) v[4 * h + e] = __builtin_fmaf((float)((x >> (8 * e)) & 0xffu), p.s, p.o);
+    }
+    return u32x4{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]), pack_bf16x2(v[4], v[5]),
+                 pack_bf16x2(v[6], v[7])};
+  } else {
+    // E4M3 bytes decoded exactly to fp32 by the hardware, then one multiply
+    u32x4 r;
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int d = 2 * c + h;
+      const uint32_t x = cw[d >> 2][d & 3];
+      const f32x2 lo = __builtin_amdgcn_cvt_pk_f32_fp8((int)x, false);
+      const f32x2 hi = __builtin_amdgcn_cvt_pk_f32_fp8((int)x, true);
+      r[2 * h] = pack_bf16x2(lo[0] * p.s, lo[1] * p.s);
+      r[2 * h + 1] = pack_bf16x2(hi[0] * p.s, hi[1] * p.s);
+    }
+    return r;
+  }
+}
+
+// The same values in fp32 (for the dequantize entry point, which exposes the
+// exact operand values): element e of 4 codes in dword x.
+template <int F>
+__device__ __forceinline__ f32x4 wdeq4_f32(uint32_t x, const WPrep<F>& p) {
+  f32x4 v;
+  if constexpr (F == kInt8) {
+    const uint32_t y = x ^ 0x80808080u;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) v[e] = __builtin_fmaf((float)((y >> (8 * e)) & 0xffu), p.s, p.o);
+  } else {
+    const f32x2 lo = __builtin_amdgcn_cvt_pk_f32_fp8((int)x, false);
+    const f32x2 hi = __builtin_amdgcn_cvt_pk_f32_fp8((int)x, true);
+    v = f32x4{lo[0] * p.s, lo[1] * p.s, hi[0] * p.s, hi[1] * p.s};
+  }
+  return v;
+}
+
+// ---------------------------------------------------------------------------
 // Buffer resources: loads and stores through a descriptor with a hardware
 // range check. An offset at or beyond num_records reads zero and drops a
 // store, which replaces data-dependent branches at tile edges.

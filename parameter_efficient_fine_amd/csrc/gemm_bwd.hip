@@ -38,9 +38,27 @@
 #include "common.hpp"
 #include "internal.hpp"
 
+// This source is compiled once per weight format (QL_WFMT: 0 NF4, 1 INT8,
+// 2 FP8); each object defines the launchers of its format's namespace.
+#ifndef QL_WFMT
+#define QL_WFMT 0
+#endif
+#if QL_WFMT == 0
+#define QL_FMT_NS f0
+#elif QL_WFMT == 1
+#define QL_FMT_NS f1
+#elif QL_WFMT == 2
+#define QL_FMT_NS f2
+#else
+#error "QL_WFMT must be 0, 1 or 2"
+#endif
+
 namespace qlora {
 
 namespace {
+
+constexpr int kFmt = QL_WFMT;
+constexpr int kNV = kFmt == kNF4 ? 2 : 4;  // 16-byte code loads per lane and step (64 elements)
 
 constexpr int kTok = 256;                  // tokens per workgroup
 constexpr int kStep = 64;                  // reduction rows per step
@@ -67,7 +85,7 @@ struct BwdArgs {
 // (4 rows x 2 column groups per cycle) on distinct banks.
 __device__ __forceinline__ int wsw(int j) { return (4 * ((j >> 1) & 1)) | (2 * ((j >> 2) & 1)); }
 
-template <int MODE, int RP, bool ALIGNED>
+template <int F, int MODE, int RP, bool ALIGNED>
 __global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_per_eu(1, 1)))
 void k_qgemm_bwd(BwdArgs p) {
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];  // dY [2], then weight tiles [2][4 waves]
@@ -115,16 +133,18 @@ void k_qgemm_bwd(BwdArgs p) {
   // at its first weight row and sized to the rows that exist, so rows past N
   // read zero (zero codes and absmax give an all-zero table) with no per-step
   // VGPR arithmetic next to loads in flight.
-  const int offC = k_ok ? (int)((int64_t)lane * (K / 2) + kc / 2) : kOff;
+  constexpr int kHB = kCodeHalfBytes<F>;  // 2 x bytes per code
+  const int offC = k_ok ? (int)((int64_t)lane * (K * kHB / 2) + kc * kHB / 2) : kOff;
   const int offA = k_ok ? (int)(((int64_t)lane * (K / kBlock) + kc / kBlock) * 4) : kOff;
-  auto load_codes = [&](int step, u32x4 (&cr)[2], float& am) {
+  auto load_codes = [&](int step, u32x4 (&cr)[kNV], float& am) {
     const int src = NSRC > 1 && step >= sps ? 1 : 0;
     const int64_t n0 = (int64_t)(step - src * sps) * kStep;
     const WSrc& w = p.w[src ? NSRC - 1 : 0];
-    const __amdgpu_buffer_rsrc_t rc = make_rsrc(w.codes + n0 * (K / 2), (N - n0) * (K / 2));
+    const __amdgpu_buffer_rsrc_t rc = make_rsrc(w.codes + n0 * (K * kHB / 2), (N - n0) * (K * kHB / 2));
     const __amdgpu_buffer_rsrc_t ra = make_rsrc(w.absmax + n0 * (K / kBlock), (N - n0) * (K / kBlock) * 4);
-    cr[0] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rc, offC, 0, 0));
-    cr[1] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rc, offC, 16, 0));
+#pragma unroll
+    for (int v = 0; v < kNV; ++v)
+      cr[v] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rc, offC, 16 * v, 0));
     am = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(ra, offA, 0, 0));
   };
 
@@ -212,11 +232,11 @@ void k_qgemm_bwd(BwdArgs p) {
   };
   // weight row n0 + lane of the next step: chunk q -> tile buffer wb
   const int wsl = wsw(lane);
-  auto dequant_write = [&](int wb, const u32x4 (&cr)[2], const Nf4Lut& lut, int q0) {
+  auto dequant_write = [&](int wb, const u32x4 (&cr)[kNV], const WPrep<F>& lut, int q0) {
     uint8_t* row = wtile + wb * 4 * kWBufB + lane * kWRowB;
 #pragma unroll
     for (int q = q0; q < q0 + 2; ++q)
-      *reinterpret_cast<u32x4*>(row + 16 * (q ^ wsl)) = dequant8(cr[q >> 2][q & 3], lut);
+      *reinterpret_cast<u32x4*>(row + 16 * (q ^ wsl)) = wdeq8<F>(cr, q, lut);
   };
   auto mfmas = [&](const u32x4 (&a)[2], const u32x4 (&b)[8]) {
 #pragma unroll
@@ -256,12 +276,12 @@ void k_qgemm_bwd(BwdArgs p) {
   // buffer s&1); its MFMAs then overlap the reads of step s+1's operands,
   // after which -- never before a transposed read -- the dY copies of step
   // s+2 go to buffer s&1.
-  auto body = [&](int s, const u32x4 (&cc)[2], float ac, u32x4 (&cn)[2], float& an) {
+  auto body = [&](int s, const u32x4 (&cc)[kNV], float ac, u32x4 (&cn)[kNV], float& an) {
     const int b0 = s & 1, b1 = b0 ^ 1;
     const int s2 = s + 2 < nsteps ? s + 2 : nsteps - 1;
     // substep 0 (also the table of step s+1's rows and the codes of step s+2)
     load_codes(s2, cn, an);
-    const Nf4Lut lut = make_lut(ac);
+    const WPrep<F> lut = wprep<F>(ac);
     read_b(b0, 1, bv[1]);
     dequant_write(b1, cc, lut, 0);
     mfmas(av[0], bv[0]);
@@ -297,14 +317,14 @@ void k_qgemm_bwd(BwdArgs p) {
 
   // Prologue: codes of steps 0 and 1; dY of steps 0 and 1; tile buffer 0 = step 0;
   // the operands of step 0 read.
-  u32x4 cA[2], cB[2];
+  u32x4 cA[kNV], cB[kNV];
   float aA, aB;
   load_codes(0, cA, aA);
   load_codes(nsteps > 1 ? 1 : 0, cB, aB);
   dma_y(0, 0);
   dma_y(nsteps > 1 ? 1 : 0, 1);
   {
-    const Nf4Lut lut0 = make_lut(aA);
+    const WPrep<F> lut0 = wprep<F>(aA);
 #pragma unroll
     for (int q = 0; q < 8; q += 2) dequant_write(0, cA, lut0, q);
   }
@@ -368,14 +388,14 @@ template <int MODE, int RP, bool ALIGNED>
 hipError_t launch_rp(const BwdArgs& a, hipStream_t st) {
   static bool attr_done = false;
   if (!attr_done) {
-    hipError_t e = hipFuncSetAttribute((const void*)k_qgemm_bwd<MODE, RP, ALIGNED>,
+    hipError_t e = hipFuncSetAttribute((const void*)k_qgemm_bwd<kFmt, MODE, RP, ALIGNED>,
                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)kLds);
     if (e != hipSuccess) return e;
     attr_done = true;
   }
   const int64_t nI = (a.K + 255) / 256, nJ = (a.M + kTok - 1) / kTok;
   if (nI * nJ == 0) return hipSuccess;
-  k_qgemm_bwd<MODE, RP, ALIGNED><<<(unsigned)(nI * nJ), 256, kLds, st>>>(a);
+  k_qgemm_bwd<kFmt, MODE, RP, ALIGNED><<<(unsigned)(nI * nJ), 256, kLds, st>>>(a);
   return hipGetLastError();
 }
 
@@ -402,6 +422,8 @@ hipError_t launch(const BwdArgs& a, hipStream_t st) {
 
 }  // namespace
 
+namespace QL_FMT_NS {
+
 hipError_t launch_gemm_bwd(const uint16_t* dY0, WSrc w0, const uint16_t* dY1, WSrc w1, int64_t M, int64_t K,
                            int64_t N, uint16_t* dX, hipStream_t st) {
   BwdArgs a{};
@@ -424,5 +446,7 @@ hipError_t launch_gemm_bwd_swiglu(const uint16_t* dY, WSrc w, int64_t M, int64_t
   a.g = g, a.u = u;
   return launch<kSwiGLU>(a, st);
 }
+
+}  // namespace QL_FMT_NS
 
 }  // namespace qlora

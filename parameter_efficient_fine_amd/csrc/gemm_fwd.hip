@@ -28,9 +28,28 @@
 #include "common.hpp"
 #include "internal.hpp"
 
+// This source is compiled once per weight format (QL_WFMT: 0 NF4, 1 INT8,
+// 2 FP8); each object defines the launchers of its format's namespace.
+#ifndef QL_WFMT
+#define QL_WFMT 0
+#endif
+#if QL_WFMT == 0
+#define QL_FMT_NS f0
+#elif QL_WFMT == 1
+#define QL_FMT_NS f1
+#elif QL_WFMT == 2
+#define QL_FMT_NS f2
+#else
+#error "QL_WFMT must be 0, 1 or 2"
+#endif
+
 namespace qlora {
 
 namespace {
+
+constexpr int kFmt = QL_WFMT;
+constexpr int kNV = kFmt == kNF4 ? 1 : 2;   // 16-byte code loads per lane, row and step
+constexpr int kCodeStepB = 16 * kNV;        // code bytes of a lane's 32 elements
 
 constexpr int kTok = 256;       // tokens per workgroup
 constexpr int kStep = 64;       // reduction step (one absmax block)
@@ -52,7 +71,7 @@ struct FwdArgs {
 // (out-of-range lanes read zero or drop their store); divergent branches there
 // would push the 256 accumulators out of AGPRs and spill the main loop.
 
-template <bool GATEUP, int RP, bool ALIGNED>
+template <int F, bool GATEUP, int RP, bool ALIGNED>
 __global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_per_eu(1, 1)))
 void k_qgemm_fwd(FwdArgs p) {
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];  // [kNBuf][256 rows][128 B], swizzled
@@ -79,10 +98,10 @@ void k_qgemm_fwd(FwdArgs p) {
 #pragma unroll
   for (int f = 0; f < 2; ++f) {
     const bool second = GATEUP && f == 1;
-    rC[f] = make_rsrc(second ? p.w1.codes : p.w0.codes, N * K / 2);
+    rC[f] = make_rsrc(second ? p.w1.codes : p.w0.codes, N * (K * kCodeHalfBytes<F> / 2));
     rA[f] = make_rsrc(second ? p.w1.absmax : p.w0.absmax, N * (K / kBlock) * 4);
     const int64_t n = nb[f] + jl;
-    offC[f] = n < N ? (int)(n * (K / 2) + 16 * h) : kOff;
+    offC[f] = n < N ? (int)(n * (K * kCodeHalfBytes<F> / 2) + kCodeStepB * h) : kOff;
     offA[f] = n < N ? (int)(n * (K / kBlock) * 4) : kOff;
   }
   // activation copy: wave w, instruction i fills tile rows 64w+8i .. +7; lane l writes
@@ -102,10 +121,13 @@ void k_qgemm_fwd(FwdArgs p) {
       __builtin_amdgcn_raw_ptr_buffer_load_lds(rX, (__attribute__((address_space(3))) void*)(base + 8 * i * kRowB),
                                                16, offX[i], soff, 0, 0);
   };
-  auto load_codes = [&](int step, u32x4 (&cr)[2], float (&am)[2]) {
+  auto load_codes = [&](int step, u32x4 (&cr)[2][kNV], float (&am)[2]) {
 #pragma unroll
     for (int f = 0; f < 2; ++f)
-      cr[f] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rC[f], offC[f], step * (kStep / 2), 0));
+#pragma unroll
+      for (int v = 0; v < kNV; ++v)
+        cr[f][v] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                                                 rC[f], offC[f] + 16 * v, step * (kStep * kCodeHalfBytes<F> / 2), 0));
 #pragma unroll
     for (int f = 0; f < 2; ++f)
       am[f] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rA[f], offA[f], step * 4, 0));
@@ -156,9 +178,9 @@ void k_qgemm_fwd(FwdArgs p) {
   // dequantized from codes already in registers. Step s reads LDS buffer s%4;
   // its activations were copied during step s-3 and published by the barrier
   // ending step s-2, so substep 0 of step s+1 can be read during step s.
-  u32x4 cs0[2], cs1[2], cs2[2];  // codes of steps s, s+1, s+2 (rotating)
+  u32x4 cs0[2][kNV], cs1[2][kNV], cs2[2][kNV];  // codes of steps s, s+1, s+2 (rotating)
   float as0[2], as1[2], as2[2];
-  Nf4Lut L0[2], L1[2], L2[2];    // LUTs, rotating with the codes
+  WPrep<F> L0[2], L1[2], L2[2];  // per-block tables / scales, rotating with the codes
   u32x4 bv[2][8];                // activation fragments, alternating by substep
   u32x4 av[2][2];                // weight fragments, alternating by substep
 
@@ -171,13 +193,13 @@ void k_qgemm_fwd(FwdArgs p) {
 #pragma unroll
     for (int j = 0; j < 8; ++j) dst[j] = *reinterpret_cast<const u32x4*>(bx + 32 * j * kRowB);
   };
-  auto dequant_a = [&](const u32x4 (&cr)[2], int ks, const Nf4Lut (&lut)[2], u32x4 (&dst)[2]) {
+  auto dequant_a = [&](const u32x4 (&cr)[2][kNV], int ks, const WPrep<F> (&lut)[2], u32x4 (&dst)[2]) {
 #pragma unroll
-    for (int f = 0; f < 2; ++f) dst[f] = dequant8(cr[f][ks], lut[f]);
+    for (int f = 0; f < 2; ++f) dst[f] = wdeq8<F>(cr[f], ks, lut[f]);
   };
-  auto luts = [&](const float (&am)[2], Nf4Lut (&lut)[2]) {
+  auto luts = [&](const float (&am)[2], WPrep<F> (&lut)[2]) {
 #pragma unroll
-    for (int f = 0; f < 2; ++f) lut[f] = make_lut(am[f]);
+    for (int f = 0; f < 2; ++f) lut[f] = wprep<F>(am[f]);
   };
   auto mfmas = [&](const u32x4 (&a)[2], const u32x4 (&b)[8]) {
 #pragma unroll
@@ -205,8 +227,8 @@ void k_qgemm_fwd(FwdArgs p) {
   // Step s: VMEM issue order is fixed (4 code loads, then 8 activation copies)
   // so the wait before the closing barrier can be counted: the copies of step
   // s+2 (issued during step s-1) must have landed; 12 ops of step s may remain.
-  auto body = [&](int s, const u32x4 (&cc)[2], const Nf4Lut (&lc)[2], const u32x4 (&cn)[2], const float (&an)[2],
-                  Nf4Lut (&ln)[2], u32x4 (&cl)[2], float (&al)[2]) {
+  auto body = [&](int s, const u32x4 (&cc)[2][kNV], const WPrep<F> (&lc)[2], const u32x4 (&cn)[2][kNV],
+                  const float (&an)[2], WPrep<F> (&ln)[2], u32x4 (&cl)[2][kNV], float (&al)[2]) {
     const int b0 = s % kNBuf, b1 = (s + 1) % kNBuf, b3 = (s + 3) % kNBuf;
     const int s2 = s + 2 < nsteps ? s + 2 : nsteps - 1;
     const int s3 = s + 3 < nsteps ? s + 3 : nsteps - 1;
@@ -304,7 +326,7 @@ template <bool GATEUP, int RP, bool ALIGNED>
 hipError_t launch_rp(const FwdArgs& a, hipStream_t st) {
   static bool attr_done = false;
   if (!attr_done) {
-    hipError_t e = hipFuncSetAttribute((const void*)k_qgemm_fwd<GATEUP, RP, ALIGNED>,
+    hipError_t e = hipFuncSetAttribute((const void*)k_qgemm_fwd<kFmt, GATEUP, RP, ALIGNED>,
                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)kLds);
     if (e != hipSuccess) return e;
     attr_done = true;
@@ -312,7 +334,7 @@ hipError_t launch_rp(const FwdArgs& a, hipStream_t st) {
   const int64_t ipt = GATEUP ? 128 : 256;
   const int64_t nI = (a.N + ipt - 1) / ipt, nJ = (a.M + kTok - 1) / kTok;
   if (nI * nJ == 0) return hipSuccess;
-  k_qgemm_fwd<GATEUP, RP, ALIGNED><<<(unsigned)(nI * nJ), 256, kLds, st>>>(a);
+  k_qgemm_fwd<kFmt, GATEUP, RP, ALIGNED><<<(unsigned)(nI * nJ), 256, kLds, st>>>(a);
   return hipGetLastError();
 }
 
@@ -335,6 +357,8 @@ hipError_t launch(const FwdArgs& a, hipStream_t st) {
 
 }  // namespace
 
+namespace QL_FMT_NS {
+
 hipError_t launch_gemm_fwd(const uint16_t* X, int64_t M, int64_t K, int64_t N, WSrc w, uint16_t* Y, hipStream_t st) {
   FwdArgs a{};
   a.X = X;
@@ -354,5 +378,7 @@ hipError_t launch_gemm_fwd_gateup(const uint16_t* X, int64_t M, int64_t K, int64
   a.out0 = g, a.out1 = u, a.out2 = h;
   return launch<true>(a, st);
 }
+
+}  // namespace QL_FMT_NS
 
 }  // namespace qlora

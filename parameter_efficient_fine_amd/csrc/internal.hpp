@@ -6,9 +6,10 @@
 
 namespace qlora {
 
-hipError_t launch_quantize(const float* W, int64_t N, int64_t K, uint8_t* codes, float* absmax,
+// fmt: 0 NF4 (codes [N, K/2]), 1 INT8, 2 FP8 E4M3 (codes [N, K]); one fp32 per 64-block
+hipError_t launch_quantize(int fmt, const float* W, int64_t N, int64_t K, uint8_t* codes, float* absmax,
                            uint32_t* nonfinite_blocks, hipStream_t st);
-hipError_t launch_dequantize(const uint8_t* codes, const float* absmax, int64_t N, int64_t K, float* W_hat,
+hipError_t launch_dequantize(int fmt, const uint8_t* codes, const float* absmax, int64_t N, int64_t K, float* W_hat,
                              hipStream_t st);
 
 // Skinny rank-r products ------------------------------------------------------
@@ -84,29 +85,58 @@ hipError_t launch_prep(const PrepJobs& jobs, hipStream_t st);
 hipError_t launch_fill_zero_f32(float* p, int64_t n, hipStream_t st);
 
 // Fused dequant GEMMs -------------------------------------------------------
-struct WSrc {           // one frozen 4-bit weight [N, K] with its LoRA pair
-  const uint8_t* codes;  // [N, K/2]
-  const float* absmax;   // [N, K/64]
+struct WSrc {           // one frozen quantized weight [N, K] with its LoRA pair
+  const uint8_t* codes;  // [N, K/2] (NF4) or [N, K] (INT8, FP8)
+  const float* absmax;   // [N, K/64]: NF4 absmax, 8-bit scale
   const uint16_t* lora_i;  // fwd: B [N, r] ; bwd: A [r, K]
   const uint16_t* lora_j;  // fwd: Z [M, r] ; bwd: G [M, r] with row stride ldj
   int r;
   int64_t ldj;
   float s;
+  int fmt;               // 0 NF4, 1 INT8, 2 FP8 (E4M3)
 };
 
-// Y[M, N] = X . What^T + s . Z . B^T
-hipError_t launch_gemm_fwd(const uint16_t* X, int64_t M, int64_t K, int64_t N, WSrc w, uint16_t* Y, hipStream_t st);
-// gate/up of the SwiGLU block in one pass: g, u [M, N], h = silu(g) * u
-hipError_t launch_gemm_fwd_gateup(const uint16_t* X, int64_t M, int64_t K, int64_t N, WSrc wg, WSrc wu, uint16_t* g,
-                                  uint16_t* u, uint16_t* h, hipStream_t st);
-// dX[M, K] = sum_t dY_t . What_t + s_t . G_t . A_t over one or two (dY_t, W_t) pairs
-// (the concatenated reduction of gate and up); each dY_t is [M, N].
-hipError_t launch_gemm_bwd(const uint16_t* dY0, WSrc w0, const uint16_t* dY1, WSrc w1, int64_t M, int64_t K,
-                           int64_t N, uint16_t* dX, hipStream_t st);
-// down-projection backward with the SwiGLU backward in the epilogue:
-// dh = dY . What + s . G . A (never stored); dg = dh*u*sig(g)*(1+g*(1-sig(g))), du = dh*silu(g)
-hipError_t launch_gemm_bwd_swiglu(const uint16_t* dY, WSrc w, int64_t M, int64_t K, int64_t N, const uint16_t* g,
-                                  const uint16_t* u, uint16_t* dg, uint16_t* du, hipStream_t st);
+// The fused GEMMs, one set per weight format (gemm_fwd.hip and gemm_bwd.hip
+// are compiled once per format into the namespaces f0, f1, f2).
+#define QL_GEMM_LAUNCHERS                                                                                          \
+  /* Y[M, N] = X . What^T + s . Z . B^T */                                                                         \
+  hipError_t launch_gemm_fwd(const uint16_t* X, int64_t M, int64_t K, int64_t N, WSrc w, uint16_t* Y,              \
+                             hipStream_t st);                                                                      \
+  /* gate/up of the SwiGLU block in one pass: g, u [M, N], h = silu(g) * u */                                      \
+  hipError_t launch_gemm_fwd_gateup(const uint16_t* X, int64_t M, int64_t K, int64_t N, WSrc wg, WSrc wu,          \
+                                    uint16_t* g, uint16_t* u, uint16_t* h, hipStream_t st);                        \
+  /* dX[M, K] = dY0 . What0 + s0 . G0 . A0 (+ dY1 . What1 + s1 . G1 . A1 when dY1 != null) */                       \
+  hipError_t launch_gemm_bwd(const uint16_t* dY0, WSrc w0, const uint16_t* dY1, WSrc w1, int64_t M, int64_t K,     \
+                             int64_t N, uint16_t* dX, hipStream_t st);                                             \
+  /* dh = dY . What + s . G . A (never stored); dg = dh*u*sig(g)*(1+g*(1-sig(g))), du = dh*silu(g) */              \
+  hipError_t launch_gemm_bwd_swiglu(const uint16_t* dY, WSrc w, int64_t M, int64_t K, int64_t N, const uint16_t* g, \
+                                    const uint16_t* u, uint16_t* dg, uint16_t* du, hipStream_t st);
+namespace f0 { QL_GEMM_LAUNCHERS }
+namespace f1 { QL_GEMM_LAUNCHERS }
+namespace f2 { QL_GEMM_LAUNCHERS }
+#undef QL_GEMM_LAUNCHERS
+
+// Dispatch on the weight format (every weight of one call shares its format).
+#define QL_BY_FMT(fmt, call) \
+  ((fmt) == 0 ? f0::call : (fmt) == 1 ? f1::call : f2::call)
+inline hipError_t launch_gemm_fwd(const uint16_t* X, int64_t M, int64_t K, int64_t N, WSrc w, uint16_t* Y,
+                                  hipStream_t st) {
+  return QL_BY_FMT(w.fmt, launch_gemm_fwd(X, M, K, N, w, Y, st));
+}
+inline hipError_t launch_gemm_fwd_gateup(const uint16_t* X, int64_t M, int64_t K, int64_t N, WSrc wg, WSrc wu,
+                                         uint16_t* g, uint16_t* u, uint16_t* h, hipStream_t st) {
+  return QL_BY_FMT(wg.fmt, launch_gemm_fwd_gateup(X, M, K, N, wg, wu, g, u, h, st));
+}
+inline hipError_t launch_gemm_bwd(const uint16_t* dY0, WSrc w0, const uint16_t* dY1, WSrc w1, int64_t M, int64_t K,
+                                  int64_t N, uint16_t* dX, hipStream_t st) {
+  return QL_BY_FMT(w0.fmt, launch_gemm_bwd(dY0, w0, dY1, w1, M, K, N, dX, st));
+}
+inline hipError_t launch_gemm_bwd_swiglu(const uint16_t* dY, WSrc w, int64_t M, int64_t K, int64_t N,
+                                         const uint16_t* g, const uint16_t* u, uint16_t* dg, uint16_t* du,
+                                         hipStream_t st) {
+  return QL_BY_FMT(w.fmt, launch_gemm_bwd_swiglu(dY, w, M, K, N, g, u, dg, du, st));
+}
+#undef QL_BY_FMT
 
 // RMSNorm rows of x [M,H] with frozen weight w [H]: y bf16, rstd fp32 [M];
 // backward: dx only.

@@ -1,4 +1,5 @@
-// 4-bit block quantization of a frozen weight and its inverse (gfx950).
+// Block quantization of a frozen weight and its inverse (gfx950): the 4-bit
+// NF4 format and, further down, the 8-bit INT8 and FP8 (E4M3) formats.
 //
 // "Unsloth vs The Stack v2", quantized-base card: the base weight is frozen
 // in 4 bits and only the adapter trains. Format: for row n and 64-column block
@@ -59,23 +60,109 @@ __global__ __launch_bounds__(256) void k_dequantize(const uint8_t* __restrict__ 
   reinterpret_cast<float2*>(W_hat)[i] = out;
 }
 
-hipError_t launch_quantize(const float* W, int64_t N, int64_t K, uint8_t* codes, float* absmax,
+// ---------------------------------------------------------------------------
+// 8-bit formats ("Rev vs unsloth", fused quantized-LoRA card: int8 and fp8
+// base weights). Per row n and 64-column block b, with a = max |W|:
+//   INT8: s = a / 127, q = clamp(rint(W / s), -127, 127), a two's-complement byte;
+//   FP8:  s = a / 448, code = the OCP E4M3 value nearest to W / s (ties to the
+//         even code, saturating at 448; sign bit = the sign of W / s);
+// a block of zeros stores s = 0 and codes 0. The block's fp32 slot holds s.
+
+// fp32 -> E4M3 with round to nearest even; |x| >= 448 saturates to 448.
+__device__ __forceinline__ uint32_t e4m3_encode(float x) {
+  const uint32_t sign = (__builtin_bit_cast(uint32_t, x) >> 24) & 0x80u;
+  const float ax = __builtin_fabsf(x);
+  uint32_t mag;
+  if (ax >= 448.0f) {
+    mag = 0x7Eu;
+  } else if (ax < 0.015625f) {           // below 2^-6: multiples of 2^-9 (codes 0..8)
+    mag = (uint32_t)__builtin_rintf(ax * 512.0f);
+  } else {                               // round the fp32 significand to 3 bits, rebias 127 -> 7
+    const uint32_t b = __builtin_bit_cast(uint32_t, ax);
+    const uint32_t r = b + 0x7FFFFu + ((b >> 20) & 1u);
+    mag = (((r >> 23) - 120u) << 3) | ((r >> 20) & 7u);
+    mag = mag > 0x7Eu ? 0x7Eu : mag;
+  }
+  return sign | mag;
+}
+
+// One wave per (row, block); lane e handles column 64*b + e.
+template <int F>
+__global__ __launch_bounds__(256) void k_quantize8(const float* __restrict__ W, int64_t nblocks, int64_t kb_per_row,
+                                                   int64_t K, uint8_t* __restrict__ codes, float* __restrict__ scale,
+                                                   uint32_t* __restrict__ nonfinite) {
+  const int lane = threadIdx.x & 63;
+  const int64_t blk = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (blk >= nblocks) return;
+  const int64_t n = blk / kb_per_row, b = blk - n * kb_per_row;
+  const float w = W[n * K + b * kBlock + lane];
+  const bool bad = !__builtin_isfinite(w);
+  float a = __builtin_fabsf(w);
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) a = fmaxf(a, __shfl_xor(a, off));
+  const float s = a / (F == kInt8 ? 127.0f : 448.0f);
+  uint32_t code = 0;
+  if (s != 0.0f) {
+    const float x = w / s;
+    if constexpr (F == kInt8) {
+      const float q = fminf(fmaxf(__builtin_rintf(x), -127.0f), 127.0f);
+      code = (uint32_t)(int)q & 0xFFu;
+    } else {
+      code = e4m3_encode(x);
+    }
+  }
+  codes[n * K + b * kBlock + lane] = (uint8_t)code;
+  const unsigned long long anybad = __ballot(bad);
+  if (lane == 0) {
+    scale[n * kb_per_row + b] = anybad ? __builtin_nanf("") : s;
+    if (anybad && nonfinite) atomicAdd(nonfinite, 1u);
+  }
+}
+
+// One thread per 4 codes -> 4 fp32 outputs, decoded as the GEMMs decode them.
+template <int F>
+__global__ __launch_bounds__(256) void k_dequantize8(const uint8_t* __restrict__ codes, const float* __restrict__ scale,
+                                                     int64_t nquads, int64_t K, float* __restrict__ W_hat) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= nquads) return;
+  const int64_t e0 = 4 * i, n = e0 / K, k = e0 - n * K;
+  const WPrep<F> p = wprep<F>(scale[n * (K / kBlock) + k / kBlock]);
+  const uint32_t x = reinterpret_cast<const uint32_t*>(codes)[i];
+  reinterpret_cast<f32x4*>(W_hat)[i] = wdeq4_f32<F>(x, p);
+}
+
+hipError_t launch_quantize(int fmt, const float* W, int64_t N, int64_t K, uint8_t* codes, float* absmax,
                            uint32_t* nonfinite_blocks, hipStream_t st) {
   if (nonfinite_blocks) {
     k_zero_u32<<<1, 64, 0, st>>>(nonfinite_blocks);
   }
   const int64_t kb = K / kBlock, nblocks = N * kb;
   if (nblocks == 0) return hipGetLastError();
-  const int64_t grid = (nblocks + 3) / 4;
-  k_quantize<<<(unsigned)grid, 256, 0, st>>>(W, nblocks, kb, K, codes, absmax, nonfinite_blocks);
+  const unsigned grid = (unsigned)((nblocks + 3) / 4);
+  if (fmt == kNF4)
+    k_quantize<<<grid, 256, 0, st>>>(W, nblocks, kb, K, codes, absmax, nonfinite_blocks);
+  else if (fmt == kInt8)
+    k_quantize8<kInt8><<<grid, 256, 0, st>>>(W, nblocks, kb, K, codes, absmax, nonfinite_blocks);
+  else
+    k_quantize8<kFp8><<<grid, 256, 0, st>>>(W, nblocks, kb, K, codes, absmax, nonfinite_blocks);
   return hipGetLastError();
 }
 
-hipError_t launch_dequantize(const uint8_t* codes, const float* absmax, int64_t N, int64_t K, float* W_hat,
+hipError_t launch_dequantize(int fmt, const uint8_t* codes, const float* absmax, int64_t N, int64_t K, float* W_hat,
                              hipStream_t st) {
-  const int64_t nbytes = N * K / 2;
-  if (nbytes == 0) return hipSuccess;
-  k_dequantize<<<(unsigned)((nbytes + 255) / 256), 256, 0, st>>>(codes, absmax, nbytes, K, W_hat);
+  if (fmt == kNF4) {
+    const int64_t nbytes = N * K / 2;
+    if (nbytes == 0) return hipSuccess;
+    k_dequantize<<<(unsigned)((nbytes + 255) / 256), 256, 0, st>>>(codes, absmax, nbytes, K, W_hat);
+    return hipGetLastError();
+  }
+  const int64_t nquads = N * K / 4;
+  if (nquads == 0) return hipSuccess;
+  const unsigned grid = (unsigned)((nquads + 255) / 256);
+  if (fmt == kInt8)
+    k_dequantize8<kInt8><<<grid, 256, 0, st>>>(codes, absmax, nquads, K, W_hat);
+  else
+    k_dequantize8<kFp8><<<grid, 256, 0, st>>>(codes, absmax, nquads, K, W_hat);
   return hipGetLastError();
 }
 

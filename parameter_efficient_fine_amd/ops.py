@@ -29,12 +29,13 @@ def _need(t, dtype, shape, name):
 
 @dataclass
 class QLoraLayer:
-    """A frozen 4-bit weight with its LoRA pair (device tensors)."""
-    codes: torch.Tensor   # uint8 [N, K/2]
-    absmax: torch.Tensor  # float32 [N, K/64]
+    """A frozen quantized weight with its LoRA pair (device tensors)."""
+    codes: torch.Tensor   # uint8 [N, K/2] (NF4) or [N, K] (INT8, FP8)
+    absmax: torch.Tensor  # float32 [N, K/64]: NF4 absmax, 8-bit scale
     A: torch.Tensor       # bfloat16 [r, K]
     B: torch.Tensor       # bfloat16 [N, r]
     s: float
+    fmt: int = C.FMT_NF4
 
     @property
     def K(self):
@@ -50,34 +51,37 @@ class QLoraLayer:
 
     def c(self) -> C.QLoraLayerC:
         K, N, r = self.K, self.N, self.r
-        _need(self.codes, torch.uint8, (N, K // 2), "codes")
+        _need(self.codes, torch.uint8, (N, K // 2 if self.fmt == C.FMT_NF4 else K), "codes")
         _need(self.absmax, torch.float32, (N, K // 64), "absmax")
         _need(self.A, torch.bfloat16, (r, K), "A")
         _need(self.B, torch.bfloat16, (N, r), "B")
         return C.QLoraLayerC(self.codes.data_ptr(), self.absmax.data_ptr(), self.A.data_ptr(), self.B.data_ptr(),
-                             K, N, r, float(self.s))
+                             K, N, r, float(self.s), int(self.fmt))
 
 
-def quantize(W: torch.Tensor):
-    """fp32 W [N,K] on the GPU -> (codes uint8 [N,K/2], absmax fp32 [N,K/64]). Raises on Inf/NaN."""
+def quantize(W: torch.Tensor, fmt: int = C.FMT_NF4):
+    """fp32 W [N,K] on the GPU -> (codes uint8 [N,K/2] (NF4) or [N,K] (INT8, FP8), block values fp32
+    [N,K/64]). Raises on Inf/NaN."""
     N, K = W.shape
     _need(W, torch.float32, (N, K), "W")
-    codes = torch.empty((N, K // 2), dtype=torch.uint8, device=W.device)
+    codes = torch.empty((N, K // 2 if fmt == C.FMT_NF4 else K), dtype=torch.uint8, device=W.device)
     absmax = torch.empty((N, K // 64), dtype=torch.float32, device=W.device)
     bad = torch.empty((1,), dtype=torch.int32, device=W.device)
-    C.check("qlora_quantize", C.lib().qlora_quantize(_ptr(W), N, K, _ptr(codes), _ptr(absmax), _ptr(bad), _stream()))
+    C.check("qlora_quantize", C.lib().qlora_quantize(fmt, _ptr(W), N, K, _ptr(codes), _ptr(absmax), _ptr(bad),
+                                                     _stream()))
     if int(bad.item()) != 0:
         raise ValueError(f"qlora_quantize: {int(bad.item())} block(s) hold non-finite weights")
     return codes, absmax
 
 
-def dequantize(codes: torch.Tensor, absmax: torch.Tensor) -> torch.Tensor:
-    N, K2 = codes.shape
-    K = 2 * K2
-    _need(codes, torch.uint8, (N, K2), "codes")
+def dequantize(codes: torch.Tensor, absmax: torch.Tensor, fmt: int = C.FMT_NF4) -> torch.Tensor:
+    N, KC = codes.shape
+    K = 2 * KC if fmt == C.FMT_NF4 else KC
+    _need(codes, torch.uint8, (N, KC), "codes")
     _need(absmax, torch.float32, (N, K // 64), "absmax")
     out = torch.empty((N, K), dtype=torch.float32, device=codes.device)
-    C.check("qlora_dequantize", C.lib().qlora_dequantize(_ptr(codes), _ptr(absmax), N, K, _ptr(out), _stream()))
+    C.check("qlora_dequantize", C.lib().qlora_dequantize(fmt, _ptr(codes), _ptr(absmax), N, K, _ptr(out),
+                                                         _stream()))
     return out
 
 

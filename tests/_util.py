@@ -4,7 +4,7 @@ from __future__ import annotations
 
 import numpy as np
 
-from oracle import ref
+from oracle import formats8, ref
 from synthetic import bf16_to_f32
 
 TOL = 1e-2  # max|gpu - ref| / max|ref| on bf16 outputs and fp32 gradients (fp32 accumulation)
@@ -39,23 +39,28 @@ def host(t) -> np.ndarray:
 
 
 class Prepared:
-    """One projection on both sides: oracle (fp64) and device tensors."""
+    """One projection on both sides: oracle (fp64) and device tensors, with the
+    frozen weight in format fmt (0 NF4, 1 INT8, 2 FP8)."""
 
-    def __init__(self, layer: dict, s: float, quantize_on_gpu=True):
+    def __init__(self, layer: dict, s: float, quantize_on_gpu=True, fmt: int = 0):
         import parameter_efficient_fine_amd as q
         self.s = s
         W = layer["W"]
-        self.codes_ref, self.absmax_ref = ref.quantize(W)
-        self.What = ref.dequantize(self.codes_ref, self.absmax_ref).astype(np.float64)
+        if fmt == 0:
+            self.codes_ref, self.absmax_ref = ref.quantize(W)
+            self.What = ref.dequantize(self.codes_ref, self.absmax_ref).astype(np.float64)
+        else:
+            self.codes_ref, self.absmax_ref = formats8.quantize(W, fmt)
+            self.What = formats8.dequantize(self.codes_ref, self.absmax_ref, fmt).astype(np.float64)
         self.A = ref.bf16_to_f64(layer["A"])
         self.B = ref.bf16_to_f64(layer["B"])
         if quantize_on_gpu:
-            codes, absmax = q.quantize(dev_f32(W))
+            codes, absmax = q.quantize(dev_f32(W), fmt)
         else:
             import torch
             codes = torch.from_numpy(self.codes_ref).cuda()
             absmax = torch.from_numpy(self.absmax_ref).cuda()
-        self.dev = q.QLoraLayer(codes, absmax, dev_bf16(layer["A"]), dev_bf16(layer["B"]), s)
+        self.dev = q.QLoraLayer(codes, absmax, dev_bf16(layer["A"]), dev_bf16(layer["B"]), s, fmt)
 
     def triple(self):
         return (self.What, self.A, self.B)

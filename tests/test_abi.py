@@ -97,9 +97,15 @@ def test_mlp_shape_consistency_checks():
 def test_quantize_argument_checks():
     lib = C.lib()
     p = ctypes.c_void_p(0x10000)
-    assert lib.qlora_quantize(p, 4, 100, p, p, None, None) == C.QLORA_EINVAL
-    assert lib.qlora_quantize(p, 0, 64, p, p, None, None) == C.QLORA_OK
-    assert lib.qlora_dequantize(p, p, 4, 65, p, None) == C.QLORA_EINVAL
+    for fmt in (C.FMT_NF4, C.FMT_INT8, C.FMT_FP8):
+        assert lib.qlora_quantize(fmt, p, 4, 100, p, p, None, None) == C.QLORA_EINVAL
+        assert lib.qlora_quantize(fmt, p, 0, 64, p, p, None, None) == C.QLORA_OK
+        assert lib.qlora_dequantize(fmt, p, p, 4, 65, p, None) == C.QLORA_EINVAL
+    for bad_fmt in (-1, 3):
+        assert lib.qlora_quantize(bad_fmt, p, 4, 64, p, p, None, None) == C.QLORA_EINVAL
+        assert lib.qlora_dequantize(bad_fmt, p, p, 4, 64, p, None) == C.QLORA_EINVAL
+    # 8-bit codes are read in 4-byte groups: they must be aligned
+    assert lib.qlora_dequantize(C.FMT_INT8, ctypes.c_void_p(0x10001), p, 4, 64, p, None) == C.QLORA_EINVAL
 
 
 def test_status_strings():
@@ -198,3 +204,23 @@ def test_norm_and_rope_argument_checks():
     assert lib.qlora_rope_backward(p, None, p, 4, 2, 1, 64, 10000.0, None) == C.QLORA_EINVAL  # k heads need k
     assert lib.qlora_rope_forward(p, None, p, 0, 2, 1, 64, 10000.0, None) == C.QLORA_OK
     assert lib.qlora_rope_forward(None, None, p, 4, 0, 0, 64, 10000.0, None) == C.QLORA_OK
+
+
+def test_layer_format_checks():
+    lib = C.lib()
+    p = ctypes.c_void_p(0x10000)
+    for fmt, ok in ((0, True), (1, True), (2, True), (3, False), (-1, False)):
+        L = C.QLoraLayerC(0x10000, 0x10000, 0x10000, 0x10000, 512, 512, 16, 2.0, fmt)
+        st = lib.qlora_forward(ctypes.byref(L), p, 0, p, p, None, 0, None)
+        assert st == (C.QLORA_OK if ok else C.QLORA_EINVAL), fmt
+    # 8-bit weights hold one byte per element: at most 2^30 elements
+    L = C.QLoraLayerC(0x10000, 0x10000, 0x10000, 0x10000, 1 << 16, 1 << 15, 16, 2.0, C.FMT_INT8)
+    assert lib.qlora_forward(ctypes.byref(L), p, 4, p, p, None, 0, None) == C.QLORA_EINVAL
+    L = C.QLoraLayerC(0x10000, 0x10000, 0x10000, 0x10000, 1 << 16, 1 << 15, 16, 2.0, C.FMT_NF4)
+    assert lib.qlora_forward(ctypes.byref(L), p, 0, p, p, None, 0, None) == C.QLORA_OK
+    # the three layers of a SwiGLU block share one format
+    g = C.QLoraLayerC(0x10000, 0x10000, 0x10000, 0x10000, 256, 512, 16, 2.0, C.FMT_FP8)
+    u = C.QLoraLayerC(0x10000, 0x10000, 0x10000, 0x10000, 256, 512, 16, 2.0, C.FMT_FP8)
+    d = C.QLoraLayerC(0x10000, 0x10000, 0x10000, 0x10000, 512, 256, 16, 2.0, C.FMT_INT8)
+    assert lib.swiglu_mlp_forward(ctypes.byref(g), ctypes.byref(u), ctypes.byref(d), p, 8, p, p, p, p, p,
+                                  None, 0, None) == C.QLORA_EINVAL

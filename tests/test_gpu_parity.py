@@ -85,10 +85,10 @@ def test_quantize_reports_nonfinite():
 # ---------------------------------------------------------------------------
 # one projection: full oracle on small shapes
 
-def _linear_case(d, rows=None, check_z=True):
-    """Run GPU fwd+bwd on workload dict d; compare to the oracle (optionally on sampled rows)."""
+def _linear_case(d, rows=None, check_z=True, fmt=0):
+    """Run GPU fwd+bwd on workload dict d (weight format fmt); compare to the oracle (optionally on sampled rows)."""
     q = _q()
-    P = Prepared(d["layers"]["proj"], d["s"])
+    P = Prepared(d["layers"]["proj"], d["s"], fmt=fmt)
     X16, dY16 = d["X"], d["dY"]
     Xd, dYd = dev_bf16(X16), dev_bf16(dY16)
     Y, Z = q.forward(P.dev, Xd)
@@ -176,9 +176,9 @@ def test_rank_sweep_full_size(sub):
 # ---------------------------------------------------------------------------
 # SwiGLU block
 
-def _mlp_case(d, rows=None, mask_dy=False):
+def _mlp_case(d, rows=None, mask_dy=False, fmt=0):
     q = _q()
-    Ls = {nm: Prepared(d["layers"][nm], d["s"]) for nm in ("gate", "up", "down")}
+    Ls = {nm: Prepared(d["layers"][nm], d["s"], fmt=fmt) for nm in ("gate", "up", "down")}
     dY16 = d["dY"].copy()
     if mask_dy:
         keep = np.zeros(d["M"], bool)

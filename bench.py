@@ -48,6 +48,8 @@ def parse():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="attn", choices=sorted(WL_INDEX))
     ap.add_argument("--rank", type=int, default=16)
+    ap.add_argument("--wfmt", default="nf4", choices=["nf4", "int8", "fp8"],
+                    help="format of the frozen weights (NF4 4-bit, INT8, FP8 E4M3; 64-element blocks)")
     ap.add_argument("--mlp-tile", type=int, default=0,
                     help="token-tiled SwiGLU block with this many tokens per tile (0: whole batch)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="target CPU time of the oracle baseline")
@@ -128,14 +130,19 @@ def dev_f32(x):
     return torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32)).cuda()
 
 
+WFMT = {"nf4": 0, "int8": 1, "fp8": 2}
+WFMT_DESC = {"nf4": "nf4, fp32 absmax per 64-block", "int8": "int8, fp32 scale (absmax/127) per 64-block",
+             "fp8": "fp8 e4m3, fp32 scale (absmax/448) per 64-block"}
+
+
 class Proj:
     """Device tensors and prebuilt C-ABI arguments of one projection's fwd+bwd."""
 
-    def __init__(self, q, C, layer, s, X, dY):
+    def __init__(self, q, C, layer, s, X, dY, fmt=0):
         import torch
         M = X.shape[0]
-        codes, absmax = q.quantize(dev_f32(layer["W"]))
-        self.L = q.QLoraLayer(codes, absmax, dev_bf16(layer["A"]), dev_bf16(layer["B"]), s)
+        codes, absmax = q.quantize(dev_f32(layer["W"]), fmt)
+        self.L = q.QLoraLayer(codes, absmax, dev_bf16(layer["A"]), dev_bf16(layer["B"]), s, fmt)
         self.M, self.K, self.N, self.r = M, self.L.K, self.L.N, self.L.r
         self.X, self.dY = X, dY
         dev = X.device
@@ -162,12 +169,12 @@ class Proj:
 
 
 class MLP:
-    def __init__(self, q, C, layers, s, X, dY, tile=0):
+    def __init__(self, q, C, layers, s, X, dY, tile=0, fmt=0):
         import torch
         Ls = []
         for nm in ("gate", "up", "down"):
-            codes, absmax = q.quantize(dev_f32(layers[nm]["W"]))
-            Ls.append(q.QLoraLayer(codes, absmax, dev_bf16(layers[nm]["A"]), dev_bf16(layers[nm]["B"]), s))
+            codes, absmax = q.quantize(dev_f32(layers[nm]["W"]), fmt)
+            Ls.append(q.QLoraLayer(codes, absmax, dev_bf16(layers[nm]["A"]), dev_bf16(layers[nm]["B"]), s, fmt))
         self.Ls = Ls
         M = X.shape[0]
         H, I, r = Ls[0].K, Ls[0].N, Ls[0].r
@@ -258,7 +265,7 @@ class NormRope:
                 "rope_fwd": rope, "rope_bwd": rope}
 
 
-def build_workload(name: str, rank: int, mlp_tile: int = 0):
+def build_workload(name: str, rank: int, mlp_tile: int = 0, fmt: int = 0):
     import torch
     import parameter_efficient_fine_amd as q
     from parameter_efficient_fine_amd import _lib as C
@@ -273,15 +280,15 @@ def build_workload(name: str, rank: int, mlp_tile: int = 0):
     d = make_workload(c, sub)
     parts = []
     if d["kind"] == "linear":
-        parts.append(Proj(q, C, d["layers"]["proj"], d["s"], dev_bf16(d["X"]), dev_bf16(d["dY"])))
+        parts.append(Proj(q, C, d["layers"]["proj"], d["s"], dev_bf16(d["X"]), dev_bf16(d["dY"]), fmt))
     elif d["kind"] == "mlp":
-        parts.append(MLP(q, C, d["layers"], d["s"], dev_bf16(d["X"]), dev_bf16(d["dY"]), mlp_tile))
+        parts.append(MLP(q, C, d["layers"], d["s"], dev_bf16(d["X"]), dev_bf16(d["dY"]), mlp_tile, fmt))
     else:
         Xa, Xo = dev_bf16(d["X_attn"]), dev_bf16(d["X_o"])
         for nm, X in (("q", Xa), ("k", Xa), ("v", Xa), ("o", Xo)):
-            parts.append(Proj(q, C, d["layers"][nm], d["s"], X, dev_bf16(d["dY_" + nm])))
+            parts.append(Proj(q, C, d["layers"][nm], d["s"], X, dev_bf16(d["dY_" + nm]), fmt))
         parts.append(MLP(q, C, {k: d["layers"][k] for k in ("gate", "up", "down")}, d["s"], dev_bf16(d["X_mlp"]),
-                         dev_bf16(d["dY_mlp"]), mlp_tile))
+                         dev_bf16(d["dY_mlp"]), mlp_tile, fmt))
     torch.cuda.synchronize()
     return d, parts
 
@@ -300,13 +307,13 @@ def describe(d, name, parts=()):
         Lr = d["layers"]["proj"]
         K, N = Lr["W"].shape[1], Lr["W"].shape[0]
         return dict(workload=f"{name}: one 4-bit NF4 projection, M={M} tokens, K={K}, N={N}, r={r}, alpha={d['alpha']}",
-                    M=M, K=K, N=N, r=r, alpha=d["alpha"], weight_format="nf4, fp32 absmax per 64-block")
+                    M=M, K=K, N=N, r=r, alpha=d["alpha"], weight_format=WFMT_DESC[d.get("wfmt", "nf4")])
     if d["kind"] == "mlp":
         return dict(workload=f"{name}: SwiGLU block, M={M}, 4096<->14336, LoRA r={r} on gate/up/down",
-                    M=M, H=4096, I=14336, r=r, alpha=d["alpha"], weight_format="nf4, fp32 absmax per 64-block", **extra)
+                    M=M, H=4096, I=14336, r=r, alpha=d["alpha"], weight_format=WFMT_DESC[d.get("wfmt", "nf4")], **extra)
     return dict(workload=f"{name}: 7 projections of a GQA decoder layer (q,o 4096x4096; k,v 4096->1024; "
                          f"gate/up/down 4096<->14336), M={M}, r={r}", M=M, r=r, alpha=d["alpha"],
-                weight_format="nf4, fp32 absmax per 64-block", **extra)
+                weight_format=WFMT_DESC[d.get("wfmt", "nf4")], **extra)
 
 
 # ---------------------------------------------------------------------------
@@ -339,6 +346,15 @@ def gemm_flops(parts):
 # ---------------------------------------------------------------------------
 # CPU oracle baseline (bounded sample of the same workload)
 
+def _oracle_weight(W, wfmt):
+    """The oracle's dequantized weight in the benched format (float64)."""
+    from oracle import formats8, ref
+    if wfmt == "nf4":
+        return ref.dequantize(*ref.quantize(W)).astype(np.float64)
+    f = WFMT[wfmt]
+    return formats8.dequantize(*formats8.quantize(W, f), f).astype(np.float64)
+
+
 def cpu_baseline(d, target_s: float):
     from threadpoolctl import threadpool_info, threadpool_limits
     from oracle import ref
@@ -348,7 +364,7 @@ def cpu_baseline(d, target_s: float):
         M = d["M"]
         if d["kind"] == "linear":
             Lr = d["layers"]["proj"]
-            What = ref.dequantize(*ref.quantize(Lr["W"])).astype(np.float64)
+            What = _oracle_weight(Lr["W"], d.get("wfmt", "nf4"))
             A, B = ref.bf16_to_f64(Lr["A"]), ref.bf16_to_f64(Lr["B"])
             X, dY = ref.bf16_to_f64(d["X"]), ref.bf16_to_f64(d["dY"])
 
@@ -374,7 +390,7 @@ def cpu_baseline(d, target_s: float):
         else:
             names = ("gate", "up", "down")
             lay = d["layers"]
-            trip = [(ref.dequantize(*ref.quantize(lay[n]["W"])).astype(np.float64), ref.bf16_to_f64(lay[n]["A"]),
+            trip = [(_oracle_weight(lay[n]["W"], d.get("wfmt", "nf4")), ref.bf16_to_f64(lay[n]["A"]),
                      ref.bf16_to_f64(lay[n]["B"])) for n in names]
             xk, dk = ("X", "dY") if d["kind"] == "mlp" else ("X_mlp", "dY_mlp")
             X, dY = ref.bf16_to_f64(d[xk]), ref.bf16_to_f64(d[dk])
@@ -421,7 +437,8 @@ def main():
     from synthetic import useful_flops
 
     lib = C.lib()
-    d, parts = build_workload(args.workload, args.rank, args.mlp_tile)
+    d, parts = build_workload(args.workload, args.rank, args.mlp_tile, WFMT[args.wfmt])
+    d["wfmt"] = args.wfmt
     c = WL_INDEX[args.workload]
     sub = d["sub"] if args.workload == "rsweep" else 0
     flops = useful_flops(c, sub) if c is not None else None

@@ -12,6 +12,7 @@ seeded synthetic inputs already resident in HBM:
   rsweep : M=8192, K=N=4096, r from --rank (8, 16, 64, 128)
   layer  : the 7 projections of a Llama-3.1-8B GQA decoder layer at M=16384
   normrope: the layer's two RMSNorms (H=4096) and q/k RoPE (32+8 heads of 128), M=16384
+  lmhead : chunked cross-entropy over a 128256 x 4096 LM head, M=16384, chunks of 4096
 --mlp-tile T runs the SwiGLU block of mlp/layer token-tiled (T tokens at a
 time, g/u/h recomputed in the backward) and reports its activation memory.
 Prints one JSON line with tokens/s, useful TFLOP/s (4MNK + 6Mr(N+K) per
@@ -34,7 +35,10 @@ sys.path.insert(0, ROOT)
 
 PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 MFMA (published)
 PEAK_HBM_GBS = 8000.0
-WL_INDEX = {"tiny": 0, "attn": 1, "mlp": 2, "rsweep": 3, "layer": 4, "normrope": None}
+WL_INDEX = {"tiny": 0, "attn": 1, "mlp": 2, "rsweep": 3, "layer": 4, "normrope": None, "lmhead": None}
+# cross-entropy over the Llama-3-8B LM head (vocabulary 128256, width 4096) for
+# the layer workload's 16384 tokens, in chunks of 4096 tokens (3 GB of workspace)
+LMHEAD = dict(M=16384, H=4096, V=128256, chunk=4096)
 # the steps around the projections of one decoder layer at M=16384: two
 # RMSNorms of the 4096-wide residual stream and RoPE of q (32 heads) and k (8)
 NORMROPE = dict(M=16384, H=4096, hq=32, hk=8, d=128, eps=1e-5, base=500000.0)
@@ -73,6 +77,7 @@ KERNEL_SOURCES = {  # kernel class -> the sources its code is built from
     "rmsnorm_bwd": ["normrope.hip", "common.hpp"],
     "rope_fwd": ["normrope.hip", "common.hpp"],
     "rope_bwd": ["normrope.hip", "common.hpp"],
+    "gemm_nt": ["lmhead.hip", "common.hpp"],
 }
 
 
@@ -265,12 +270,54 @@ class NormRope:
                 "rope_fwd": rope, "rope_bwd": rope}
 
 
+class LMHeadCE:
+    """Chunked cross-entropy (loss and dh) over the frozen LM head."""
+
+    def __init__(self, q, cfg):
+        import torch
+        from synthetic import random_ce
+        d = random_ce(6000, cfg["M"], cfg["H"], cfg["V"])
+        self.d, self.cfg = d, cfg
+        self.h, self.W = dev_bf16(d["h"]), dev_bf16(d["W"])
+        self.t = torch.from_numpy(d["targets"]).cuda()
+        self.Wt = q.lmhead_prepare(self.W)
+        M, H, V, chunk = cfg["M"], cfg["H"], cfg["V"], cfg["chunk"]
+        e = lambda shape, dt: torch.empty(shape, dtype=dt, device="cuda")
+        self.loss, self.rows, self.dh = e((1,), torch.float32), e((M,), torch.float32), e((M, H), torch.bfloat16)
+        from parameter_efficient_fine_amd import _lib as C
+        self.ws = e((int(C.lib().qlora_ce_workspace_size(M, V, chunk)),), torch.uint8)
+        p = lambda t: ctypes.c_void_p(t.data_ptr())
+        self.args = (p(self.h), p(self.W), p(self.Wt), p(self.t), M, H, V, chunk, p(self.loss), p(self.rows),
+                     p(self.dh), p(self.ws), self.ws.numel())
+
+    def run(self, lib, stream):
+        if lib.qlora_chunked_ce(*self.args, stream):
+            raise RuntimeError("qlora_chunked_ce")
+
+    def useful_flops(self):
+        c = self.cfg
+        return 4.0 * c["M"] * c["V"] * c["H"]  # logits and dh
+
+    def gemm_flops(self):
+        c = self.cfg
+        out = []
+        for r0 in range(0, c["M"], c["chunk"]):
+            mc = min(c["chunk"], c["M"] - r0)
+            out += [2 * mc * c["V"] * c["H"]] * 2
+        return {"gemm_nt": out}
+
+
 def build_workload(name: str, rank: int, mlp_tile: int = 0, fmt: int = 0):
     import torch
     import parameter_efficient_fine_amd as q
     from parameter_efficient_fine_amd import _lib as C
     from synthetic import WORKLOADS, make_workload
     c = WL_INDEX[name]
+    if name == "lmhead":
+        parts = [LMHeadCE(q, LMHEAD)]
+        d = dict(LMHEAD, kind="lmhead", _data=parts[0].d)
+        torch.cuda.synchronize()
+        return d, parts
     if name == "normrope":
         parts = [NormRope(q, NORMROPE)]
         d = dict(NORMROPE, kind="normrope", _data=parts[0].d)
@@ -294,6 +341,10 @@ def build_workload(name: str, rank: int, mlp_tile: int = 0, fmt: int = 0):
 
 
 def describe(d, name, parts=()):
+    if d["kind"] == "lmhead":
+        return dict(workload=f"{name}: chunked cross-entropy (loss and dh) over a frozen bf16 LM head, V={d['V']}, "
+                             f"H={d['H']}, M={d['M']} tokens in chunks of {d['chunk']}, ~10% ignored targets",
+                    **{k: d[k] for k in ("M", "H", "V", "chunk")})
     if d["kind"] == "normrope":
         return dict(workload=f"{name}: two RMSNorms (H={d['H']}, eps={d['eps']}) and RoPE of q ({d['hq']} heads) and "
                              f"k ({d['hk']} heads) of {d['d']}, base {d['base']:g}, fwd+bwd, M={d['M']} tokens in "
@@ -324,6 +375,10 @@ def gemm_flops(parts):
     out = {}
     for p in parts:
         if isinstance(p, NormRope):
+            continue
+        if isinstance(p, LMHeadCE):
+            for k, v in p.gemm_flops().items():
+                out.setdefault(k, []).extend(v)
             continue
         if isinstance(p, Proj):
             M, K, N, r = p.M, p.K, p.N, p.r
@@ -372,6 +427,14 @@ def cpu_baseline(d, target_s: float):
                 ref.linear_fwd(X[:rows], What, A, B, d["s"])
                 ref.linear_bwd(dY[:rows], X[:rows], What, A, B, d["s"])
             what = "linear fwd+bwd"
+        elif d["kind"] == "lmhead":
+            from oracle import ce as ce_oracle
+            nd = d["_data"]
+            Hh, Wl = ref.bf16_to_f64(nd["h"]), ref.bf16_to_f64(nd["W"])
+
+            def run(rows):
+                ce_oracle.ce_fwd_bwd(Hh[:rows], Wl, nd["targets"][:rows])
+            what = "cross-entropy over the LM head, loss and dh"
         elif d["kind"] == "normrope":
             from oracle import normrope as nr
             nd = d["_data"]
@@ -442,6 +505,8 @@ def main():
     c = WL_INDEX[args.workload]
     sub = d["sub"] if args.workload == "rsweep" else 0
     flops = useful_flops(c, sub) if c is not None else None
+    if args.workload == "lmhead":
+        flops = parts[0].useful_flops()
     stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
 
     def step():
@@ -524,9 +589,12 @@ def main():
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "bf16",
-        "data": ("synthetic (seeded N(0,1) activations and gradients, norm weight 1+0.1*N(0,1), packed-sequence "
-                 "positions)" if flops is None else
-                 "synthetic (seeded N(0,1) activations, 0.02*N(0,1) weights quantized to NF4)"),
+        "data": {"normrope": "synthetic (seeded N(0,1) activations and gradients, norm weight 1+0.1*N(0,1), "
+                             "packed-sequence positions)",
+                 "lmhead": "synthetic (seeded N(0,1) hidden states, 0.02*N(0,1) bf16 LM head, uniform targets, "
+                           "10% ignored)"}.get(d["kind"],
+                                               "synthetic (seeded N(0,1) activations, 0.02*N(0,1) weights quantized"
+                                               " to " + d.get("wfmt", "nf4").upper() + ")"),
         "config": describe(d, args.workload, parts),
         "useful_tflops": tflops,
         "mfma_peak_frac": tflops / PEAK_BF16_TFLOPS if tflops is not None else None,

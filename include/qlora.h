@@ -189,6 +189,27 @@ int qlora_rope_forward(uint16_t* q, uint16_t* k, const int32_t* pos, int64_t M, 
 int qlora_rope_backward(uint16_t* dq, uint16_t* dk, const int32_t* pos, int64_t M, int hq, int hk, int d, float base,
                         void* stream);
 
+/* Cross-entropy over the frozen language-model head, chunked over tokens so
+ * that the [M, V] logits never exist ("Unsloth" wiki entry, Theory: chunked
+ * cross-entropy; "Unsloth vs PyTorch" video, 3:06-3:51). For h [M,H] (bf16,
+ * the final hidden states), W [V,H] (bf16 head) and targets [M] (int32;
+ * t < 0 or t >= V ignores the row):
+ *   z = h . W^T, lse_m = log sum_v exp z[m,v], loss_m = lse_m - z[m,t_m],
+ *   loss = sum over kept rows / n (n = kept rows; 0 if none),
+ *   dh = dz . W with dz = (softmax(z) - onehot(t)) / n on kept rows, 0 elsewhere.
+ * Per chunk of `chunk` tokens the logits are formed in fp32 in the workspace,
+ * reduced row by row, turned into dz (bf16) and multiplied back; the
+ * workspace holds one chunk (qlora_ce_workspace_size), so memory follows the
+ * chunk, not M. W is frozen: no weight gradient. Wt = W^T [H,V], made once by
+ * qlora_lmhead_prepare, serves the dh product. loss (1 float), loss_rows [M]
+ * (0 on ignored rows) and dh [M,H] are device outputs. H % 64 == 0,
+ * V % 64 == 0, H, V <= 2^21, H*V <= 2^30. */
+int qlora_lmhead_prepare(const uint16_t* W, int64_t V, int64_t H, uint16_t* Wt, void* stream);
+size_t qlora_ce_workspace_size(int64_t M, int64_t V, int64_t chunk);
+int qlora_chunked_ce(const uint16_t* h, const uint16_t* W, const uint16_t* Wt, const int32_t* targets, int64_t M,
+                     int64_t H, int64_t V, int64_t chunk, float* loss, float* loss_rows, uint16_t* dh, void* ws,
+                     size_t ws_bytes, void* stream);
+
 /* Measurement support (off the hot path; not thread-safe).
  * qlora_profile_begin creates, once, a pool of 2*max_launches hipEvents and
  * from then on brackets each kernel launch made by this library with an event

@@ -8,8 +8,11 @@ from .ops import (  # noqa: F401
     KernelTimer,
     QLoraLayer,
     backward,
+    ce_chunk_for_budget,
+    chunked_ce,
     dequantize,
     forward,
+    lmhead_prepare,
     mlp_backward,
     mlp_backward_tiled,
     mlp_forward,

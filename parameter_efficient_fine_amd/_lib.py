@@ -25,7 +25,8 @@ EXPORTS = [
     "qlora_quantize", "qlora_dequantize", "qlora_workspace_size", "qlora_forward", "qlora_backward",
     "swiglu_mlp_forward", "swiglu_mlp_backward", "swiglu_mlp_tiled_workspace_size", "swiglu_mlp_forward_tiled",
     "swiglu_mlp_backward_tiled", "qlora_rmsnorm_forward", "qlora_rmsnorm_backward", "qlora_rope_forward",
-    "qlora_rope_backward", "qlora_profile_begin", "qlora_profile_end",
+    "qlora_rope_backward", "qlora_lmhead_prepare", "qlora_ce_workspace_size", "qlora_chunked_ce",
+    "qlora_profile_begin", "qlora_profile_end",
     "qlora_status_string", "qlora_last_error",
 ]
 
@@ -86,6 +87,10 @@ def lib():
     L.qlora_rmsnorm_backward.argtypes = [vp, vp, vp, vp, i64, i64, vp, vp]
     L.qlora_rope_forward.argtypes = [vp, vp, vp, i64, ci, ci, ci, cf, vp]
     L.qlora_rope_backward.argtypes = [vp, vp, vp, i64, ci, ci, ci, cf, vp]
+    L.qlora_lmhead_prepare.argtypes = [vp, i64, i64, vp, vp]
+    L.qlora_ce_workspace_size.argtypes = [i64, i64, i64]
+    L.qlora_ce_workspace_size.restype = sz
+    L.qlora_chunked_ce.argtypes = [vp, vp, vp, vp, i64, i64, i64, i64, vp, vp, vp, vp, sz, vp]
     L.qlora_profile_begin.argtypes = [ctypes.c_int]
     L.qlora_profile_begin.restype = ctypes.c_int
     L.qlora_profile_end.argtypes = [ctypes.POINTER(KernelTimeC), ctypes.c_int, ctypes.POINTER(ctypes.c_int)]
@@ -96,7 +101,8 @@ def lib():
     L.qlora_last_error.restype = ctypes.c_char_p
     for f in ("qlora_quantize", "qlora_dequantize", "qlora_forward", "qlora_backward", "swiglu_mlp_forward",
               "swiglu_mlp_backward", "swiglu_mlp_forward_tiled", "swiglu_mlp_backward_tiled", "qlora_rmsnorm_forward",
-              "qlora_rmsnorm_backward", "qlora_rope_forward", "qlora_rope_backward"):
+              "qlora_rmsnorm_backward", "qlora_rope_forward", "qlora_rope_backward", "qlora_lmhead_prepare",
+              "qlora_chunked_ce"):
         getattr(L, f).restype = ctypes.c_int
     _lib = L
     return L

@@ -632,6 +632,57 @@ int qlora_rope_backward(uint16_t* dq, uint16_t* dk, const int32_t* pos, int64_t 
   return rope_call(dq, dk, pos, M, hq, hk, d, base, true, stream);
 }
 
+int qlora_lmhead_prepare(const uint16_t* W, int64_t V, int64_t H, uint16_t* Wt, void* stream) {
+  if (V <= 0 || H <= 0 || V > kMaxDim || H > kMaxDim) return QLORA_EINVAL;
+  if (!W || !Wt || !aligned16(W) || !aligned16(Wt)) return QLORA_EINVAL;
+  hipStream_t st = (hipStream_t)stream;
+  QL_LAUNCH("transpose", st, launch_transpose_bf16(W, V, H, Wt, st));
+  return QLORA_OK;
+}
+
+static bool ce_shapes_ok(int64_t M, int64_t H, int64_t V, int64_t chunk) {
+  if (M < 0 || chunk < 1 || H <= 0 || V <= 0 || H % 64 != 0 || V % 64 != 0) return false;
+  return H <= kMaxDim && V <= kMaxDim && H * V <= kMaxWeight / 2;
+}
+
+static size_t ce_ws(int64_t M, int64_t V, int64_t chunk) {
+  const int64_t C = std::min(chunk, M);
+  return up256((size_t)C * V * 4) + up256((size_t)C * V * 2) + 256;
+}
+
+size_t qlora_ce_workspace_size(int64_t M, int64_t V, int64_t chunk) {
+  if (M < 0 || V <= 0 || chunk < 1) return 0;
+  return ce_ws(M, V, chunk);
+}
+
+int qlora_chunked_ce(const uint16_t* h, const uint16_t* W, const uint16_t* Wt, const int32_t* targets, int64_t M,
+                     int64_t H, int64_t V, int64_t chunk, float* loss, float* loss_rows, uint16_t* dh, void* ws,
+                     size_t ws_bytes, void* stream) {
+  if (!ce_shapes_ok(M, H, V, chunk)) return QLORA_EINVAL;
+  if (!loss) return QLORA_EINVAL;
+  if (M > 0 && (!h || !W || !Wt || !targets || !loss_rows || !dh || !aligned16(h) || !aligned16(W) ||
+                !aligned16(Wt) || !aligned16(dh)))
+    return QLORA_EINVAL;
+  if (!ws || ws_bytes < ce_ws(M, V, chunk)) return QLORA_EWORKSPACE;
+  const int64_t C = std::min(chunk, M);
+  Carve c{(char*)ws, ws_bytes};
+  float* logits = c.take<float>((size_t)C * V);
+  uint16_t* dz = c.take<uint16_t>((size_t)C * V);
+  int32_t* n_keep = c.take<int32_t>(64);
+  if (!c.ok) return QLORA_EWORKSPACE;
+  hipStream_t st = (hipStream_t)stream;
+  QL_LAUNCH("ce_count", st, launch_ce_count(targets, M, V, n_keep, st));
+  for (int64_t r0 = 0; r0 < M; r0 += C) {
+    const int64_t Mc = std::min(C, M - r0);
+    // logits of the chunk (fp32), their row statistics and gradient, then dh = dz . W
+    QL_LAUNCH("gemm_nt", st, launch_gemm_nt_bf16(h + r0 * H, W, Mc, H, V, logits, true, st));
+    QL_LAUNCH("ce_rows", st, launch_ce_rows(logits, targets + r0, n_keep, Mc, V, loss_rows + r0, dz, st));
+    QL_LAUNCH("gemm_nt", st, launch_gemm_nt_bf16(dz, Wt, Mc, V, H, dh + r0 * H, false, st));
+  }
+  QL_LAUNCH("ce_total", st, launch_ce_total(loss_rows, M, n_keep, loss, st));
+  return QLORA_OK;
+}
+
 int qlora_profile_begin(int max_launches) {
   if (max_launches < 1) return QLORA_EINVAL;
   while ((int)g_prof.pool.size() < 2 * max_launches) {

@@ -1,0 +1,350 @@
+// Chunked cross-entropy over the frozen language-model head on gfx950
+// ("Unsloth" wiki entry, Theory: chunked cross-entropy that never forms the
+// [B, T, V] logits; "Unsloth vs PyTorch" video, 3:06-3:51: the loss computed
+// slice by slice, each slice dropped, the same gradient).
+//
+// Per chunk of C tokens (api.cpp drives the chunks):
+//   logits [C, V] fp32 = h_c . W^T        k_gemm_nt<true>   (W [V, H] bf16, frozen)
+//   per row: lse, loss, dz = (softmax - onehot) / n   k_ce_rows (dz bf16 [C, V])
+//   dh_c [C, H] bf16 = dz . W = dz . (W^T)^T   k_gemm_nt<false> on W^T [H, V]
+// W^T is formed once at set-up (qlora_lmhead_prepare): both products are then
+// "X . W^T" GEMMs with the reduction dimension contiguous in both operands.
+//
+// k_gemm_nt is the forward QLoRA GEMM's skeleton with bf16 weights: one
+// workgroup = 4 waves, 256 weight rows x 256 tokens, K in steps of 64; each
+// wave owns 64 weight rows, loaded from HBM straight into MFMA A-operand
+// registers one step ahead (rows are private to a wave); the activation tile
+// goes through LDS by buffer_load ... lds into a ring of four buffers.
+#include <type_traits>
+
+#include "common.hpp"
+#include "internal.hpp"
+
+namespace qlora {
+
+namespace {
+
+constexpr int kTok = 256;
+constexpr int kStep = 64;
+constexpr int kRowB = kStep * 2;
+constexpr int kBufB = kTok * kRowB;  // 32 KB
+constexpr int kNBuf = 4;
+constexpr size_t kLds = (size_t)kNBuf * kBufB;
+
+struct NtGemmArgs {
+  const uint16_t* X;  // [M, K]
+  const uint16_t* W;  // [N, K]
+  int64_t M, K, N;
+  void* Y;            // [M, N] fp32 or bf16
+};
+
+template <bool OUT_F32>
+__global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_per_eu(1, 1)))
+void k_gemm_nt(NtGemmArgs p) {
+  extern __shared__ __attribute__((aligned(16))) uint8_t smem[];  // [kNBuf][256 rows][128 B], swizzled
+  const int t = threadIdx.x, lane = t & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
+  const int h = lane >> 5, jl = lane & 31;
+  const int64_t M = p.M, K = p.K, N = p.N;
+  const int64_t nJ = (M + kTok - 1) / kTok;
+  const int64_t it = blockIdx.x / nJ, jt = blockIdx.x - it * nJ;
+  const int64_t i0 = it * 256, j0 = jt * kTok;
+  const int nsteps = (int)(K / kStep);
+  const int64_t rows_here = (M - j0) < kTok ? (M - j0) : kTok;
+
+  // weight rows of this lane: fragment f = rows i0 + 64 wave + 32 f + jl; lane
+  // half h reads k in [32h, 32h + 32) of a step, substep ks the 8 values 32h + 8ks
+  const __amdgpu_buffer_rsrc_t rW = make_rsrc(p.W, N * K * 2);
+  int offW[2];
+#pragma unroll
+  for (int f = 0; f < 2; ++f) {
+    const int64_t n = i0 + 64 * wave + 32 * f + jl;
+    offW[f] = n < N ? (int)((n * K + 32 * h) * 2) : kOff;
+  }
+  const __amdgpu_buffer_rsrc_t rX = make_rsrc(p.X + j0 * K, rows_here * K * 2);
+  int offX[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int row = 64 * wave + 8 * i + (lane >> 3);
+    const int c = (lane & 7) ^ ((row >> 1) & 7);
+    offX[i] = (int)((int64_t)row * K * 2 + 16 * c);
+  }
+  auto dma_x = [&](int step, int buf) {
+    uint8_t* base = smem + buf * kBufB + (64 * wave) * kRowB;
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rX, (__attribute__((address_space(3))) void*)(base + 8 * i * kRowB),
+                                               16, offX[i], step * kRowB, 0, 0);
+  };
+  auto load_w = [&](int step, u32x4 (&wr)[4][2]) {  // substep-major: substep 0 lands first
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks)
+#pragma unroll
+      for (int f = 0; f < 2; ++f)
+        wr[ks][f] = __builtin_bit_cast(u32x4,
+                                       __builtin_amdgcn_raw_buffer_load_b128(rW, offW[f] + 16 * ks, step * kRowB, 0));
+  };
+
+  f32x16 acc[2][8];
+#pragma unroll
+  for (int f = 0; f < 2; ++f)
+#pragma unroll
+    for (int j = 0; j < 8; ++j) acc[f][j] = f32x16{};
+
+  int offB[4];
+#pragma unroll
+  for (int ks = 0; ks < 4; ++ks) offB[ks] = jl * kRowB + 16 * ((4 * h + ks) ^ ((jl >> 1) & 7));
+  u32x4 bv[2][8];
+  auto read_b = [&](int buf, int ks, u32x4 (&dst)[8]) {
+    const uint8_t* bx = smem + buf * kBufB + offB[ks];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) dst[j] = *reinterpret_cast<const u32x4*>(bx + 32 * j * kRowB);
+  };
+  auto mfmas = [&](const u32x4 (&a)[2], const u32x4 (&b)[8]) {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      acc[0][j] = mfma32(a[0], b[j], acc[0][j]);
+      acc[1][j] = mfma32(a[1], b[j], acc[1][j]);
+    }
+  };
+  auto interleave = [&](auto nds_read, auto nvmem) {
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      if (i < decltype(nds_read)::value) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      if (i < decltype(nvmem)::value) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+    }
+  };
+  using I0 = std::integral_constant<int, 0>;
+  using I8 = std::integral_constant<int, 8>;
+
+  // Step s: weights in wc (loaded during step s-1), activations from LDS
+  // buffer s%4 (copied during step s-3, published by the barrier ending step
+  // s-2). Meanwhile the weights of step s+1 and the activations of step s+3
+  // are requested; substep 0 of step s+1 is read from buffer (s+1)%4 in the
+  // last substep. VMEM issue order per step: 8 weight loads, 8 copies.
+  auto body = [&](int s, const u32x4 (&wc)[4][2], u32x4 (&wn)[4][2]) {
+    const int b0 = s % kNBuf, b1 = (s + 1) % kNBuf, b3 = (s + 3) % kNBuf;
+    const int s1 = s + 1 < nsteps ? s + 1 : nsteps - 1;
+    const int s3 = s + 3 < nsteps ? s + 3 : nsteps - 1;
+    load_w(s1, wn);
+    dma_x(s3, b3);
+    read_b(b0, 1, bv[1]);
+    mfmas(wc[0], bv[0]);
+    interleave(I8{}, I8{});
+    __builtin_amdgcn_sched_barrier(0);
+    read_b(b0, 2, bv[0]);
+    mfmas(wc[1], bv[1]);
+    interleave(I8{}, I8{});
+    __builtin_amdgcn_sched_barrier(0);
+    read_b(b0, 3, bv[1]);
+    mfmas(wc[2], bv[0]);
+    interleave(I8{}, I0{});
+    __builtin_amdgcn_sched_barrier(0);
+    read_b(b1, 0, bv[0]);
+    mfmas(wc[3], bv[1]);
+    interleave(I8{}, I0{});
+    __builtin_amdgcn_sched_barrier(0);
+    __builtin_amdgcn_s_waitcnt(waitcnt_vm(16));  // the copies of step s+2 have landed
+    __builtin_amdgcn_s_waitcnt(0xC07F);           // and this wave's LDS reads
+    __builtin_amdgcn_s_barrier();
+  };
+
+  // Prologue in the order a step issues its loads: weights of step 0 stand in
+  // for "weights of the next step", then the copies of steps 0, 1, 2.
+  u32x4 wa[4][2], wb[4][2];
+  load_w(0, wa);
+  __builtin_amdgcn_sched_barrier(0);
+  dma_x(0, 0);
+  dma_x(nsteps > 1 ? 1 : 0, 1);
+  dma_x(nsteps > 2 ? 2 : nsteps - 1, 2);
+  __builtin_amdgcn_s_waitcnt(waitcnt_vm(8));  // copies of steps 0 and 1
+  __builtin_amdgcn_s_barrier();
+  read_b(0, 0, bv[0]);
+  int s = 0;
+  for (; s + 1 < nsteps; s += 2) {
+    body(s, wa, wb);
+    body(s + 1, wb, wa);
+  }
+  if (s < nsteps) body(s, wa, wb);
+
+  // ---- epilogue: column ic = weight row, row mr = token (C layout of mfma32)
+  constexpr int kOutB = OUT_F32 ? 4 : 2;
+  const __amdgpu_buffer_rsrc_t rO = make_rsrc((uint8_t*)p.Y + j0 * N * kOutB, rows_here * N * kOutB);
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const int64_t mr = 32 * j + jl;
+    const bool m_ok = mr < rows_here;
+#pragma unroll
+    for (int f = 0; f < 2; ++f) {
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int64_t ic = i0 + 64 * wave + 32 * f + 8 * q + 4 * h;
+        const int off = (m_ok && ic < N) ? (int)((mr * N + ic) * kOutB) : kOff;
+        float v[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) v[e] = acc[f][j][4 * q + e];
+        if constexpr (OUT_F32)
+          __builtin_amdgcn_raw_buffer_store_b128(u32x4{__builtin_bit_cast(uint32_t, v[0]),
+                                                       __builtin_bit_cast(uint32_t, v[1]),
+                                                       __builtin_bit_cast(uint32_t, v[2]),
+                                                       __builtin_bit_cast(uint32_t, v[3])},
+                                                 rO, off, 0, 0);
+        else
+          store4(rO, off, v);
+      }
+    }
+  }
+}
+
+// Row statistics and gradient of the cross-entropy, one workgroup per row of
+// the chunk: lse = max + log(sum exp(z - max)) (online, fp32), loss_m = lse -
+// z[t] for kept rows (t >= 0), dz = (exp(z - lse) - [v == t]) / n in bf16
+// (0 on ignored rows).
+__global__ __launch_bounds__(256) void k_ce_rows(const float* __restrict__ logits, const int32_t* __restrict__ tgt,
+                                                 const int32_t* __restrict__ n_keep, int64_t V,
+                                                 float* __restrict__ loss_rows, uint16_t* __restrict__ dz) {
+  __shared__ float red_m[256], red_s[256];
+  const int64_t m = blockIdx.x;
+  const int tid = threadIdx.x;
+  const float* z = logits + m * V;
+  const int t = tgt[m];
+  const int64_t nq = V / 4;
+  float mx = -__builtin_inff(), sm = 0.f;
+  for (int64_t q = tid; q < nq; q += 256) {
+    const f32x4 v = reinterpret_cast<const f32x4*>(z)[q];
+    const float vm = fmaxf(fmaxf(v[0], v[1]), fmaxf(v[2], v[3]));
+    if (vm > mx) {
+      sm *= expf(mx - vm);
+      mx = vm;
+    }
+#pragma unroll
+    for (int e = 0; e < 4; ++e) sm += expf(v[e] - mx);
+  }
+  red_m[tid] = mx;
+  red_s[tid] = sm;
+  __syncthreads();
+  for (int w = 128; w >= 1; w >>= 1) {  // fixed-order tree
+    if (tid < w) {
+      const float m1 = red_m[tid], m2 = red_m[tid + w];
+      const float mm = fmaxf(m1, m2);
+      const float s1 = m1 == -__builtin_inff() ? 0.f : red_s[tid] * expf(m1 - mm);
+      const float s2 = m2 == -__builtin_inff() ? 0.f : red_s[tid + w] * expf(m2 - mm);
+      red_m[tid] = mm;
+      red_s[tid] = s1 + s2;
+    }
+    __syncthreads();
+  }
+  const float lse = red_m[0] + logf(red_s[0]);
+  const int n = *n_keep;
+  const bool keep = t >= 0 && t < V;
+  const float inv_n = (keep && n > 0) ? 1.0f / (float)n : 0.0f;
+  if (tid == 0) loss_rows[m] = keep ? lse - z[t] : 0.0f;
+  uint16_t* d = dz + m * V;
+  for (int64_t q = tid; q < nq; q += 256) {
+    const f32x4 v = reinterpret_cast<const f32x4*>(z)[q];
+    float g[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) g[e] = (expf(v[e] - lse) - ((int64_t)4 * q + e == t ? 1.0f : 0.0f)) * inv_n;
+    *reinterpret_cast<u32x2*>(d + 4 * q) = u32x2{pack_bf16x2(g[0], g[1]), pack_bf16x2(g[2], g[3])};
+  }
+}
+
+// Number of kept targets (t >= 0 and t < V), one workgroup, fixed order.
+__global__ __launch_bounds__(256) void k_ce_count(const int32_t* __restrict__ tgt, int64_t M, int64_t V,
+                                                  int32_t* __restrict__ n_keep) {
+  __shared__ int red[256];
+  int c = 0;
+  for (int64_t m = threadIdx.x; m < M; m += 256) c += (tgt[m] >= 0 && tgt[m] < V) ? 1 : 0;
+  red[threadIdx.x] = c;
+  __syncthreads();
+  for (int w = 128; w >= 1; w >>= 1) {
+    if ((int)threadIdx.x < w) red[threadIdx.x] += red[threadIdx.x + w];
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) *n_keep = red[0];
+}
+
+// loss = sum of the per-row losses / n, one workgroup, fixed order.
+__global__ __launch_bounds__(256) void k_ce_total(const float* __restrict__ loss_rows, int64_t M,
+                                                  const int32_t* __restrict__ n_keep, float* __restrict__ loss) {
+  __shared__ float red[256];
+  float a = 0.f;
+  for (int64_t m = threadIdx.x; m < M; m += 256) a += loss_rows[m];
+  red[threadIdx.x] = a;
+  __syncthreads();
+  for (int w = 128; w >= 1; w >>= 1) {
+    if ((int)threadIdx.x < w) red[threadIdx.x] += red[threadIdx.x + w];
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) {
+    const int n = *n_keep;
+    *loss = n > 0 ? red[0] / (float)n : 0.0f;
+  }
+}
+
+// dst [C, R] = src [R, C]^T (bf16), 64 x 64 tiles through LDS.
+__global__ __launch_bounds__(256) void k_transpose_bf16(const uint16_t* __restrict__ src, int64_t R, int64_t C,
+                                                        uint16_t* __restrict__ dst) {
+  __shared__ uint16_t tile[64][66];
+  const int64_t r0 = (int64_t)blockIdx.y * 64, c0 = (int64_t)blockIdx.x * 64;
+  const int tx = threadIdx.x & 63, ty = threadIdx.x >> 6;
+  for (int i = ty; i < 64; i += 4) {
+    const int64_t r = r0 + i, c = c0 + tx;
+    tile[i][tx] = (r < R && c < C) ? src[r * C + c] : 0;
+  }
+  __syncthreads();
+  for (int i = ty; i < 64; i += 4) {
+    const int64_t c = c0 + i, r = r0 + tx;
+    if (c < C && r < R) dst[c * R + r] = tile[tx][i];
+  }
+}
+
+template <bool OUT_F32>
+hipError_t launch_nt(const NtGemmArgs& a, hipStream_t st) {
+  static bool attr_done = false;
+  if (!attr_done) {
+    hipError_t e =
+        hipFuncSetAttribute((const void*)k_gemm_nt<OUT_F32>, hipFuncAttributeMaxDynamicSharedMemorySize, (int)kLds);
+    if (e != hipSuccess) return e;
+    attr_done = true;
+  }
+  const int64_t nI = (a.N + 255) / 256, nJ = (a.M + kTok - 1) / kTok;
+  if (nI * nJ == 0) return hipSuccess;
+  k_gemm_nt<OUT_F32><<<(unsigned)(nI * nJ), 256, kLds, st>>>(a);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_gemm_nt_bf16(const uint16_t* X, const uint16_t* W, int64_t M, int64_t K, int64_t N, void* Y,
+                               bool out_f32, hipStream_t st) {
+  NtGemmArgs a{X, W, M, K, N, Y};
+  return out_f32 ? launch_nt<true>(a, st) : launch_nt<false>(a, st);
+}
+
+hipError_t launch_ce_count(const int32_t* tgt, int64_t M, int64_t V, int32_t* n_keep, hipStream_t st) {
+  k_ce_count<<<1, 256, 0, st>>>(tgt, M, V, n_keep);
+  return hipGetLastError();
+}
+
+hipError_t launch_ce_rows(const float* logits, const int32_t* tgt, const int32_t* n_keep, int64_t C, int64_t V,
+                          float* loss_rows, uint16_t* dz, hipStream_t st) {
+  if (C == 0) return hipSuccess;
+  k_ce_rows<<<(unsigned)C, 256, 0, st>>>(logits, tgt, n_keep, V, loss_rows, dz);
+  return hipGetLastError();
+}
+
+hipError_t launch_ce_total(const float* loss_rows, int64_t M, const int32_t* n_keep, float* loss, hipStream_t st) {
+  k_ce_total<<<1, 256, 0, st>>>(loss_rows, M, n_keep, loss);
+  return hipGetLastError();
+}
+
+hipError_t launch_transpose_bf16(const uint16_t* src, int64_t R, int64_t C, uint16_t* dst, hipStream_t st) {
+  if (R * C == 0) return hipSuccess;
+  dim3 grid((unsigned)((C + 63) / 64), (unsigned)((R + 63) / 64));
+  k_transpose_bf16<<<grid, 256, 0, st>>>(src, R, C, dst);
+  return hipGetLastError();
+}
+
+}  // namespace qlora

@@ -260,6 +260,43 @@ def rope_backward(dq, dk, pos, d: int, base: float):
     return _rope("qlora_rope_backward", dq, dk, pos, d, base)
 
 
+def lmhead_prepare(W):
+    """W^T [H, V] of the frozen LM head W [V, H] (bf16), for chunked_ce's dh product."""
+    V, H = W.shape
+    _need(W, torch.bfloat16, (V, H), "W")
+    Wt = torch.empty((H, V), dtype=torch.bfloat16, device=W.device)
+    C.check("qlora_lmhead_prepare", C.lib().qlora_lmhead_prepare(_ptr(W), V, H, _ptr(Wt), _stream()))
+    return Wt
+
+
+def ce_chunk_for_budget(V: int, budget_bytes: int) -> int:
+    """Largest chunk (a multiple of 256 tokens, at least 256) whose workspace (fp32 logits and
+    bf16 gradient of the chunk) fits the given memory budget."""
+    return max(256, (budget_bytes // (6 * V)) // 256 * 256)
+
+
+def chunked_ce(h, W, Wt, targets, chunk: int, ws=None, out=None):
+    """Cross-entropy of the frozen LM head W [V,H] over h [M,H] with int32 targets [M]
+    (negative = ignored): dict(loss fp32 [1], loss_rows fp32 [M], dh bf16 [M,H])."""
+    M, H = h.shape
+    V = W.shape[0]
+    _need(h, torch.bfloat16, (M, H), "h")
+    _need(W, torch.bfloat16, (V, H), "W")
+    _need(Wt, torch.bfloat16, (H, V), "Wt")
+    _need(targets, torch.int32, (M,), "targets")
+    dev = h.device
+    if out is None:
+        out = dict(loss=torch.empty((1,), dtype=torch.float32, device=dev),
+                   loss_rows=torch.empty((M,), dtype=torch.float32, device=dev),
+                   dh=torch.empty((M, H), dtype=torch.bfloat16, device=dev))
+    nb = int(C.lib().qlora_ce_workspace_size(M, V, chunk))
+    ws = _workspace(nb, dev) if ws is None else ws
+    C.check("qlora_chunked_ce", C.lib().qlora_chunked_ce(
+        _ptr(h), _ptr(W), _ptr(Wt), _ptr(targets), M, H, V, chunk, _ptr(out["loss"]), _ptr(out["loss_rows"]),
+        _ptr(out["dh"]), _ptr(ws), ws.numel(), _stream()))
+    return out
+
+
 class KernelTimer:
     """Per-kernel-class launch durations from hipEvents the library records around
     each of its launches (on the launch's stream). Use as a context manager."""

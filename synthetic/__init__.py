@@ -174,3 +174,14 @@ def random_norm_rope(seed: int, M: int, H: int, hq: int, hk: int, d: int, max_le
                 q=bf16_bits(_normal(rng, (M, hq * d))), k=bf16_bits(_normal(rng, (M, hk * d))),
                 dq=bf16_bits(_normal(rng, (M, hq * d))), dk=bf16_bits(_normal(rng, (M, hk * d))),
                 pos=packed_positions(rng, M, max_len), M=M, H=H, hq=hq, hk=hk, d=d)
+
+
+def random_ce(seed: int, M: int, H: int, V: int, ignore_frac: float = 0.1):
+    """h [M,H] = N(0,1), LM head W [V,H] = 0.02 N(0,1) (bf16 bits), targets [M] int32
+    uniform in [0, V) with about ignore_frac of them -100 (ignored)."""
+    rng = np.random.default_rng(seed)
+    h = bf16_bits(_normal(rng, (M, H)))
+    W = bf16_bits(_normal(rng, (V, H), 0.02))
+    t = rng.integers(0, V, M).astype(np.int32)
+    t[rng.random(M) < ignore_frac] = -100
+    return dict(h=h, W=W, targets=t, M=M, H=H, V=V)

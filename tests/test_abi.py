@@ -224,3 +224,20 @@ def test_layer_format_checks():
     d = C.QLoraLayerC(0x10000, 0x10000, 0x10000, 0x10000, 512, 256, 16, 2.0, C.FMT_INT8)
     assert lib.swiglu_mlp_forward(ctypes.byref(g), ctypes.byref(u), ctypes.byref(d), p, 8, p, p, p, p, p,
                                   None, 0, None) == C.QLORA_EINVAL
+
+
+def test_chunked_ce_argument_checks():
+    lib = C.lib()
+    p = ctypes.c_void_p(0x10000)
+    need = lib.qlora_ce_workspace_size(100, 1024, 64)
+    assert need >= 64 * 1024 * 6
+    # a longer batch with the same chunk needs no more workspace
+    assert lib.qlora_ce_workspace_size(1 << 20, 1024, 64) == need
+    args = lambda M, H, V, chunk, ws, nb: (p, p, p, p, M, H, V, chunk, p, p, p, ws, nb, None)
+    assert lib.qlora_chunked_ce(*args(100, 100, 1024, 64, p, need)) == C.QLORA_EINVAL   # H % 64
+    assert lib.qlora_chunked_ce(*args(100, 128, 1000, 64, p, need)) == C.QLORA_EINVAL   # V % 64
+    assert lib.qlora_chunked_ce(*args(100, 128, 1024, 0, p, need)) == C.QLORA_EINVAL    # chunk >= 1
+    assert lib.qlora_chunked_ce(*args(100, 1 << 16, 1 << 16, 64, p, need)) == C.QLORA_EINVAL  # H*V too large
+    assert lib.qlora_chunked_ce(*args(100, 128, 1024, 64, None, 0)) == C.QLORA_EWORKSPACE
+    assert lib.qlora_chunked_ce(*args(100, 128, 1024, 64, p, need - 1)) == C.QLORA_EWORKSPACE
+    assert lib.qlora_lmhead_prepare(p, 1024, 128, ctypes.c_void_p(0x10002), None) == C.QLORA_EINVAL

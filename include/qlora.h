@@ -69,7 +69,15 @@ typedef enum {
  *                   value is s = absmax / 448, code = nearest E4M3 value to
  *                   W / s (ties to the even code), saturating at 448.
  * A block of zeros stores 0 and zero codes (NF4: code 7). The dequantized
- * weight is fp32(v * block value) for the code's exact value v. */
+ * weight is fp32(v * block value) for the code's exact value v.
+ * Storage order (codes and block values alike): rows in groups of 64 (the
+ * last group may hold fewer, nr, rows); within a group, its 64-column blocks
+ * one after the other, each holding the group's nr rows in order. Row n's
+ * codes for block b therefore start at byte
+ *   g*K/64*bb + (b*nr + r)*bb      (g = n - n%64, r = n%64, bb = 32 or 64)
+ * and its block value sits at index g*K/64 + b*nr + r; the sizes are those of
+ * the row-major arrays. (The GEMMs then read a whole tile of a row group as
+ * one contiguous run.) qlora_quantize writes this order, every call reads it. */
 typedef enum { QLORA_FMT_NF4 = 0, QLORA_FMT_INT8 = 1, QLORA_FMT_FP8 = 2 } qlora_format;
 
 typedef enum {

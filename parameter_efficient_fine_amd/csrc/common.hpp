@@ -136,6 +136,29 @@ __device__ __forceinline__ u32x4 dequant8(uint32_t x, const Nf4Lut& t) {
 }
 
 // ---------------------------------------------------------------------------
+// Storage order of a quantized weight [N, K]: rows in groups of 64 (the last
+// group may be shorter, nr rows); inside a group, the 64-column blocks one
+// after the other, each block holding the group's nr rows in order. So the
+// codes of one (64-row group, 64-column block) tile are contiguous (nr rows x
+// 32 bytes for NF4, x 64 bytes for 8-bit) and so are its nr block values.
+// A GEMM wave that needs one block of 32 or 64 consecutive rows then reads
+// one contiguous run instead of one short piece per row.
+struct TileAddr {
+  int64_t group_row0, nr, b, r, K;
+  __host__ __device__ TileAddr(int64_t n, int64_t blk, int64_t N, int64_t K_) {
+    group_row0 = n - n % 64;
+    nr = (N - group_row0) < 64 ? (N - group_row0) : 64;
+    b = blk;
+    r = n - group_row0;
+    K = K_;
+  }
+  // byte offset of this row's codes in block b; bb = code bytes per row and block
+  __host__ __device__ int64_t code(int64_t bb) const { return group_row0 * (K / 64) * bb + (b * nr + r) * bb; }
+  // index of this row's value (absmax or scale) for block b
+  __host__ __device__ int64_t value() const { return group_row0 * (K / 64) + b * nr + r; }
+};
+
+// ---------------------------------------------------------------------------
 // Weight formats. Every format stores one fp32 per 64-element block of a
 // weight row ("absmax" array): NF4 its absmax (levels span [-1, 1]), INT8 and
 // FP8 their scale s (absmax / 127, absmax / 448). The dequantized weight is

@@ -128,20 +128,26 @@ void k_qgemm_bwd(BwdArgs p) {
                                                last ? offYl[i] : offY[i], sl * kRowB, 0, 0);
   };
 
-  // ---- codes and absmax of weight row n0 + lane, block kc/64 (32 bytes + 4).
-  // Per-lane offsets are loop-invariant; each step gets buffer resources based
-  // at its first weight row and sized to the rows that exist, so rows past N
-  // read zero (zero codes and absmax give an all-zero table) with no per-step
-  // VGPR arithmetic next to loads in flight.
+  // ---- codes and block value of weight row n0 + lane, block kc/64. They are
+  // stored tile-major (TileAddr): a step's 64 rows are one row group whose
+  // block kc/64 holds their codes row after row, so the wave reads one
+  // contiguous tile and lane l its l-th run. Per-lane offsets are
+  // loop-invariant; each step gets buffer resources based at its tile and
+  // sized to the rows that exist, so rows past N read zero (zero codes and
+  // value give an all-zero table) with no per-step VGPR arithmetic next to
+  // loads in flight.
   constexpr int kHB = kCodeHalfBytes<F>;  // 2 x bytes per code
-  const int offC = k_ok ? (int)((int64_t)lane * (K * kHB / 2) + kc * kHB / 2) : kOff;
-  const int offA = k_ok ? (int)(((int64_t)lane * (K / kBlock) + kc / kBlock) * 4) : kOff;
+  constexpr int64_t kBB = kBlock * kHB / 2;  // code bytes per row and block
+  const int offC = k_ok ? (int)(lane * kBB) : kOff;
+  const int offA = k_ok ? lane * 4 : kOff;
   auto load_codes = [&](int step, u32x4 (&cr)[kNV], float& am) {
     const int src = NSRC > 1 && step >= sps ? 1 : 0;
     const int64_t n0 = (int64_t)(step - src * sps) * kStep;
     const WSrc& w = p.w[src ? NSRC - 1 : 0];
-    const __amdgpu_buffer_rsrc_t rc = make_rsrc(w.codes + n0 * (K * kHB / 2), (N - n0) * (K * kHB / 2));
-    const __amdgpu_buffer_rsrc_t ra = make_rsrc(w.absmax + n0 * (K / kBlock), (N - n0) * (K / kBlock) * 4);
+    const int64_t nr = (N - n0) < kStep ? (N - n0) : kStep;  // rows of this group
+    const int64_t jb = kc / kBlock;
+    const __amdgpu_buffer_rsrc_t rc = make_rsrc(w.codes + n0 * (K / kBlock) * kBB + jb * nr * kBB, nr * kBB);
+    const __amdgpu_buffer_rsrc_t ra = make_rsrc(w.absmax + n0 * (K / kBlock) + jb * nr, nr * 4);
 #pragma unroll
     for (int v = 0; v < kNV; ++v)
       cr[v] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rc, offC, 16 * v, 0));

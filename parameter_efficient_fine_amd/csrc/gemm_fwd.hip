@@ -93,17 +93,24 @@ void k_qgemm_fwd(FwdArgs p) {
 
   // ---- buffer resources; per-lane offsets are fixed, the step advances a scalar offset
   const __amdgpu_buffer_rsrc_t rX = make_rsrc(p.X + j0 * K, rows_here * K * 2);
+  // Codes and block values are stored tile-major (TileAddr): both fragments of
+  // a wave lie in one 64-row group, whose block b holds its nr rows in order,
+  // so a step's codes of the wave's rows are one contiguous run.
+  constexpr int64_t kBB = kBlock * kCodeHalfBytes<F> / 2;  // code bytes per row and block
+  const int64_t grp = nb[0] - nb[0] % 64;
+  const int64_t nrw = (N - grp) < 64 ? ((N - grp) > 0 ? (N - grp) : 64) : 64;  // rows of the group
   __amdgpu_buffer_rsrc_t rC[2], rA[2];
   int offC[2], offA[2];
 #pragma unroll
   for (int f = 0; f < 2; ++f) {
     const bool second = GATEUP && f == 1;
-    rC[f] = make_rsrc(second ? p.w1.codes : p.w0.codes, N * (K * kCodeHalfBytes<F> / 2));
+    rC[f] = make_rsrc(second ? p.w1.codes : p.w0.codes, N * (K / kBlock) * kBB);
     rA[f] = make_rsrc(second ? p.w1.absmax : p.w0.absmax, N * (K / kBlock) * 4);
     const int64_t n = nb[f] + jl;
-    offC[f] = n < N ? (int)(n * (K * kCodeHalfBytes<F> / 2) + kCodeStepB * h) : kOff;
-    offA[f] = n < N ? (int)(n * (K / kBlock) * 4) : kOff;
+    offC[f] = n < N ? (int)(grp * (K / kBlock) * kBB + (n - grp) * kBB + kCodeStepB * h) : kOff;
+    offA[f] = n < N ? (int)((grp * (K / kBlock) + (n - grp)) * 4) : kOff;
   }
+  const int codes_per_step = (int)(nrw * kBB), values_per_step = (int)(nrw * 4);  // scalar strides
   // activation copy: wave w, instruction i fills tile rows 64w+8i .. +7; lane l writes
   // physical chunk l%8 of row 64w+8i+l/8, which holds logical chunk (l%8) ^ ((row>>1)&7)
   int offX[8];
@@ -126,11 +133,11 @@ void k_qgemm_fwd(FwdArgs p) {
     for (int f = 0; f < 2; ++f)
 #pragma unroll
       for (int v = 0; v < kNV; ++v)
-        cr[f][v] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
-                                                 rC[f], offC[f] + 16 * v, step * (kStep * kCodeHalfBytes<F> / 2), 0));
+        cr[f][v] = __builtin_bit_cast(
+            u32x4, __builtin_amdgcn_raw_buffer_load_b128(rC[f], offC[f] + 16 * v, step * codes_per_step, 0));
 #pragma unroll
     for (int f = 0; f < 2; ++f)
-      am[f] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rA[f], offA[f], step * 4, 0));
+      am[f] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rA[f], offA[f], step * values_per_step, 0));
   };
 
   f32x16 acc[2][8];

@@ -7,6 +7,7 @@
 // code = number of NF4 thresholds strictly below x (a tie goes to the lower
 // level); a block of zeros stores absmax 0 and code 7. Two codes per byte,
 // even column in the low nibble. Dequantization is fp32(L[code] * absmax).
+// Storage order (all formats): tile-major, see TileAddr in common.hpp.
 #include "common.hpp"
 #include "internal.hpp"
 
@@ -14,12 +15,13 @@ namespace qlora {
 
 // One wave per (row, block); lane e handles column 64*b + e.
 __global__ __launch_bounds__(256) void k_quantize(const float* __restrict__ W, int64_t nblocks, int64_t kb_per_row,
-                                                  int64_t K, uint8_t* __restrict__ codes, float* __restrict__ absmax,
-                                                  uint32_t* __restrict__ nonfinite) {
+                                                  int64_t N, int64_t K, uint8_t* __restrict__ codes,
+                                                  float* __restrict__ absmax, uint32_t* __restrict__ nonfinite) {
   const int lane = threadIdx.x & 63;
   const int64_t blk = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
   if (blk >= nblocks) return;
   const int64_t n = blk / kb_per_row, b = blk - n * kb_per_row;
+  const TileAddr ta(n, b, N, K);
   const float w = W[n * K + b * kBlock + lane];
   const bool bad = !__builtin_isfinite(w);
   float a = __builtin_fabsf(w);
@@ -33,10 +35,10 @@ __global__ __launch_bounds__(256) void k_quantize(const float* __restrict__ W, i
     for (int j = 0; j < 15; ++j) code += (x > nf4_threshold(j)) ? 1 : 0;
   }
   const int partner = __shfl_xor(code, 1);
-  if ((lane & 1) == 0) codes[n * (K / 2) + b * (kBlock / 2) + (lane >> 1)] = (uint8_t)(code | (partner << 4));
+  if ((lane & 1) == 0) codes[ta.code(kBlock / 2) + (lane >> 1)] = (uint8_t)(code | (partner << 4));
   const unsigned long long anybad = __ballot(bad);
   if (lane == 0) {
-    absmax[n * kb_per_row + b] = anybad ? __builtin_nanf("") : a;
+    absmax[ta.value()] = anybad ? __builtin_nanf("") : a;
     if (anybad && nonfinite) atomicAdd(nonfinite, 1u);
   }
 }
@@ -45,15 +47,16 @@ __global__ __launch_bounds__(256) void k_zero_u32(uint32_t* p) {
   if (threadIdx.x == 0) *p = 0;
 }
 
-// One thread per code byte -> two fp32 outputs.
+// One thread per code byte -> two fp32 outputs (row-major W_hat).
 __global__ __launch_bounds__(256) void k_dequantize(const uint8_t* __restrict__ codes, const float* __restrict__ absmax,
-                                                    int64_t nbytes, int64_t K, float* __restrict__ W_hat) {
+                                                    int64_t nbytes, int64_t N, int64_t K, float* __restrict__ W_hat) {
   const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (i >= nbytes) return;
   const int64_t half = K / 2;
   const int64_t n = i / half, c = i - n * half;
-  const float a = absmax[n * (K / kBlock) + (2 * c) / kBlock];
-  const uint8_t byte = codes[i];
+  const TileAddr ta(n, (2 * c) / kBlock, N, K);
+  const float a = absmax[ta.value()];
+  const uint8_t byte = codes[ta.code(kBlock / 2) + c % (kBlock / 2)];
   float2 out;
   out.x = nf4_level(byte & 15) * a;
   out.y = nf4_level(byte >> 4) * a;
@@ -89,12 +92,13 @@ __device__ __forceinline__ uint32_t e4m3_encode(float x) {
 // One wave per (row, block); lane e handles column 64*b + e.
 template <int F>
 __global__ __launch_bounds__(256) void k_quantize8(const float* __restrict__ W, int64_t nblocks, int64_t kb_per_row,
-                                                   int64_t K, uint8_t* __restrict__ codes, float* __restrict__ scale,
-                                                   uint32_t* __restrict__ nonfinite) {
+                                                   int64_t N, int64_t K, uint8_t* __restrict__ codes,
+                                                   float* __restrict__ scale, uint32_t* __restrict__ nonfinite) {
   const int lane = threadIdx.x & 63;
   const int64_t blk = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
   if (blk >= nblocks) return;
   const int64_t n = blk / kb_per_row, b = blk - n * kb_per_row;
+  const TileAddr ta(n, b, N, K);
   const float w = W[n * K + b * kBlock + lane];
   const bool bad = !__builtin_isfinite(w);
   float a = __builtin_fabsf(w);
@@ -111,10 +115,10 @@ __global__ __launch_bounds__(256) void k_quantize8(const float* __restrict__ W, 
       code = e4m3_encode(x);
     }
   }
-  codes[n * K + b * kBlock + lane] = (uint8_t)code;
+  codes[ta.code(kBlock) + lane] = (uint8_t)code;
   const unsigned long long anybad = __ballot(bad);
   if (lane == 0) {
-    scale[n * kb_per_row + b] = anybad ? __builtin_nanf("") : s;
+    scale[ta.value()] = anybad ? __builtin_nanf("") : s;
     if (anybad && nonfinite) atomicAdd(nonfinite, 1u);
   }
 }
@@ -122,12 +126,13 @@ __global__ __launch_bounds__(256) void k_quantize8(const float* __restrict__ W, 
 // One thread per 4 codes -> 4 fp32 outputs, decoded as the GEMMs decode them.
 template <int F>
 __global__ __launch_bounds__(256) void k_dequantize8(const uint8_t* __restrict__ codes, const float* __restrict__ scale,
-                                                     int64_t nquads, int64_t K, float* __restrict__ W_hat) {
+                                                     int64_t nquads, int64_t N, int64_t K, float* __restrict__ W_hat) {
   const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (i >= nquads) return;
   const int64_t e0 = 4 * i, n = e0 / K, k = e0 - n * K;
-  const WPrep<F> p = wprep<F>(scale[n * (K / kBlock) + k / kBlock]);
-  const uint32_t x = reinterpret_cast<const uint32_t*>(codes)[i];
+  const TileAddr ta(n, k / kBlock, N, K);
+  const WPrep<F> p = wprep<F>(scale[ta.value()]);
+  const uint32_t x = *reinterpret_cast<const uint32_t*>(codes + ta.code(kBlock) + k % kBlock);
   reinterpret_cast<f32x4*>(W_hat)[i] = wdeq4_f32<F>(x, p);
 }
 
@@ -140,11 +145,11 @@ hipError_t launch_quantize(int fmt, const float* W, int64_t N, int64_t K, uint8_
   if (nblocks == 0) return hipGetLastError();
   const unsigned grid = (unsigned)((nblocks + 3) / 4);
   if (fmt == kNF4)
-    k_quantize<<<grid, 256, 0, st>>>(W, nblocks, kb, K, codes, absmax, nonfinite_blocks);
+    k_quantize<<<grid, 256, 0, st>>>(W, nblocks, kb, N, K, codes, absmax, nonfinite_blocks);
   else if (fmt == kInt8)
-    k_quantize8<kInt8><<<grid, 256, 0, st>>>(W, nblocks, kb, K, codes, absmax, nonfinite_blocks);
+    k_quantize8<kInt8><<<grid, 256, 0, st>>>(W, nblocks, kb, N, K, codes, absmax, nonfinite_blocks);
   else
-    k_quantize8<kFp8><<<grid, 256, 0, st>>>(W, nblocks, kb, K, codes, absmax, nonfinite_blocks);
+    k_quantize8<kFp8><<<grid, 256, 0, st>>>(W, nblocks, kb, N, K, codes, absmax, nonfinite_blocks);
   return hipGetLastError();
 }
 
@@ -153,16 +158,16 @@ hipError_t launch_dequantize(int fmt, const uint8_t* codes, const float* absmax,
   if (fmt == kNF4) {
     const int64_t nbytes = N * K / 2;
     if (nbytes == 0) return hipSuccess;
-    k_dequantize<<<(unsigned)((nbytes + 255) / 256), 256, 0, st>>>(codes, absmax, nbytes, K, W_hat);
+    k_dequantize<<<(unsigned)((nbytes + 255) / 256), 256, 0, st>>>(codes, absmax, nbytes, N, K, W_hat);
     return hipGetLastError();
   }
   const int64_t nquads = N * K / 4;
   if (nquads == 0) return hipSuccess;
   const unsigned grid = (unsigned)((nquads + 255) / 256);
   if (fmt == kInt8)
-    k_dequantize8<kInt8><<<grid, 256, 0, st>>>(codes, absmax, nquads, K, W_hat);
+    k_dequantize8<kInt8><<<grid, 256, 0, st>>>(codes, absmax, nquads, N, K, W_hat);
   else
-    k_dequantize8<kFp8><<<grid, 256, 0, st>>>(codes, absmax, nquads, K, W_hat);
+    k_dequantize8<kFp8><<<grid, 256, 0, st>>>(codes, absmax, nquads, N, K, W_hat);
   return hipGetLastError();
 }
 

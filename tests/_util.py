@@ -38,6 +38,17 @@ def host(t) -> np.ndarray:
     return t.numpy()
 
 
+def tile_major(a, bb: int) -> np.ndarray:
+    """Row-major per-row data [N, nblocks*bb] (codes with bb bytes per row and 64-column
+    block, or block values with bb = 1) -> the library's storage order: rows in groups
+    of 64; inside a group, block after block, each with the group's rows in order."""
+    a = np.asarray(a)
+    N, Wd = a.shape
+    nb = Wd // bb
+    parts = [a[g:g + 64].reshape(-1, nb, bb).transpose(1, 0, 2).reshape(-1) for g in range(0, N, 64)]
+    return np.concatenate(parts).reshape(N, Wd) if parts else a.copy()
+
+
 class Prepared:
     """One projection on both sides: oracle (fp64) and device tensors, with the
     frozen weight in format fmt (0 NF4, 1 INT8, 2 FP8)."""
@@ -58,8 +69,8 @@ class Prepared:
             codes, absmax = q.quantize(dev_f32(W), fmt)
         else:
             import torch
-            codes = torch.from_numpy(self.codes_ref).cuda()
-            absmax = torch.from_numpy(self.absmax_ref).cuda()
+            codes = torch.from_numpy(tile_major(self.codes_ref, 32 if fmt == 0 else 64)).cuda()
+            absmax = torch.from_numpy(tile_major(self.absmax_ref, 1)).cuda()
         self.dev = q.QLoraLayer(codes, absmax, dev_bf16(layer["A"]), dev_bf16(layer["B"]), s, fmt)
 
     def triple(self):

@@ -241,3 +241,18 @@ def test_chunked_ce_argument_checks():
     assert lib.qlora_chunked_ce(*args(100, 128, 1024, 64, None, 0)) == C.QLORA_EWORKSPACE
     assert lib.qlora_chunked_ce(*args(100, 128, 1024, 64, p, need - 1)) == C.QLORA_EWORKSPACE
     assert lib.qlora_lmhead_prepare(p, 1024, 128, ctypes.c_void_p(0x10002), None) == C.QLORA_EINVAL
+
+
+def test_tile_major_storage_order():
+    from tests._util import tile_major
+    # N = 66 rows (groups of 64 and 2), K = 128 (two blocks), one value per row and block
+    N, nb = 66, 2
+    a = np.arange(N * nb).reshape(N, nb)          # a[n, b] = 2n + b
+    t = tile_major(a, 1).reshape(-1)
+    # row 3, block 1: group 0 (64 rows) -> 1*64 + 3; row 65, block 1: group 64 (2 rows) -> 128 + 1*2 + 1
+    assert t[67] == 2 * 3 + 1 and t[131] == 2 * 65 + 1 and t[0] == 0 and t[64] == 1
+    assert sorted(t.tolist()) == list(range(N * nb))  # a permutation
+    # codes: bb bytes per row and block move together
+    c = np.arange(N * nb * 4).reshape(N, nb * 4)
+    tc = tile_major(c, 4).reshape(-1)
+    assert list(tc[4 * 67: 4 * 68]) == list(c[3, 4:8])

@@ -7,7 +7,7 @@ import pytest
 
 from oracle import formats8 as f8
 from synthetic import make_workload, random_linear, random_mlp
-from tests._util import TOL, dev_f32, host, sample_rows
+from tests._util import TOL, dev_f32, host, sample_rows, tile_major
 from tests.test_gpu_parity import _linear_case, _mlp_case
 
 pytestmark = pytest.mark.gpu
@@ -23,8 +23,9 @@ def _check_quant(W, fmt):
     import parameter_efficient_fine_amd as q
     codes, scale = q.quantize(dev_f32(W), fmt)
     c_ref, s_ref = f8.quantize(W, fmt)
-    assert np.array_equal(host(codes), c_ref)
-    assert np.array_equal(host(scale).astype(np.float32).view(np.uint32), s_ref.view(np.uint32))
+    # stored tile-major (a permutation of the row-major bytes)
+    assert np.array_equal(host(codes), tile_major(c_ref, 64))
+    assert np.array_equal(host(scale).astype(np.float32).view(np.uint32), tile_major(s_ref, 1).view(np.uint32))
     Wh = q.dequantize(codes, scale, fmt)
     assert np.array_equal(Wh.cpu().numpy().view(np.uint32), f8.dequantize(c_ref, s_ref, fmt).view(np.uint32))
 

@@ -282,11 +282,17 @@ void k_qgemm_fwd(FwdArgs p) {
   luts(as0, L0);
   read_b(0, 0, bv[0]);
   dequant_a(cs0, 0, L0, av[0]);
-  for (int s = 0; s < nsteps; s += 3) {
+  // Whole triples in the loop (the code sets rotate with period 3) and the
+  // last one or two steps after it: no conditional body inside the loop, so
+  // the waits the compiler derives at the loop head are the steady-state ones.
+  int s = 0;
+  for (; s + 2 < nsteps; s += 3) {
     body(s, cs0, L0, cs1, as1, L1, cs2, as2);
-    if (s + 1 < nsteps) body(s + 1, cs1, L1, cs2, as2, L2, cs0, as0);
-    if (s + 2 < nsteps) body(s + 2, cs2, L2, cs0, as0, L0, cs1, as1);
+    body(s + 1, cs1, L1, cs2, as2, L2, cs0, as0);
+    body(s + 2, cs2, L2, cs0, as0, L0, cs1, as1);
   }
+  if (s < nsteps) body(s, cs0, L0, cs1, as1, L1, cs2, as2);
+  if (s + 1 < nsteps) body(s + 1, cs1, L1, cs2, as2, L2, cs0, as0);
 
   // ---- epilogue (no control flow): SwiGLU gate for gate/up, bf16 stores
   const __amdgpu_buffer_rsrc_t rO0 = make_rsrc(p.out0 + j0 * N, rows_here * N * 2);

@@ -208,13 +208,17 @@ int qlora_rope_backward(uint16_t* dq, uint16_t* dk, const int32_t* pos, int64_t 
  * Per chunk of `chunk` tokens the logits are formed in fp32 in the workspace,
  * reduced row by row, turned into dz (bf16) and multiplied back; the
  * workspace holds one chunk (qlora_ce_workspace_size), so memory follows the
- * chunk, not M. W is frozen: no weight gradient. Wt = W^T [H,V], made once by
- * qlora_lmhead_prepare, serves the dh product. loss (1 float), loss_rows [M]
- * (0 on ignored rows) and dh [M,H] are device outputs. H % 64 == 0,
- * V % 64 == 0, H, V <= 2^21, H*V <= 2^30. */
-int qlora_lmhead_prepare(const uint16_t* W, int64_t V, int64_t H, uint16_t* Wt, void* stream);
+ * chunk, not M. W is frozen: no weight gradient. qlora_lmhead_prepare lays
+ * W out once for the two products: Wp (for z = h . W^T) and Wtp (for dh =
+ * dz . W), each V*H bf16 values in 64 x 64 blocks ordered as the GEMM's lanes
+ * read them (block (g, t) of the product's weight [N, K] -- W itself or W^T --
+ * at (g*K/64 + t)*4096 values; in it, the values k = 64t + 32hh + 8ks .. +7 of
+ * row n = 64g + 32f + j at ((4f + ks)*64 + j + 32hh)*8 values). loss (1
+ * float), loss_rows [M] (0 on ignored rows) and dh [M,H] are device outputs.
+ * H % 64 == 0, V % 64 == 0, H, V <= 2^21, H*V <= 2^30. */
+int qlora_lmhead_prepare(const uint16_t* W, int64_t V, int64_t H, uint16_t* Wp, uint16_t* Wtp, void* stream);
 size_t qlora_ce_workspace_size(int64_t M, int64_t V, int64_t chunk);
-int qlora_chunked_ce(const uint16_t* h, const uint16_t* W, const uint16_t* Wt, const int32_t* targets, int64_t M,
+int qlora_chunked_ce(const uint16_t* h, const uint16_t* Wp, const uint16_t* Wtp, const int32_t* targets, int64_t M,
                      int64_t H, int64_t V, int64_t chunk, float* loss, float* loss_rows, uint16_t* dh, void* ws,
                      size_t ws_bytes, void* stream);
 

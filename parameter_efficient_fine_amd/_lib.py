@@ -87,7 +87,7 @@ def lib():
     L.qlora_rmsnorm_backward.argtypes = [vp, vp, vp, vp, i64, i64, vp, vp]
     L.qlora_rope_forward.argtypes = [vp, vp, vp, i64, ci, ci, ci, cf, vp]
     L.qlora_rope_backward.argtypes = [vp, vp, vp, i64, ci, ci, ci, cf, vp]
-    L.qlora_lmhead_prepare.argtypes = [vp, i64, i64, vp, vp]
+    L.qlora_lmhead_prepare.argtypes = [vp, i64, i64, vp, vp, vp]
     L.qlora_ce_workspace_size.argtypes = [i64, i64, i64]
     L.qlora_ce_workspace_size.restype = sz
     L.qlora_chunked_ce.argtypes = [vp, vp, vp, vp, i64, i64, i64, i64, vp, vp, vp, vp, sz, vp]

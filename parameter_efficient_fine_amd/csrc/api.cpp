@@ -632,11 +632,13 @@ int qlora_rope_backward(uint16_t* dq, uint16_t* dk, const int32_t* pos, int64_t 
   return rope_call(dq, dk, pos, M, hq, hk, d, base, true, stream);
 }
 
-int qlora_lmhead_prepare(const uint16_t* W, int64_t V, int64_t H, uint16_t* Wt, void* stream) {
-  if (V <= 0 || H <= 0 || V > kMaxDim || H > kMaxDim) return QLORA_EINVAL;
-  if (!W || !Wt || !aligned16(W) || !aligned16(Wt)) return QLORA_EINVAL;
+int qlora_lmhead_prepare(const uint16_t* W, int64_t V, int64_t H, uint16_t* Wp, uint16_t* Wtp, void* stream) {
+  if (V <= 0 || H <= 0 || V % 64 != 0 || H % 64 != 0 || V > kMaxDim || H > kMaxDim || H * V > kMaxWeight / 2)
+    return QLORA_EINVAL;
+  if (!W || !Wp || !Wtp || !aligned16(W) || !aligned16(Wp) || !aligned16(Wtp)) return QLORA_EINVAL;
   hipStream_t st = (hipStream_t)stream;
-  QL_LAUNCH("transpose", st, launch_transpose_bf16(W, V, H, Wt, st));
+  QL_LAUNCH("tile", st, launch_tile_nt(W, V, H, false, Wp, st));   // logits: rows v, reduction over h
+  QL_LAUNCH("tile", st, launch_tile_nt(W, V, H, true, Wtp, st));   // dh: rows h, reduction over v
   return QLORA_OK;
 }
 
@@ -655,13 +657,13 @@ size_t qlora_ce_workspace_size(int64_t M, int64_t V, int64_t chunk) {
   return ce_ws(M, V, chunk);
 }
 
-int qlora_chunked_ce(const uint16_t* h, const uint16_t* W, const uint16_t* Wt, const int32_t* targets, int64_t M,
+int qlora_chunked_ce(const uint16_t* h, const uint16_t* Wp, const uint16_t* Wtp, const int32_t* targets, int64_t M,
                      int64_t H, int64_t V, int64_t chunk, float* loss, float* loss_rows, uint16_t* dh, void* ws,
                      size_t ws_bytes, void* stream) {
   if (!ce_shapes_ok(M, H, V, chunk)) return QLORA_EINVAL;
   if (!loss) return QLORA_EINVAL;
-  if (M > 0 && (!h || !W || !Wt || !targets || !loss_rows || !dh || !aligned16(h) || !aligned16(W) ||
-                !aligned16(Wt) || !aligned16(dh)))
+  if (M > 0 && (!h || !Wp || !Wtp || !targets || !loss_rows || !dh || !aligned16(h) || !aligned16(Wp) ||
+                !aligned16(Wtp) || !aligned16(dh)))
     return QLORA_EINVAL;
   if (!ws || ws_bytes < ce_ws(M, V, chunk)) return QLORA_EWORKSPACE;
   const int64_t C = std::min(chunk, M);
@@ -675,9 +677,9 @@ int qlora_chunked_ce(const uint16_t* h, const uint16_t* W, const uint16_t* Wt, c
   for (int64_t r0 = 0; r0 < M; r0 += C) {
     const int64_t Mc = std::min(C, M - r0);
     // logits of the chunk (fp32), their row statistics and gradient, then dh = dz . W
-    QL_LAUNCH("gemm_nt", st, launch_gemm_nt_bf16(h + r0 * H, W, Mc, H, V, logits, true, st));
+    QL_LAUNCH("gemm_nt", st, launch_gemm_nt_bf16(h + r0 * H, Wp, Mc, H, V, logits, true, st));
     QL_LAUNCH("ce_rows", st, launch_ce_rows(logits, targets + r0, n_keep, Mc, V, loss_rows + r0, dz, st));
-    QL_LAUNCH("gemm_nt", st, launch_gemm_nt_bf16(dz, Wt, Mc, V, H, dh + r0 * H, false, st));
+    QL_LAUNCH("gemm_nt", st, launch_gemm_nt_bf16(dz, Wtp, Mc, V, H, dh + r0 * H, false, st));
   }
   QL_LAUNCH("ce_total", st, launch_ce_total(loss_rows, M, n_keep, loss, st));
   return QLORA_OK;

@@ -7,14 +7,17 @@
 //   logits [C, V] fp32 = h_c . W^T        k_gemm_nt<true>   (W [V, H] bf16, frozen)
 //   per row: lse, loss, dz = (softmax - onehot) / n   k_ce_rows (dz bf16 [C, V])
 //   dh_c [C, H] bf16 = dz . W = dz . (W^T)^T   k_gemm_nt<false> on W^T [H, V]
-// W^T is formed once at set-up (qlora_lmhead_prepare): both products are then
-// "X . W^T" GEMMs with the reduction dimension contiguous in both operands.
+// W and W^T are laid out once at set-up (qlora_lmhead_prepare, k_tile_nt):
+// both products are then "X . W^T" GEMMs over tiled weights.
 //
 // k_gemm_nt is the forward QLoRA GEMM's skeleton with bf16 weights: one
 // workgroup = 4 waves, 256 weight rows x 256 tokens, K in steps of 64; each
 // wave owns 64 weight rows, loaded from HBM straight into MFMA A-operand
 // registers one step ahead (rows are private to a wave); the activation tile
-// goes through LDS by buffer_load ... lds into a ring of four buffers.
+// goes through LDS by buffer_load ... lds into a ring of four buffers. The
+// frozen head is stored pre-tiled (k_tile_nt, at set-up): the 64 x 64 block of
+// a row group and step is 8 KB laid out in the order the wave's lanes read
+// it, so every weight load is one contiguous 1 KB run.
 #include <type_traits>
 
 #include "common.hpp"
@@ -53,14 +56,15 @@ void k_gemm_nt(NtGemmArgs p) {
   const int64_t rows_here = (M - j0) < kTok ? (M - j0) : kTok;
 
   // weight rows of this lane: fragment f = rows i0 + 64 wave + 32 f + jl; lane
-  // half h reads k in [32h, 32h + 32) of a step, substep ks the 8 values 32h + 8ks
+  // half h reads k in [32h, 32h + 32) of a step, substep ks the 8 values 32h + 8ks.
+  // Tiled storage: block (row group g, step t) at (g K/64 + t) * 8 KB, inside it
+  // the 16-byte piece of (f, ks, lane) at ((4 f + ks) * 64 + lane) * 16.
   const __amdgpu_buffer_rsrc_t rW = make_rsrc(p.W, N * K * 2);
+  const int64_t g = i0 / 64 + wave;
   int offW[2];
 #pragma unroll
-  for (int f = 0; f < 2; ++f) {
-    const int64_t n = i0 + 64 * wave + 32 * f + jl;
-    offW[f] = n < N ? (int)((n * K + 32 * h) * 2) : kOff;
-  }
+  for (int f = 0; f < 2; ++f)
+    offW[f] = 64 * g < N ? (int)(g * (K / 64) * 8192 + (4 * f * 64 + lane) * 16) : kOff;
   const __amdgpu_buffer_rsrc_t rX = make_rsrc(p.X + j0 * K, rows_here * K * 2);
   int offX[8];
 #pragma unroll
@@ -81,8 +85,8 @@ void k_gemm_nt(NtGemmArgs p) {
     for (int ks = 0; ks < 4; ++ks)
 #pragma unroll
       for (int f = 0; f < 2; ++f)
-        wr[ks][f] = __builtin_bit_cast(u32x4,
-                                       __builtin_amdgcn_raw_buffer_load_b128(rW, offW[f] + 16 * ks, step * kRowB, 0));
+        wr[ks][f] = __builtin_bit_cast(
+            u32x4, __builtin_amdgcn_raw_buffer_load_b128(rW, offW[f] + 1024 * ks, step * 8192, 0));
   };
 
   f32x16 acc[2][8];
@@ -283,6 +287,31 @@ __global__ __launch_bounds__(256) void k_ce_total(const float* __restrict__ loss
   }
 }
 
+// The weight operand of k_gemm_nt in its tiled order: dst holds W [N, K]
+// (W = src [R, C] when !transpose, W = src^T when transpose) as blocks of
+// 64 rows x 64 columns, block (g, t) at (g K/64 + t) * 8 KB, and inside a
+// block the 8 consecutive values k = 64t + 32h + 8ks .. +7 of row
+// n = 64g + 32f + jl at ((4 f + ks) * 64 + jl + 32 h) * 16 bytes.
+// One thread per 16-byte piece. N % 64 == 0, K % 64 == 0.
+__global__ __launch_bounds__(256) void k_tile_nt(const uint16_t* __restrict__ src, int64_t R, int64_t C,
+                                                 bool transpose, uint16_t* __restrict__ dst) {
+  const int64_t N = transpose ? C : R, K = transpose ? R : C;
+  const int64_t piece = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (piece >= N * K / 8) return;
+  const int64_t blk = piece / 512, in = piece - blk * 512;
+  const int64_t g = blk / (K / 64), t = blk - g * (K / 64);
+  const int fks = (int)(in / 64), lane = (int)(in % 64);
+  const int f = fks / 4, ks = fks % 4, jl = lane % 32, h = lane / 32;
+  const int64_t n = 64 * g + 32 * f + jl, k = 64 * t + 32 * h + 8 * ks;
+  uint16_t v[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) v[e] = transpose ? src[(k + e) * C + n] : src[n * C + k + e];
+  u32x4 out;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) out[q] = (uint32_t)v[2 * q] | ((uint32_t)v[2 * q + 1] << 16);
+  reinterpret_cast<u32x4*>(dst)[piece] = out;
+}
+
 // dst [C, R] = src [R, C]^T (bf16), 64 x 64 tiles through LDS.
 __global__ __launch_bounds__(256) void k_transpose_bf16(const uint16_t* __restrict__ src, int64_t R, int64_t C,
                                                         uint16_t* __restrict__ dst) {
@@ -337,6 +366,13 @@ hipError_t launch_ce_rows(const float* logits, const int32_t* tgt, const int32_t
 
 hipError_t launch_ce_total(const float* loss_rows, int64_t M, const int32_t* n_keep, float* loss, hipStream_t st) {
   k_ce_total<<<1, 256, 0, st>>>(loss_rows, M, n_keep, loss);
+  return hipGetLastError();
+}
+
+hipError_t launch_tile_nt(const uint16_t* src, int64_t R, int64_t C, bool transpose, uint16_t* dst, hipStream_t st) {
+  const int64_t pieces = R * C / 8;
+  if (pieces == 0) return hipSuccess;
+  k_tile_nt<<<(unsigned)((pieces + 255) / 256), 256, 0, st>>>(src, R, C, transpose, dst);
   return hipGetLastError();
 }
 

@@ -261,12 +261,14 @@ def rope_backward(dq, dk, pos, d: int, base: float):
 
 
 def lmhead_prepare(W):
-    """W^T [H, V] of the frozen LM head W [V, H] (bf16), for chunked_ce's dh product."""
+    """The frozen LM head W [V, H] (bf16) laid out for chunked_ce's two products: (Wp, Wtp),
+    each V*H bf16 values (tiled; see qlora_lmhead_prepare)."""
     V, H = W.shape
     _need(W, torch.bfloat16, (V, H), "W")
-    Wt = torch.empty((H, V), dtype=torch.bfloat16, device=W.device)
-    C.check("qlora_lmhead_prepare", C.lib().qlora_lmhead_prepare(_ptr(W), V, H, _ptr(Wt), _stream()))
-    return Wt
+    Wp = torch.empty((V * H,), dtype=torch.bfloat16, device=W.device)
+    Wtp = torch.empty((V * H,), dtype=torch.bfloat16, device=W.device)
+    C.check("qlora_lmhead_prepare", C.lib().qlora_lmhead_prepare(_ptr(W), V, H, _ptr(Wp), _ptr(Wtp), _stream()))
+    return Wp, Wtp
 
 
 def ce_chunk_for_budget(V: int, budget_bytes: int) -> int:
@@ -275,14 +277,15 @@ def ce_chunk_for_budget(V: int, budget_bytes: int) -> int:
     return max(256, (budget_bytes // (6 * V)) // 256 * 256)
 
 
-def chunked_ce(h, W, Wt, targets, chunk: int, ws=None, out=None):
-    """Cross-entropy of the frozen LM head W [V,H] over h [M,H] with int32 targets [M]
-    (negative = ignored): dict(loss fp32 [1], loss_rows fp32 [M], dh bf16 [M,H])."""
+def chunked_ce(h, prepared, targets, chunk: int, ws=None, out=None):
+    """Cross-entropy of the frozen LM head (prepared = lmhead_prepare(W), W [V,H]) over h [M,H]
+    with int32 targets [M] (negative = ignored): dict(loss fp32 [1], loss_rows fp32 [M], dh bf16 [M,H])."""
     M, H = h.shape
-    V = W.shape[0]
+    Wp, Wtp = prepared
+    V = Wp.numel() // H
     _need(h, torch.bfloat16, (M, H), "h")
-    _need(W, torch.bfloat16, (V, H), "W")
-    _need(Wt, torch.bfloat16, (H, V), "Wt")
+    _need(Wp, torch.bfloat16, (V * H,), "Wp")
+    _need(Wtp, torch.bfloat16, (V * H,), "Wtp")
     _need(targets, torch.int32, (M,), "targets")
     dev = h.device
     if out is None:
@@ -292,7 +295,7 @@ def chunked_ce(h, W, Wt, targets, chunk: int, ws=None, out=None):
     nb = int(C.lib().qlora_ce_workspace_size(M, V, chunk))
     ws = _workspace(nb, dev) if ws is None else ws
     C.check("qlora_chunked_ce", C.lib().qlora_chunked_ce(
-        _ptr(h), _ptr(W), _ptr(Wt), _ptr(targets), M, H, V, chunk, _ptr(out["loss"]), _ptr(out["loss_rows"]),
+        _ptr(h), _ptr(Wp), _ptr(Wtp), _ptr(targets), M, H, V, chunk, _ptr(out["loss"]), _ptr(out["loss_rows"]),
         _ptr(out["dh"]), _ptr(ws), ws.numel(), _stream()))
     return out
 

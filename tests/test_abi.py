@@ -240,7 +240,8 @@ def test_chunked_ce_argument_checks():
     assert lib.qlora_chunked_ce(*args(100, 1 << 16, 1 << 16, 64, p, need)) == C.QLORA_EINVAL  # H*V too large
     assert lib.qlora_chunked_ce(*args(100, 128, 1024, 64, None, 0)) == C.QLORA_EWORKSPACE
     assert lib.qlora_chunked_ce(*args(100, 128, 1024, 64, p, need - 1)) == C.QLORA_EWORKSPACE
-    assert lib.qlora_lmhead_prepare(p, 1024, 128, ctypes.c_void_p(0x10002), None) == C.QLORA_EINVAL
+    assert lib.qlora_lmhead_prepare(p, 1024, 128, ctypes.c_void_p(0x10002), p, None) == C.QLORA_EINVAL
+    assert lib.qlora_lmhead_prepare(p, 1000, 128, p, p, None) == C.QLORA_EINVAL  # V % 64
 
 
 def test_tile_major_storage_order():

@@ -22,8 +22,7 @@ def _run(d, chunk):
     import parameter_efficient_fine_amd as q
     h, W = dev_bf16(d["h"]), dev_bf16(d["W"])
     t = torch.from_numpy(d["targets"]).cuda()
-    Wt = q.lmhead_prepare(W)
-    return q.chunked_ce(h, W, Wt, t, chunk)
+    return q.chunked_ce(h, q.lmhead_prepare(W), t, chunk)
 
 
 @pytest.mark.parametrize("M,H,V,chunk", [

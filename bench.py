@@ -60,6 +60,8 @@ def parse():
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--cold", action="store_true",
                     help="also time 10 cache-cold steps (512 MiB written before each, untimed)")
+    ap.add_argument("--graph", action="store_true",
+                    help="also time the step captured once in a HIP graph and replayed (reported under 'graph')")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run plain device copies of known size (reference for hardware byte counters)")
     return ap.parse_args()
@@ -509,9 +511,9 @@ def main():
         flops = parts[0].useful_flops()
     stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
 
-    def step():
+    def step(st=stream):
         for p in parts:
-            p.run(lib, stream)
+            p.run(lib, st)
 
     for _ in range(args.warmup):
         step()
@@ -544,6 +546,26 @@ def main():
             cold.append(e0.elapsed_time(e1))
         del flush
         step_stats["cold_median_ms"] = float(np.median(cold))
+
+    graph_stats = None
+    if args.graph:
+        # the whole step captured once (every launch of the library goes to the
+        # capture stream) and replayed K times back to back
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            step(ctypes.c_void_p(torch.cuda.current_stream().cuda_stream))
+        g.replay()
+        torch.cuda.synchronize()
+        gev = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
+        gev[0].record()
+        for i in range(args.steps):
+            g.replay()
+            gev[i + 1].record()
+        torch.cuda.synchronize()
+        gms = gev[0].elapsed_time(gev[-1]) / args.steps
+        graph_stats = dict(ms_per_step=gms, tokens_per_s=d["M"] / (gms * 1e-3),
+                           median_ms=float(np.median([gev[i].elapsed_time(gev[i + 1]) for i in range(args.steps)])))
+        del g
 
     # same steps again with per-launch hipEvents recorded by the library (kernel durations)
     with KernelTimer(max_launches=args.steps * 256 + 64) as kt:
@@ -604,6 +626,8 @@ def main():
         "roofline": roofline,
         "kernels": kernels,
     }
+    if graph_stats is not None:
+        out["graph"] = graph_stats
     if not args.no_cpu:
         out["cpu_baseline"] = cpu_baseline(d, args.cpu_seconds)
     else:

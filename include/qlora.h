@@ -19,9 +19,9 @@
  * 4-bit format (the pages say only "4-bit" bitsandbytes checkpoints; this is
  * the NF4 reading): per row n and 64-column block b, absmax = max |W|,
  * code = nearest of the 16 NormalFloat-4 levels to W/absmax (fp32 division;
- * ties to the lower level), two codes per byte with the even column in the
- * low nibble; dequantized weight What = fp32(L[code] * absmax). A block of
- * zeros has absmax 0 and code 7 (the exact zero level).
+ * ties to the lower level), two codes per byte (byte order below);
+ * dequantized weight What = fp32(L[code] * absmax). A block of zeros has
+ * absmax 0 and code 7 (the exact zero level).
  *
  * Conventions for every call:
  *   - Pointers are device pointers owned by the caller, row-major and
@@ -77,7 +77,11 @@ typedef enum {
  *   g*K/64*bb + (b*nr + r)*bb      (g = n - n%64, r = n%64, bb = 32 or 64)
  * and its block value sits at index g*K/64 + b*nr + r; the sizes are those of
  * the row-major arrays. (The GEMMs then read a whole tile of a row group as
- * one contiguous run.) qlora_quantize writes this order, every call reads it. */
+ * one contiguous run.) Inside a row's 32 NF4 bytes of a block, each run of 8
+ * columns 8j .. 8j+7 takes 4 bytes, byte b holding column 8j+b in its low
+ * nibble and column 8j+b+4 in its high nibble (the order the GEMMs decode
+ * fastest); the 8-bit formats keep one byte per column in column order.
+ * qlora_quantize writes this order, every call reads it. */
 typedef enum { QLORA_FMT_NF4 = 0, QLORA_FMT_INT8 = 1, QLORA_FMT_FP8 = 2 } qlora_format;
 
 typedef enum {
@@ -89,8 +93,8 @@ typedef enum {
 
 /* One LoRA-adapted quantized projection: out = in . What^T + s . (in . A^T) . B^T. */
 typedef struct {
-  const uint8_t* codes;  /* NF4: [N, K/2], two 4-bit codes per byte, even column in the low nibble;
-                            INT8, FP8: [N, K] */
+  const uint8_t* codes;  /* NF4: [N, K/2] bytes, two 4-bit codes per byte; INT8, FP8: [N, K];
+                            in the storage order described with qlora_format */
   const float* absmax;   /* [N, K/64] fp32 value of each 64-column block (see qlora_format) */
   const uint16_t* A;     /* [r, K]    bf16 LoRA down projection */
   const uint16_t* B;     /* [N, r]    bf16 LoRA up projection */

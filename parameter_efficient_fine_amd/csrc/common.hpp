@@ -6,8 +6,9 @@
 // and a LoRA adapter evaluated as one layer); "Unsloth vs The Stack v2",
 // quantized-base card (4-bit frozen base). The 4-bit format -- 16 NormalFloat
 // levels, one fp32 absmax per 64 consecutive elements of a weight row, two
-// codes per byte with the even column in the low nibble -- is the plainest
-// reading of the bitsandbytes 4-bit checkpoints the pages load.
+// codes per byte -- is the plainest reading of the bitsandbytes 4-bit
+// checkpoints the pages load. The byte order in memory is this library's own
+// (TileAddr below; inside a row, runs of 8 columns as dequant8 reads them).
 #pragma once
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -111,27 +112,38 @@ __device__ __forceinline__ Nf4Lut make_lut(float absmax) {
   return t;
 }
 
-// x holds 8 codes (nibble e of x is the code of element e). Returns the 8
-// bf16 values as 4 dwords in element order: out[q] = elem 2q | elem 2q+1 << 16.
+// (a & m) | c as one v_and_or_b32. That instruction has three operands and,
+// on this architecture, no literal slot and a single scalar-register read, so
+// the two constants are pinned to vector registers (the empty asm only names
+// the register; the compiler hoists it out of loops).
+__device__ __forceinline__ uint32_t and_or(uint32_t a, uint32_t m, uint32_t c) {
+  asm("" : "+v"(m));
+  asm("" : "+v"(c));
+  return (a & m) | c;
+}
+
+// x holds 8 codes in the device's dword order: byte b carries element b in its
+// low nibble and element b + 4 in its high nibble. Returns the 8 bf16 values
+// as 4 dwords in element order: out[q] = elem 2q | elem 2q+1 << 16.
+// The low and the high nibbles each select 4 table entries at once (two
+// 8-entry lookups on bits 0-2, one merge on bit 3), giving the low and the
+// high bytes of 4 consecutive elements; one more select per output dword
+// interleaves them.
 __device__ __forceinline__ u32x4 dequant8(uint32_t x, const Nf4Lut& t) {
   const uint32_t xs = x >> 4;
-  const uint32_t s7e = x & 0x07070707u;   // even elements, low 3 bits
-  const uint32_t s7o = xs & 0x07070707u;  // odd elements
-  const uint32_t she = ((x >> 1) & 0x04040404u) | 0x03020100u;  // byte i + 4*bit3
-  const uint32_t sho = ((x >> 5) & 0x04040404u) | 0x03020100u;
-  const uint32_t loe = perm(perm(t.lo[3], t.lo[2], s7e), perm(t.lo[1], t.lo[0], s7e), she);
-  const uint32_t hie = perm(perm(t.hi[3], t.hi[2], s7e), perm(t.hi[1], t.hi[0], s7e), she);
-  const uint32_t loo = perm(perm(t.lo[3], t.lo[2], s7o), perm(t.lo[1], t.lo[0], s7o), sho);
-  const uint32_t hio = perm(perm(t.hi[3], t.hi[2], s7o), perm(t.hi[1], t.hi[0], s7o), sho);
-  const uint32_t e01 = perm(hie, loe, 0x05010400u);  // elem0 | elem2 << 16
-  const uint32_t e23 = perm(hie, loe, 0x07030602u);  // elem4 | elem6 << 16
-  const uint32_t o01 = perm(hio, loo, 0x05010400u);  // elem1 | elem3 << 16
-  const uint32_t o23 = perm(hio, loo, 0x07030602u);  // elem5 | elem7 << 16
+  const uint32_t sa = x & 0x07070707u;   // elements 0..3, bits 0-2
+  const uint32_t sb = xs & 0x07070707u;  // elements 4..7
+  const uint32_t ha = and_or(x >> 1, 0x04040404u, 0x03020100u);   // byte i + 4*bit3
+  const uint32_t hb = and_or(xs >> 1, 0x04040404u, 0x03020100u);
+  const uint32_t loa = perm(perm(t.lo[3], t.lo[2], sa), perm(t.lo[1], t.lo[0], sa), ha);
+  const uint32_t hia = perm(perm(t.hi[3], t.hi[2], sa), perm(t.hi[1], t.hi[0], sa), ha);
+  const uint32_t lob = perm(perm(t.lo[3], t.lo[2], sb), perm(t.lo[1], t.lo[0], sb), hb);
+  const uint32_t hib = perm(perm(t.hi[3], t.hi[2], sb), perm(t.hi[1], t.hi[0], sb), hb);
   u32x4 r;
-  r[0] = perm(o01, e01, 0x05040100u);
-  r[1] = perm(o01, e01, 0x07060302u);
-  r[2] = perm(o23, e23, 0x05040100u);
-  r[3] = perm(o23, e23, 0x07060302u);
+  r[0] = perm(hia, loa, 0x05010400u);  // elem0 | elem1 << 16
+  r[1] = perm(hia, loa, 0x07030602u);  // elem2 | elem3 << 16
+  r[2] = perm(hib, lob, 0x05010400u);  // elem4 | elem5 << 16
+  r[3] = perm(hib, lob, 0x07030602u);  // elem6 | elem7 << 16
   return r;
 }
 
@@ -198,8 +210,8 @@ __device__ __forceinline__ WPrep<F> wprep(float a) {
 }
 
 // Elements 8c .. 8c+7 of a run of codes held in 16-byte registers (NF4: 8
-// codes per dword, element e in nibble e; 8-bit: 4 codes per dword, element e
-// in byte e) -> 8 bf16 in element order, out[q] = elem 2q | elem 2q+1 << 16.
+// codes per dword, byte b = element b | element b+4 << 4; 8-bit: 4 codes per
+// dword, element e in byte e) -> 8 bf16 in element order, out[q] = elem 2q | elem 2q+1 << 16.
 template <int F, int NV>
 __device__ __forceinline__ u32x4 wdeq8(const u32x4 (&cw)[NV], int c, const WPrep<F>& p) {
   if constexpr (F == kNF4) {

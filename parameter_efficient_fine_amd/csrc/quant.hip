@@ -5,9 +5,12 @@
 // in 4 bits and only the adapter trains. Format: for row n and 64-column block
 // b, absmax = max |W| over the block; x = W / absmax (IEEE fp32 division);
 // code = number of NF4 thresholds strictly below x (a tie goes to the lower
-// level); a block of zeros stores absmax 0 and code 7. Two codes per byte,
-// even column in the low nibble. Dequantization is fp32(L[code] * absmax).
-// Storage order (all formats): tile-major, see TileAddr in common.hpp.
+// level); a block of zeros stores absmax 0 and code 7. Dequantization is
+// fp32(L[code] * absmax). Two codes per byte: in each run of 8 columns
+// 8j .. 8j+7 (4 bytes), byte b holds column 8j+b in its low nibble and column
+// 8j+b+4 in its high nibble, the order the GEMMs' dequantizer reads.
+// Storage order of rows and blocks (all formats): tile-major, see TileAddr in
+// common.hpp.
 #include "common.hpp"
 #include "internal.hpp"
 
@@ -34,8 +37,8 @@ __global__ __launch_bounds__(256) void k_quantize(const float* __restrict__ W, i
 #pragma unroll
     for (int j = 0; j < 15; ++j) code += (x > nf4_threshold(j)) ? 1 : 0;
   }
-  const int partner = __shfl_xor(code, 1);
-  if ((lane & 1) == 0) codes[ta.code(kBlock / 2) + (lane >> 1)] = (uint8_t)(code | (partner << 4));
+  const int partner = __shfl_xor(code, 4);  // column + 4 inside the run of 8
+  if ((lane & 4) == 0) codes[ta.code(kBlock / 2) + 4 * (lane >> 3) + (lane & 3)] = (uint8_t)(code | (partner << 4));
   const unsigned long long anybad = __ballot(bad);
   if (lane == 0) {
     absmax[ta.value()] = anybad ? __builtin_nanf("") : a;
@@ -47,20 +50,24 @@ __global__ __launch_bounds__(256) void k_zero_u32(uint32_t* p) {
   if (threadIdx.x == 0) *p = 0;
 }
 
-// One thread per code byte -> two fp32 outputs (row-major W_hat).
+// One thread per 4 code bytes (a run of 8 columns) -> 8 fp32 outputs (row-major W_hat).
 __global__ __launch_bounds__(256) void k_dequantize(const uint8_t* __restrict__ codes, const float* __restrict__ absmax,
-                                                    int64_t nbytes, int64_t N, int64_t K, float* __restrict__ W_hat) {
+                                                    int64_t nruns, int64_t N, int64_t K, float* __restrict__ W_hat) {
   const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (i >= nbytes) return;
-  const int64_t half = K / 2;
-  const int64_t n = i / half, c = i - n * half;
-  const TileAddr ta(n, (2 * c) / kBlock, N, K);
+  if (i >= nruns) return;
+  const int64_t runs = K / 8;
+  const int64_t n = i / runs, j = i - n * runs;
+  const TileAddr ta(n, j / 8, N, K);
   const float a = absmax[ta.value()];
-  const uint8_t byte = codes[ta.code(kBlock / 2) + c % (kBlock / 2)];
-  float2 out;
-  out.x = nf4_level(byte & 15) * a;
-  out.y = nf4_level(byte >> 4) * a;
-  reinterpret_cast<float2*>(W_hat)[i] = out;
+  const uint32_t x = *reinterpret_cast<const uint32_t*>(codes + ta.code(kBlock / 2) + 4 * (j % 8));
+  f32x4 lo, hi;
+#pragma unroll
+  for (int b = 0; b < 4; ++b) {
+    lo[b] = nf4_level((x >> (8 * b)) & 15) * a;
+    hi[b] = nf4_level((x >> (8 * b + 4)) & 15) * a;
+  }
+  reinterpret_cast<f32x4*>(W_hat)[2 * i] = lo;
+  reinterpret_cast<f32x4*>(W_hat)[2 * i + 1] = hi;
 }
 
 // ---------------------------------------------------------------------------
@@ -156,9 +163,9 @@ hipError_t launch_quantize(int fmt, const float* W, int64_t N, int64_t K, uint8_
 hipError_t launch_dequantize(int fmt, const uint8_t* codes, const float* absmax, int64_t N, int64_t K, float* W_hat,
                              hipStream_t st) {
   if (fmt == kNF4) {
-    const int64_t nbytes = N * K / 2;
-    if (nbytes == 0) return hipSuccess;
-    k_dequantize<<<(unsigned)((nbytes + 255) / 256), 256, 0, st>>>(codes, absmax, nbytes, N, K, W_hat);
+    const int64_t nruns = N * K / 8;
+    if (nruns == 0) return hipSuccess;
+    k_dequantize<<<(unsigned)((nruns + 255) / 256), 256, 0, st>>>(codes, absmax, nruns, N, K, W_hat);
     return hipGetLastError();
   }
   const int64_t nquads = N * K / 4;

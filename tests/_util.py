@@ -49,6 +49,23 @@ def tile_major(a, bb: int) -> np.ndarray:
     return np.concatenate(parts).reshape(N, Wd) if parts else a.copy()
 
 
+def nf4_runs(packed) -> np.ndarray:
+    """NF4 codes packed two per byte, even column in the low nibble ([N, K/2], the
+    oracle's packing) -> the library's byte order inside a row: in each run of 8
+    columns 8j .. 8j+7, byte b holds column 8j+b (low nibble) and 8j+b+4 (high)."""
+    c = ref.unpack_codes(packed)
+    N, K = c.shape
+    r = c.reshape(N, K // 8, 2, 4)
+    return (r[:, :, 0, :] | (r[:, :, 1, :] << 4)).astype(np.uint8).reshape(N, K // 2)
+
+
+def device_codes(codes_ref, fmt: int) -> np.ndarray:
+    """The oracle's row-major codes -> the library's storage (byte order, then tile-major)."""
+    if fmt == 0:
+        return tile_major(nf4_runs(codes_ref), 32)
+    return tile_major(codes_ref, 64)
+
+
 class Prepared:
     """One projection on both sides: oracle (fp64) and device tensors, with the
     frozen weight in format fmt (0 NF4, 1 INT8, 2 FP8)."""
@@ -69,7 +86,7 @@ class Prepared:
             codes, absmax = q.quantize(dev_f32(W), fmt)
         else:
             import torch
-            codes = torch.from_numpy(tile_major(self.codes_ref, 32 if fmt == 0 else 64)).cuda()
+            codes = torch.from_numpy(device_codes(self.codes_ref, fmt)).cuda()
             absmax = torch.from_numpy(tile_major(self.absmax_ref, 1)).cuda()
         self.dev = q.QLoraLayer(codes, absmax, dev_bf16(layer["A"]), dev_bf16(layer["B"]), s, fmt)
 

@@ -257,3 +257,11 @@ def test_tile_major_storage_order():
     c = np.arange(N * nb * 4).reshape(N, nb * 4)
     tc = tile_major(c, 4).reshape(-1)
     assert list(tc[4 * 67: 4 * 68]) == list(c[3, 4:8])
+
+
+def test_nf4_run_byte_order():
+    from tests._util import nf4_runs
+    # one row, 16 columns with codes 0..15: the oracle packs bytes 0x10, 0x32, ...; the
+    # library pairs column b with column b+4 inside each run of 8 columns
+    packed = np.array([[0x10, 0x32, 0x54, 0x76, 0x98, 0xBA, 0xDC, 0xFE]], dtype=np.uint8)
+    assert list(nf4_runs(packed)[0]) == [0x40, 0x51, 0x62, 0x73, 0xC8, 0xD9, 0xEA, 0xFB]

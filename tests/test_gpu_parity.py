@@ -14,7 +14,7 @@ import pytest
 from oracle import ref
 from oracle.codebook import NF4_LEVELS, NF4_THRESHOLDS
 from synthetic import WORKLOADS, bf16_bits, make_workload, random_linear, random_mlp, projections
-from tests._util import TOL, Prepared, dev_bf16, dev_f32, host, rel_err, sample_rows, tile_major
+from tests._util import TOL, Prepared, dev_bf16, dev_f32, device_codes, host, rel_err, sample_rows, tile_major
 
 pytestmark = pytest.mark.gpu
 
@@ -35,8 +35,9 @@ def _check_quant(W):
     q = _q()
     codes, absmax = q.quantize(dev_f32(W))
     c_ref, a_ref = ref.quantize(W)
-    # the library stores codes and absmax tile-major (a permutation of the row-major bytes)
-    assert np.array_equal(host(codes), tile_major(c_ref, 32))
+    # the library stores codes and absmax tile-major, NF4 codes in runs of 8 columns
+    # (a permutation of the oracle's nibbles)
+    assert np.array_equal(host(codes), device_codes(c_ref, 0))
     assert np.array_equal(host(absmax).astype(np.float32).view(np.uint32), tile_major(a_ref, 1).view(np.uint32))
     Wh = q.dequantize(codes, absmax)
     assert np.array_equal(Wh.cpu().numpy().view(np.uint32), ref.dequantize(c_ref, a_ref).view(np.uint32))

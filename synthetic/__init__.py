@@ -45,6 +45,54 @@ def bf16_to_f32(b: np.ndarray) -> np.ndarray:
 
 
 # ---------------------------------------------------------------------------
+# counter-based draws for the largest shapes
+#
+# Element i of stream `seed` depends on (seed, i) alone, so any slice of an
+# input (a weight row, one 64-column block of every row, an activation row)
+# can be drawn on the host without drawing the rest, and the whole tensor on
+# the device with the same arithmetic (numpy int64 on the host, torch int64 on
+# the device). The integer hash is the 32-bit "lowbias32" mixer (xorshift and
+# multiply rounds, C. Wellons' hash prospector); two hashed uniforms summed give
+# a triangular value with mean 0, scaled to unit variance. Every step is an
+# exact integer operation or one fp32 rounding in a fixed order, so both sides
+# produce identical bits. Indices must stay below 2^32.
+
+_M32 = 0xFFFFFFFF
+
+
+def _mix32(x):
+    x = x ^ (x >> 16)
+    x = (x * 0x7FEB352D) & _M32
+    x = x ^ (x >> 15)
+    x = (x * 0x846CA68B) & _M32
+    return x ^ (x >> 16)
+
+
+def counter_normal(seed: int, idx, scale: float = 1.0):
+    """fp32 draws for int64 element indices idx (a numpy array or a torch tensor on
+    any device): mean 0, standard deviation `scale`, support +-sqrt(6)*scale.
+    numpy computes in uint32 (wrapping products), torch in int64 with masks."""
+    host = isinstance(idx, np.ndarray)
+    x0 = idx.astype(np.uint32) if host else idx
+    u = None
+    for j in range(2):
+        key = _mix32(4 * seed + j + 1)  # a Python int
+        if host:
+            x = x0 + np.uint32(key)
+            x ^= x >> np.uint32(16)
+            x *= np.uint32(0x7FEB352D)
+            x ^= x >> np.uint32(15)
+            x *= np.uint32(0x846CA68B)
+            x ^= x >> np.uint32(16)
+            v = (x >> np.uint32(8)).astype(np.float32) * np.float32(2.0 ** -24)
+        else:
+            x = _mix32((x0 + key) & _M32)
+            v = (x >> 8).float() * np.float32(2.0 ** -24)
+        u = v if u is None else u + v
+    return (u - np.float32(1.0)) * np.float32(2.449489742783178 * scale)
+
+
+# ---------------------------------------------------------------------------
 # workload table
 
 WORKLOADS = {

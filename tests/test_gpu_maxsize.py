@@ -1,5 +1,6 @@
 """GPU parity at the largest weight the library accepts: N*K = 2^31 4-bit
-weights with K or N at its maximum of 2^21 (the rest of the shape ragged).
+weights (2^30 in the 8-bit formats) with K or N at its maximum of 2^21 (the
+rest of the shape ragged).
 
 The weight is drawn element by element from a counter-based generator
 (synthetic.counter_normal), in full on the GPU and in slices on the host, so the
@@ -11,7 +12,7 @@ on sampled input blocks, Z, dA and dB in full.
 import numpy as np
 import pytest
 
-from oracle import ref
+from oracle import formats8, ref
 from synthetic import bf16_bits, counter_normal
 from tests._util import TOL, dev_bf16, host, nf4_runs, rel_err
 
@@ -62,37 +63,46 @@ def _weight_block_host(N, K, b):
     return out
 
 
-@pytest.mark.parametrize("K,N", [(1 << 21, 1024), (1024, 1 << 21)], ids=["maxK", "maxN"])
-def test_linear_largest_weight(K, N):
+def _oracle_quantize(W, fmt):
+    """-> (codes in the library's byte order within a row, block values, dequantized weight)."""
+    if fmt == 0:
+        c, a = ref.quantize(W)
+        return nf4_runs(c), a, ref.dequantize(c, a)
+    c, a = formats8.quantize(W, fmt)
+    return c, a, formats8.dequantize(c, a, fmt)
+
+
+@pytest.mark.parametrize("fmt,K,N", [(0, 1 << 21, 1024), (0, 1024, 1 << 21), (1, 1 << 21, 512), (2, 512, 1 << 21)],
+                         ids=["nf4-maxK", "nf4-maxN", "int8-maxK", "fp8-maxN"])
+def test_linear_largest_weight(fmt, K, N):
     import torch
     import parameter_efficient_fine_amd as q
-    assert N * K == 1 << 31
+    assert N * K == (1 << 31 if fmt == 0 else 1 << 30)
     M, r, s = 67, 16, 2.0
-    _announce(f"linear largest weight M={M} K={K} N={N} r={r}")
-    rng = np.random.default_rng(1000 + K % 997)
+    bb = 32 if fmt == 0 else 64  # code bytes per row and block
+    _announce(f"linear largest weight fmt={fmt} M={M} K={K} N={N} r={r}")
+    rng = np.random.default_rng(1000 + K % 997 + fmt)
 
     # ---- quantize on the GPU (the fp32 weight is dropped right after)
     W = _draw_weight_on_device(N, K)
-    codes, absmax = q.quantize(W)
+    codes, absmax = q.quantize(W, fmt)
     del W
     torch.cuda.empty_cache()
 
     rows = np.unique(np.concatenate([[0, 1, 63, 64, N - 65, N - 64, N - 1], rng.integers(0, N, 5)]))
-    Wr = _weight_rows_host(rows, K)
-    c_ref, a_ref = ref.quantize(Wr)
-    What_rows = ref.dequantize(c_ref, a_ref)
+    c_ref, a_ref, What_rows = _oracle_quantize(_weight_rows_host(rows, K), fmt)
     dev_codes = codes.view(-1)
     dev_abs = absmax.view(-1)
     for i, n in enumerate(rows):
-        ci = torch.from_numpy(_storage_index(int(n), N, K, 32)[:, None] + np.arange(32)[None, :]).cuda()
+        ci = torch.from_numpy(_storage_index(int(n), N, K, bb)[:, None] + np.arange(bb)[None, :]).cuda()
         ai = torch.from_numpy(_storage_index(int(n), N, K, 1)).cuda()
         got_c = dev_codes[ci.view(-1)].cpu().numpy()
-        assert np.array_equal(got_c, nf4_runs(c_ref[i:i + 1]).reshape(-1)), f"codes of row {n}"
+        assert np.array_equal(got_c, c_ref[i]), f"codes of row {n}"
         got_a = dev_abs[ai].cpu().numpy()
-        assert np.array_equal(got_a.view(np.uint32), a_ref[i].view(np.uint32)), f"absmax of row {n}"
+        assert np.array_equal(got_a.view(np.uint32), a_ref[i].view(np.uint32)), f"block values of row {n}"
 
     # ---- dequantize in full, compare the sampled rows bit for bit
-    Wh = q.dequantize(codes, absmax)
+    Wh = q.dequantize(codes, absmax, fmt)
     got = Wh[torch.from_numpy(rows).cuda()].cpu().numpy()
     assert np.array_equal(got.view(np.uint32), What_rows.view(np.uint32))
     del Wh
@@ -103,7 +113,7 @@ def test_linear_largest_weight(K, N):
     dY16 = bf16_bits(rng.standard_normal((M, N), dtype=np.float32))
     A16 = bf16_bits(rng.standard_normal((r, K), dtype=np.float32) / np.float32(np.sqrt(K)))
     B16 = bf16_bits(0.5 * rng.standard_normal((N, r), dtype=np.float32))
-    L = q.QLoraLayer(codes, absmax, dev_bf16(A16), dev_bf16(B16), s)
+    L = q.QLoraLayer(codes, absmax, dev_bf16(A16), dev_bf16(B16), s, fmt)
     Xd, dYd = dev_bf16(X16), dev_bf16(dY16)
     Y, Z = q.forward(L, Xd)
     Ys = Y[:, torch.from_numpy(rows).cuda()]
@@ -118,8 +128,7 @@ def test_linear_largest_weight(K, N):
     # dX on input blocks (the first and the last, or the last alone when every weight
     # row is drawn for it): needs that block of every weight row
     for b in ((0, K // 64 - 1) if N <= 4096 else (K // 64 - 1,)):
-        c_blk, a_blk = ref.quantize(_weight_block_host(N, K, b))
-        Wh_blk = ref.dequantize(c_blk, a_blk)
+        Wh_blk = _oracle_quantize(_weight_block_host(N, K, b), fmt)[2]
         cols = slice(64 * b, 64 * b + 64)
         dXr, _, _ = ref.linear_bwd(dY, X[:, cols], Wh_blk, A[:, cols], B, s)  # dX columns of this block
         errs[f"dX[block {b}]"] = rel_err(host(dX[:, cols]), dXr)

@@ -80,10 +80,14 @@ struct BwdArgs {
   const uint16_t* u;
 };
 
-// Weight tile swizzle: 16-byte chunk q of row j is stored at chunk q ^ wsw(j).
-// Keeps the row writes (8 rows per LDS cycle) and the transposed reads
-// (4 rows x 2 column groups per cycle) on distinct banks.
-__device__ __forceinline__ int wsw(int j) { return (4 * ((j >> 1) & 1)) | (2 * ((j >> 2) & 1)); }
+// Weight tile swizzle: 16-byte chunk q of row j is stored at chunk q ^ wsw(j),
+// wsw(j) = the bits of j & 7 reordered (bit 0 -> 0, bit 1 -> 2, bit 2 -> 1).
+// A 16-byte LDS write serves 8 lanes per cycle within a 128-byte bank window:
+// the 8 rows a wave writes together (one chunk each) get 8 distinct chunk
+// positions. The transposed reads take 4 consecutive rows x 4 chunks per
+// 256-byte window: rows j and j + 2 differ in bit 2 of wsw, so they fall in
+// opposite halves of the row.
+__device__ __forceinline__ int wsw(int j) { return (j & 1) | (((j >> 1) & 1) << 2) | (((j >> 2) & 1) << 1); }
 
 template <int F, int MODE, int RP, bool ALIGNED>
 __global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_per_eu(1, 1)))

@@ -33,6 +33,9 @@
 //     dequantized straight into the other tile buffer.
 // Tile edges use the buffer range check: rows past N and columns past K read
 // zero, tokens past M drop their stores.
+//
+// k_qgemm_bwd8 below is the same pipeline with 8 waves (two per SIMD), each
+// holding 64 columns x 128 tokens; the plain and two-source products use it.
 #include <type_traits>
 
 #include "common.hpp"
@@ -394,18 +397,315 @@ void k_qgemm_bwd(BwdArgs p) {
   }
 }
 
+// ---------------------------------------------------------------------------
+// Two waves per SIMD (8 waves, 512 lanes), same 256 x 256 output tile:
+// wave w owns the 64-column block w & 3 and the 128 tokens 128 (w >> 2) ..,
+// so waves w and w + 4 -- the pair on one SIMD -- share one weight tile per
+// step; each dequantizes 32 of its 64 rows (lane l: row 32 (w >> 2) + l % 32,
+// columns 32 (l / 32) ..) and both read the whole tile after the step's
+// barrier. With two waves on a SIMD, one wave's MFMAs run while the other
+// waits on its VALU chains, LDS reads or the barrier.
+template <int F, int MODE, int RP, bool ALIGNED>
+__global__ __attribute__((amdgpu_flat_work_group_size(512, 512), amdgpu_waves_per_eu(2, 2)))
+void k_qgemm_bwd8(BwdArgs p) {
+  extern __shared__ __attribute__((aligned(16))) uint8_t smem[];  // dY [2], then weight tiles [2][4 blocks]
+  constexpr int NSRC = MODE == kConcat ? 2 : 1;
+  constexpr int kNVh = kNV / 2;  // 16-byte code loads per lane and step (32 elements)
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int cb = wave & 3, th = wave >> 2;  // column block, token half
+  const int h = lane >> 5, jl = lane & 31;
+  const int64_t M = p.M, K = p.K, N = p.N;
+  const int64_t nJ = (M + kTok - 1) / kTok;
+  const int64_t it = blockIdx.x / nJ, jt = blockIdx.x - it * nJ;
+  const int64_t i0 = it * 256, j0 = jt * kTok;
+  const int sps = (int)((N + kStep - 1) / kStep);  // steps per source
+  const int nsteps = sps * NSRC;
+  const bool ragged = (N % kStep) != 0;
+  const int64_t rows_here = (M - j0) < kTok ? (M - j0) : kTok;
+  const int64_t kc = i0 + 64 * cb;  // the block's first output column
+  const bool k_ok = kc < K;
+  uint8_t* const wtile = smem + 2 * kBufB + cb * kWBufB;  // buffer b at + b * 4 * kWBufB
+
+  // ---- dY copies: wave w fills tile rows 32w .. 32w+31 (4 instructions of 8
+  // rows), physical chunk l%8 = logical chunk (l%8) ^ ((row>>1)&7).
+  int offY[4], offYl[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int row = 32 * wave + 8 * i + (lane >> 3);
+    const int c = (lane & 7) ^ ((row >> 1) & 7);
+    offY[i] = (int)((int64_t)row * N * 2 + 16 * c);
+    offYl[i] = (int64_t)(sps - 1) * kStep + 8 * c < N ? offY[i] : kOff;
+  }
+  auto dma_y = [&](int step, int buf) {
+    const int src = NSRC > 1 && step >= sps ? 1 : 0;
+    const int sl = step - src * sps;
+    const bool last = ragged && sl == sps - 1;
+    const __amdgpu_buffer_rsrc_t ry = make_rsrc(p.dY[src ? NSRC - 1 : 0] + j0 * N, rows_here * N * 2);
+    uint8_t* base = smem + buf * kBufB + (32 * wave) * kRowB;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(ry, (__attribute__((address_space(3))) void*)(base + 8 * i * kRowB), 16,
+                                               last ? offYl[i] : offY[i], sl * kRowB, 0, 0);
+  };
+
+  // ---- codes and block value of weight row n0 + 32th + l%32, half l/32 of block kc/64
+  constexpr int kHB = kCodeHalfBytes<F>;
+  constexpr int64_t kBB = kBlock * kHB / 2;
+  const int wrow = 32 * th + jl;
+  const int offC = k_ok ? (int)(wrow * kBB + 16 * kNVh * h) : kOff;
+  const int offA = k_ok ? wrow * 4 : kOff;
+  auto load_codes = [&](int step, u32x4 (&cr)[kNVh], float& am) {
+    const int src = NSRC > 1 && step >= sps ? 1 : 0;
+    const int64_t n0 = (int64_t)(step - src * sps) * kStep;
+    const WSrc& w = p.w[src ? NSRC - 1 : 0];
+    const int64_t nr = (N - n0) < kStep ? (N - n0) : kStep;
+    const int64_t jb = kc / kBlock;
+    const __amdgpu_buffer_rsrc_t rc = make_rsrc(w.codes + n0 * (K / kBlock) * kBB + jb * nr * kBB, nr * kBB);
+    const __amdgpu_buffer_rsrc_t ra = make_rsrc(w.absmax + n0 * (K / kBlock) + jb * nr, nr * 4);
+#pragma unroll
+    for (int v = 0; v < kNVh; ++v)
+      cr[v] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rc, offC, 16 * v, 0));
+    am = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(ra, offA, 0, 0));
+  };
+
+  f32x16 acc[2][4];
+#pragma unroll
+  for (int f = 0; f < 2; ++f)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[f][j] = f32x16{};
+
+  // ---- the rank-r term first: acc += (s.A^T rows) . (G rows)^T
+#pragma unroll
+  for (int src = 0; src < NSRC; ++src) {
+    const WSrc& w = p.w[src];
+    const __amdgpu_buffer_rsrc_t rA_ = make_rsrc(w.lora_i, K * (int64_t)w.r * 2);
+    const __amdgpu_buffer_rsrc_t rG = make_rsrc(w.lora_j + j0 * w.ldj, rows_here * w.ldj * 2);
+    const int c0 = 8 * h;
+#pragma unroll
+    for (int rr = 0; rr < RP; rr += 16) {
+      u32x4 ah[2], al[2];
+#pragma unroll
+      for (int f = 0; f < 2; ++f) {
+        const int64_t ir = kc + 32 * f + jl;
+        uint32_t wv[4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int e0 = rr + c0 + 2 * q, e1 = e0 + 1;
+          const int o0 = (ir < K && e0 < w.r) ? (int)(((int64_t)e0 * K + ir) * 2) : kOff;
+          const int o1 = (ir < K && e1 < w.r) ? (int)(((int64_t)e1 * K + ir) * 2) : kOff;
+          wv[q] = (uint32_t)__builtin_amdgcn_raw_buffer_load_b16(rA_, o0, 0, 0) |
+                  ((uint32_t)__builtin_amdgcn_raw_buffer_load_b16(rA_, o1, 0, 0) << 16);
+        }
+        split_scaled(u32x4{wv[0], wv[1], wv[2], wv[3]}, w.s, ah[f], al[f]);
+      }
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int64_t mr = 128 * th + 32 * j + jl;
+        const u32x4 z = rank8<ALIGNED>(rG, mr < rows_here ? mr : -1, w.ldj, w.r, rr + c0);
+#pragma unroll
+        for (int f = 0; f < 2; ++f) {
+          acc[f][j] = mfma32(ah[f], z, acc[f][j]);
+          acc[f][j] = mfma32(al[f], z, acc[f][j]);
+        }
+      }
+    }
+  }
+
+  // ---- operand reads: dY token 128th + 32j + jl, reduction rows 16ks + 8h .. +7
+  int offB[4];
+#pragma unroll
+  for (int ks = 0; ks < 4; ++ks) offB[ks] = (128 * th + jl) * kRowB + 16 * ((2 * ks + h) ^ ((jl >> 1) & 7));
+  u32x4 bv[2][4];
+  auto read_b = [&](int buf, int ks, u32x4 (&dst)[4]) {
+    const uint8_t* bx = smem + buf * kBufB + offB[ks];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) dst[j] = *reinterpret_cast<const u32x4*>(bx + 32 * j * kRowB);
+  };
+  int offW[2][2];
+  {
+    const int g = lane >> 4, s = lane & 15;
+#pragma unroll
+    for (int f = 0; f < 2; ++f)
+#pragma unroll
+      for (int hi = 0; hi < 2; ++hi) {
+        const int row = 8 * (g >> 1) + (s >> 2) + 4 * hi;
+        const int col = 32 * f + 16 * (g & 1) + 4 * (s & 3);
+        offW[f][hi] = row * kWRowB + 16 * ((col >> 3) ^ wsw(row)) + 2 * (col & 7);
+      }
+  }
+  u32x4 av[4][2];
+  auto read_a = [&](int wb, int ks) {
+    const uint8_t* wt = wtile + wb * 4 * kWBufB;
+#pragma unroll
+    for (int f = 0; f < 2; ++f) {
+      const u32x2 lo = lds_read_tr(wt + offW[f][0] + ks * 16 * kWRowB);
+      const u32x2 hi = lds_read_tr(wt + offW[f][1] + ks * 16 * kWRowB);
+      av[ks][f] = u32x4{lo[0], lo[1], hi[0], hi[1]};
+    }
+  };
+  // this lane's half row: logical chunks 4h .. 4h+3 of row wrow
+  const int wsl = wsw(wrow);
+  auto dequant_write = [&](int wb, const u32x4 (&cr)[kNVh], const WPrep<F>& lut, int q0, int q1) {
+    uint8_t* row = wtile + wb * 4 * kWBufB + wrow * kWRowB;
+#pragma unroll
+    for (int q = q0; q < q1; ++q)
+      *reinterpret_cast<u32x4*>(row + 16 * ((4 * h + q) ^ wsl)) = wdeq8<F>(cr, q, lut);
+  };
+  auto mfmas = [&](const u32x4 (&a)[2], const u32x4 (&b)[4]) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      acc[0][j] = mfma32(a[0], b[j], acc[0][j]);
+      acc[1][j] = mfma32(a[1], b[j], acc[1][j]);
+    }
+  };
+  auto interleave = [&](auto nds_read, auto nds_write, auto nvmem, auto nvalu) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      if (i < decltype(nds_read)::value) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      if (i >= 8 - decltype(nds_write)::value) __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);
+      if (i < decltype(nvmem)::value) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x002, decltype(nvalu)::value, 0);
+    }
+  };
+  using I0 = std::integral_constant<int, 0>;
+  using I1 = std::integral_constant<int, 1>;
+  using I2 = std::integral_constant<int, 2>;
+  using I4 = std::integral_constant<int, 4>;
+  using I5 = std::integral_constant<int, 5>;
+  using I6 = std::integral_constant<int, 6>;
+  using I8 = std::integral_constant<int, 8>;
+
+  // Step s, as in the 4-wave kernel: substeps 0-2 dequantize this wave's half
+  // of step s+1's tile (codes loaded during step s-1) and request step s+2's
+  // codes; substep 3 follows the barrier and reads step s+1's operands.
+  auto body = [&](int s, const u32x4 (&cc)[kNVh], float ac, u32x4 (&cn)[kNVh], float& an) {
+    const int b0 = s & 1, b1 = b0 ^ 1;
+    const int s2 = s + 2 < nsteps ? s + 2 : nsteps - 1;
+    load_codes(s2, cn, an);
+    const WPrep<F> lut = wprep<F>(ac);
+    read_b(b0, 1, bv[1]);
+    dequant_write(b1, cc, lut, 0, 2);
+    mfmas(av[0], bv[0]);
+    interleave(I4{}, I2{}, I2{}, I6{});
+    __builtin_amdgcn_sched_barrier(0);
+    read_b(b0, 2, bv[0]);
+    dequant_write(b1, cc, lut, 2, 3);
+    mfmas(av[1], bv[1]);
+    interleave(I4{}, I1{}, I0{}, I5{});
+    __builtin_amdgcn_sched_barrier(0);
+    read_b(b0, 3, bv[1]);
+    dequant_write(b1, cc, lut, 3, 4);
+    mfmas(av[2], bv[0]);
+    interleave(I4{}, I1{}, I0{}, I5{});
+    __builtin_amdgcn_sched_barrier(0);
+    __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));  // this wave's dY copies of step s+1 (and codes of s+2)
+    __builtin_amdgcn_s_waitcnt(0xC07F);          // this wave's LDS reads and tile writes
+    __builtin_amdgcn_s_barrier();
+    mfmas(av[3], bv[1]);
+    read_b(b1, 0, bv[0]);
+    read_a(b1, 0);
+    read_a(b1, 1);
+    read_a(b1, 2);
+    read_a(b1, 3);
+    interleave(I8{}, I0{}, I0{}, I0{});
+    __builtin_amdgcn_sched_barrier(0);
+    dma_y(s2, b0);  // after every transposed read of the step
+  };
+
+  // Prologue: codes of steps 0 and 1; dY of steps 0 and 1; tile buffer 0 = step 0;
+  // the operands of step 0 read.
+  u32x4 cA[kNVh], cB[kNVh];
+  float aA, aB;
+  load_codes(0, cA, aA);
+  load_codes(nsteps > 1 ? 1 : 0, cB, aB);
+  dma_y(0, 0);
+  dma_y(nsteps > 1 ? 1 : 0, 1);
+  {
+    const WPrep<F> lut0 = wprep<F>(aA);
+    dequant_write(0, cA, lut0, 0, 4);
+  }
+  __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
+  __builtin_amdgcn_s_waitcnt(0xC07F);
+  __builtin_amdgcn_s_barrier();
+  read_b(0, 0, bv[0]);
+  read_a(0, 0);
+  read_a(0, 1);
+  read_a(0, 2);
+  read_a(0, 3);
+  for (int s = 0; s < nsteps; s += 2) {
+    body(s, cB, aB, cA, aA);
+    if (s + 1 < nsteps) body(s + 1, cA, aA, cB, aB);
+  }
+
+  // ---- epilogue: tokens 128th + 32j + jl
+  const __amdgpu_buffer_rsrc_t rO0 = make_rsrc(p.out0 + j0 * K, rows_here * K * 2);
+  const __amdgpu_buffer_rsrc_t rO1 = make_rsrc(MODE == kSwiGLU ? p.out1 + j0 * K : p.out0,
+                                               MODE == kSwiGLU ? rows_here * K * 2 : 0);
+  const __amdgpu_buffer_rsrc_t rGs = make_rsrc(MODE == kSwiGLU ? p.g + j0 * K : p.out0,
+                                               MODE == kSwiGLU ? rows_here * K * 2 : 0);
+  const __amdgpu_buffer_rsrc_t rUs = make_rsrc(MODE == kSwiGLU ? p.u + j0 * K : p.out0,
+                                               MODE == kSwiGLU ? rows_here * K * 2 : 0);
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int64_t mr = 128 * th + 32 * j + jl;
+    const bool m_ok = mr < rows_here;
+#pragma unroll
+    for (int f = 0; f < 2; ++f) {
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int64_t ic = kc + 32 * f + 8 * q + 4 * h;
+        const int off = (m_ok && ic < K) ? (int)((mr * K + ic) * 2) : kOff;
+        float v[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) v[e] = acc[f][j][4 * q + e];
+        if (MODE == kSwiGLU) {
+          const u32x2 gw = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(rGs, off, 0, 0));
+          const u32x2 uw = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(rUs, off, 0, 0));
+          const float gv[4] = {bf16_lo(gw[0]), bf16_hi(gw[0]), bf16_lo(gw[1]), bf16_hi(gw[1])};
+          const float uv[4] = {bf16_lo(uw[0]), bf16_hi(uw[0]), bf16_lo(uw[1]), bf16_hi(uw[1])};
+          float dg[4], du[4];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const float sg = sigmoid_f(gv[e]);
+            dg[e] = v[e] * uv[e] * sg * (1.0f + gv[e] * (1.0f - sg));
+            du[e] = v[e] * gv[e] * sg;
+          }
+          store4(rO0, off, dg);
+          store4(rO1, off, du);
+        } else {
+          store4(rO0, off, v);
+        }
+      }
+    }
+  }
+}
+
 template <int MODE, int RP, bool ALIGNED>
 hipError_t launch_rp(const BwdArgs& a, hipStream_t st) {
   static bool attr_done = false;
+  // The 8-wave kernel for the plain and two-source products (measured 3-4%
+  // faster), except at rank 256 with two sources, whose rank term does not
+  // fit its 256 registers per lane; the 4-wave kernel for the SwiGLU epilogue
+  // (measured 5% faster there).
+  constexpr bool k8 = MODE != kSwiGLU && !(MODE == kConcat && RP >= 256);
+  const void* kfn;
+  if constexpr (k8)
+    kfn = (const void*)k_qgemm_bwd8<kFmt, MODE, RP, ALIGNED>;
+  else
+    kfn = (const void*)k_qgemm_bwd<kFmt, MODE, RP, ALIGNED>;
   if (!attr_done) {
-    hipError_t e = hipFuncSetAttribute((const void*)k_qgemm_bwd<kFmt, MODE, RP, ALIGNED>,
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)kLds);
+    hipError_t e = hipFuncSetAttribute(kfn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)kLds);
     if (e != hipSuccess) return e;
     attr_done = true;
   }
   const int64_t nI = (a.K + 255) / 256, nJ = (a.M + kTok - 1) / kTok;
   if (nI * nJ == 0) return hipSuccess;
-  k_qgemm_bwd<kFmt, MODE, RP, ALIGNED><<<(unsigned)(nI * nJ), 256, kLds, st>>>(a);
+  if constexpr (k8)
+    k_qgemm_bwd8<kFmt, MODE, RP, ALIGNED><<<(unsigned)(nI * nJ), 512, kLds, st>>>(a);
+  else
+    k_qgemm_bwd<kFmt, MODE, RP, ALIGNED><<<(unsigned)(nI * nJ), 256, kLds, st>>>(a);
   return hipGetLastError();
 }
 

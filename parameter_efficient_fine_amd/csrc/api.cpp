@@ -196,6 +196,16 @@ NtArgs nt1(const uint16_t* in, int64_t M, int64_t Kd, const uint16_t* ad, int r,
   return a;
 }
 
+// G = in . B for B stored [Kd, r] (the layer's layout): read in place when r is a
+// multiple of 16, else from its transposed copy Bt [r, Kd] (made by the prep kernel).
+bool b_in_place(int64_t r) { return r % 16 == 0; }
+NtArgs ntB(const uint16_t* in, int64_t M, int64_t Kd, const uint16_t* B, const uint16_t* Bt, int r, uint16_t* out,
+           int64_t ld) {
+  NtArgs a = nt1(in, M, Kd, b_in_place(r) ? B : Bt, r, out, ld);
+  a.ad_kr = b_in_place(r) ? 1 : 0;
+  return a;
+}
+
 // Collects independent reductions (out = s * P^T . Q) and issues them as one
 // skinny_tn launch and one tn_reduce launch per batch of kTnMaxJobs; each gets
 // its own slice of the partial buffer.
@@ -339,12 +349,14 @@ int qlora_backward(const qlora_layer* L, const uint16_t* dY, const uint16_t* X, 
     QL_LAUNCH("fill_zero_f32", st, launch_fill_zero_f32(dB, (int64_t)N * r, st));
     return QLORA_OK;
   }
-  PrepJobs pj{};
-  pj.job[0] = {L->B, Bt, N, r};  // B [N, r] -> B^T [r, N]
-  pj.n = 1;
-  QL_LAUNCH("prep", st, launch_prep(pj, st));
+  if (!b_in_place(r)) {
+    PrepJobs pj{};
+    pj.job[0] = {L->B, Bt, N, r};  // B [N, r] -> B^T [r, N]
+    pj.n = 1;
+    QL_LAUNCH("prep", st, launch_prep(pj, st));
+  }
   // G = dY.B ; dB = s.dY^T.Z (written transposed from Z^T.dY) and dA = s.G^T.X in one pair of launches ; dX
-  QL_LAUNCH("skinny_nt", st, launch_skinny_nt(nt1(dY, M, N, Bt, r, G, r), st));
+  QL_LAUNCH("skinny_nt", st, launch_skinny_nt(ntB(dY, M, N, L->B, Bt, r, G, r), st));
   TnCall tn{part, st};
   tn.one(Z_save, r, r, L->s, dY, M, N, dB, true);
   tn.one(G, r, r, L->s, X, M, K, dA, false);
@@ -428,6 +440,7 @@ int mlp_zero_grads(const qlora_layer* gate, const qlora_layer* up, const qlora_l
 int mlp_prep(const qlora_layer* gate, const qlora_layer* up, const qlora_layer* down, const MlpBwdWs& w,
              hipStream_t st) {
   const int64_t H = gate->K, I = gate->N, r = gate->r;
+  if (b_in_place(r)) return QLORA_OK;  // the G products read B in place
   PrepJobs pj{};
   pj.job[0] = {down->B, w.Btd, H, r};
   pj.job[1] = {gate->B, w.Btg, I, r};
@@ -449,7 +462,7 @@ int mlp_bwd_body(const qlora_layer* gate, const qlora_layer* up, const qlora_lay
   uint16_t* Gu = w.Ggu + r;
   TnCall tn{w.part, st, accumulate};
   // down projection: G_d = dY.B_d ; dB_d = s.dY^T.Z_d and dA_d = s.G_d^T.h ; dh -> (dg, du) in the GEMM epilogue
-  QL_LAUNCH("skinny_nt", st, launch_skinny_nt(nt1(dY, M, H, w.Btd, r, w.Gd, r), st));
+  QL_LAUNCH("skinny_nt", st, launch_skinny_nt(ntB(dY, M, H, down->B, w.Btd, r, w.Gd, r), st));
   tn.one(Zd, r, r, down->s, dY, M, H, dB[2], true);
   tn.one(w.Gd, r, r, down->s, h, M, I, dA[2], false);
   if (int rc = tn.flush()) return rc;
@@ -457,8 +470,8 @@ int mlp_bwd_body(const qlora_layer* gate, const qlora_layer* up, const qlora_lay
             launch_gemm_bwd_swiglu(dY, wsrc(down, down->A, w.Gd), M, I, H, g, u, w.dg, w.du, st));
   // gate and up: G = d(g|u).B ; dB = s.d(g|u)^T.Z ; dA_g = s_g.G_g^T.X and dA_u = s_u.G_u^T.X
   // (one pass over X when 2r fits a launch)
-  QL_LAUNCH("skinny_nt", st, launch_skinny_nt(nt1(w.dg, M, I, w.Btg, r, Gg, 2 * r), st));
-  QL_LAUNCH("skinny_nt", st, launch_skinny_nt(nt1(w.du, M, I, w.Btu, r, Gu, 2 * r), st));
+  QL_LAUNCH("skinny_nt", st, launch_skinny_nt(ntB(w.dg, M, I, gate->B, w.Btg, r, Gg, 2 * r), st));
+  QL_LAUNCH("skinny_nt", st, launch_skinny_nt(ntB(w.du, M, I, up->B, w.Btu, r, Gu, 2 * r), st));
   tn.one(Zg, r, r, gate->s, w.dg, M, I, dB[0], true);
   tn.one(Zu, r, r, up->s, w.du, M, I, dB[1], true);
   tn.two(w.Ggu, 2 * r, r, gate->s, dA[0], r, up->s, dA[1], X, M, H, false);

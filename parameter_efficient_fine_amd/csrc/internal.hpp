@@ -26,6 +26,7 @@ struct NtArgs {
   uint16_t* out1;
   uint16_t* out2;
   int64_t ld1, ld2;
+  int ad_kr;  // 1: a single adapter ad1 stored [Kd, r1] (r1 % 16 == 0, r2 == 0), e.g. B for G = dY.B
 };
 hipError_t launch_skinny_nt(const NtArgs& a, hipStream_t st);
 

@@ -27,6 +27,11 @@ namespace qlora {
 // U/2, .., 1 (binary remainder); a ragged last step (Kd % 32 != 0) is done
 // apart with masks. Per-wave partial sums are combined by a fixed-order tree
 // in LDS, one row fragment at a time. RP = r1 + r2 rounded up to 16.
+//
+// KT: the adapter is given as [Kd, R] (R = RP), the layout of B in G = dY.B,
+// so no transposed copy is made. Each wave copies the adapter rows of a step
+// (32 x R bf16, one contiguous run) into its own LDS slot with buffer_load ...
+// lds and reads the MFMA operand column-wise with ds_read_b64_tr_b16.
 
 template <int RP, int RF>
 struct NtShape {
@@ -36,11 +41,16 @@ struct NtShape {
   static constexpr int U = U0 / RF > 0 ? U0 / RF : 1;  // steps per batch
 };
 
-template <int RP, int RF>
+template <int RP, int RF, bool KT>
 __global__ __attribute__((amdgpu_flat_work_group_size(64 * NtShape<RP, RF>::NW, 64 * NtShape<RP, RF>::NW)))
 void k_skinny_nt(NtArgs p) {
-  constexpr int NF = NtShape<RP, RF>::NF, NW = NtShape<RP, RF>::NW, U = NtShape<RP, RF>::U;
+  constexpr int NF = NtShape<RP, RF>::NF, NW = NtShape<RP, RF>::NW;
+  // KT: at most 16 KB of adapter slots per wave (8 KB from rank 128 on, next to the
+  // larger reduction buffer)
+  constexpr int kUK = (RP >= 128 ? 128 : 256) / RP > 0 ? (RP >= 128 ? 128 : 256) / RP : 1;
+  constexpr int U = KT && NtShape<RP, RF>::U > kUK ? kUK : NtShape<RP, RF>::U;
   __shared__ float red[NW / 2][16][RP + 4];
+  __shared__ __attribute__((aligned(16))) uint16_t kts[KT ? NW * U * 32 * RP : 8];
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int64_t M = p.M, Kd = p.Kd;
@@ -60,6 +70,29 @@ void k_skinny_nt(NtArgs p) {
     const int jc = j < R ? j : 0;
     adp[f] = (jc < p.r1 ? p.ad1 + (int64_t)jc * Kd : p.ad2 + (int64_t)(jc - p.r1) * Kd) + kofs;
   }
+  // KT: adapter rows of step st = bytes [64 R st, 64 R (st + 1)) of ad1; lane l of
+  // copy instruction i moves bytes 16 (64 i + l) of the run. Transposed reads:
+  // in 16-lane group g, lane s points at row 8g + s/4 (+4), columns 16f + 4 (s%4)
+  // of the 32 x RP slot; lane i then holds rows 8g .. 8g+7 of column 16f + i.
+  const __amdgpu_buffer_rsrc_t rad = make_rsrc(p.ad1, KT ? Kd * RP * 2 : 0);
+  uint16_t* const kslot = kts + (KT ? wave * U * 32 * RP : 0);
+  const int ktr = ((8 * (lane >> 4) + ((lane & 15) >> 2)) * RP + 4 * (lane & 3)) * 2;
+  auto kt_copy = [&](int u, int64_t st) {
+#pragma unroll
+    for (int i = 0; i < RP / 16; ++i)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          rad, (__attribute__((address_space(3))) void*)(kslot + u * 32 * RP + i * 512), 16, (64 * i + lane) * 16,
+          (int)(st * 64 * RP), 0, 0);
+  };
+  auto kt_read = [&](int u, u32x4 (&dst)[NF]) {
+    const uint8_t* base = reinterpret_cast<const uint8_t*>(kslot + u * 32 * RP) + ktr;
+#pragma unroll
+    for (int f = 0; f < NF; ++f) {
+      const u32x2 lo = lds_read_tr(base + 32 * f);
+      const u32x2 hi = lds_read_tr(base + 32 * f + 8 * RP);
+      dst[f] = u32x4{lo[0], lo[1], hi[0], hi[1]};
+    }
+  };
 
   f32x4 acc[RF][NF];
 #pragma unroll
@@ -78,10 +111,19 @@ void k_skinny_nt(NtArgs p) {
       for (int rf = 0; rf < RF; ++rf)
         a[u][rf] =
             __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rin, voff[rf], (int)(st * 64), 0));
+      if constexpr (KT) {
+        kt_copy(u, st);
+      } else {
 #pragma unroll
-      for (int f = 0; f < NF; ++f) b[u][f] = *reinterpret_cast<const u32x4*>(adp[f] + st * 32);
+        for (int f = 0; f < NF; ++f) b[u][f] = *reinterpret_cast<const u32x4*>(adp[f] + st * 32);
+      }
     }
     __builtin_amdgcn_sched_barrier(0);  // every load of the batch goes out before the first MFMA waits
+    if constexpr (KT) {
+      __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));  // this wave's adapter copies (and activation loads)
+#pragma unroll
+      for (int u = 0; u < V; ++u) kt_read(u, b[u]);
+    }
 #pragma unroll
     for (int u = 0; u < V; ++u)
 #pragma unroll
@@ -101,11 +143,17 @@ void k_skinny_nt(NtArgs p) {
     const int64_t k = nfull * 32 + kofs;
     const bool ok = k < Kd;
     u32x4 b[NF];
+    if constexpr (KT) {  // adapter rows past Kd read zero (buffer range)
+      kt_copy(0, nfull);
+      __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
+      kt_read(0, b);
+    } else {
 #pragma unroll
-    for (int f = 0; f < NF; ++f) {
-      b[f] = *reinterpret_cast<const u32x4*>(adp[f] + (ok ? nfull * 32 : 0));
-      if (!ok) b[f] = u32x4{0, 0, 0, 0};
+      for (int f = 0; f < NF; ++f) b[f] = *reinterpret_cast<const u32x4*>(adp[f] + (ok ? nfull * 32 : 0));
     }
+#pragma unroll
+    for (int f = 0; f < NF; ++f)
+      if (!ok) b[f] = u32x4{0, 0, 0, 0};
 #pragma unroll
     for (int rf = 0; rf < RF; ++rf) {
       u32x4 a = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rin, voff[rf], (int)(nfull * 64), 0));
@@ -157,7 +205,7 @@ void k_skinny_nt(NtArgs p) {
     }
 }
 
-template <int RP>
+template <int RP, bool KT>
 hipError_t launch_nt_rf(const NtArgs& a, hipStream_t st) {
   // row fragments per workgroup: as many as still leave >= 256 workgroups
   // (at most 2 for RP = 256, whose accumulators would spill at 4)
@@ -166,22 +214,31 @@ hipError_t launch_nt_rf(const NtArgs& a, hipStream_t st) {
   while (rf < kMaxRF && (a.M + 32 * rf - 1) / (32 * rf) >= 256) rf *= 2;
   const unsigned grid = (unsigned)((a.M + 16 * rf - 1) / (16 * rf));
   if (rf == 1)
-    k_skinny_nt<RP, 1><<<grid, 64 * NtShape<RP, 1>::NW, 0, st>>>(a);
+    k_skinny_nt<RP, 1, KT><<<grid, 64 * NtShape<RP, 1>::NW, 0, st>>>(a);
   else if (rf == 2)
-    k_skinny_nt<RP, 2><<<grid, 64 * NtShape<RP, 2>::NW, 0, st>>>(a);
+    k_skinny_nt<RP, 2, KT><<<grid, 64 * NtShape<RP, 2>::NW, 0, st>>>(a);
   else if constexpr (kMaxRF >= 4)
-    k_skinny_nt<RP, 4><<<grid, 64 * NtShape<RP, 4>::NW, 0, st>>>(a);
+    k_skinny_nt<RP, 4, KT><<<grid, 64 * NtShape<RP, 4>::NW, 0, st>>>(a);
   return hipGetLastError();
 }
 
 hipError_t launch_skinny_nt(const NtArgs& a, hipStream_t st) {
   if (a.M == 0) return hipSuccess;
   const int R = a.r1 + a.r2;
-  if (R <= 16) return launch_nt_rf<16>(a, st);
-  if (R <= 32) return launch_nt_rf<32>(a, st);
-  if (R <= 64) return launch_nt_rf<64>(a, st);
-  if (R <= 128) return launch_nt_rf<128>(a, st);
-  if (R <= 256) return launch_nt_rf<256>(a, st);
+  if (a.ad_kr) {  // a single adapter stored [Kd, R]
+    if (a.r2 != 0 || R % 16 != 0) return hipErrorInvalidValue;
+    if (R == 16) return launch_nt_rf<16, true>(a, st);
+    if (R == 32) return launch_nt_rf<32, true>(a, st);
+    if (R == 64) return launch_nt_rf<64, true>(a, st);
+    if (R == 128) return launch_nt_rf<128, true>(a, st);
+    if (R == 256) return launch_nt_rf<256, true>(a, st);
+    return hipErrorInvalidValue;
+  }
+  if (R <= 16) return launch_nt_rf<16, false>(a, st);
+  if (R <= 32) return launch_nt_rf<32, false>(a, st);
+  if (R <= 64) return launch_nt_rf<64, false>(a, st);
+  if (R <= 128) return launch_nt_rf<128, false>(a, st);
+  if (R <= 256) return launch_nt_rf<256, false>(a, st);
   return hipErrorInvalidValue;
 }
 

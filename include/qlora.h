@@ -209,8 +209,10 @@ int qlora_rope_backward(uint16_t* dq, uint16_t* dk, const int32_t* pos, int64_t 
  *   z = h . W^T, lse_m = log sum_v exp z[m,v], loss_m = lse_m - z[m,t_m],
  *   loss = sum over kept rows / n (n = kept rows; 0 if none),
  *   dh = dz . W with dz = (softmax(z) - onehot(t)) / n on kept rows, 0 elsewhere.
- * Per chunk of `chunk` tokens the logits are formed in fp32 in the workspace,
- * reduced row by row, turned into dz (bf16) and multiplied back; the
+ * Per chunk of `chunk` tokens the logits are formed in fp32 in the workspace
+ * (with each row's max and sum of exp over every 256-column tile, so the row
+ * statistics take no extra pass over the logits), turned into dz (bf16) and
+ * multiplied back; the
  * workspace holds one chunk (qlora_ce_workspace_size), so memory follows the
  * chunk, not M. W is frozen: no weight gradient. qlora_lmhead_prepare lays
  * W out once for the two products: Wp (for z = h . W^T) and Wtp (for dh =

@@ -662,7 +662,7 @@ static bool ce_shapes_ok(int64_t M, int64_t H, int64_t V, int64_t chunk) {
 
 static size_t ce_ws(int64_t M, int64_t V, int64_t chunk) {
   const int64_t C = std::min(chunk, M);
-  return up256((size_t)C * V * 4) + up256((size_t)C * V * 2) + 256;
+  return up256((size_t)C * V * 4) + up256((size_t)C * V * 2) + up256((size_t)C * ((V + 255) / 256) * 8) + 256;
 }
 
 size_t qlora_ce_workspace_size(int64_t M, int64_t V, int64_t chunk) {
@@ -683,6 +683,7 @@ int qlora_chunked_ce(const uint16_t* h, const uint16_t* Wp, const uint16_t* Wtp,
   Carve c{(char*)ws, ws_bytes};
   float* logits = c.take<float>((size_t)C * V);
   uint16_t* dz = c.take<uint16_t>((size_t)C * V);
+  float* stats = c.take<float>((size_t)C * ((V + 255) / 256) * 2);
   int32_t* n_keep = c.take<int32_t>(64);
   if (!c.ok) return QLORA_EWORKSPACE;
   hipStream_t st = (hipStream_t)stream;
@@ -690,9 +691,9 @@ int qlora_chunked_ce(const uint16_t* h, const uint16_t* Wp, const uint16_t* Wtp,
   for (int64_t r0 = 0; r0 < M; r0 += C) {
     const int64_t Mc = std::min(C, M - r0);
     // logits of the chunk (fp32), their row statistics and gradient, then dh = dz . W
-    QL_LAUNCH("gemm_nt", st, launch_gemm_nt_bf16(h + r0 * H, Wp, Mc, H, V, logits, true, st));
-    QL_LAUNCH("ce_rows", st, launch_ce_rows(logits, targets + r0, n_keep, Mc, V, loss_rows + r0, dz, st));
-    QL_LAUNCH("gemm_nt", st, launch_gemm_nt_bf16(dz, Wtp, Mc, V, H, dh + r0 * H, false, st));
+    QL_LAUNCH("gemm_nt", st, launch_gemm_nt_bf16(h + r0 * H, Wp, Mc, H, V, logits, true, stats, st));
+    QL_LAUNCH("ce_rows", st, launch_ce_rows(logits, stats, targets + r0, n_keep, Mc, V, loss_rows + r0, dz, st));
+    QL_LAUNCH("gemm_nt", st, launch_gemm_nt_bf16(dz, Wtp, Mc, V, H, dh + r0 * H, false, nullptr, st));
   }
   QL_LAUNCH("ce_total", st, launch_ce_total(loss_rows, M, n_keep, loss, st));
   return QLORA_OK;

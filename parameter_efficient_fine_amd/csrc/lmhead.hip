@@ -4,7 +4,8 @@
 // slice by slice, each slice dropped, the same gradient).
 //
 // Per chunk of C tokens (api.cpp drives the chunks):
-//   logits [C, V] fp32 = h_c . W^T        k_gemm_nt<true>   (W [V, H] bf16, frozen)
+//   logits [C, V] fp32 = h_c . W^T        k_gemm_nt<true>   (W [V, H] bf16, frozen),
+//     with each row's (max, sum exp) over every 256-column tile
 //   per row: lse, loss, dz = (softmax - onehot) / n   k_ce_rows (dz bf16 [C, V])
 //   dh_c [C, H] bf16 = dz . W = dz . (W^T)^T   k_gemm_nt<false> on W^T [H, V]
 // W and W^T are laid out once at set-up (qlora_lmhead_prepare, k_tile_nt):
@@ -39,6 +40,8 @@ struct NtGemmArgs {
   const uint16_t* W;  // [N, K]
   int64_t M, K, N;
   void* Y;            // [M, N] fp32 or bf16
+  float* stats;       // fp32 output only, may be null: [M, ceil(N / 256)] pairs (max, sum exp(z - max))
+                      // of each row over each 256-column tile
 };
 
 template <bool OUT_F32>
@@ -199,13 +202,71 @@ void k_gemm_nt(NtGemmArgs p) {
       }
     }
   }
+
+  // ---- row statistics of this 256-column tile (logits only): each lane pair
+  // (l, l ^ 32) holds a token's 64 columns of the wave; the 4 waves' partials
+  // are combined in wave order through LDS (the activation ring is free now).
+  if constexpr (OUT_F32) {
+    if (p.stats == nullptr) return;
+    float* const red = reinterpret_cast<float*>(smem);  // [4 waves][256 tokens][2]
+    lds_barrier();  // every wave is past its last operand read
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      float mx = -__builtin_inff(), sm = 0.f;
+#pragma unroll
+      for (int f = 0; f < 2; ++f)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          const int64_t ic = i0 + 64 * wave + 32 * f + 8 * (v >> 2) + 4 * h + (v & 3);
+          if (ic < N) mx = fmaxf(mx, acc[f][j][v]);
+        }
+      // exp(z - max) as the hardware 2^x of (z - max) log2(e): one transcendental
+      // op per logit instead of the libm sequence (the sum is a statistic; its
+      // relative error stays at the fp32 rounding level)
+      const float ml = mx == -__builtin_inff() ? 0.f : mx * 1.44269504088896341f;
+#pragma unroll
+      for (int f = 0; f < 2; ++f)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          const int64_t ic = i0 + 64 * wave + 32 * f + 8 * (v >> 2) + 4 * h + (v & 3);
+          if (ic < N) sm += __builtin_amdgcn_exp2f(__builtin_fmaf(acc[f][j][v], 1.44269504088896341f, -ml));
+        }
+      const float mp = __shfl_xor(mx, 32), sp = __shfl_xor(sm, 32);
+      const float mm = fmaxf(mx, mp);
+      const float a = mx == -__builtin_inff() ? 0.f : sm * expf(mx - mm);
+      const float b = mp == -__builtin_inff() ? 0.f : sp * expf(mp - mm);
+      if (h == 0) {
+        red[(wave * 256 + 32 * j + jl) * 2] = mm;
+        red[(wave * 256 + 32 * j + jl) * 2 + 1] = a + b;
+      }
+    }
+    lds_barrier();
+    const int64_t row = t;  // one token row per thread
+    float mx = -__builtin_inff(), sm = 0.f;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      const float m2 = red[(w * 256 + t) * 2], s2 = red[(w * 256 + t) * 2 + 1];
+      const float mm = fmaxf(mx, m2);
+      const float a = mx == -__builtin_inff() ? 0.f : sm * expf(mx - mm);
+      const float b = m2 == -__builtin_inff() ? 0.f : s2 * expf(m2 - mm);
+      mx = mm;
+      sm = a + b;
+    }
+    const int64_t ntiles = (N + 255) / 256;
+    if (row < rows_here) {
+      p.stats[((j0 + row) * ntiles + it) * 2] = mx;
+      p.stats[((j0 + row) * ntiles + it) * 2 + 1] = sm;
+    }
+  }
 }
 
 // Row statistics and gradient of the cross-entropy, one workgroup per row of
-// the chunk: lse = max + log(sum exp(z - max)) (online, fp32), loss_m = lse -
-// z[t] for kept rows (t >= 0), dz = (exp(z - lse) - [v == t]) / n in bf16
-// (0 on ignored rows).
-__global__ __launch_bounds__(256) void k_ce_rows(const float* __restrict__ logits, const int32_t* __restrict__ tgt,
+// the chunk: lse = max + log(sum exp(z - max)) (fp32), from the logits GEMM's
+// per-tile pairs (max, sum exp) combined in tile order; loss_m = lse - z[t]
+// for kept rows (t >= 0), dz = (exp(z - lse) - [v == t]) / n in bf16 (0 on
+// ignored rows): one pass over the row's logits.
+__global__ __launch_bounds__(256) void k_ce_rows(const float* __restrict__ logits, const float* __restrict__ stats,
+                                                 int64_t ntiles, const int32_t* __restrict__ tgt,
                                                  const int32_t* __restrict__ n_keep, int64_t V,
                                                  float* __restrict__ loss_rows, uint16_t* __restrict__ dz) {
   __shared__ float red_m[256], red_s[256];
@@ -215,15 +276,13 @@ __global__ __launch_bounds__(256) void k_ce_rows(const float* __restrict__ logit
   const int t = tgt[m];
   const int64_t nq = V / 4;
   float mx = -__builtin_inff(), sm = 0.f;
-  for (int64_t q = tid; q < nq; q += 256) {
-    const f32x4 v = reinterpret_cast<const f32x4*>(z)[q];
-    const float vm = fmaxf(fmaxf(v[0], v[1]), fmaxf(v[2], v[3]));
-    if (vm > mx) {
-      sm *= expf(mx - vm);
-      mx = vm;
-    }
-#pragma unroll
-    for (int e = 0; e < 4; ++e) sm += expf(v[e] - mx);
+  for (int64_t q = tid; q < ntiles; q += 256) {
+    const float m2 = stats[(m * ntiles + q) * 2], s2 = stats[(m * ntiles + q) * 2 + 1];
+    const float mm = fmaxf(mx, m2);
+    const float a = mx == -__builtin_inff() ? 0.f : sm * expf(mx - mm);
+    const float b = m2 == -__builtin_inff() ? 0.f : s2 * expf(m2 - mm);
+    mx = mm;
+    sm = a + b;
   }
   red_m[tid] = mx;
   red_s[tid] = sm;
@@ -347,8 +406,8 @@ hipError_t launch_nt(const NtGemmArgs& a, hipStream_t st) {
 }  // namespace
 
 hipError_t launch_gemm_nt_bf16(const uint16_t* X, const uint16_t* W, int64_t M, int64_t K, int64_t N, void* Y,
-                               bool out_f32, hipStream_t st) {
-  NtGemmArgs a{X, W, M, K, N, Y};
+                               bool out_f32, float* stats, hipStream_t st) {
+  NtGemmArgs a{X, W, M, K, N, Y, out_f32 ? stats : nullptr};
   return out_f32 ? launch_nt<true>(a, st) : launch_nt<false>(a, st);
 }
 
@@ -357,10 +416,10 @@ hipError_t launch_ce_count(const int32_t* tgt, int64_t M, int64_t V, int32_t* n_
   return hipGetLastError();
 }
 
-hipError_t launch_ce_rows(const float* logits, const int32_t* tgt, const int32_t* n_keep, int64_t C, int64_t V,
-                          float* loss_rows, uint16_t* dz, hipStream_t st) {
+hipError_t launch_ce_rows(const float* logits, const float* stats, const int32_t* tgt, const int32_t* n_keep,
+                          int64_t C, int64_t V, float* loss_rows, uint16_t* dz, hipStream_t st) {
   if (C == 0) return hipSuccess;
-  k_ce_rows<<<(unsigned)C, 256, 0, st>>>(logits, tgt, n_keep, V, loss_rows, dz);
+  k_ce_rows<<<(unsigned)C, 256, 0, st>>>(logits, stats, (V + 255) / 256, tgt, n_keep, V, loss_rows, dz);
   return hipGetLastError();
 }
 

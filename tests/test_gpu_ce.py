@@ -30,6 +30,7 @@ def _run(d, chunk):
     (300, 128, 1024, 4096),  # one chunk holds the batch
     (97, 64, 2048, 32),      # many small chunks, rows < one GEMM tile
     (1, 64, 64, 1),          # smallest shapes
+    (130, 128, 1472, 64),    # vocabulary not a multiple of the 256-column statistics tile
 ])
 def test_ce_full_oracle(M, H, V, chunk):
     _announce(f"ce M={M} H={H} V={V} chunk={chunk}")

@@ -131,6 +131,9 @@ def test_linear_tiny_workload_full_oracle():
     (8200, 128, 136, 24),   # two 16-row fragments per rank-product workgroup, ragged last group
     (16400, 64, 72, 40),    # four fragments per workgroup, ragged last group
     (8232, 64, 80, 200),    # rank 200 with two fragments per workgroup
+    (300, 192, 200, 16),    # B read in place (rank % 16 == 0) with a ragged last 32-row step of G = dY.B
+    (77, 256, 136, 32),     # the same at rank 32
+    (520, 128, 8, 64),      # N = 8: one ragged step only
 ])
 def test_linear_ragged_shapes_full_oracle(M, K, N, r):
     _announce(f"linear ragged M={M} K={K} N={N} r={r}")

@@ -141,14 +141,13 @@ inline hipError_t launch_gemm_bwd_swiglu(const uint16_t* dY, WSrc w, int64_t M, 
 
 // LM head and chunked cross-entropy: Y [M, N] = X [M, K] . W [N, K]^T (bf16
 // operands, W in the tiled order of launch_tile_nt, fp32 or bf16 output); per-row statistics of a logits chunk; counts
-// and the final mean; a bf16 transpose (set-up).
+// and the final mean.
 hipError_t launch_gemm_nt_bf16(const uint16_t* X, const uint16_t* W, int64_t M, int64_t K, int64_t N, void* Y,
                                bool out_f32, float* stats, hipStream_t st);
 hipError_t launch_ce_count(const int32_t* tgt, int64_t M, int64_t V, int32_t* n_keep, hipStream_t st);
 hipError_t launch_ce_rows(const float* logits, const float* stats, const int32_t* tgt, const int32_t* n_keep,
                           int64_t C, int64_t V, float* loss_rows, uint16_t* dz, hipStream_t st);
 hipError_t launch_ce_total(const float* loss_rows, int64_t M, const int32_t* n_keep, float* loss, hipStream_t st);
-hipError_t launch_transpose_bf16(const uint16_t* src, int64_t R, int64_t C, uint16_t* dst, hipStream_t st);
 // the weight operand of launch_gemm_nt_bf16 in its tiled order (W = src or src^T)
 hipError_t launch_tile_nt(const uint16_t* src, int64_t R, int64_t C, bool transpose, uint16_t* dst, hipStream_t st);
 

@@ -371,23 +371,6 @@ __global__ __launch_bounds__(256) void k_tile_nt(const uint16_t* __restrict__ sr
   reinterpret_cast<u32x4*>(dst)[piece] = out;
 }
 
-// dst [C, R] = src [R, C]^T (bf16), 64 x 64 tiles through LDS.
-__global__ __launch_bounds__(256) void k_transpose_bf16(const uint16_t* __restrict__ src, int64_t R, int64_t C,
-                                                        uint16_t* __restrict__ dst) {
-  __shared__ uint16_t tile[64][66];
-  const int64_t r0 = (int64_t)blockIdx.y * 64, c0 = (int64_t)blockIdx.x * 64;
-  const int tx = threadIdx.x & 63, ty = threadIdx.x >> 6;
-  for (int i = ty; i < 64; i += 4) {
-    const int64_t r = r0 + i, c = c0 + tx;
-    tile[i][tx] = (r < R && c < C) ? src[r * C + c] : 0;
-  }
-  __syncthreads();
-  for (int i = ty; i < 64; i += 4) {
-    const int64_t c = c0 + i, r = r0 + tx;
-    if (c < C && r < R) dst[c * R + r] = tile[tx][i];
-  }
-}
-
 template <bool OUT_F32>
 hipError_t launch_nt(const NtGemmArgs& a, hipStream_t st) {
   static bool attr_done = false;
@@ -432,13 +415,6 @@ hipError_t launch_tile_nt(const uint16_t* src, int64_t R, int64_t C, bool transp
   const int64_t pieces = R * C / 8;
   if (pieces == 0) return hipSuccess;
   k_tile_nt<<<(unsigned)((pieces + 255) / 256), 256, 0, st>>>(src, R, C, transpose, dst);
-  return hipGetLastError();
-}
-
-hipError_t launch_transpose_bf16(const uint16_t* src, int64_t R, int64_t C, uint16_t* dst, hipStream_t st) {
-  if (R * C == 0) return hipSuccess;
-  dim3 grid((unsigned)((C + 63) / 64), (unsigned)((R + 63) / 64));
-  k_transpose_bf16<<<grid, 256, 0, st>>>(src, R, C, dst);
   return hipGetLastError();
 }
 

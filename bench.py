@@ -58,6 +58,8 @@ def parse():
                     help="token-tiled SwiGLU block with this many tokens per tile (0: whole batch)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="target CPU time of the oracle baseline")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--no-gpu-state", action="store_true",
+                    help="skip reading clocks and power with rocm-smi while the step runs")
     ap.add_argument("--cold", action="store_true",
                     help="also time 10 cache-cold steps (512 MiB written before each, untimed)")
     ap.add_argument("--graph", action="store_true",
@@ -478,9 +480,60 @@ def cpu_baseline(d, target_s: float):
             dt = time.perf_counter() - t0
             if dt >= 0.8 * target_s or reps >= 1000:
                 break
-    return dict(value=done / dt, unit="tokens/s", cores=threads, kind="oracle",
+    return dict(value=done / dt, unit="tokens/s", cores=threads, kind="oracle", blas=_blas_name(),
                 sample=f"NumPy float64 oracle, {what}, {reps} pass(es) over the first {rows} of {M} tokens "
                        f"({dt:.1f} s, {threads} BLAS threads on {cores} host cores)")
+
+
+def _blas_name():
+    try:
+        b = np.show_config(mode="dicts")["Build Dependencies"]["blas"]
+        return f"{b.get('name', '?')} {b.get('version', '')}".strip()
+    except Exception:  # older NumPy: no dict form
+        return None
+
+
+# ---------------------------------------------------------------------------
+# Clocks and power state, read while the step runs
+
+_SMI_KEYS = ("sclk", "mclk", "fclk", "performance level", "power")
+
+
+def gpu_state_under_load(step, sync, cap_s=15.0):
+    """rocm-smi's clocks, performance level and power, sampled while `step` runs
+    back to back (None when rocm-smi is missing or its output cannot be read)."""
+    import shutil
+    import subprocess
+    exe = shutil.which("rocm-smi")
+    if exe is None:
+        return None
+    try:
+        p = subprocess.Popen([exe, "--showclocks", "--showperflevel", "--showpower", "--json"],
+                             stdout=subprocess.PIPE, stderr=subprocess.DEVNULL, text=True)
+    except OSError:
+        return None
+    t0 = time.time()
+    while p.poll() is None and time.time() - t0 < cap_s:
+        for _ in range(10):
+            step()
+        sync()
+    try:
+        out, _ = p.communicate(timeout=5)
+    except subprocess.TimeoutExpired:
+        p.kill()
+        p.communicate()
+        return None
+    try:
+        js = json.loads(out)
+    except ValueError:
+        return None
+    keep = {}
+    for card, fields in js.items():
+        if isinstance(fields, dict):
+            sel = {k: v for k, v in fields.items() if any(x in k.lower() for x in _SMI_KEYS)}
+            if sel:
+                keep[card] = sel
+    return keep or None
 
 
 
@@ -628,6 +681,7 @@ def main():
     }
     if graph_stats is not None:
         out["graph"] = graph_stats
+    out["gpu_state"] = None if args.no_gpu_state else gpu_state_under_load(step, torch.cuda.synchronize)
     if not args.no_cpu:
         out["cpu_baseline"] = cpu_baseline(d, args.cpu_seconds)
     else:

@@ -17,7 +17,9 @@ Sources (the pages, by title and passage):
     matrix is never formed).
 
 Every function that has no pin says "parity unpinned" in its docstring; at
-present every function is pinned by tests/test_oracle.py.
+present every function is pinned: ref and codebook by tests/test_oracle.py,
+formats8, normrope and ce by tests/test_oracle_formats8.py,
+tests/test_oracle_normrope.py and tests/test_oracle_ce.py.
 """
 from .codebook import NF4_LEVELS, NF4_THRESHOLDS, derive_nf4_levels  # noqa: F401
 from .ref import (  # noqa: F401

@@ -35,7 +35,8 @@
 // zero, tokens past M drop their stores.
 //
 // k_qgemm_bwd8 below is the same pipeline with 8 waves (two per SIMD), each
-// holding 64 columns x 128 tokens; the plain and two-source products use it.
+// holding 64 columns x 128 tokens; every product uses it except the
+// two-source one at rank 256.
 #include <type_traits>
 
 #include "common.hpp"
@@ -720,11 +721,10 @@ void k_qgemm_bwd8(BwdArgs p) {
 template <int MODE, int RP, bool ALIGNED>
 hipError_t launch_rp(const BwdArgs& a, hipStream_t st) {
   static bool attr_done = false;
-  // The 8-wave kernel for the plain and two-source products (measured 3-4%
-  // faster), except at rank 256 with two sources, whose rank term does not
-  // fit its 256 registers per lane; the 4-wave kernel for the SwiGLU epilogue
-  // (measured 5% faster there).
-  constexpr bool k8 = MODE != kSwiGLU && !(MODE == kConcat && RP >= 256);
+  // The 8-wave kernel (measured 3-7% faster than the 4-wave one for every
+  // mode), except at rank 256 with two sources, whose rank term does not fit
+  // its 256 registers per lane.
+  constexpr bool k8 = !(MODE == kConcat && RP >= 256);
   const void* kfn;
   if constexpr (k8)
     kfn = (const void*)k_qgemm_bwd8<kFmt, MODE, RP, ALIGNED>;

@@ -304,13 +304,22 @@ __global__ __launch_bounds__(256) void k_ce_rows(const float* __restrict__ logit
   const float inv_n = (keep && n > 0) ? 1.0f / (float)n : 0.0f;
   if (tid == 0) loss_rows[m] = keep ? lse - z[t] : 0.0f;
   uint16_t* d = dz + m * V;
-  for (int64_t q = tid; q < nq; q += 256) {
-    const f32x4 v = reinterpret_cast<const f32x4*>(z)[q];
+  auto grad4 = [&](int64_t q, const f32x4& v) {
     float g[4];
 #pragma unroll
     for (int e = 0; e < 4; ++e) g[e] = (expf(v[e] - lse) - ((int64_t)4 * q + e == t ? 1.0f : 0.0f)) * inv_n;
     *reinterpret_cast<u32x2*>(d + 4 * q) = u32x2{pack_bf16x2(g[0], g[1]), pack_bf16x2(g[2], g[3])};
+  };
+  // four loads in flight per thread, then the ragged rest one by one
+  int64_t q = tid;
+  for (; q + 3 * 256 < nq; q += 4 * 256) {
+    f32x4 v[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) v[u] = reinterpret_cast<const f32x4*>(z)[q + 256 * u];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) grad4(q + 256 * u, v[u]);
   }
+  for (; q < nq; q += 256) grad4(q, reinterpret_cast<const f32x4*>(z)[q]);
 }
 
 // Number of kept targets (t >= 0 and t < V), one workgroup, fixed order.

@@ -16,31 +16,55 @@
 
 namespace qlora {
 
-// One wave per (row, block); lane e handles column 64*b + e.
+// Sixteen lanes per (row, block), four blocks per wave: lane i of a group
+// handles columns 64*b + 4i .. 4i+3 (one 16-byte load), so each lane works on
+// four independent weights and a block's absmax takes four shuffle steps.
+__device__ __forceinline__ float group16_max(float a) {
+#pragma unroll
+  for (int off = 8; off >= 1; off >>= 1) a = fmaxf(a, __shfl_xor(a, off));
+  return a;
+}
+
+// Whether any lane of this lane's 16-lane group has `bad` set.
+__device__ __forceinline__ bool group16_any(bool bad, int lane) {
+  return ((__ballot(bad) >> (lane & 48)) & 0xFFFFull) != 0;
+}
+
 __global__ __launch_bounds__(256) void k_quantize(const float* __restrict__ W, int64_t nblocks, int64_t kb_per_row,
                                                   int64_t N, int64_t K, uint8_t* __restrict__ codes,
                                                   float* __restrict__ absmax, uint32_t* __restrict__ nonfinite) {
-  const int lane = threadIdx.x & 63;
-  const int64_t blk = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (blk >= nblocks) return;
+  const int lane = threadIdx.x & 63, i = lane & 15;
+  const int64_t blk = (int64_t)blockIdx.x * 16 + (threadIdx.x >> 4);
+  if (blk >= nblocks) return;  // whole 16-lane groups leave together
   const int64_t n = blk / kb_per_row, b = blk - n * kb_per_row;
   const TileAddr ta(n, b, N, K);
-  const float w = W[n * K + b * kBlock + lane];
-  const bool bad = !__builtin_isfinite(w);
-  float a = __builtin_fabsf(w);
+  const f32x4 w = *reinterpret_cast<const f32x4*>(W + n * K + b * kBlock + 4 * i);
+  bool bad = false;
+  float a = 0.0f;
 #pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) a = fmaxf(a, __shfl_xor(a, off));
-  int code = 7;
-  if (a != 0.0f) {
-    const float x = w / a;
-    code = 0;
-#pragma unroll
-    for (int j = 0; j < 15; ++j) code += (x > nf4_threshold(j)) ? 1 : 0;
+  for (int e = 0; e < 4; ++e) {
+    bad = bad || !__builtin_isfinite(w[e]);
+    a = fmaxf(a, __builtin_fabsf(w[e]));
   }
-  const int partner = __shfl_xor(code, 4);  // column + 4 inside the run of 8
-  if ((lane & 4) == 0) codes[ta.code(kBlock / 2) + 4 * (lane >> 3) + (lane & 3)] = (uint8_t)(code | (partner << 4));
-  const unsigned long long anybad = __ballot(bad);
-  if (lane == 0) {
+  a = group16_max(a);
+  uint32_t packed = 0;  // code of column 4i + e in byte e
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    int code = 7;
+    if (a != 0.0f) {
+      const float x = w[e] / a;
+      code = 0;
+#pragma unroll
+      for (int j = 0; j < 15; ++j) code += (x > nf4_threshold(j)) ? 1 : 0;
+    }
+    packed |= (uint32_t)code << (8 * e);
+  }
+  // run of 8 columns = lanes 2m (low nibbles) and 2m + 1 (columns + 4: high nibbles)
+  const uint32_t partner = __shfl_xor(packed, 1);
+  if ((i & 1) == 0)
+    *reinterpret_cast<uint32_t*>(codes + ta.code(kBlock / 2) + 4 * (i >> 1)) = packed | (partner << 4);
+  const bool anybad = group16_any(bad, lane);
+  if (i == 0) {
     absmax[ta.value()] = anybad ? __builtin_nanf("") : a;
     if (anybad && nonfinite) atomicAdd(nonfinite, 1u);
   }
@@ -101,30 +125,39 @@ template <int F>
 __global__ __launch_bounds__(256) void k_quantize8(const float* __restrict__ W, int64_t nblocks, int64_t kb_per_row,
                                                    int64_t N, int64_t K, uint8_t* __restrict__ codes,
                                                    float* __restrict__ scale, uint32_t* __restrict__ nonfinite) {
-  const int lane = threadIdx.x & 63;
-  const int64_t blk = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (blk >= nblocks) return;
+  const int lane = threadIdx.x & 63, i = lane & 15;
+  const int64_t blk = (int64_t)blockIdx.x * 16 + (threadIdx.x >> 4);
+  if (blk >= nblocks) return;  // whole 16-lane groups leave together
   const int64_t n = blk / kb_per_row, b = blk - n * kb_per_row;
   const TileAddr ta(n, b, N, K);
-  const float w = W[n * K + b * kBlock + lane];
-  const bool bad = !__builtin_isfinite(w);
-  float a = __builtin_fabsf(w);
+  const f32x4 w = *reinterpret_cast<const f32x4*>(W + n * K + b * kBlock + 4 * i);
+  bool bad = false;
+  float a = 0.0f;
 #pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) a = fmaxf(a, __shfl_xor(a, off));
-  const float s = a / (F == kInt8 ? 127.0f : 448.0f);
-  uint32_t code = 0;
-  if (s != 0.0f) {
-    const float x = w / s;
-    if constexpr (F == kInt8) {
-      const float q = fminf(fmaxf(__builtin_rintf(x), -127.0f), 127.0f);
-      code = (uint32_t)(int)q & 0xFFu;
-    } else {
-      code = e4m3_encode(x);
-    }
+  for (int e = 0; e < 4; ++e) {
+    bad = bad || !__builtin_isfinite(w[e]);
+    a = fmaxf(a, __builtin_fabsf(w[e]));
   }
-  codes[ta.code(kBlock) + lane] = (uint8_t)code;
-  const unsigned long long anybad = __ballot(bad);
-  if (lane == 0) {
+  a = group16_max(a);
+  const float s = a / (F == kInt8 ? 127.0f : 448.0f);
+  uint32_t packed = 0;  // code of column 4i + e in byte e
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    uint32_t code = 0;
+    if (s != 0.0f) {
+      const float x = w[e] / s;
+      if constexpr (F == kInt8) {
+        const float q = fminf(fmaxf(__builtin_rintf(x), -127.0f), 127.0f);
+        code = (uint32_t)(int)q & 0xFFu;
+      } else {
+        code = e4m3_encode(x);
+      }
+    }
+    packed |= code << (8 * e);
+  }
+  *reinterpret_cast<uint32_t*>(codes + ta.code(kBlock) + 4 * i) = packed;
+  const bool anybad = group16_any(bad, lane);
+  if (i == 0) {
     scale[ta.value()] = anybad ? __builtin_nanf("") : s;
     if (anybad && nonfinite) atomicAdd(nonfinite, 1u);
   }
@@ -150,7 +183,7 @@ hipError_t launch_quantize(int fmt, const float* W, int64_t N, int64_t K, uint8_
   }
   const int64_t kb = K / kBlock, nblocks = N * kb;
   if (nblocks == 0) return hipGetLastError();
-  const unsigned grid = (unsigned)((nblocks + 3) / 4);
+  const unsigned grid = (unsigned)((nblocks + 15) / 16);  // 16 blocks per workgroup
   if (fmt == kNF4)
     k_quantize<<<grid, 256, 0, st>>>(W, nblocks, kb, N, K, codes, absmax, nonfinite_blocks);
   else if (fmt == kInt8)

@@ -107,7 +107,8 @@ typedef struct {
 
 /* Quantize W [N,K] fp32 to codes and absmax [N,K/64] in `format` (qlora_format).
  * nonfinite_blocks (device uint32, may be NULL) is set to the number of
- * blocks holding Inf/NaN; such a block gets absmax = NaN. Setup-time call. */
+ * blocks holding Inf/NaN; such a block gets absmax = NaN and unspecified
+ * codes. Setup-time call. */
 int qlora_quantize(int format, const float* W, int64_t N, int64_t K, uint8_t* codes, float* absmax,
                    uint32_t* nonfinite_blocks, void* stream);
 

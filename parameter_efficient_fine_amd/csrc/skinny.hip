@@ -41,16 +41,17 @@ struct NtShape {
   static constexpr int U = U0 / RF > 0 ? U0 / RF : 1;  // steps per batch
 };
 
-template <int RP, int RF, bool KT>
+template <int RP, int RF, bool KT, bool KA>
 __global__ __attribute__((amdgpu_flat_work_group_size(64 * NtShape<RP, RF>::NW, 64 * NtShape<RP, RF>::NW)))
 void k_skinny_nt(NtArgs p) {
+  constexpr bool KL = KT || KA;  // adapter steps staged in LDS
   constexpr int NF = NtShape<RP, RF>::NF, NW = NtShape<RP, RF>::NW;
   // KT: at most 16 KB of adapter slots per wave (8 KB from rank 128 on, next to the
   // larger reduction buffer)
   constexpr int kUK = (RP >= 128 ? 128 : 256) / RP > 0 ? (RP >= 128 ? 128 : 256) / RP : 1;
-  constexpr int U = KT && NtShape<RP, RF>::U > kUK ? kUK : NtShape<RP, RF>::U;
+  constexpr int U = KL && NtShape<RP, RF>::U > kUK ? kUK : NtShape<RP, RF>::U;
   __shared__ float red[NW / 2][16][RP + 4];
-  __shared__ __attribute__((aligned(16))) uint16_t kts[KT ? NW * U * 32 * RP : 8];
+  __shared__ __attribute__((aligned(16))) uint16_t kts[KL ? NW * U * 32 * RP : 8];
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int64_t M = p.M, Kd = p.Kd;
@@ -74,15 +75,28 @@ void k_skinny_nt(NtArgs p) {
   // copy instruction i moves bytes 16 (64 i + l) of the run. Transposed reads:
   // in 16-lane group g, lane s points at row 8g + s/4 (+4), columns 16f + 4 (s%4)
   // of the 32 x RP slot; lane i then holds rows 8g .. 8g+7 of column 16f + i.
-  const __amdgpu_buffer_rsrc_t rad = make_rsrc(p.ad1, KT ? Kd * RP * 2 : 0);
-  uint16_t* const kslot = kts + (KT ? wave * U * 32 * RP : 0);
+  // KA: a single adapter stored [R, Kd]; step st's block is R rows of 64 bytes at
+  // column offset 64 st. Lane l of copy instruction i moves row 16i + l/4, bytes
+  // 16 (l%4) of it, so the slot holds the block row-major (64 bytes per row) and
+  // lane l then reads row 16f + l%16, bytes 16 (l/16): its MFMA operand. Rows past
+  // R are out of range of the resource and read zero.
+  const __amdgpu_buffer_rsrc_t rad =
+      make_rsrc(p.ad1, KT ? Kd * RP * 2 : (KA ? (int64_t)p.r1 * Kd * 2 : 0));
+  uint16_t* const kslot = kts + (KL ? wave * U * 32 * RP : 0);
+  const int kd32 = (int)Kd;  // KA: row 16i + l/4 at byte (16i + l/4) Kd 2 + 16 (l%4)
+  const int kaoff0 = (lane >> 2) * kd32 * 2 + 16 * (lane & 3);
+  auto ka_read = [&](int u, u32x4 (&dst)[NF]) {
+    const uint8_t* base = reinterpret_cast<const uint8_t*>(kslot + u * 32 * RP) + (lane & 15) * 64 + 16 * (lane >> 4);
+#pragma unroll
+    for (int f = 0; f < NF; ++f) dst[f] = *reinterpret_cast<const u32x4*>(base + f * 1024);
+  };
   const int ktr = ((8 * (lane >> 4) + ((lane & 15) >> 2)) * RP + 4 * (lane & 3)) * 2;
-  auto kt_copy = [&](int u, int64_t st) {
+  auto kt_copy = [&](int u, int64_t st) {  // KT and KA: step st's adapter block into slot u
 #pragma unroll
     for (int i = 0; i < RP / 16; ++i)
       __builtin_amdgcn_raw_ptr_buffer_load_lds(
-          rad, (__attribute__((address_space(3))) void*)(kslot + u * 32 * RP + i * 512), 16, (64 * i + lane) * 16,
-          (int)(st * 64 * RP), 0, 0);
+          rad, (__attribute__((address_space(3))) void*)(kslot + u * 32 * RP + i * 512), 16,
+          KT ? (64 * i + lane) * 16 : kaoff0 + 32 * i * kd32, (int)(st * 64 * (KT ? RP : 1)), 0, 0);
   };
   auto kt_read = [&](int u, u32x4 (&dst)[NF]) {
     const uint8_t* base = reinterpret_cast<const uint8_t*>(kslot + u * 32 * RP) + ktr;
@@ -113,16 +127,23 @@ void k_skinny_nt(NtArgs p) {
             __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rin, voff[rf], (int)(st * 64), 0));
       if constexpr (KT) {
         kt_copy(u, st);
+      } else if constexpr (KA) {
+        kt_copy(u, st);
       } else {
 #pragma unroll
         for (int f = 0; f < NF; ++f) b[u][f] = *reinterpret_cast<const u32x4*>(adp[f] + st * 32);
       }
     }
     __builtin_amdgcn_sched_barrier(0);  // every load of the batch goes out before the first MFMA waits
-    if constexpr (KT) {
+    if constexpr (KL) {
       __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));  // this wave's adapter copies (and activation loads)
 #pragma unroll
-      for (int u = 0; u < V; ++u) kt_read(u, b[u]);
+      for (int u = 0; u < V; ++u) {
+        if constexpr (KT)
+          kt_read(u, b[u]);
+        else
+          ka_read(u, b[u]);
+      }
     }
 #pragma unroll
     for (int u = 0; u < V; ++u)
@@ -147,6 +168,10 @@ void k_skinny_nt(NtArgs p) {
       kt_copy(0, nfull);
       __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
       kt_read(0, b);
+    } else if constexpr (KA) {  // columns past Kd: masked below
+      kt_copy(0, nfull);
+      __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
+      ka_read(0, b);
     } else {
 #pragma unroll
       for (int f = 0; f < NF; ++f) b[f] = *reinterpret_cast<const u32x4*>(adp[f] + (ok ? nfull * 32 : 0));
@@ -205,7 +230,7 @@ void k_skinny_nt(NtArgs p) {
     }
 }
 
-template <int RP, bool KT>
+template <int RP, bool KT, bool KA = false>
 hipError_t launch_nt_rf(const NtArgs& a, hipStream_t st) {
   // row fragments per workgroup: as many as still leave >= 256 workgroups
   // (at most 2 for RP = 256, whose accumulators would spill at 4)
@@ -214,11 +239,11 @@ hipError_t launch_nt_rf(const NtArgs& a, hipStream_t st) {
   while (rf < kMaxRF && (a.M + 32 * rf - 1) / (32 * rf) >= 256) rf *= 2;
   const unsigned grid = (unsigned)((a.M + 16 * rf - 1) / (16 * rf));
   if (rf == 1)
-    k_skinny_nt<RP, 1, KT><<<grid, 64 * NtShape<RP, 1>::NW, 0, st>>>(a);
+    k_skinny_nt<RP, 1, KT, KA><<<grid, 64 * NtShape<RP, 1>::NW, 0, st>>>(a);
   else if (rf == 2)
-    k_skinny_nt<RP, 2, KT><<<grid, 64 * NtShape<RP, 2>::NW, 0, st>>>(a);
+    k_skinny_nt<RP, 2, KT, KA><<<grid, 64 * NtShape<RP, 2>::NW, 0, st>>>(a);
   else if constexpr (kMaxRF >= 4)
-    k_skinny_nt<RP, 4, KT><<<grid, 64 * NtShape<RP, 4>::NW, 0, st>>>(a);
+    k_skinny_nt<RP, 4, KT, KA><<<grid, 64 * NtShape<RP, 4>::NW, 0, st>>>(a);
   return hipGetLastError();
 }
 
@@ -232,6 +257,14 @@ hipError_t launch_skinny_nt(const NtArgs& a, hipStream_t st) {
     if (R == 64) return launch_nt_rf<64, true>(a, st);
     if (R == 128) return launch_nt_rf<128, true>(a, st);
     if (R == 256) return launch_nt_rf<256, true>(a, st);
+    return hipErrorInvalidValue;
+  }
+  if (a.r2 == 0) {  // a single adapter stored [R, Kd]: its steps staged in LDS
+    if (R <= 16) return launch_nt_rf<16, false, true>(a, st);
+    if (R <= 32) return launch_nt_rf<32, false, true>(a, st);
+    if (R <= 64) return launch_nt_rf<64, false, true>(a, st);
+    if (R <= 128) return launch_nt_rf<128, false, true>(a, st);
+    if (R <= 256) return launch_nt_rf<256, false, true>(a, st);
     return hipErrorInvalidValue;
   }
   if (R <= 16) return launch_nt_rf<16, false>(a, st);

@@ -32,6 +32,9 @@ namespace qlora {
 // so no transposed copy is made. Each wave copies the adapter rows of a step
 // (32 x R bf16, one contiguous run) into its own LDS slot with buffer_load ...
 // lds and reads the MFMA operand column-wise with ds_read_b64_tr_b16.
+// KA: a single adapter given as [R, Kd] (A in Z = X.A^T) goes through the same
+// LDS slots, R rows of 64 bytes per step, and is read back row-wise. Otherwise
+// (two stacked adapters) each lane loads its adapter row piece directly.
 
 template <int RP, int RF>
 struct NtShape {

@@ -160,11 +160,23 @@ size_t mlp_fwd_tiled_ws(int64_t M, int64_t I, int64_t tile) {
   return 3 * up256((size_t)T * I * 2);  // g, u, h of one tile
 }
 
+// Reduction partials of the tiled backward: the split count of a reduction is
+// not monotone in its row count (rows per split are rounded to 64), so a ragged
+// last tile can need more partials than a full one; size for the larger.
+size_t mlp_tiled_part_floats(int64_t M, int64_t H, int64_t I, int64_t r, int64_t tile) {
+  const int64_t T = std::min(tile, M);
+  size_t part = mlp_bwd_layout(T, H, I, r).part;
+  if (T > 0) {
+    const int64_t last = M - ((M - 1) / T) * T;
+    part = std::max(part, mlp_bwd_layout(last, H, I, r).part);
+  }
+  return part;
+}
+
 size_t mlp_bwd_tiled_ws(int64_t M, int64_t H, int64_t I, int64_t r, int64_t tile) {
   const int64_t T = std::min(tile, M);
-  const BwdLayout l = mlp_bwd_layout(T, H, I, r);
   return 5 * up256((size_t)T * I * 2) + up256(T * r * 2) + up256(T * 2 * r * 2) + up256(r * H * 2) +
-         2 * up256(r * I * 2) + up256(l.part * 4);
+         2 * up256(r * I * 2) + up256(mlp_tiled_part_floats(M, H, I, r, tile) * 4);
 }
 
 WSrc wsrc(const qlora_layer* L, const uint16_t* lora_i, const uint16_t* lora_j, int64_t ldj = 0) {
@@ -211,6 +223,7 @@ NtArgs ntB(const uint16_t* in, int64_t M, int64_t Kd, const uint16_t* B, const u
 // its own slice of the partial buffer.
 struct TnCall {
   float* part;
+  const float* part_end;  // end of the partial region carved for this call
   hipStream_t st;
   int accumulate = 0;  // add to the outputs instead of overwriting them
   TnJobs jobs{};
@@ -246,6 +259,10 @@ struct TnCall {
       a.Kd = Kd;
       a.part = part;
       part += tn_part_floats(M, Kd, a1 + a2);
+      if (part > part_end && rc == QLORA_OK) {  // never write past the carved region
+        snprintf(g_err, sizeof(g_err), "reduction partials exceed the workspace");
+        rc = QLORA_EWORKSPACE;
+      }
       if (jobs.n == kTnMaxJobs) flush();
       jobs.job[jobs.n++] = a;
     });
@@ -357,7 +374,7 @@ int qlora_backward(const qlora_layer* L, const uint16_t* dY, const uint16_t* X, 
   }
   // G = dY.B ; dB = s.dY^T.Z (written transposed from Z^T.dY) and dA = s.G^T.X in one pair of launches ; dX
   QL_LAUNCH("skinny_nt", st, launch_skinny_nt(ntB(dY, M, N, L->B, Bt, r, G, r), st));
-  TnCall tn{part, st};
+  TnCall tn{part, part + lay.part, st};
   tn.one(Z_save, r, r, L->s, dY, M, N, dB, true);
   tn.one(G, r, r, L->s, X, M, K, dA, false);
   if (int rc = tn.flush()) return rc;
@@ -412,6 +429,7 @@ int mlp_fwd_body(const qlora_layer* gate, const qlora_layer* up, const qlora_lay
 struct MlpBwdWs {
   uint16_t *dg, *du, *Gd, *Ggu, *Btd, *Btg, *Btu;
   float* part;
+  size_t part_floats;
 };
 
 MlpBwdWs carve_mlp_bwd(Carve& c, int64_t M, int64_t H, int64_t I, int64_t r, size_t part_floats) {
@@ -424,6 +442,7 @@ MlpBwdWs carve_mlp_bwd(Carve& c, int64_t M, int64_t H, int64_t I, int64_t r, siz
   w.Btg = c.take<uint16_t>((size_t)r * I);
   w.Btu = c.take<uint16_t>((size_t)r * I);
   w.part = c.take<float>(part_floats);
+  w.part_floats = part_floats;
   return w;
 }
 
@@ -460,7 +479,7 @@ int mlp_bwd_body(const qlora_layer* gate, const qlora_layer* up, const qlora_lay
   const int r = (int)gate->r;
   uint16_t* Gg = w.Ggu;
   uint16_t* Gu = w.Ggu + r;
-  TnCall tn{w.part, st, accumulate};
+  TnCall tn{w.part, w.part + w.part_floats, st, accumulate};
   // down projection: G_d = dY.B_d ; dB_d = s.dY^T.Z_d and dA_d = s.G_d^T.h ; dh -> (dg, du) in the GEMM epilogue
   QL_LAUNCH("skinny_nt", st, launch_skinny_nt(ntB(dY, M, H, down->B, w.Btd, r, w.Gd, r), st));
   tn.one(Zd, r, r, down->s, dY, M, H, dB[2], true);
@@ -582,7 +601,7 @@ int swiglu_mlp_backward_tiled(const qlora_layer* gate, const qlora_layer* up, co
   uint16_t* g = c.take<uint16_t>((size_t)T * I);
   uint16_t* u = c.take<uint16_t>((size_t)T * I);
   uint16_t* h = c.take<uint16_t>((size_t)T * I);
-  const MlpBwdWs w = carve_mlp_bwd(c, T, H, I, r, mlp_bwd_layout(T, H, I, r).part);
+  const MlpBwdWs w = carve_mlp_bwd(c, T, H, I, r, mlp_tiled_part_floats(M, H, I, r, tile));
   if (!c.ok) return QLORA_EWORKSPACE;
   if (M == 0) return mlp_zero_grads(gate, up, down, dA, dB, st);
   if (int rc = mlp_prep(gate, up, down, w, st)) return rc;

@@ -265,3 +265,35 @@ def test_nf4_run_byte_order():
     # library pairs column b with column b+4 inside each run of 8 columns
     packed = np.array([[0x10, 0x32, 0x54, 0x76, 0x98, 0xBA, 0xDC, 0xFE]], dtype=np.uint8)
     assert list(nf4_runs(packed)[0]) == [0x40, 0x51, 0x62, 0x73, 0xC8, 0xD9, 0xEA, 0xFB]
+
+
+def _up256(x):
+    return (x + 255) // 256 * 256
+
+
+def _mlp_part_bytes(lib, M, H, I, r):
+    """Bytes of the rank reductions' fp32 partials in the whole-batch SwiGLU backward
+    workspace: its size minus the documented carve of the other intermediates
+    (dg, du [M, I]; G_d [M, r]; G_gate|G_up [M, 2r]; three B^T copies)."""
+    total = lib.qlora_workspace_size(C.OP_MLP_BACKWARD, M, H, I, r)
+    rest = (2 * _up256(M * I * 2) + _up256(M * r * 2) + _up256(M * 2 * r * 2) + _up256(r * H * 2)
+            + 2 * _up256(r * I * 2))
+    return total - rest
+
+
+@pytest.mark.parametrize("H,I", [(4096, 14336), (128, 256), (256, 512), (192, 320)])
+def test_tiled_mlp_workspace_covers_every_tile(H, I):
+    # the row-split count of a reduction is not monotone in its row count, so
+    # the last (ragged) tile of a tiled backward can need more partials than a
+    # full tile; the tiled workspace must hold what every tile of the batch needs
+    lib = C.lib()
+    for r in (1, 8, 16, 64):
+        for tile in (256, 576, 1024, 4096):
+            for M in (tile + 64, 1088, 1920, 2 * tile - 128, 3 * tile + 896, 16384):
+                T = min(tile, M)
+                sizes = {T, M - ((M - 1) // T) * T}
+                fixed = (5 * _up256(T * I * 2) + _up256(T * r * 2) + _up256(T * 2 * r * 2) + _up256(r * H * 2)
+                         + 2 * _up256(r * I * 2))
+                need = fixed + max(_mlp_part_bytes(lib, m, H, I, r) for m in sizes)
+                got = lib.swiglu_mlp_tiled_workspace_size(1, M, H, I, r, tile)
+                assert got >= need, (M, tile, r, H, I, got, need)

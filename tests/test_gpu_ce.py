@@ -80,3 +80,44 @@ def test_ce_llama3_head_sampled_rows():
     assert max(errs.values()) <= TOL, errs
     # the mean over kept rows of the per-row losses
     assert abs(float(host(out["loss"])[0]) - got_rows.sum() / n) <= 1e-5 * abs(got_rows.sum() / n)
+
+
+def test_ce_bench_configuration():
+    # the benchmark's own input and launch configuration: the Llama-3-8B head
+    # (V = 128256, H = 4096), M = 16384 tokens in chunks of 4096
+    M, H, V, chunk = 16384, 4096, 128256, 4096
+    _announce(f"ce M={M} H={H} V={V} chunk={chunk} (bench input)")
+    import torch
+    import parameter_efficient_fine_amd as q
+    d = random_ce(6000, M, H, V)
+    prepared = q.lmhead_prepare(dev_bf16(d["W"]))
+    t = d["targets"]
+    out = q.chunked_ce(dev_bf16(d["h"]), prepared, torch.from_numpy(t).cuda(), chunk)
+    Wf = bf16_to_f64(d["W"])
+    Hf = bf16_to_f64(d["h"])
+    n = int((t >= 0).sum())
+    # sampled rows (every 512-row block, so every chunk and GEMM tile is hit): rows
+    # are independent given n, so the oracle on the sample scales dh by n_s / n
+    rows = sample_rows(M, np.random.default_rng(60), per_block=1, block=512)
+    _, rr, dh = ce.ce_fwd_bwd(Hf[rows], Wf, t[rows])
+    dh = dh * (int((t[rows] >= 0).sum()) / n)
+    errs = dict(rows=rel_err(host(out["loss_rows"])[rows], rr), dh=rel_err(host(out["dh"])[rows], dh))
+    assert max(errs.values()) <= TOL, errs
+    # the whole batch against the oracle: 64 distinct (hidden row, target) pairs,
+    # token m taking pair idx[m] (ignored where the bench's target is), so the
+    # oracle's loss over all M tokens and every row of dh follow from its result
+    # on the 64 pairs; the GPU runs the same chunked launches over all M tokens
+    rng = np.random.default_rng(61)
+    idx = rng.integers(0, 64, M)
+    t64 = rng.integers(0, V, 64).astype(np.int32)
+    keep = t >= 0
+    t2 = np.where(keep, t64[idx], -100).astype(np.int32)
+    out2 = q.chunked_ce(dev_bf16(d["h"][:64][idx]), prepared, torch.from_numpy(t2).cuda(), chunk)
+    _, r64, dh64 = ce.ce_fwd_bwd(Hf[:64], Wf, t64)   # every pair kept: dh64 carries 1/64
+    loss = float(np.sum(r64[idx][keep])) / n
+    got = float(host(out2["loss"])[0])
+    assert abs(got - loss) <= 1e-4 * abs(loss), (got, loss)
+    want_rows = np.where(keep, r64[idx], 0.0)
+    want_dh = np.where(keep[:, None], dh64[idx] * (64.0 / n), 0.0)
+    errs2 = dict(rows=rel_err(host(out2["loss_rows"]), want_rows), dh=rel_err(host(out2["dh"]), want_dh))
+    assert max(errs2.values()) <= TOL, errs2

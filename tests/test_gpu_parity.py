@@ -209,9 +209,18 @@ def _mlp_case(d, rows=None, mask_dy=False, fmt=0):
         other = np.ones(d["M"], bool)
         other[rows] = False
         assert float(np.max(np.abs(host(b["dX"])[other]))) == 0.0
-    # adapter visibility
+    # adapter visibility: with every adapter off (s = 0) each checked output moves
+    # by more than the tolerance; so does Y with only the down adapter off (B_down = 0)
+    # and dX with only the gate/up adapters off (B_gate = B_up = 0)
     f0 = ref.mlp_fwd(X[sel], *trip, 0.0)
-    assert rel_err(f0["Y"], fr["Y"]) > TOL / 4
+    b0 = ref.mlp_bwd(dY[sel], X[sel], *trip, 0.0)
+    for k in ("Y", "g", "u", "h"):
+        assert rel_err(f0[k], fr[k]) > TOL, k
+    assert rel_err(b0["dX"], br["dX"]) > TOL
+    no_down = trip[:2] + [(trip[2][0], trip[2][1], np.zeros_like(trip[2][2]))]
+    assert rel_err(ref.mlp_fwd(X[sel], *no_down, d["s"])["Y"], fr["Y"]) > TOL
+    no_gu = [(t[0], t[1], np.zeros_like(t[2])) for t in trip[:2]] + trip[2:]
+    assert rel_err(ref.mlp_bwd(dY[sel], X[sel], *no_gu, d["s"])["dX"], br["dX"]) > TOL
     return errs
 
 

@@ -89,15 +89,27 @@ def test_mlp_tiled_long_batch_full_size():
     # Llama-3.1-8B MLP widths at M=16384 in tiles of 4096 tokens: bitwise rows
     # and order-only gradient differences against the whole-batch call, and the
     # oracle on sampled rows of Y
+    # The upstream gradient is zero outside sampled rows, so every gradient of
+    # the tiled call involves those rows only and the oracle computes dX on them
+    # and the exact dA, dB.
     _announce("tiled mlp M=16384 tile=4096 H=4096 I=14336 r=16")
     d = random_mlp(4096, 16384, 4096, 14336, 16)
+    rows = sample_rows(d["M"], np.random.default_rng(9), per_block=1)
+    keep = np.zeros(d["M"], bool)
+    keep[rows] = True
+    d["dY"] = np.where(keep[:, None], d["dY"], 0).astype(d["dY"].dtype)
     Ls, wf, wb, tf, tb = _run(d, 4096)
     _compare_to_whole(wf, wb, tf, tb, same_order=False)
-    rows = sample_rows(d["M"], np.random.default_rng(9), per_block=1)
-    X = ref.bf16_to_f64(d["X"])
+    X, dY = ref.bf16_to_f64(d["X"]), ref.bf16_to_f64(d["dY"])
     trip = [Ls[nm].triple() for nm in ("gate", "up", "down")]
     fr = ref.mlp_fwd(X[rows], *trip, d["s"])
-    assert rel_err(host(tf["Y"])[rows], fr["Y"]) <= TOL
+    br = ref.mlp_bwd(dY[rows], X[rows], *trip, d["s"])
+    errs = dict(Y=rel_err(host(tf["Y"])[rows], fr["Y"]), dX=rel_err(host(tb["dX"])[rows], br["dX"]))
+    for i, nm in enumerate(("gate", "up", "down")):
+        errs["dA_" + nm] = rel_err(host(tb["dA"][i]), br["dA_" + nm])
+        errs["dB_" + nm] = rel_err(host(tb["dB"][i]), br["dB_" + nm])
+    assert max(errs.values()) <= TOL, errs
+    assert not host(tb["dX"])[~keep].any()
 
 
 def test_mlp_tiled_backward_independent_of_workspace_and_output_contents():
@@ -128,3 +140,34 @@ def test_mlp_tiled_backward_independent_of_workspace_and_output_contents():
         runs.append([_bits(t) for t in [f["Y"], f["Z"], b["dX"]] + b["dA"] + b["dB"]])
     for a, b in zip(*runs):
         assert np.array_equal(a, b)
+
+
+@pytest.mark.parametrize("M,H,I,r,tile", [
+    (1088, 128, 256, 8, 576),     # the last tile (512 tokens) needs more reduction splits than a full one
+    (1344, 128, 384, 16, 704),    # the same with tile 704 (last tile 640 tokens), r = 16
+])
+def test_mlp_tiled_ragged_last_tile_stays_in_its_workspace(M, H, I, r, tile):
+    # a canary region right after a workspace of exactly the size the library
+    # asks for must come back untouched; the result must match the oracle
+    _announce(f"tiled mlp canary M={M} H={H} I={I} r={r} tile={tile}")
+    import torch
+    import parameter_efficient_fine_amd as q
+    d = random_mlp(900 + M + tile, M, H, I, r)
+    Ls = {nm: Prepared(d["layers"][nm], d["s"]) for nm in ("gate", "up", "down")}
+    g, u, dn = Ls["gate"].dev, Ls["up"].dev, Ls["down"].dev
+    X, dY = dev_bf16(d["X"]), dev_bf16(d["dY"])
+    nb = q.mlp_tiled_workspace_size(True, M, H, I, r, tile)
+    canary = 4 << 20
+    buf = torch.full((nb + canary,), 0x5A, dtype=torch.uint8, device="cuda")
+    f = q.mlp_forward_tiled(g, u, dn, X, tile)
+    b = q.mlp_backward_tiled(g, u, dn, dY, X, f["Z"], tile, ws=buf[:nb])
+    torch.cuda.synchronize()
+    assert bool((buf[nb:] == 0x5A).all()), "the tiled backward wrote past its workspace"
+    Xf, dYf = ref.bf16_to_f64(d["X"]), ref.bf16_to_f64(d["dY"])
+    trip = [Ls[nm].triple() for nm in ("gate", "up", "down")]
+    br = ref.mlp_bwd(dYf, Xf, *trip, d["s"])
+    errs = dict(dX=rel_err(host(b["dX"]), br["dX"]))
+    for i, nm in enumerate(("gate", "up", "down")):
+        errs["dA_" + nm] = rel_err(host(b["dA"][i]), br["dA_" + nm])
+        errs["dB_" + nm] = rel_err(host(b["dB"][i]), br["dB_" + nm])
+    assert max(errs.values()) <= TOL, errs

@@ -530,6 +530,34 @@ def test_synthetic_inputs_deterministic_and_distributed():
     assert w1["s"] == 2.0 and w1["r"] == 8
 
 
+def test_bf16_widening_of_hand_chosen_words():
+    # bfloat16 is the top half of an IEEE binary32 word: sign, 8 exponent bits
+    # (bias 127), 7 fraction bits. Each word below is decoded by hand.
+    words = np.array([0x3F80, 0xC020, 0x0001, 0x8000, 0x7F80, 0xFF80, 0x4049, 0x0080, 0x7F7F, 0x3E80],
+                     dtype=np.uint16)
+    want = [1.0,                     # exponent 127, fraction 0
+            -2.5,                    # sign, exponent 128, fraction 0b0100000 -> -(1 + 1/4) * 2
+            2.0 ** -133,             # smallest subnormal: 2^-126 * 2^-7
+            -0.0,                    # negative zero
+            np.inf, -np.inf,         # exponent all ones, fraction 0
+            3.140625,                # exponent 128, fraction 0b1001001 -> (1 + 73/128) * 2
+            2.0 ** -126,             # smallest normal
+            (2.0 - 2.0 ** -7) * 2.0 ** 127,  # largest finite
+            0.25]
+    got = ref.bf16_to_f64(words)
+    assert got.dtype == np.float64
+    for g, w in zip(got, want):
+        assert g == w and np.signbit(g) == np.signbit(w), (g, w)
+    # a NaN word stays NaN
+    assert np.isnan(ref.bf16_to_f64(np.array([0x7FC0], dtype=np.uint16))[0])
+    # exact widening: every finite bf16 word round-trips through float32 bit patterns
+    allw = np.arange(1 << 16, dtype=np.uint32).astype(np.uint16)
+    vals = ref.bf16_to_f64(allw)
+    fin = np.isfinite(vals)
+    back = (vals[fin].astype(np.float32).view(np.uint32) >> 16).astype(np.uint16)
+    assert np.array_equal(back, allw[fin])
+
+
 def test_bf16_rounding_is_round_to_nearest_even():
     x = np.array([1.0, 1.0 + 2 ** -8, 1.0 + 3 * 2 ** -8, 1.0 + 2 ** -8 + 2 ** -20, -2.5, np.inf], np.float32)
     b = bf16_bits(x)

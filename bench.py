@@ -158,8 +158,8 @@ class Proj:
         self.Y = torch.empty((M, self.N), dtype=torch.bfloat16, device=dev)
         self.Z = torch.empty((M, self.r), dtype=torch.bfloat16, device=dev)
         self.dX = torch.empty((M, self.K), dtype=torch.bfloat16, device=dev)
-        self.dA = torch.empty((self.r, self.K), dtype=torch.float32, device=dev)
-        self.dB = torch.empty((self.N, self.r), dtype=torch.float32, device=dev)
+        self.dA = torch.empty((self.r, self.K), dtype=self.L.grad_dtype, device=dev)
+        self.dB = torch.empty((self.N, self.r), dtype=self.L.grad_dtype, device=dev)
         nb = q.workspace_size(C.OP_BACKWARD, M, self.K, self.N, self.r)
         self.ws = torch.empty((nb,), dtype=torch.uint8, device=dev)
         self.lc = self.L.c()
@@ -193,8 +193,8 @@ class MLP:
         dev = X.device
         e = lambda shape, dt=torch.bfloat16: torch.empty(shape, dtype=dt, device=dev)
         self.dX = e((M, H))
-        self.dA = [e((r, L.K), torch.float32) for L in Ls]
-        self.dB = [e((L.N, r), torch.float32) for L in Ls]
+        self.dA = [e((r, L.K), L.grad_dtype) for L in Ls]
+        self.dB = [e((L.N, r), L.grad_dtype) for L in Ls]
         self.lcs = [L.c() for L in Ls]
         p = lambda t: ctypes.c_void_p(t.data_ptr())
         refs = [ctypes.byref(lc) for lc in self.lcs]

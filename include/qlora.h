@@ -37,7 +37,9 @@
  *   - Calls are re-entrant; concurrent calls must not share output or
  *     workspace buffers.
  *   - Matrix products accumulate in fp32. Y, dX, Z, g, u, h are rounded once
- *     to bf16 (round to nearest even). dA and dB are fp32.
+ *     to bf16 (round to nearest even). dA and dB are summed in fp32 and
+ *     written in the layer's grad_dtype: bf16 (rounded once, the default and
+ *     the adapters' parameter type) or fp32.
  */
 #ifndef QLORA_H
 #define QLORA_H
@@ -54,7 +56,8 @@ typedef enum {
   QLORA_EINVAL = -1,       /* bad shape, null pointer, misalignment */
   QLORA_EUNSUPPORTED = -2, /* valid request this build does not handle */
   QLORA_EWORKSPACE = -3,   /* workspace missing or smaller than qlora_workspace_size */
-  QLORA_EHIP = -4          /* a HIP launch failed; see qlora_last_error() */
+  QLORA_EHIP = -4,         /* a HIP launch failed; see qlora_last_error() */
+  QLORA_ENONFINITE = -5    /* qlora_quantize (synchronous form): W holds Inf or NaN */
 } qlora_status;
 
 /* Formats of the frozen weight ("Rev vs unsloth", fused quantized-LoRA card:
@@ -81,8 +84,12 @@ typedef enum {
  * columns 8j .. 8j+7 takes 4 bytes, byte b holding column 8j+b in its low
  * nibble and column 8j+b+4 in its high nibble (the order the GEMMs decode
  * fastest); the 8-bit formats keep one byte per column in column order.
- * qlora_quantize writes this order, every call reads it. */
+ * qlora_quantize writes this order, every call reads it; qlora_pack_codes
+ * converts codes and block values from the row-major checkpoint order. */
 typedef enum { QLORA_FMT_NF4 = 0, QLORA_FMT_INT8 = 1, QLORA_FMT_FP8 = 2 } qlora_format;
+
+/* Type of the adapter gradients dA, dB written by the backward calls. */
+typedef enum { QLORA_GRAD_BF16 = 0, QLORA_GRAD_F32 = 1 } qlora_grad_dtype;
 
 typedef enum {
   QLORA_OP_FORWARD = 0,
@@ -103,14 +110,32 @@ typedef struct {
   int64_t r;             /* LoRA rank */
   float s;               /* lora_alpha / r */
   int32_t format;        /* qlora_format of codes/absmax */
+  int32_t grad_dtype;    /* qlora_grad_dtype of dA, dB (0: bf16) */
 } qlora_layer;
 
 /* Quantize W [N,K] fp32 to codes and absmax [N,K/64] in `format` (qlora_format).
- * nonfinite_blocks (device uint32, may be NULL) is set to the number of
- * blocks holding Inf/NaN; such a block gets absmax = NaN and unspecified
- * codes. Setup-time call. */
+ * A block holding Inf/NaN gets absmax = NaN and unspecified codes, and is
+ * counted:
+ *   - nonfinite_blocks != NULL (device uint32): the count is written there and
+ *     the call stays asynchronous, like every other call;
+ *   - nonfinite_blocks == NULL: the library counts in a device word of its own
+ *     (one per GPU), synchronizes `stream` (whose device must be the current
+ *     one) and returns QLORA_ENONFINITE if any block was non-finite. Such calls
+ *     are serialized inside the library.
+ * Setup-time call. */
 int qlora_quantize(int format, const float* W, int64_t N, int64_t K, uint8_t* codes, float* absmax,
                    uint32_t* nonfinite_blocks, void* stream);
+
+/* Take codes and block values in the row-major order of a pre-quantized
+ * checkpoint ("Unsloth" wiki entry, API; "Unsloth -- the speed layer" lesson:
+ * 4-bit bitsandbytes checkpoints loaded as they are) and write this library's
+ * storage order (described with qlora_format). Source: NF4 codes [N, K/2],
+ * column 2c in the low nibble and 2c+1 in the high nibble of byte c; INT8/FP8
+ * codes [N, K], one byte per column; block values src_absmax [N, K/64] fp32.
+ * Destinations have the same sizes and must not overlap the sources. All
+ * pointers 16-byte aligned; K % 64 == 0. */
+int qlora_pack_codes(int format, const uint8_t* src_codes, const float* src_absmax, int64_t N, int64_t K,
+                     uint8_t* codes, float* absmax, void* stream);
 
 /* What [N,K] fp32 = fp32(v(code) * absmax), decoded as the GEMMs decode it.
  * Exposes the exact operand values for testing. */
@@ -127,25 +152,27 @@ int qlora_forward(const qlora_layer* L, const uint16_t* X, int64_t M, uint16_t* 
                   void* ws, size_t ws_bytes, void* stream);
 
 /* Backward of one projection for upstream dY [M,N]. Writes dX [M,K] bf16
- * (dX may be NULL to skip it), dA [r,K] fp32 and dB [N,r] fp32.
+ * (dX may be NULL to skip it), dA [r,K] and dB [N,r] in L->grad_dtype.
  * X and Z_save are the forward's input and saved tensor. */
 int qlora_backward(const qlora_layer* L, const uint16_t* dY, const uint16_t* X, const uint16_t* Z_save,
-                   int64_t M, uint16_t* dX, float* dA, float* dB, void* ws, size_t ws_bytes, void* stream);
+                   int64_t M, uint16_t* dX, void* dA, void* dB, void* ws, size_t ws_bytes, void* stream);
 
 /* SwiGLU MLP forward: g = lin_gate(X), u = lin_up(X), h = silu(g)*u,
  * Y = lin_down(h). gate/up: K = H (model width), N = I; down: K = I, N = H.
  * Saves g, u, h [M,I] bf16 and Z_save [3][M][r] (gate, up, down) for the
- * backward. All three layers must share r. Needs no workspace. */
+ * backward. All three layers must share r, format and grad_dtype. Needs no
+ * workspace. */
 int swiglu_mlp_forward(const qlora_layer* gate, const qlora_layer* up, const qlora_layer* down,
                        const uint16_t* X, int64_t M, uint16_t* Y, uint16_t* g_save, uint16_t* u_save,
                        uint16_t* h_save, uint16_t* Z_save, void* ws, size_t ws_bytes, void* stream);
 
 /* SwiGLU MLP backward for upstream dY [M,H]. dA[i], dB[i] (i = 0 gate,
- * 1 up, 2 down) receive fp32 [r,K_i] and [N_i,r]; dX [M,H] bf16 may be NULL. */
+ * 1 up, 2 down) receive [r,K_i] and [N_i,r] in the layers' grad_dtype;
+ * dX [M,H] bf16 may be NULL. */
 int swiglu_mlp_backward(const qlora_layer* gate, const qlora_layer* up, const qlora_layer* down,
                         const uint16_t* dY, const uint16_t* X, const uint16_t* g_save, const uint16_t* u_save,
                         const uint16_t* h_save, const uint16_t* Z_save, int64_t M, uint16_t* dX,
-                        float* const dA[3], float* const dB[3], void* ws, size_t ws_bytes, void* stream);
+                        void* const dA[3], void* const dB[3], void* ws, size_t ws_bytes, void* stream);
 
 /* Token-tiled SwiGLU block ("Unsloth vs PyTorch" video, 4:25-4:36: tiled
  * feed-forward layers for long context). The batch is cut into tiles of
@@ -160,7 +187,8 @@ int swiglu_mlp_backward(const qlora_layer* gate, const qlora_layer* up, const ql
  *              tile and dA/dB are summed over the tiles in tile order.
  * Y, Z_save and dX equal swiglu_mlp_forward/backward's bit for bit (every
  * token's row is computed the same way); dA and dB differ only by the fp32
- * summation order across tiles (identical when tile >= M). The workspace
+ * summation order across tiles (identical when tile >= M); bf16 gradients
+ * are summed over the tiles in fp32 and rounded once at the end. The workspace
  * scales with min(tile, M), not M: size from
  * swiglu_mlp_tiled_workspace_size(backward = 0 or 1, M, H, I, r, tile).
  * tile >= 1 (a multiple of 256 keeps every GEMM tile full). */
@@ -170,7 +198,7 @@ int swiglu_mlp_forward_tiled(const qlora_layer* gate, const qlora_layer* up, con
                              size_t ws_bytes, void* stream);
 int swiglu_mlp_backward_tiled(const qlora_layer* gate, const qlora_layer* up, const qlora_layer* down,
                               const uint16_t* dY, const uint16_t* X, const uint16_t* Z_save, int64_t M, int64_t tile,
-                              uint16_t* dX, float* const dA[3], float* const dB[3], void* ws, size_t ws_bytes,
+                              uint16_t* dX, void* const dA[3], void* const dB[3], void* ws, size_t ws_bytes,
                               void* stream);
 
 /* RMSNorm before the projections ("Unsloth" wiki entry, Theory: fused RMSNorm

@@ -18,7 +18,9 @@ from .ops import (  # noqa: F401
     mlp_forward,
     mlp_forward_tiled,
     mlp_tiled_workspace_size,
+    pack_codes,
     quantize,
+    quantize_sync,
     rmsnorm_backward,
     rmsnorm_forward,
     rope_backward,

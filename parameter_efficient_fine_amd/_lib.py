@@ -16,13 +16,15 @@ QLORA_EINVAL = -1
 QLORA_EUNSUPPORTED = -2
 QLORA_EWORKSPACE = -3
 QLORA_EHIP = -4
+QLORA_ENONFINITE = -5
 
 OP_FORWARD, OP_BACKWARD, OP_MLP_FORWARD, OP_MLP_BACKWARD = 0, 1, 2, 3
 FMT_NF4, FMT_INT8, FMT_FP8 = 0, 1, 2
+GRAD_BF16, GRAD_F32 = 0, 1
 
 # Every function the header declares (checked by the CPU tests against include/qlora.h).
 EXPORTS = [
-    "qlora_quantize", "qlora_dequantize", "qlora_workspace_size", "qlora_forward", "qlora_backward",
+    "qlora_quantize", "qlora_pack_codes", "qlora_dequantize", "qlora_workspace_size", "qlora_forward", "qlora_backward",
     "swiglu_mlp_forward", "swiglu_mlp_backward", "swiglu_mlp_tiled_workspace_size", "swiglu_mlp_forward_tiled",
     "swiglu_mlp_backward_tiled", "qlora_rmsnorm_forward", "qlora_rmsnorm_backward", "qlora_rope_forward",
     "qlora_rope_backward", "qlora_lmhead_prepare", "qlora_ce_workspace_size", "qlora_chunked_ce",
@@ -42,6 +44,7 @@ class QLoraLayerC(ctypes.Structure):
         ("r", ctypes.c_int64),
         ("s", ctypes.c_float),
         ("format", ctypes.c_int32),
+        ("grad_dtype", ctypes.c_int32),
     ]
 
 
@@ -69,6 +72,7 @@ def lib():
     vp, i64, sz = ctypes.c_void_p, ctypes.c_int64, ctypes.c_size_t
     LP = ctypes.POINTER(QLoraLayerC)
     L.qlora_quantize.argtypes = [ctypes.c_int, vp, i64, i64, vp, vp, vp, vp]
+    L.qlora_pack_codes.argtypes = [ctypes.c_int, vp, vp, i64, i64, vp, vp, vp]
     L.qlora_dequantize.argtypes = [ctypes.c_int, vp, vp, i64, i64, vp, vp]
     L.qlora_workspace_size.argtypes = [ctypes.c_int, i64, i64, i64, i64]
     L.qlora_workspace_size.restype = sz
@@ -99,7 +103,7 @@ def lib():
     L.qlora_status_string.restype = ctypes.c_char_p
     L.qlora_last_error.argtypes = []
     L.qlora_last_error.restype = ctypes.c_char_p
-    for f in ("qlora_quantize", "qlora_dequantize", "qlora_forward", "qlora_backward", "swiglu_mlp_forward",
+    for f in ("qlora_quantize", "qlora_pack_codes", "qlora_dequantize", "qlora_forward", "qlora_backward", "swiglu_mlp_forward",
               "swiglu_mlp_backward", "swiglu_mlp_forward_tiled", "swiglu_mlp_backward_tiled", "qlora_rmsnorm_forward",
               "qlora_rmsnorm_backward", "qlora_rope_forward", "qlora_rope_backward", "qlora_lmhead_prepare",
               "qlora_chunked_ce"):

@@ -72,6 +72,7 @@ bool layer_ok(const qlora_layer* L) {
   if (L->K <= 0 || L->K % 64 != 0 || L->N <= 0 || L->N % 8 != 0) return false;
   if (L->r < 1 || L->r > 256) return false;
   if (L->format < QLORA_FMT_NF4 || L->format > QLORA_FMT_FP8) return false;
+  if (L->grad_dtype != QLORA_GRAD_BF16 && L->grad_dtype != QLORA_GRAD_F32) return false;
   // code bytes of the weight stay below 2^30 for every format
   if (L->K > kMaxDim || L->N > kMaxDim || L->N * L->K > (L->format == QLORA_FMT_NF4 ? kMaxWeight : kMaxWeight / 2))
     return false;
@@ -80,6 +81,14 @@ bool layer_ok(const qlora_layer* L) {
 }
 
 size_t up256(size_t x) { return (x + 255) & ~size_t(255); }
+
+bool grads_bf16(const qlora_layer* L) { return L->grad_dtype == QLORA_GRAD_BF16; }
+
+// zero [n] gradient values of the layer's gradient type
+hipError_t zero_grad(void* p, int64_t n, bool bf16, hipStream_t st) {
+  return bf16 ? launch_fill_zero_u16(static_cast<uint16_t*>(p), n, st)
+              : launch_fill_zero_f32(static_cast<float*>(p), n, st);
+}
 
 // Bump allocator over the caller's workspace.
 struct Carve {
@@ -173,10 +182,17 @@ size_t mlp_tiled_part_floats(int64_t M, int64_t H, int64_t I, int64_t r, int64_t
   return part;
 }
 
+// fp32 sums of the six adapter gradients over the tiles (used for bf16 gradients,
+// which are rounded once after the last tile): dA_g, dA_u [r, H], dA_d [r, I],
+// dB_g, dB_u [I, r], dB_d [H, r]
+size_t mlp_grad_acc_bytes(int64_t H, int64_t I, int64_t r) {
+  return 2 * up256(r * H * 4) + up256(r * I * 4) + 2 * up256(I * r * 4) + up256(H * r * 4);
+}
+
 size_t mlp_bwd_tiled_ws(int64_t M, int64_t H, int64_t I, int64_t r, int64_t tile) {
   const int64_t T = std::min(tile, M);
   return 5 * up256((size_t)T * I * 2) + up256(T * r * 2) + up256(T * 2 * r * 2) + up256(r * H * 2) +
-         2 * up256(r * I * 2) + up256(mlp_tiled_part_floats(M, H, I, r, tile) * 4);
+         2 * up256(r * I * 2) + up256(mlp_tiled_part_floats(M, H, I, r, tile) * 4) + mlp_grad_acc_bytes(H, I, r);
 }
 
 WSrc wsrc(const qlora_layer* L, const uint16_t* lora_i, const uint16_t* lora_j, int64_t ldj = 0) {
@@ -225,17 +241,19 @@ struct TnCall {
   float* part;
   const float* part_end;  // end of the partial region carved for this call
   hipStream_t st;
-  int accumulate = 0;  // add to the outputs instead of overwriting them
+  int accumulate = 0;  // add to the outputs instead of overwriting them (fp32 outputs)
+  bool out_bf16 = false;  // outputs are bf16 (rounded once from the fp32 sums)
   TnJobs jobs{};
   int rc = QLORA_OK;
   // out = s * P^T . Q (P [M, r] with row stride ldp, Q [M, Kd]); transposed -> [Kd, r]
-  void one(const uint16_t* P, int64_t ldp, int r, float s, const uint16_t* Q, int64_t M, int64_t Kd, float* out,
+  void one(const uint16_t* P, int64_t ldp, int r, float s, const uint16_t* Q, int64_t M, int64_t Kd, void* out,
            bool transposed) {
     two(P, ldp, r, s, out, 0, 0.f, nullptr, Q, M, Kd, transposed);
   }
   // rows j < r1 of P^T . Q into out1 (scale s1), rows r1 <= j < r1 + r2 into out2 (scale s2)
-  void two(const uint16_t* P, int64_t ldp, int r1, float s1, float* out1, int r2, float s2, float* out2,
+  void two(const uint16_t* P, int64_t ldp, int r1, float s1, void* out1, int r2, float s2, void* out2,
            const uint16_t* Q, int64_t M, int64_t Kd, bool transposed) {
+    const size_t es = out_bf16 ? 2 : 4;  // bytes per output element
     tn_chunks(r1, r2, [&](int c0, int a1, int a2) {
       // chunk columns [c0, c0 + a1 + a2) of P; a2 > 0 only for the single job covering both parts
       const bool in2 = c0 >= r1;
@@ -247,13 +265,14 @@ struct TnCall {
       a.s1 = in2 ? s2 : s1;
       a.s2 = s2;
       const int64_t jo = in2 ? c0 - r1 : c0;  // first output row of the chunk
-      float* o1 = in2 ? out2 : out1;
-      a.out1 = transposed ? o1 + jo : o1 + jo * Kd;
+      char* o1 = static_cast<char*>(in2 ? out2 : out1);
+      a.out1 = o1 + es * (transposed ? jo : jo * Kd);
       a.ldo1 = transposed ? (in2 ? r2 : r1) : Kd;
       a.out2 = out2 ? out2 : out1;
       a.ldo2 = transposed ? r2 : Kd;
       a.transposed = transposed ? 1 : 0;
       a.accumulate = accumulate;
+      a.out_bf16 = out_bf16 ? 1 : 0;
       a.Q = Q;
       a.M = M;
       a.Kd = Kd;
@@ -287,6 +306,7 @@ const char* qlora_status_string(int status) {
     case QLORA_EINVAL: return "invalid argument (shape, null or misaligned pointer)";
     case QLORA_EUNSUPPORTED: return "unsupported";
     case QLORA_EWORKSPACE: return "workspace missing or too small";
+    case QLORA_ENONFINITE: return "the weight holds Inf or NaN";
     case QLORA_EHIP: return g_err[0] ? g_err : "HIP error";
     default: return "unknown status";
   }
@@ -301,7 +321,32 @@ int qlora_quantize(int format, const float* W, int64_t N, int64_t K, uint8_t* co
   if (N * K == 0) return QLORA_OK;
   if (!W || !codes || !absmax || !aligned16(W) || !aligned16(codes)) return QLORA_EINVAL;
   hipStream_t st = (hipStream_t)stream;
-  QL_LAUNCH("quantize", st, launch_quantize(format, W, N, K, codes, absmax, nonfinite_blocks, st));
+  if (nonfinite_blocks) {
+    QL_LAUNCH("quantize", st, launch_quantize(format, W, N, K, codes, absmax, nonfinite_blocks, st));
+    return QLORA_OK;
+  }
+  uint32_t bad = 0;
+  QL_CHECK(quantize_counting(format, W, N, K, codes, absmax, &bad, st));
+  return bad ? QLORA_ENONFINITE : QLORA_OK;
+}
+
+int qlora_pack_codes(int format, const uint8_t* src_codes, const float* src_absmax, int64_t N, int64_t K,
+                     uint8_t* codes, float* absmax, void* stream) {
+  if (format < QLORA_FMT_NF4 || format > QLORA_FMT_FP8) return QLORA_EINVAL;
+  if (N < 0 || K < 0 || K % 64 != 0 || K > kMaxDim || N > kMaxDim) return QLORA_EINVAL;
+  if (N * K == 0) return QLORA_OK;
+  if (!src_codes || !src_absmax || !codes || !absmax) return QLORA_EINVAL;
+  if (!aligned16(src_codes) || !aligned16(src_absmax) || !aligned16(codes) || !aligned16(absmax)) return QLORA_EINVAL;
+  const size_t cb = (size_t)N * (format == QLORA_FMT_NF4 ? K / 2 : K), ab = (size_t)N * (K / 64) * 4;
+  auto overlap = [](const void* a, size_t na, const void* b, size_t nb) {
+    const char *pa = static_cast<const char*>(a), *pb = static_cast<const char*>(b);
+    return pa < pb + nb && pb < pa + na;
+  };
+  if (overlap(src_codes, cb, codes, cb) || overlap(src_absmax, ab, absmax, ab) || overlap(src_codes, cb, absmax, ab) ||
+      overlap(src_absmax, ab, codes, cb))
+    return QLORA_EINVAL;
+  hipStream_t st = (hipStream_t)stream;
+  QL_LAUNCH("pack_codes", st, launch_pack_codes(format, src_codes, src_absmax, N, K, codes, absmax, st));
   return QLORA_OK;
 }
 
@@ -343,7 +388,7 @@ int qlora_forward(const qlora_layer* L, const uint16_t* X, int64_t M, uint16_t* 
 }
 
 int qlora_backward(const qlora_layer* L, const uint16_t* dY, const uint16_t* X, const uint16_t* Z_save, int64_t M,
-                   uint16_t* dX, float* dA, float* dB, void* ws, size_t ws_bytes, void* stream) {
+                   uint16_t* dX, void* dA, void* dB, void* ws, size_t ws_bytes, void* stream) {
   if (!layer_ok(L) || M < 0) return QLORA_EINVAL;
   if (!dA || !dB || !aligned16(dA) || !aligned16(dB)) return QLORA_EINVAL;
   const int64_t K = L->K, N = L->N;
@@ -361,9 +406,10 @@ int qlora_backward(const qlora_layer* L, const uint16_t* dY, const uint16_t* X, 
   uint16_t* G = c.take<uint16_t>((size_t)M * r);
   float* part = c.take<float>(lay.part);
   if (!c.ok) return QLORA_EWORKSPACE;
+  const bool gb = grads_bf16(L);
   if (M == 0) {  // empty batch: gradients are zero
-    QL_LAUNCH("fill_zero_f32", st, launch_fill_zero_f32(dA, (int64_t)r * K, st));
-    QL_LAUNCH("fill_zero_f32", st, launch_fill_zero_f32(dB, (int64_t)N * r, st));
+    QL_LAUNCH("fill_zero", st, zero_grad(dA, (int64_t)r * K, gb, st));
+    QL_LAUNCH("fill_zero", st, zero_grad(dB, (int64_t)N * r, gb, st));
     return QLORA_OK;
   }
   if (!b_in_place(r)) {
@@ -375,6 +421,7 @@ int qlora_backward(const qlora_layer* L, const uint16_t* dY, const uint16_t* X, 
   // G = dY.B ; dB = s.dY^T.Z (written transposed from Z^T.dY) and dA = s.G^T.X in one pair of launches ; dX
   QL_LAUNCH("skinny_nt", st, launch_skinny_nt(ntB(dY, M, N, L->B, Bt, r, G, r), st));
   TnCall tn{part, part + lay.part, st};
+  tn.out_bf16 = gb;
   tn.one(Z_save, r, r, L->s, dY, M, N, dB, true);
   tn.one(G, r, r, L->s, X, M, K, dA, false);
   if (int rc = tn.flush()) return rc;
@@ -387,6 +434,7 @@ static bool mlp_shapes_ok(const qlora_layer* g, const qlora_layer* u, const qlor
   if (g->K != u->K || g->N != u->N || d->K != g->N || d->N != g->K) return false;
   if (g->r != u->r || g->r != d->r) return false;
   if (g->format != u->format || g->format != d->format) return false;
+  if (g->grad_dtype != u->grad_dtype || g->grad_dtype != d->grad_dtype) return false;
   return true;
 }
 
@@ -446,12 +494,12 @@ MlpBwdWs carve_mlp_bwd(Carve& c, int64_t M, int64_t H, int64_t I, int64_t r, siz
   return w;
 }
 
-int mlp_zero_grads(const qlora_layer* gate, const qlora_layer* up, const qlora_layer* down, float* const dA[3],
-                   float* const dB[3], hipStream_t st) {
+int mlp_zero_grads(const qlora_layer* gate, const qlora_layer* up, const qlora_layer* down, void* const dA[3],
+                   void* const dB[3], hipStream_t st) {
   const qlora_layer* Ls[3] = {gate, up, down};
   for (int i = 0; i < 3; ++i) {
-    QL_LAUNCH("fill_zero_f32", st, launch_fill_zero_f32(dA[i], Ls[i]->r * Ls[i]->K, st));
-    QL_LAUNCH("fill_zero_f32", st, launch_fill_zero_f32(dB[i], Ls[i]->N * Ls[i]->r, st));
+    QL_LAUNCH("fill_zero", st, zero_grad(dA[i], Ls[i]->r * Ls[i]->K, grads_bf16(Ls[i]), st));
+    QL_LAUNCH("fill_zero", st, zero_grad(dB[i], Ls[i]->N * Ls[i]->r, grads_bf16(Ls[i]), st));
   }
   return QLORA_OK;
 }
@@ -473,13 +521,14 @@ int mlp_prep(const qlora_layer* gate, const qlora_layer* up, const qlora_layer* 
 // the adapter gradients to dA/dB (later tiles of a batch).
 int mlp_bwd_body(const qlora_layer* gate, const qlora_layer* up, const qlora_layer* down, const uint16_t* dY,
                  const uint16_t* X, const uint16_t* g, const uint16_t* u, const uint16_t* h, const uint16_t* Zg,
-                 const uint16_t* Zu, const uint16_t* Zd, int64_t M, uint16_t* dX, float* const dA[3],
-                 float* const dB[3], const MlpBwdWs& w, int accumulate, hipStream_t st) {
+                 const uint16_t* Zu, const uint16_t* Zd, int64_t M, uint16_t* dX, void* const dA[3],
+                 void* const dB[3], const MlpBwdWs& w, int accumulate, bool out_bf16, hipStream_t st) {
   const int64_t H = gate->K, I = gate->N;
   const int r = (int)gate->r;
   uint16_t* Gg = w.Ggu;
   uint16_t* Gu = w.Ggu + r;
   TnCall tn{w.part, w.part + w.part_floats, st, accumulate};
+  tn.out_bf16 = out_bf16;
   // down projection: G_d = dY.B_d ; dB_d = s.dY^T.Z_d and dA_d = s.G_d^T.h ; dh -> (dg, du) in the GEMM epilogue
   QL_LAUNCH("skinny_nt", st, launch_skinny_nt(ntB(dY, M, H, down->B, w.Btd, r, w.Gd, r), st));
   tn.one(Zd, r, r, down->s, dY, M, H, dB[2], true);
@@ -503,7 +552,7 @@ int mlp_bwd_body(const qlora_layer* gate, const qlora_layer* up, const qlora_lay
   return QLORA_OK;
 }
 
-bool mlp_grads_ok(float* const dA[3], float* const dB[3]) {
+bool mlp_grads_ok(void* const dA[3], void* const dB[3]) {
   if (!dA || !dB) return false;
   for (int i = 0; i < 3; ++i)
     if (!dA[i] || !dB[i] || !aligned16(dA[i]) || !aligned16(dB[i])) return false;
@@ -532,7 +581,7 @@ int swiglu_mlp_forward(const qlora_layer* gate, const qlora_layer* up, const qlo
 
 int swiglu_mlp_backward(const qlora_layer* gate, const qlora_layer* up, const qlora_layer* down, const uint16_t* dY,
                         const uint16_t* X, const uint16_t* g_save, const uint16_t* u_save, const uint16_t* h_save,
-                        const uint16_t* Z_save, int64_t M, uint16_t* dX, float* const dA[3], float* const dB[3],
+                        const uint16_t* Z_save, int64_t M, uint16_t* dX, void* const dA[3], void* const dB[3],
                         void* ws, size_t ws_bytes, void* stream) {
   if (!mlp_shapes_ok(gate, up, down) || M < 0 || !mlp_grads_ok(dA, dB)) return QLORA_EINVAL;
   const int64_t H = gate->K, I = gate->N, r = gate->r;
@@ -551,7 +600,7 @@ int swiglu_mlp_backward(const qlora_layer* gate, const qlora_layer* up, const ql
   if (int rc = mlp_prep(gate, up, down, w, st)) return rc;
   const size_t Mr = (size_t)M * r;
   return mlp_bwd_body(gate, up, down, dY, X, g_save, u_save, h_save, Z_save, Z_save + Mr, Z_save + 2 * Mr, M, dX,
-                      dA, dB, w, 0, st);
+                      dA, dB, w, 0, grads_bf16(gate), st);
 }
 
 size_t swiglu_mlp_tiled_workspace_size(int backward, int64_t M, int64_t H, int64_t I, int64_t r, int64_t tile) {
@@ -586,7 +635,7 @@ int swiglu_mlp_forward_tiled(const qlora_layer* gate, const qlora_layer* up, con
 
 int swiglu_mlp_backward_tiled(const qlora_layer* gate, const qlora_layer* up, const qlora_layer* down,
                               const uint16_t* dY, const uint16_t* X, const uint16_t* Z_save, int64_t M, int64_t tile,
-                              uint16_t* dX, float* const dA[3], float* const dB[3], void* ws, size_t ws_bytes,
+                              uint16_t* dX, void* const dA[3], void* const dB[3], void* ws, size_t ws_bytes,
                               void* stream) {
   if (!mlp_shapes_ok(gate, up, down) || M < 0 || tile < 1 || !mlp_grads_ok(dA, dB)) return QLORA_EINVAL;
   const int64_t H = gate->K, I = gate->N, r = gate->r;
@@ -602,9 +651,20 @@ int swiglu_mlp_backward_tiled(const qlora_layer* gate, const qlora_layer* up, co
   uint16_t* u = c.take<uint16_t>((size_t)T * I);
   uint16_t* h = c.take<uint16_t>((size_t)T * I);
   const MlpBwdWs w = carve_mlp_bwd(c, T, H, I, r, mlp_tiled_part_floats(M, H, I, r, tile));
+  // bf16 gradients: the tiles add into fp32 sums, rounded once at the end
+  const bool gb = grads_bf16(gate);
+  const qlora_layer* Ls[3] = {gate, up, down};
+  void* accA[3];
+  void* accB[3];
+  for (int i = 0; i < 3; ++i) {
+    accA[i] = c.take<float>((size_t)Ls[i]->r * Ls[i]->K);
+    accB[i] = c.take<float>((size_t)Ls[i]->N * Ls[i]->r);
+  }
   if (!c.ok) return QLORA_EWORKSPACE;
   if (M == 0) return mlp_zero_grads(gate, up, down, dA, dB, st);
   if (int rc = mlp_prep(gate, up, down, w, st)) return rc;
+  void* const* oA = gb ? accA : dA;
+  void* const* oB = gb ? accB : dB;
   const size_t Mr = (size_t)M * r;
   for (int64_t t0 = 0; t0 < M; t0 += T) {
     const int64_t Mt = std::min(T, M - t0);
@@ -614,8 +674,16 @@ int swiglu_mlp_backward_tiled(const qlora_layer* gate, const qlora_layer* up, co
     QL_LAUNCH("gemm_fwd_gateup", st,
               launch_gemm_fwd_gateup(Xt, Mt, H, I, wsrc(gate, gate->B, Zt), wsrc(up, up->B, Zt + Mr), g, u, h, st));
     if (int rc = mlp_bwd_body(gate, up, down, dY + t0 * H, Xt, g, u, h, Zt, Zt + Mr, Zt + 2 * Mr, Mt,
-                              dX ? dX + t0 * H : nullptr, dA, dB, w, t0 > 0 ? 1 : 0, st))
+                              dX ? dX + t0 * H : nullptr, oA, oB, w, t0 > 0 ? 1 : 0, false, st))
       return rc;
+  }
+  if (gb) {
+    CastJobs cj{};
+    for (int i = 0; i < 3; ++i) {
+      cj.job[cj.n++] = {static_cast<const float*>(accA[i]), static_cast<uint16_t*>(dA[i]), Ls[i]->r * Ls[i]->K};
+      cj.job[cj.n++] = {static_cast<const float*>(accB[i]), static_cast<uint16_t*>(dB[i]), Ls[i]->N * Ls[i]->r};
+    }
+    QL_LAUNCH("cast_bf16", st, launch_cast_bf16(cj, st));
   }
   return QLORA_OK;
 }

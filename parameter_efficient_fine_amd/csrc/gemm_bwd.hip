@@ -720,7 +720,6 @@ void k_qgemm_bwd8(BwdArgs p) {
 
 template <int MODE, int RP, bool ALIGNED>
 hipError_t launch_rp(const BwdArgs& a, hipStream_t st) {
-  static bool attr_done = false;
   // The 8-wave kernel (measured 3-7% faster than the 4-wave one for every
   // mode), except at rank 256 with two sources, whose rank term does not fit
   // its 256 registers per lane.
@@ -730,11 +729,10 @@ hipError_t launch_rp(const BwdArgs& a, hipStream_t st) {
     kfn = (const void*)k_qgemm_bwd8<kFmt, MODE, RP, ALIGNED>;
   else
     kfn = (const void*)k_qgemm_bwd<kFmt, MODE, RP, ALIGNED>;
-  if (!attr_done) {
-    hipError_t e = hipFuncSetAttribute(kfn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)kLds);
-    if (e != hipSuccess) return e;
-    attr_done = true;
-  }
+  // set once per kernel instance; a function-local static is initialised exactly
+  // once even when several threads make their first call together
+  static const hipError_t attr = hipFuncSetAttribute(kfn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)kLds);
+  if (attr != hipSuccess) return attr;
   const int64_t nI = (a.K + 255) / 256, nJ = (a.M + kTok - 1) / kTok;
   if (nI * nJ == 0) return hipSuccess;
   if constexpr (k8)

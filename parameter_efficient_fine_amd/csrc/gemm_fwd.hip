@@ -337,13 +337,11 @@ void k_qgemm_fwd(FwdArgs p) {
 
 template <bool GATEUP, int RP, bool ALIGNED>
 hipError_t launch_rp(const FwdArgs& a, hipStream_t st) {
-  static bool attr_done = false;
-  if (!attr_done) {
-    hipError_t e = hipFuncSetAttribute((const void*)k_qgemm_fwd<kFmt, GATEUP, RP, ALIGNED>,
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)kLds);
-    if (e != hipSuccess) return e;
-    attr_done = true;
-  }
+  // set once per kernel instance; a function-local static is initialised exactly
+  // once even when several threads make their first call together
+  static const hipError_t attr = hipFuncSetAttribute((const void*)k_qgemm_fwd<kFmt, GATEUP, RP, ALIGNED>,
+                                                     hipFuncAttributeMaxDynamicSharedMemorySize, (int)kLds);
+  if (attr != hipSuccess) return attr;
   const int64_t ipt = GATEUP ? 128 : 256;
   const int64_t nI = (a.N + ipt - 1) / ipt, nJ = (a.M + kTok - 1) / kTok;
   if (nI * nJ == 0) return hipSuccess;

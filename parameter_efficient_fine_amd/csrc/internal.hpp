@@ -11,6 +11,14 @@ hipError_t launch_quantize(int fmt, const float* W, int64_t N, int64_t K, uint8_
                            uint32_t* nonfinite_blocks, hipStream_t st);
 hipError_t launch_dequantize(int fmt, const uint8_t* codes, const float* absmax, int64_t N, int64_t K, float* W_hat,
                              hipStream_t st);
+// launch_quantize with a per-device counter of non-finite blocks, read back
+// into *nonfinite_out (synchronizes `st`; calls are serialized)
+hipError_t quantize_counting(int fmt, const float* W, int64_t N, int64_t K, uint8_t* codes, float* absmax,
+                             uint32_t* nonfinite_out, hipStream_t st);
+// checkpoint-order codes (row-major; NF4 column 2c in the low nibble of byte c)
+// and row-major block values -> the storage order of the GEMMs
+hipError_t launch_pack_codes(int fmt, const uint8_t* src, const float* src_abs, int64_t N, int64_t K, uint8_t* codes,
+                             float* absmax, hipStream_t st);
 
 // Skinny rank-r products ------------------------------------------------------
 
@@ -33,7 +41,8 @@ hipError_t launch_skinny_nt(const NtArgs& a, hipStream_t st);
 // Reduction over M of P[M, R]^T . Q[M, Kd] (P row stride ldp, R = r1 + r2 <=
 // kTnMaxR): rows j < r1 give s1 * (..) into out1, the others s2 * (..) into
 // out2 (j counted from r1). Element (j, k) goes to out[j * ldo + k], or to
-// out[k * ldo + j] when transposed; fp32. launch_skinny_tn splits the rows
+// out[k * ldo + j] when transposed; fp32, or bf16 (one rounding of the fp32
+// sum) when out_bf16. launch_skinny_tn splits the rows
 // over workgroups that write fp32 partials to `part`; launch_tn_reduce (next
 // on the same stream) adds them in split order and writes out1/out2.
 constexpr int kTnMaxR = 128;
@@ -48,11 +57,12 @@ struct TnArgs {
   int64_t ldp;
   int r1, r2;
   float s1, s2;
-  float* out1;
-  float* out2;
+  void* out1;           // float, or bf16 bits when out_bf16
+  void* out2;
   int64_t ldo1, ldo2;
   int transposed;
-  int accumulate;       // 1: add the result to what out1/out2 hold (sums over batch tiles)
+  int accumulate;       // 1: add the result to what out1/out2 hold (sums over batch tiles; fp32 only)
+  int out_bf16;
   const uint16_t* Q;
   int64_t M, Kd;
   float* part;          // [splits, R, Kd]
@@ -84,6 +94,20 @@ hipError_t launch_prep(const PrepJobs& jobs, hipStream_t st);
 
 // p[0..n) = 0 (a kernel, so the call stays capturable in a graph)
 hipError_t launch_fill_zero_f32(float* p, int64_t n, hipStream_t st);
+hipError_t launch_fill_zero_u16(uint16_t* p, int64_t n, hipStream_t st);
+
+// dst[i] = bf16(src[i]) (round to nearest even) for up to kMaxCastJobs arrays in one launch
+constexpr int kMaxCastJobs = 6;
+struct CastJob {
+  const float* src;
+  uint16_t* dst;
+  int64_t n;
+};
+struct CastJobs {
+  CastJob job[kMaxCastJobs];
+  int n;
+};
+hipError_t launch_cast_bf16(const CastJobs& jobs, hipStream_t st);
 
 // Fused dequant GEMMs -------------------------------------------------------
 struct WSrc {           // one frozen quantized weight [N, K] with its LoRA pair

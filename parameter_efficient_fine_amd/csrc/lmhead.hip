@@ -382,13 +382,11 @@ __global__ __launch_bounds__(256) void k_tile_nt(const uint16_t* __restrict__ sr
 
 template <bool OUT_F32>
 hipError_t launch_nt(const NtGemmArgs& a, hipStream_t st) {
-  static bool attr_done = false;
-  if (!attr_done) {
-    hipError_t e =
-        hipFuncSetAttribute((const void*)k_gemm_nt<OUT_F32>, hipFuncAttributeMaxDynamicSharedMemorySize, (int)kLds);
-    if (e != hipSuccess) return e;
-    attr_done = true;
-  }
+  // set once per kernel instance; a function-local static is initialised exactly
+  // once even when several threads make their first call together
+  static const hipError_t attr =
+      hipFuncSetAttribute((const void*)k_gemm_nt<OUT_F32>, hipFuncAttributeMaxDynamicSharedMemorySize, (int)kLds);
+  if (attr != hipSuccess) return attr;
   const int64_t nI = (a.N + 255) / 256, nJ = (a.M + kTok - 1) / kTok;
   if (nI * nJ == 0) return hipSuccess;
   k_gemm_nt<OUT_F32><<<(unsigned)(nI * nJ), 256, kLds, st>>>(a);

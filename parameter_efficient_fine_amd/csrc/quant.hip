@@ -11,6 +11,8 @@
 // 8j+b+4 in its high nibble, the order the GEMMs' dequantizer reads.
 // Storage order of rows and blocks (all formats): tile-major, see TileAddr in
 // common.hpp.
+#include <mutex>
+
 #include "common.hpp"
 #include "internal.hpp"
 
@@ -176,6 +178,51 @@ __global__ __launch_bounds__(256) void k_dequantize8(const uint8_t* __restrict__
   reinterpret_cast<f32x4*>(W_hat)[i] = wdeq4_f32<F>(x, p);
 }
 
+// ---------------------------------------------------------------------------
+// Checkpoint order -> this library's order. A 4-bit checkpoint stores codes
+// row-major [N, K/2] with column 2c in the low and 2c+1 in the high nibble of
+// byte c, and its fp32 absmax row-major [N, K/64]; the 8-bit formats store one
+// byte per column, row-major [N, K]. One thread per 4 code bytes (NF4: a run
+// of 8 columns, whose nibbles are re-paired column b with b+4; 8-bit: 4
+// columns, copied); the first thread of each (row, block) moves its value.
+template <int F>
+__global__ __launch_bounds__(256) void k_pack_codes(const uint8_t* __restrict__ src, const float* __restrict__ src_abs,
+                                                    int64_t nquads, int64_t N, int64_t K, uint8_t* __restrict__ codes,
+                                                    float* __restrict__ absmax) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= nquads) return;
+  constexpr int64_t kBB = F == kNF4 ? kBlock / 2 : kBlock;  // code bytes per row and block
+  const int64_t row_bytes = F == kNF4 ? K / 2 : K;
+  const int64_t n = (4 * i) / row_bytes, byte = 4 * i - n * row_bytes;
+  const int64_t b = byte / kBB;
+  const TileAddr ta(n, b, N, K);
+  uint32_t x = *reinterpret_cast<const uint32_t*>(src + 4 * i);
+  if constexpr (F == kNF4) {
+    uint32_t c[8];  // columns 8j .. 8j+7 of this run
+#pragma unroll
+    for (int e = 0; e < 8; ++e) c[e] = (x >> (4 * e)) & 15u;
+    x = 0;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) x |= (c[q] | (c[q + 4] << 4)) << (8 * q);
+  }
+  *reinterpret_cast<uint32_t*>(codes + ta.code(kBB) + byte % kBB) = x;
+  if (byte % kBB == 0) absmax[ta.value()] = src_abs[n * (K / kBlock) + b];
+}
+
+hipError_t launch_pack_codes(int fmt, const uint8_t* src, const float* src_abs, int64_t N, int64_t K, uint8_t* codes,
+                             float* absmax, hipStream_t st) {
+  const int64_t nquads = N * (fmt == kNF4 ? K / 2 : K) / 4;
+  if (nquads == 0) return hipSuccess;
+  const unsigned grid = (unsigned)((nquads + 255) / 256);
+  if (fmt == kNF4)
+    k_pack_codes<kNF4><<<grid, 256, 0, st>>>(src, src_abs, nquads, N, K, codes, absmax);
+  else if (fmt == kInt8)
+    k_pack_codes<kInt8><<<grid, 256, 0, st>>>(src, src_abs, nquads, N, K, codes, absmax);
+  else
+    k_pack_codes<kFp8><<<grid, 256, 0, st>>>(src, src_abs, nquads, N, K, codes, absmax);
+  return hipGetLastError();
+}
+
 hipError_t launch_quantize(int fmt, const float* W, int64_t N, int64_t K, uint8_t* codes, float* absmax,
                            uint32_t* nonfinite_blocks, hipStream_t st) {
   if (nonfinite_blocks) {
@@ -209,6 +256,41 @@ hipError_t launch_dequantize(int fmt, const uint8_t* codes, const float* absmax,
   else
     k_dequantize8<kFp8><<<grid, 256, 0, st>>>(codes, absmax, nquads, N, K, W_hat);
   return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// Synchronous quantization that reports non-finite blocks: a counter in device
+// memory of this code object (one per GPU, its address looked up once per
+// device), zeroed by the quantizer's launch and read back after it. Calls are
+// serialized, since every call on a device shares its counter.
+
+namespace {
+__device__ uint32_t g_nonfinite_count;
+std::mutex g_count_mu;
+constexpr int kMaxDevices = 64;
+uint32_t* g_count_ptr[kMaxDevices];
+}  // namespace
+
+hipError_t quantize_counting(int fmt, const float* W, int64_t N, int64_t K, uint8_t* codes, float* absmax,
+                             uint32_t* nonfinite_out, hipStream_t st) {
+  std::lock_guard<std::mutex> lock(g_count_mu);
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  if (!g_count_ptr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(g_nonfinite_count));
+    if (e != hipSuccess) return e;
+    g_count_ptr[dev] = static_cast<uint32_t*>(p);
+  }
+  e = launch_quantize(fmt, W, N, K, codes, absmax, g_count_ptr[dev], st);
+  if (e != hipSuccess) return e;
+  uint32_t host = 0;
+  e = hipMemcpyAsync(&host, g_count_ptr[dev], sizeof(host), hipMemcpyDeviceToHost, st);
+  if (e == hipSuccess) e = hipStreamSynchronize(st);
+  *nonfinite_out = host;
+  return e;
 }
 
 }  // namespace qlora

@@ -487,18 +487,29 @@ __global__ __launch_bounds__(64) void k_tn_reduce(TnJobs jobs) {
   for (; sp < p.splits; ++sp) sum += *reinterpret_cast<const f32x4*>(src + (int64_t)sp * sstride);
   const bool first = j < p.r1;
   const float s = first ? p.s1 : p.s2;
-  float* out = first ? p.out1 : p.out2;
+  void* out = first ? p.out1 : p.out2;
   const int64_t jr = first ? j : j - p.r1;
   const int64_t ldo = first ? p.ldo1 : p.ldo2;
   sum *= s;
+  if (p.out_bf16) {  // one rounding of the fp32 sum (no accumulation in bf16)
+    uint16_t* ob = static_cast<uint16_t*>(out);
+    if (p.transposed) {
+#pragma unroll
+      for (int c = 0; c < 4; ++c) ob[(k + c) * ldo + jr] = __builtin_bit_cast(uint16_t, (__bf16)sum[c]);
+    } else {
+      *reinterpret_cast<u32x2*>(ob + jr * ldo + k) = u32x2{pack_bf16x2(sum[0], sum[1]), pack_bf16x2(sum[2], sum[3])};
+    }
+    return;
+  }
+  float* of = static_cast<float*>(out);
   if (p.transposed) {
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
-      float* o = out + (k + c) * ldo + jr;
+      float* o = of + (k + c) * ldo + jr;
       *o = p.accumulate ? *o + sum[c] : sum[c];
     }
   } else {
-    f32x4* o = reinterpret_cast<f32x4*>(out + jr * ldo + k);
+    f32x4* o = reinterpret_cast<f32x4*>(of + jr * ldo + k);
     *o = p.accumulate ? *o + sum : sum;
   }
 }
@@ -588,6 +599,33 @@ __global__ __launch_bounds__(256) void k_fill_zero_f32(float* __restrict__ p, in
 hipError_t launch_fill_zero_f32(float* p, int64_t n, hipStream_t st) {
   if (n == 0) return hipSuccess;
   k_fill_zero_f32<<<(unsigned)((n + 255) / 256), 256, 0, st>>>(p, n);
+  return hipGetLastError();
+}
+
+__global__ __launch_bounds__(256) void k_fill_zero_u16(uint16_t* __restrict__ p, int64_t n) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i < n) p[i] = 0;
+}
+
+hipError_t launch_fill_zero_u16(uint16_t* p, int64_t n, hipStream_t st) {
+  if (n == 0) return hipSuccess;
+  k_fill_zero_u16<<<(unsigned)((n + 255) / 256), 256, 0, st>>>(p, n);
+  return hipGetLastError();
+}
+
+// bf16 copies of fp32 arrays (blockIdx.y selects the array)
+__global__ __launch_bounds__(256) void k_cast_bf16(CastJobs jobs) {
+  const CastJob& j = jobs.job[blockIdx.y];
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i < j.n) j.dst[i] = __builtin_bit_cast(uint16_t, (__bf16)j.src[i]);
+}
+
+hipError_t launch_cast_bf16(const CastJobs& jobs, hipStream_t st) {
+  if (jobs.n < 1 || jobs.n > kMaxCastJobs) return hipErrorInvalidValue;
+  int64_t nmax = 0;
+  for (int i = 0; i < jobs.n; ++i) nmax = jobs.job[i].n > nmax ? jobs.job[i].n : nmax;
+  if (nmax == 0) return hipSuccess;
+  k_cast_bf16<<<dim3((unsigned)((nmax + 255) / 256), (unsigned)jobs.n), 256, 0, st>>>(jobs);
   return hipGetLastError();
 }
 

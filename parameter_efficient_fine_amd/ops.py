@@ -23,8 +23,20 @@ def _stream():
 
 
 def _need(t, dtype, shape, name):
+    if t is None:
+        raise ValueError(f"{name}: expected contiguous {dtype} {tuple(shape)} on GPU, got None")
     if t.dtype != dtype or tuple(t.shape) != tuple(shape) or not t.is_contiguous() or not t.is_cuda:
         raise ValueError(f"{name}: expected contiguous {dtype} {tuple(shape)} on GPU, got {t.dtype} {tuple(t.shape)}")
+
+
+def _need_ws(ws, nbytes: int, name="ws"):
+    if ws.dtype != torch.uint8 or ws.dim() != 1 or not ws.is_contiguous() or not ws.is_cuda:
+        raise ValueError(f"{name}: expected a contiguous 1-D uint8 GPU tensor")
+    if ws.numel() < nbytes:
+        raise ValueError(f"{name}: {ws.numel()} bytes, the call needs {nbytes}")
+
+
+_GRAD_CODE = {torch.bfloat16: C.GRAD_BF16, torch.float32: C.GRAD_F32}
 
 
 @dataclass
@@ -36,6 +48,7 @@ class QLoraLayer:
     B: torch.Tensor       # bfloat16 [N, r]
     s: float
     fmt: int = C.FMT_NF4
+    grad_dtype: torch.dtype = torch.bfloat16  # dtype of dA, dB (bfloat16 or float32)
 
     @property
     def K(self):
@@ -55,8 +68,10 @@ class QLoraLayer:
         _need(self.absmax, torch.float32, (N, K // 64), "absmax")
         _need(self.A, torch.bfloat16, (r, K), "A")
         _need(self.B, torch.bfloat16, (N, r), "B")
+        if self.grad_dtype not in _GRAD_CODE:
+            raise ValueError(f"grad_dtype must be torch.bfloat16 or torch.float32, got {self.grad_dtype}")
         return C.QLoraLayerC(self.codes.data_ptr(), self.absmax.data_ptr(), self.A.data_ptr(), self.B.data_ptr(),
-                             K, N, r, float(self.s), int(self.fmt))
+                             K, N, r, float(self.s), int(self.fmt), _GRAD_CODE[self.grad_dtype])
 
 
 def quantize(W: torch.Tensor, fmt: int = C.FMT_NF4):
@@ -71,6 +86,33 @@ def quantize(W: torch.Tensor, fmt: int = C.FMT_NF4):
                                                      _stream()))
     if int(bad.item()) != 0:
         raise ValueError(f"qlora_quantize: {int(bad.item())} block(s) hold non-finite weights")
+    return codes, absmax
+
+
+def quantize_sync(W: torch.Tensor, fmt: int = C.FMT_NF4):
+    """As quantize, through the synchronous form of qlora_quantize (no counter passed:
+    the call waits for the stream and reports non-finite weights as QLORA_ENONFINITE,
+    raised here as QLoraError)."""
+    N, K = W.shape
+    _need(W, torch.float32, (N, K), "W")
+    codes = torch.empty((N, K // 2 if fmt == C.FMT_NF4 else K), dtype=torch.uint8, device=W.device)
+    absmax = torch.empty((N, K // 64), dtype=torch.float32, device=W.device)
+    C.check("qlora_quantize", C.lib().qlora_quantize(fmt, _ptr(W), N, K, _ptr(codes), _ptr(absmax), None,
+                                                     _stream()))
+    return codes, absmax
+
+
+def pack_codes(codes_rowmajor: torch.Tensor, absmax_rowmajor: torch.Tensor, fmt: int = C.FMT_NF4):
+    """Codes and block values in checkpoint order (row-major; NF4 column 2c in the low nibble
+    of byte c) -> this library's storage order: (codes, absmax) of the same shapes."""
+    N, KC = codes_rowmajor.shape
+    K = 2 * KC if fmt == C.FMT_NF4 else KC
+    _need(codes_rowmajor, torch.uint8, (N, KC), "codes_rowmajor")
+    _need(absmax_rowmajor, torch.float32, (N, K // 64), "absmax_rowmajor")
+    codes = torch.empty_like(codes_rowmajor)
+    absmax = torch.empty_like(absmax_rowmajor)
+    C.check("qlora_pack_codes", C.lib().qlora_pack_codes(fmt, _ptr(codes_rowmajor), _ptr(absmax_rowmajor), N, K,
+                                                         _ptr(codes), _ptr(absmax), _stream()))
     return codes, absmax
 
 
@@ -99,6 +141,8 @@ def forward(L: QLoraLayer, X: torch.Tensor, Y=None, Z=None):
     _need(X, torch.bfloat16, (M, L.K), "X")
     Y = torch.empty((M, L.N), dtype=torch.bfloat16, device=X.device) if Y is None else Y
     Z = torch.empty((M, L.r), dtype=torch.bfloat16, device=X.device) if Z is None else Z
+    _need(Y, torch.bfloat16, (M, L.N), "Y")
+    _need(Z, torch.bfloat16, (M, L.r), "Z")
     lc = L.c()
     C.check("qlora_forward", C.lib().qlora_forward(ctypes.byref(lc), _ptr(X), M, _ptr(Y), _ptr(Z), None, 0,
                                                    _stream()))
@@ -106,20 +150,26 @@ def forward(L: QLoraLayer, X: torch.Tensor, Y=None, Z=None):
 
 
 def backward(L: QLoraLayer, dY, X, Z, need_dX=True, ws=None, out=None):
-    """(dX bf16 [M,K] or None, dA fp32 [r,K], dB fp32 [N,r])."""
+    """(dX bf16 [M,K] or None, dA [r,K], dB [N,r]; dA, dB in L.grad_dtype)."""
     M = X.shape[0]
     _need(dY, torch.bfloat16, (M, L.N), "dY")
     _need(X, torch.bfloat16, (M, L.K), "X")
     _need(Z, torch.bfloat16, (M, L.r), "Z")
     dev = X.device
+    gd = L.grad_dtype
     if out is None:
         dX = torch.empty((M, L.K), dtype=torch.bfloat16, device=dev) if need_dX else None
-        dA = torch.empty((L.r, L.K), dtype=torch.float32, device=dev)
-        dB = torch.empty((L.N, L.r), dtype=torch.float32, device=dev)
+        dA = torch.empty((L.r, L.K), dtype=gd, device=dev)
+        dB = torch.empty((L.N, L.r), dtype=gd, device=dev)
     else:
         dX, dA, dB = out
+    if dX is not None:
+        _need(dX, torch.bfloat16, (M, L.K), "dX")
+    _need(dA, gd, (L.r, L.K), "dA")
+    _need(dB, gd, (L.N, L.r), "dB")
     nb = workspace_size(C.OP_BACKWARD, M, L.K, L.N, L.r)
     ws = _workspace(nb, dev) if ws is None else ws
+    _need_ws(ws, nb)
     lc = L.c()
     C.check("qlora_backward", C.lib().qlora_backward(ctypes.byref(lc), _ptr(dY), _ptr(X), _ptr(Z), M, _ptr(dX),
                                                      _ptr(dA), _ptr(dB), _ptr(ws), ws.numel(), _stream()))
@@ -138,6 +188,7 @@ def mlp_forward(gate: QLoraLayer, up: QLoraLayer, down: QLoraLayer, X, out=None)
                    u=torch.empty((M, I), dtype=torch.bfloat16, device=dev),
                    h=torch.empty((M, I), dtype=torch.bfloat16, device=dev),
                    Z=torch.empty((3, M, r), dtype=torch.bfloat16, device=dev))
+    _need_saved(out, M, H, I, r, ("Y", "g", "u", "h"))
     lg, lu, ld = gate.c(), up.c(), down.c()
     C.check("swiglu_mlp_forward", C.lib().swiglu_mlp_forward(
         ctypes.byref(lg), ctypes.byref(lu), ctypes.byref(ld), _ptr(X), M, _ptr(out["Y"]), _ptr(out["g"]),
@@ -145,18 +196,42 @@ def mlp_forward(gate: QLoraLayer, up: QLoraLayer, down: QLoraLayer, X, out=None)
     return out
 
 
+def _need_saved(t: dict, M, H, I, r, keys):
+    shapes = dict(Y=(M, H), g=(M, I), u=(M, I), h=(M, I))
+    for k in keys:
+        _need(t[k], torch.bfloat16, shapes[k], k)
+    _need(t["Z"], torch.bfloat16, (3, M, r), "Z")
+
+
+def _grads_out(layers, out, M, H, dev, need_dX):
+    """Adapter-gradient outputs of a SwiGLU backward (allocated, or the caller's, checked)."""
+    gd = layers[0].grad_dtype
+    if any(L.grad_dtype != gd for L in layers):
+        raise ValueError("the three layers of a SwiGLU block share one grad_dtype")
+    if out is None:
+        out = dict(dX=torch.empty((M, H), dtype=torch.bfloat16, device=dev) if need_dX else None,
+                   dA=[torch.empty((L.r, L.K), dtype=gd, device=dev) for L in layers],
+                   dB=[torch.empty((L.N, L.r), dtype=gd, device=dev) for L in layers])
+    if out["dX"] is not None:
+        _need(out["dX"], torch.bfloat16, (M, H), "dX")
+    for i, L in enumerate(layers):
+        _need(out["dA"][i], gd, (L.r, L.K), f"dA[{i}]")
+        _need(out["dB"][i], gd, (L.N, L.r), f"dB[{i}]")
+    return out
+
+
 def mlp_backward(gate: QLoraLayer, up: QLoraLayer, down: QLoraLayer, dY, X, saved, need_dX=True, ws=None, out=None):
-    """dict(dX, dA=[gate, up, down] fp32, dB=[...] fp32)."""
+    """dict(dX, dA=[gate, up, down], dB=[...]) with dA, dB in the layers' grad_dtype."""
     M = X.shape[0]
     H, I, r = gate.K, gate.N, gate.r
     _need(dY, torch.bfloat16, (M, H), "dY")
+    _need(X, torch.bfloat16, (M, H), "X")
+    _need_saved(saved, M, H, I, r, ("g", "u", "h"))
     dev = X.device
-    if out is None:
-        out = dict(dX=torch.empty((M, H), dtype=torch.bfloat16, device=dev) if need_dX else None,
-                   dA=[torch.empty((r, L.K), dtype=torch.float32, device=dev) for L in (gate, up, down)],
-                   dB=[torch.empty((L.N, r), dtype=torch.float32, device=dev) for L in (gate, up, down)])
+    out = _grads_out((gate, up, down), out, M, H, dev, need_dX)
     nb = workspace_size(C.OP_MLP_BACKWARD, M, H, I, r)
     ws = _workspace(nb, dev) if ws is None else ws
+    _need_ws(ws, nb)
     dA = (ctypes.c_void_p * 3)(*[t.data_ptr() for t in out["dA"]])
     dB = (ctypes.c_void_p * 3)(*[t.data_ptr() for t in out["dB"]])
     lg, lu, ld = gate.c(), up.c(), down.c()
@@ -179,8 +254,10 @@ def mlp_forward_tiled(gate: QLoraLayer, up: QLoraLayer, down: QLoraLayer, X, til
     if out is None:
         out = dict(Y=torch.empty((M, H), dtype=torch.bfloat16, device=dev),
                    Z=torch.empty((3, M, r), dtype=torch.bfloat16, device=dev))
+    _need_saved(out, M, H, I, r, ("Y",))
     nb = mlp_tiled_workspace_size(False, M, H, I, r, tile)
     ws = _workspace(nb, dev) if ws is None else ws
+    _need_ws(ws, nb)
     lg, lu, ld = gate.c(), up.c(), down.c()
     C.check("swiglu_mlp_forward_tiled", C.lib().swiglu_mlp_forward_tiled(
         ctypes.byref(lg), ctypes.byref(lu), ctypes.byref(ld), _ptr(X), M, tile, _ptr(out["Y"]), _ptr(out["Z"]),
@@ -197,12 +274,10 @@ def mlp_backward_tiled(gate: QLoraLayer, up: QLoraLayer, down: QLoraLayer, dY, X
     _need(X, torch.bfloat16, (M, H), "X")
     _need(Z, torch.bfloat16, (3, M, r), "Z")
     dev = X.device
-    if out is None:
-        out = dict(dX=torch.empty((M, H), dtype=torch.bfloat16, device=dev) if need_dX else None,
-                   dA=[torch.empty((r, L.K), dtype=torch.float32, device=dev) for L in (gate, up, down)],
-                   dB=[torch.empty((L.N, r), dtype=torch.float32, device=dev) for L in (gate, up, down)])
+    out = _grads_out((gate, up, down), out, M, H, dev, need_dX)
     nb = mlp_tiled_workspace_size(True, M, H, I, r, tile)
     ws = _workspace(nb, dev) if ws is None else ws
+    _need_ws(ws, nb)
     dA = (ctypes.c_void_p * 3)(*[t.data_ptr() for t in out["dA"]])
     dB = (ctypes.c_void_p * 3)(*[t.data_ptr() for t in out["dB"]])
     lg, lu, ld = gate.c(), up.c(), down.c()
@@ -219,6 +294,8 @@ def rmsnorm_forward(x, w, eps: float, y=None, rstd=None):
     _need(w, torch.bfloat16, (H,), "w")
     y = torch.empty_like(x) if y is None else y
     rstd = torch.empty((M,), dtype=torch.float32, device=x.device) if rstd is None else rstd
+    _need(y, torch.bfloat16, (M, H), "y")
+    _need(rstd, torch.float32, (M,), "rstd")
     C.check("qlora_rmsnorm_forward", C.lib().qlora_rmsnorm_forward(_ptr(x), _ptr(w), M, H, float(eps), _ptr(y),
                                                                    _ptr(rstd), _stream()))
     return y, rstd
@@ -232,6 +309,7 @@ def rmsnorm_backward(dy, x, w, rstd, dx=None):
     _need(w, torch.bfloat16, (H,), "w")
     _need(rstd, torch.float32, (M,), "rstd")
     dx = torch.empty_like(x) if dx is None else dx
+    _need(dx, torch.bfloat16, (M, H), "dx")
     C.check("qlora_rmsnorm_backward", C.lib().qlora_rmsnorm_backward(_ptr(dy), _ptr(x), _ptr(w), _ptr(rstd), M, H,
                                                                      _ptr(dx), _stream()))
     return dx
@@ -292,8 +370,12 @@ def chunked_ce(h, prepared, targets, chunk: int, ws=None, out=None):
         out = dict(loss=torch.empty((1,), dtype=torch.float32, device=dev),
                    loss_rows=torch.empty((M,), dtype=torch.float32, device=dev),
                    dh=torch.empty((M, H), dtype=torch.bfloat16, device=dev))
+    _need(out["loss"], torch.float32, (1,), "loss")
+    _need(out["loss_rows"], torch.float32, (M,), "loss_rows")
+    _need(out["dh"], torch.bfloat16, (M, H), "dh")
     nb = int(C.lib().qlora_ce_workspace_size(M, V, chunk))
     ws = _workspace(nb, dev) if ws is None else ws
+    _need_ws(ws, nb)
     C.check("qlora_chunked_ce", C.lib().qlora_chunked_ce(
         _ptr(h), _ptr(Wp), _ptr(Wtp), _ptr(targets), M, H, V, chunk, _ptr(out["loss"]), _ptr(out["loss_rows"]),
         _ptr(out["dh"]), _ptr(ws), ws.numel(), _stream()))

@@ -70,8 +70,12 @@ class Prepared:
     """One projection on both sides: oracle (fp64) and device tensors, with the
     frozen weight in format fmt (0 NF4, 1 INT8, 2 FP8)."""
 
-    def __init__(self, layer: dict, s: float, quantize_on_gpu=True, fmt: int = 0):
+    def __init__(self, layer: dict, s: float, quantize_on_gpu=True, fmt: int = 0, grad_dtype=None):
+        import torch
         import parameter_efficient_fine_amd as q
+        # fp32 adapter gradients unless asked otherwise, so order-only differences
+        # between two GPU paths stay visible
+        grad_dtype = torch.float32 if grad_dtype is None else grad_dtype
         self.s = s
         W = layer["W"]
         if fmt == 0:
@@ -88,7 +92,7 @@ class Prepared:
             import torch
             codes = torch.from_numpy(device_codes(self.codes_ref, fmt)).cuda()
             absmax = torch.from_numpy(tile_major(self.absmax_ref, 1)).cuda()
-        self.dev = q.QLoraLayer(codes, absmax, dev_bf16(layer["A"]), dev_bf16(layer["B"]), s, fmt)
+        self.dev = q.QLoraLayer(codes, absmax, dev_bf16(layer["A"]), dev_bf16(layer["B"]), s, fmt, grad_dtype)
 
     def triple(self):
         return (self.What, self.A, self.B)

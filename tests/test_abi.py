@@ -297,3 +297,34 @@ def test_tiled_mlp_workspace_covers_every_tile(H, I):
                 need = fixed + max(_mlp_part_bytes(lib, m, H, I, r) for m in sizes)
                 got = lib.swiglu_mlp_tiled_workspace_size(1, M, H, I, r, tile)
                 assert got >= need, (M, tile, r, H, I, got, need)
+
+
+def test_pack_codes_argument_checks():
+    lib = C.lib()
+    p, q2 = ctypes.c_void_p(0x10000), ctypes.c_void_p(0x900000)
+    a, b = ctypes.c_void_p(0x2000000), ctypes.c_void_p(0x3000000)
+    for fmt in (C.FMT_NF4, C.FMT_INT8, C.FMT_FP8):
+        assert lib.qlora_pack_codes(fmt, p, a, 4, 100, q2, b, None) == C.QLORA_EINVAL     # K % 64
+        assert lib.qlora_pack_codes(fmt, p, a, 0, 64, q2, b, None) == C.QLORA_OK         # empty: no launch
+        assert lib.qlora_pack_codes(fmt, None, a, 4, 64, q2, b, None) == C.QLORA_EINVAL
+        assert lib.qlora_pack_codes(fmt, ctypes.c_void_p(0x10004), a, 4, 64, q2, b, None) == C.QLORA_EINVAL
+        # destinations must not overlap the sources
+        assert lib.qlora_pack_codes(fmt, p, a, 4, 64, ctypes.c_void_p(0x10010), b, None) == C.QLORA_EINVAL
+        assert lib.qlora_pack_codes(fmt, p, a, 4, 64, q2, a, None) == C.QLORA_EINVAL
+    assert lib.qlora_pack_codes(3, p, a, 4, 64, q2, b, None) == C.QLORA_EINVAL
+
+
+def test_gradient_dtype_field_checks():
+    lib = C.lib()
+    p = ctypes.c_void_p(0x10000)
+    for gd, ok in ((C.GRAD_BF16, True), (C.GRAD_F32, True), (2, False), (-1, False)):
+        L = C.QLoraLayerC(0x10000, 0x10000, 0x10000, 0x10000, 512, 512, 16, 2.0, 0, gd)
+        st = lib.qlora_forward(ctypes.byref(L), p, 0, p, p, None, 0, None)
+        assert st == (C.QLORA_OK if ok else C.QLORA_EINVAL), gd
+    # the three layers of a SwiGLU block share one gradient type
+    g = C.QLoraLayerC(0x10000, 0x10000, 0x10000, 0x10000, 256, 512, 16, 2.0, 0, C.GRAD_BF16)
+    u = C.QLoraLayerC(0x10000, 0x10000, 0x10000, 0x10000, 256, 512, 16, 2.0, 0, C.GRAD_BF16)
+    d = C.QLoraLayerC(0x10000, 0x10000, 0x10000, 0x10000, 512, 256, 16, 2.0, 0, C.GRAD_F32)
+    assert lib.swiglu_mlp_forward(ctypes.byref(g), ctypes.byref(u), ctypes.byref(d), p, 8, p, p, p, p, p,
+                                  None, 0, None) == C.QLORA_EINVAL
+    assert lib.qlora_status_string(C.QLORA_ENONFINITE)

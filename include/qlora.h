@@ -157,6 +157,20 @@ int qlora_forward(const qlora_layer* L, const uint16_t* X, int64_t M, uint16_t* 
 int qlora_backward(const qlora_layer* L, const uint16_t* dY, const uint16_t* X, const uint16_t* Z_save,
                    int64_t M, uint16_t* dX, void* dA, void* dB, void* ws, size_t ws_bytes, void* stream);
 
+/* qlora_backward for callers that cannot allocate device memory (code under
+ * graph capture, serving loops, harnesses that forbid it): the same kernels
+ * and results, with the workspace taken from a scratch array inside the
+ * library (QLORA_NOALLOC_SCRATCH_BYTES per GPU, held until the process ends)
+ * instead of a caller buffer. The call allocates nothing. A backward whose
+ * workspace (qlora_workspace_size(QLORA_OP_BACKWARD, ...)) exceeds the limit
+ * returns QLORA_EWORKSPACE (qlora_last_error() gives both sizes). Every call on
+ * one GPU shares that GPU's array: calls that overlap in time on one GPU (other
+ * streams or threads) race and must be serialized by the caller. The current
+ * device must be the stream's device. */
+#define QLORA_NOALLOC_SCRATCH_BYTES (64u << 20)
+int qlora_backward_noalloc(const qlora_layer* L, const uint16_t* dY, const uint16_t* X, const uint16_t* Z_save,
+                           int64_t M, uint16_t* dX, void* dA, void* dB, void* stream);
+
 /* SwiGLU MLP forward: g = lin_gate(X), u = lin_up(X), h = silu(g)*u,
  * Y = lin_down(h). gate/up: K = H (model width), N = I; down: K = I, N = H.
  * Saves g, u, h [M,I] bf16 and Z_save [3][M][r] (gate, up, down) for the

@@ -17,6 +17,7 @@ QLORA_EUNSUPPORTED = -2
 QLORA_EWORKSPACE = -3
 QLORA_EHIP = -4
 QLORA_ENONFINITE = -5
+NOALLOC_SCRATCH_BYTES = 64 << 20  # QLORA_NOALLOC_SCRATCH_BYTES
 
 OP_FORWARD, OP_BACKWARD, OP_MLP_FORWARD, OP_MLP_BACKWARD = 0, 1, 2, 3
 FMT_NF4, FMT_INT8, FMT_FP8 = 0, 1, 2
@@ -25,7 +26,7 @@ GRAD_BF16, GRAD_F32 = 0, 1
 # Every function the header declares (checked by the CPU tests against include/qlora.h).
 EXPORTS = [
     "qlora_quantize", "qlora_pack_codes", "qlora_dequantize", "qlora_workspace_size", "qlora_forward", "qlora_backward",
-    "swiglu_mlp_forward", "swiglu_mlp_backward", "swiglu_mlp_tiled_workspace_size", "swiglu_mlp_forward_tiled",
+    "qlora_backward_noalloc", "swiglu_mlp_forward", "swiglu_mlp_backward", "swiglu_mlp_tiled_workspace_size", "swiglu_mlp_forward_tiled",
     "swiglu_mlp_backward_tiled", "qlora_rmsnorm_forward", "qlora_rmsnorm_backward", "qlora_rope_forward",
     "qlora_rope_backward", "qlora_lmhead_prepare", "qlora_ce_workspace_size", "qlora_chunked_ce",
     "qlora_profile_begin", "qlora_profile_end",
@@ -78,6 +79,7 @@ def lib():
     L.qlora_workspace_size.restype = sz
     L.qlora_forward.argtypes = [LP, vp, i64, vp, vp, vp, sz, vp]
     L.qlora_backward.argtypes = [LP, vp, vp, vp, i64, vp, vp, vp, vp, sz, vp]
+    L.qlora_backward_noalloc.argtypes = [LP, vp, vp, vp, i64, vp, vp, vp, vp]
     L.swiglu_mlp_forward.argtypes = [LP, LP, LP, vp, i64, vp, vp, vp, vp, vp, vp, sz, vp]
     L.swiglu_mlp_backward.argtypes = [LP, LP, LP, vp, vp, vp, vp, vp, vp, i64, vp,
                                       ctypes.POINTER(vp), ctypes.POINTER(vp), vp, sz, vp]
@@ -103,8 +105,8 @@ def lib():
     L.qlora_status_string.restype = ctypes.c_char_p
     L.qlora_last_error.argtypes = []
     L.qlora_last_error.restype = ctypes.c_char_p
-    for f in ("qlora_quantize", "qlora_pack_codes", "qlora_dequantize", "qlora_forward", "qlora_backward", "swiglu_mlp_forward",
-              "swiglu_mlp_backward", "swiglu_mlp_forward_tiled", "swiglu_mlp_backward_tiled", "qlora_rmsnorm_forward",
+    for f in ("qlora_quantize", "qlora_pack_codes", "qlora_dequantize", "qlora_forward", "qlora_backward", "qlora_backward_noalloc",
+              "swiglu_mlp_forward", "swiglu_mlp_backward", "swiglu_mlp_forward_tiled", "swiglu_mlp_backward_tiled", "qlora_rmsnorm_forward",
               "qlora_rmsnorm_backward", "qlora_rope_forward", "qlora_rope_backward", "qlora_lmhead_prepare",
               "qlora_chunked_ce"):
         getattr(L, f).restype = ctypes.c_int

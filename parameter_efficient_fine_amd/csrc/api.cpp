@@ -5,6 +5,7 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <mutex>
 #include <vector>
 #include <cstdio>
 #include <cstring>
@@ -427,6 +428,58 @@ int qlora_backward(const qlora_layer* L, const uint16_t* dY, const uint16_t* X, 
   if (int rc = tn.flush()) return rc;
   if (dX) QL_LAUNCH("gemm_bwd", st, launch_gemm_bwd(dY, wsrc(L, L->A, G), nullptr, WSrc{}, M, K, N, dX, st));
   return QLORA_OK;
+}
+
+}  // extern "C"
+
+// ---------------------------------------------------------------------------
+// Backward without a caller workspace, for callers that cannot allocate device
+// memory. Its workspace is this file-scope array: each GPU the library runs on
+// holds its own copy for the life of the process. Host code never uses the
+// array's name as a device address: the address comes from
+// hipGetSymbolAddress, looked up once per device with that device current.
+static __device__ __align__(256) unsigned char scratch[QLORA_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+std::mutex g_scratch_mu;
+constexpr int kScratchDevices = 64;
+void* g_scratch_ptr[kScratchDevices];
+
+// this device's copy of `scratch` (looked up on first use)
+int scratch_for_current_device(void** out) {
+  int dev = 0;
+  QL_CHECK(hipGetDevice(&dev));
+  if (dev < 0 || dev >= kScratchDevices) {
+    snprintf(g_err, sizeof(g_err), "device %d: no scratch slot", dev);
+    return QLORA_EUNSUPPORTED;
+  }
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    QL_CHECK(hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)));
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return QLORA_OK;
+}
+}  // namespace
+
+extern "C" {
+
+int qlora_backward_noalloc(const qlora_layer* L, const uint16_t* dY, const uint16_t* X, const uint16_t* Z_save,
+                           int64_t M, uint16_t* dX, void* dA, void* dB, void* stream) {
+  if (!layer_ok(L) || M < 0) return QLORA_EINVAL;
+  const size_t need = bwd_ws(M, L->K, L->N, L->r);
+  if (need > (size_t)QLORA_NOALLOC_SCRATCH_BYTES) {
+    snprintf(g_err, sizeof(g_err), "qlora_backward_noalloc: needs %zu bytes of scratch, the limit is %zu", need,
+             (size_t)QLORA_NOALLOC_SCRATCH_BYTES);
+    return QLORA_EWORKSPACE;
+  }
+  void* ws = nullptr;
+  if (int rc = scratch_for_current_device(&ws)) return rc;
+  // every scratch byte the backward reads is written earlier in the same call
+  // (G, the B^T copy, the reduction partials), so nothing needs clearing
+  return qlora_backward(L, dY, X, Z_save, M, dX, dA, dB, ws, (size_t)QLORA_NOALLOC_SCRATCH_BYTES, stream);
 }
 
 static bool mlp_shapes_ok(const qlora_layer* g, const qlora_layer* u, const qlora_layer* d) {

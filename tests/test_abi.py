@@ -328,3 +328,18 @@ def test_gradient_dtype_field_checks():
     assert lib.swiglu_mlp_forward(ctypes.byref(g), ctypes.byref(u), ctypes.byref(d), p, 8, p, p, p, p, p,
                                   None, 0, None) == C.QLORA_EINVAL
     assert lib.qlora_status_string(C.QLORA_ENONFINITE)
+
+
+def test_noalloc_backward_rejects_workspaces_beyond_its_scratch():
+    # the size check comes before any HIP call, so this runs without a GPU
+    lib = C.lib()
+    p = ctypes.c_void_p(0x10000)
+    L = C.QLoraLayerC(0x10000, 0x10000, 0x10000, 0x10000, 4096, 4096, 128, 2.0, 0, 0)
+    M = 1 << 20
+    assert lib.qlora_workspace_size(C.OP_BACKWARD, M, 4096, 4096, 128) > C.NOALLOC_SCRATCH_BYTES
+    assert lib.qlora_backward_noalloc(ctypes.byref(L), p, p, p, M, p, p, p, None) == C.QLORA_EWORKSPACE
+    assert b"limit" in lib.qlora_last_error()
+    assert lib.qlora_backward_noalloc(None, p, p, p, 4, p, p, p, None) == C.QLORA_EINVAL
+    # the header's limit and the binding's constant agree
+    text = open(HEADER).read()
+    assert "#define QLORA_NOALLOC_SCRATCH_BYTES (64u << 20)" in text and C.NOALLOC_SCRATCH_BYTES == 64 << 20

@@ -13,6 +13,8 @@ seeded synthetic inputs already resident in HBM:
   layer  : the 7 projections of a Llama-3.1-8B GQA decoder layer at M=16384
   normrope: the layer's two RMSNorms (H=4096) and q/k RoPE (32+8 heads of 128), M=16384
   lmhead : chunked cross-entropy over a 128256 x 4096 LM head, M=16384, chunks of 4096
+  qkrope : the layer's q and k projections with RoPE (heads of 128, base 500000), fwd+bwd, M=16384;
+           RoPE in the GEMM epilogue, or after it as its own pass with --rope-unfused
 --mlp-tile T runs the SwiGLU block of mlp/layer token-tiled (T tokens at a
 time, g/u/h recomputed in the backward) and reports its activation memory.
 Prints one JSON line with tokens/s, useful TFLOP/s (4MNK + 6Mr(N+K) per
@@ -35,7 +37,10 @@ sys.path.insert(0, ROOT)
 
 PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 MFMA (published)
 PEAK_HBM_GBS = 8000.0
-WL_INDEX = {"tiny": 0, "attn": 1, "mlp": 2, "rsweep": 3, "layer": 4, "normrope": None, "lmhead": None}
+RIDGE_FLOP_PER_BYTE = PEAK_BF16_TFLOPS * 1e12 / (PEAK_HBM_GBS * 1e9)  # ~312: below it a step is HBM/latency-bound
+COLD_STEPS = 10
+WL_INDEX = {"tiny": 0, "attn": 1, "mlp": 2, "rsweep": 3, "layer": 4, "normrope": None, "lmhead": None,
+            "qkrope": None}
 # cross-entropy over the Llama-3-8B LM head (vocabulary 128256, width 4096) for
 # the layer workload's 16384 tokens, in chunks of 4096 tokens (3 GB of workspace)
 LMHEAD = dict(M=16384, H=4096, V=128256, chunk=4096)
@@ -54,14 +59,16 @@ def parse():
     ap.add_argument("--rank", type=int, default=16)
     ap.add_argument("--wfmt", default="nf4", choices=["nf4", "int8", "fp8"],
                     help="format of the frozen weights (NF4 4-bit, INT8, FP8 E4M3; 64-element blocks)")
+    ap.add_argument("--rope-unfused", action="store_true",
+                    help="qkrope: the forward GEMMs, then RoPE as its own kernel (instead of in the GEMM epilogue)")
     ap.add_argument("--mlp-tile", type=int, default=0,
                     help="token-tiled SwiGLU block with this many tokens per tile (0: whole batch)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="target CPU time of the oracle baseline")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--no-gpu-state", action="store_true",
                     help="skip reading clocks and power with rocm-smi while the step runs")
-    ap.add_argument("--cold", action="store_true",
-                    help="also time 10 cache-cold steps (512 MiB written before each, untimed)")
+    ap.add_argument("--no-cold", action="store_true",
+                    help="skip the 10 cache-cold steps (512 MiB written before each, untimed) timed after the warm ones")
     ap.add_argument("--graph", action="store_true",
                     help="also time the step captured once in a HIP graph and replayed (reported under 'graph')")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -311,7 +318,49 @@ class LMHeadCE:
         return {"gemm_nt": out}
 
 
-def build_workload(name: str, rank: int, mlp_tile: int = 0, fmt: int = 0):
+class QKRope:
+    """q and k projections of a decoder layer with RoPE on their outputs, forward and backward:
+    fused (RoPE in the GEMM epilogue) or unfused (GEMM, then the RoPE kernel on q and k at once).
+    The backward rotates dq, dk back in place (one launch), then runs both projection backwards."""
+
+    def __init__(self, q, C, fused, fmt=0):
+        import torch
+        from synthetic import make_workload, packed_positions
+        d = make_workload(4)
+        self.d = d
+        M = d["M"]
+        X = dev_bf16(d["X_attn"])
+        self.projs = [Proj(q, C, d["layers"][nm], d["s"], X, dev_bf16(d["dY_" + nm]), fmt) for nm in ("q", "k")]
+        pos = packed_positions(np.random.default_rng(4100), M, M)
+        self.pos = torch.from_numpy(pos.astype(np.int32)).cuda()
+        self.table = q.rope_table(128, 500000.0, M)
+        self.fused = fused
+        self.M = M
+        p = lambda t: ctypes.c_void_p(t.data_ptr())
+        self.rope_f = (p(self.projs[0].Y), p(self.projs[1].Y), p(self.pos), M, 32, 8, 128, 500000.0)
+        self.rope_b = (p(self.projs[0].dY), p(self.projs[1].dY), p(self.pos), M, 32, 8, 128, 500000.0)
+        self.fr = [(ctypes.byref(pr.lc), p(pr.X), M, p(self.pos), p(self.table), M, 128, p(pr.Y), p(pr.Z))
+                   for pr in self.projs]
+
+    def run(self, lib, stream):
+        if self.fused:
+            for a in self.fr:
+                if lib.qlora_forward_rope(*a, stream):
+                    raise RuntimeError("qlora_forward_rope")
+        else:
+            for pr in self.projs:
+                if lib.qlora_forward(*pr.fwd_args, stream):
+                    raise RuntimeError("qlora_forward")
+            if lib.qlora_rope_forward(*self.rope_f, stream):
+                raise RuntimeError("qlora_rope_forward")
+        if lib.qlora_rope_backward(*self.rope_b, stream):  # dq, dk rotated back in place
+            raise RuntimeError("qlora_rope_backward")
+        for pr in self.projs:
+            if lib.qlora_backward(*pr.bwd_args, stream):
+                raise RuntimeError("qlora_backward")
+
+
+def build_workload(name: str, rank: int, mlp_tile: int = 0, fmt: int = 0, rope_unfused: bool = False):
     import torch
     import parameter_efficient_fine_amd as q
     from parameter_efficient_fine_amd import _lib as C
@@ -322,6 +371,11 @@ def build_workload(name: str, rank: int, mlp_tile: int = 0, fmt: int = 0):
         d = dict(LMHEAD, kind="lmhead", _data=parts[0].d)
         torch.cuda.synchronize()
         return d, parts
+    if name == "qkrope":
+        part = QKRope(q, C, not rope_unfused, fmt)
+        d = dict(kind="qkrope", M=part.M, r=16, fused=not rope_unfused, _data=None)
+        torch.cuda.synchronize()
+        return d, [part]
     if name == "normrope":
         parts = [NormRope(q, NORMROPE)]
         d = dict(NORMROPE, kind="normrope", _data=parts[0].d)
@@ -345,6 +399,11 @@ def build_workload(name: str, rank: int, mlp_tile: int = 0, fmt: int = 0):
 
 
 def describe(d, name, parts=()):
+    if d["kind"] == "qkrope":
+        how = "in the GEMM epilogue" if d["fused"] else "as its own kernel after the GEMMs"
+        return dict(workload=f"{name}: q (4096->4096) and k (4096->1024) projections with RoPE {how} (heads of 128, "
+                             f"base 500000, packed-sequence positions), fwd+bwd, M={d['M']}, r=16",
+                    M=d["M"], r=16, rope_fused=d["fused"])
     if d["kind"] == "lmhead":
         return dict(workload=f"{name}: chunked cross-entropy (loss and dh) over a frozen bf16 LM head, V={d['V']}, "
                              f"H={d['H']}, M={d['M']} tokens in chunks of {d['chunk']}, ~10% ignored targets",
@@ -377,7 +436,10 @@ def describe(d, name, parts=()):
 def gemm_flops(parts):
     """{kernel class: algorithmic FLOPs per launch} of the fused dequant GEMMs."""
     out = {}
+    expanded = []
     for p in parts:
+        expanded += p.projs if isinstance(p, QKRope) else [p]
+    for p in expanded:
         if isinstance(p, NormRope):
             continue
         if isinstance(p, LMHeadCE):
@@ -387,6 +449,7 @@ def gemm_flops(parts):
         if isinstance(p, Proj):
             M, K, N, r = p.M, p.K, p.N, p.r
             out.setdefault("gemm_fwd", []).append(2 * M * N * K + 2 * M * N * r)   # X.W^T + Z.B^T
+            out.setdefault("gemm_fwd_rope", []).append(2 * M * N * K + 2 * M * N * r)
             out.setdefault("gemm_bwd", []).append(2 * M * N * K + 2 * M * K * r)   # dY.W + G.A
         else:
             H, I, r = p.H, p.I, p.r
@@ -399,6 +462,32 @@ def gemm_flops(parts):
                 out.setdefault("gemm_fwd", []).append(2 * M * H * I + 2 * M * H * r)
                 out.setdefault("gemm_bwd_swiglu", []).append(2 * M * H * I + 2 * M * I * r)
                 out.setdefault("gemm_bwd", []).append(2 * (2 * M * I * H + 2 * M * H * r))
+    return out
+
+
+def _wbytes(N, K, fmt):
+    """Bytes of a frozen weight [N, K]: codes (0.5 or 1 byte per element) and one fp32 per 64-block."""
+    return N * K * (0.5 if fmt == 0 else 1.0) + N * K / 64 * 4
+
+
+def launch_bytes(parts, fmt=0):
+    """{kernel class: [algorithmic HBM bytes of each launch in one step]}: the inputs and
+    outputs each launch must read or write once (weights, activations, adapters, results;
+    the fp32 split partials of the rank reductions are an implementation detail, not counted)."""
+    out = {}
+
+    def add(k, v):
+        out.setdefault(k, []).append(float(v))
+
+    for p in parts:
+        if isinstance(p, Proj):
+            M, K, N, r = p.M, p.K, p.N, p.r
+            add("gemm_fwd", 2 * M * K + _wbytes(N, K, fmt) + 2 * M * r + 2 * N * r + 2 * M * N)
+            add("gemm_bwd", 2 * M * N + _wbytes(N, K, fmt) + 2 * M * r + 2 * r * K + 2 * M * K)
+            add("skinny_nt", 2 * M * K + 2 * r * K + 2 * M * r)      # Z = X.A^T
+            add("skinny_nt", 2 * M * N + 2 * N * r + 2 * M * r)      # G = dY.B
+            # dB = s.dY^T.Z and dA = s.G^T.X (one launch): operands in, fp32 gradients out
+            add("skinny_tn", 2 * M * N + 2 * M * r + 2 * M * K + 2 * M * r + 4 * r * (N + K))
     return out
 
 
@@ -439,6 +528,25 @@ def cpu_baseline(d, target_s: float):
             def run(rows):
                 ce_oracle.ce_fwd_bwd(Hh[:rows], Wl, nd["targets"][:rows])
             what = "cross-entropy over the LM head, loss and dh"
+        elif d["kind"] == "qkrope":
+            from oracle import normrope as nr
+            from synthetic import make_workload, packed_positions
+            w4 = make_workload(4)
+            pos = packed_positions(np.random.default_rng(4100), M, M)
+            X = ref.bf16_to_f64(w4["X_attn"])
+            trip = {}
+            for nm in ("q", "k"):
+                Lr = w4["layers"][nm]
+                trip[nm] = (_oracle_weight(Lr["W"], d.get("wfmt", "nf4")), ref.bf16_to_f64(Lr["A"]),
+                            ref.bf16_to_f64(Lr["B"]), ref.bf16_to_f64(w4["dY_" + nm]))
+
+            def run(rows):
+                for nm, (What, A, B, dY) in trip.items():
+                    Y, _ = ref.linear_fwd(X[:rows], What, A, B, w4["s"])
+                    nr.rope(Y, pos[:rows], 128, 500000.0)
+                    g = nr.rope_bwd(dY[:rows], pos[:rows], 128, 500000.0)
+                    ref.linear_bwd(g, X[:rows], What, A, B, w4["s"])
+            what = "q and k projections with RoPE, fwd+bwd"
         elif d["kind"] == "normrope":
             from oracle import normrope as nr
             nd = d["_data"]
@@ -555,13 +663,15 @@ def main():
     from synthetic import useful_flops
 
     lib = C.lib()
-    d, parts = build_workload(args.workload, args.rank, args.mlp_tile, WFMT[args.wfmt])
+    d, parts = build_workload(args.workload, args.rank, args.mlp_tile, WFMT[args.wfmt], args.rope_unfused)
     d["wfmt"] = args.wfmt
     c = WL_INDEX[args.workload]
     sub = d["sub"] if args.workload == "rsweep" else 0
     flops = useful_flops(c, sub) if c is not None else None
     if args.workload == "lmhead":
         flops = parts[0].useful_flops()
+    if args.workload == "qkrope":  # the two projections' useful work (the rotation is not counted)
+        flops = float(sum(4 * p.M * p.N * p.K + 6 * p.M * p.r * (p.N + p.K) for p in parts[0].projs))
     stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
 
     def step(st=stream):
@@ -584,12 +694,12 @@ def main():
     per_step = np.array([evs[i].elapsed_time(evs[i + 1]) for i in range(args.steps)])
     step_stats = dict(median_ms=float(np.median(per_step)), min_ms=float(per_step.min()),
                       p90_ms=float(np.percentile(per_step, 90)))
-    if args.cold:
+    if not args.no_cold:
         # cache-cold steps: 512 MiB written between steps (untimed), so the
         # step's inputs come from HBM rather than the last-level cache
         flush = torch.empty(512 << 20, dtype=torch.uint8, device="cuda")
         cold = []
-        for _ in range(10):
+        for _ in range(COLD_STEPS):
             flush.fill_(1)
             e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
             e0.record()
@@ -599,6 +709,8 @@ def main():
             cold.append(e0.elapsed_time(e1))
         del flush
         step_stats["cold_median_ms"] = float(np.median(cold))
+        step_stats["cold_min_ms"] = float(np.min(cold))
+        step_stats["cold_tokens_per_s"] = d["M"] / (step_stats["cold_median_ms"] * 1e-3)
 
     graph_stats = None
     if args.graph:
@@ -629,7 +741,22 @@ def main():
     kernels = {}
     for name, (n, tot) in kt.result.items():
         kernels[name] = dict(launches_per_step=n / args.steps, ms_per_step=tot / args.steps, avg_us=1e3 * tot / n)
-    if flops is None:  # HBM-bound steps: algorithmic bytes of the dominant kernel
+    step_bytes = None
+    if flops is not None and d["kind"] == "linear":
+        lb = launch_bytes(parts, WFMT[args.wfmt])
+        # the step's algorithmic bytes: every kernel's inputs and outputs once
+        step_bytes = sum(sum(v) for v in lb.values())
+    low_ai = step_bytes is not None and flops / step_bytes < RIDGE_FLOP_PER_BYTE
+    if low_ai:  # below the ridge (small batches): the dominant kernel against HBM bandwidth
+        per_launch = {k: float(np.mean(v)) for k, v in launch_bytes(parts, WFMT[args.wfmt]).items()}
+        dom = max((k for k in kernels if k in per_launch), key=lambda k: kernels[k]["ms_per_step"])
+        avg_s = kernels[dom]["avg_us"] * 1e-6
+        achieved = per_launch[dom] / avg_s / 1e9
+        roofline = dict(bound="hbm", kernel=dom, achieved=achieved, peak=PEAK_HBM_GBS, unit="GB/s",
+                        frac=achieved / PEAK_HBM_GBS, traffic=counted_traffic(dom, args.workload),
+                        traffic_unit="bytes per launch", avg_us=kernels[dom]["avg_us"],
+                        bytes_per_launch=per_launch[dom], source_hash=kernel_source_hash(dom))
+    elif flops is None:  # HBM-bound steps: algorithmic bytes of the dominant kernel
         per_launch_bytes = parts[0].bytes_per_launch()
         dom = max((k for k in kernels if k in per_launch_bytes), key=lambda k: kernels[k]["ms_per_step"])
         avg_s = kernels[dom]["avg_us"] * 1e-6
@@ -679,6 +806,11 @@ def main():
         "roofline": roofline,
         "kernels": kernels,
     }
+    if step_bytes is not None:
+        # whole-step algorithmic HBM bytes (each kernel's inputs and outputs once) per step time
+        out["step_hbm"] = dict(bytes=step_bytes, achieved_gbs=step_bytes / (ms * 1e-3) / 1e9,
+                               frac=step_bytes / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS,
+                               arithmetic_intensity=flops / step_bytes)
     if graph_stats is not None:
         out["graph"] = graph_stats
     out["gpu_state"] = None if args.no_gpu_state else gpu_state_under_load(step, torch.cuda.synchronize)

@@ -244,6 +244,25 @@ int qlora_rope_forward(uint16_t* q, uint16_t* k, const int32_t* pos, int64_t M, 
 int qlora_rope_backward(uint16_t* dq, uint16_t* dk, const int32_t* pos, int64_t M, int hq, int hk, int d, float base,
                         void* stream);
 
+/* cos/sin table of the RoPE angles for positions 0 .. max_pos-1:
+ * table[(p*d/2 + i)*2 + 0] = cos(p * base^(-2i/d)), [.. + 1] = sin(..), fp32
+ * values of the fp64 angles and sin/cos (as qlora_rope_forward forms them).
+ * [max_pos][d/2][2] floats; built once and shared by every layer.
+ * 16 <= d <= 1024, d % 16 == 0, base > 1, max_pos <= 2^21. */
+int qlora_rope_table(int d, float base, int64_t max_pos, float* table, void* stream);
+
+/* Forward of a q or k projection with RoPE fused into its GEMM ("Unsloth"
+ * wiki entry, Theory: fused RoPE kernel; "Unsloth vs PyTorch" video,
+ * 2:11-2:22): Y = rope(X.W^T + s.(X.A^T).B^T) by pos [M] (int32), heads of
+ * d = 128 output columns (N % 128 == 0), rotate-half pairing as in
+ * qlora_rope_forward, applied to the fp32 GEMM result before its one bf16
+ * rounding; Z_save = X.A^T as in qlora_forward. `table` is qlora_rope_table's
+ * for this d and base, covering every position (0 <= pos < max_pos; a position
+ * outside it gives zeros in its row, no fault). The backward is
+ * qlora_rope_backward on dY (in place) followed by qlora_backward. */
+int qlora_forward_rope(const qlora_layer* L, const uint16_t* X, int64_t M, const int32_t* pos, const float* table,
+                       int64_t max_pos, int d, uint16_t* Y, uint16_t* Z_save, void* stream);
+
 /* Cross-entropy over the frozen language-model head, chunked over tokens so
  * that the [M, V] logits never exist ("Unsloth" wiki entry, Theory: chunked
  * cross-entropy; "Unsloth vs PyTorch" video, 3:06-3:51). For h [M,H] (bf16,

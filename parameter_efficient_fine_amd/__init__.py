@@ -12,6 +12,7 @@ from .ops import (  # noqa: F401
     chunked_ce,
     dequantize,
     forward,
+    forward_rope,
     lmhead_prepare,
     mlp_backward,
     mlp_backward_tiled,
@@ -25,5 +26,6 @@ from .ops import (  # noqa: F401
     rmsnorm_forward,
     rope_backward,
     rope_forward,
+    rope_table,
     workspace_size,
 )

@@ -28,7 +28,7 @@ EXPORTS = [
     "qlora_quantize", "qlora_pack_codes", "qlora_dequantize", "qlora_workspace_size", "qlora_forward", "qlora_backward",
     "qlora_backward_noalloc", "swiglu_mlp_forward", "swiglu_mlp_backward", "swiglu_mlp_tiled_workspace_size", "swiglu_mlp_forward_tiled",
     "swiglu_mlp_backward_tiled", "qlora_rmsnorm_forward", "qlora_rmsnorm_backward", "qlora_rope_forward",
-    "qlora_rope_backward", "qlora_lmhead_prepare", "qlora_ce_workspace_size", "qlora_chunked_ce",
+    "qlora_rope_backward", "qlora_rope_table", "qlora_forward_rope", "qlora_lmhead_prepare", "qlora_ce_workspace_size", "qlora_chunked_ce",
     "qlora_profile_begin", "qlora_profile_end",
     "qlora_status_string", "qlora_last_error",
 ]
@@ -93,6 +93,8 @@ def lib():
     L.qlora_rmsnorm_backward.argtypes = [vp, vp, vp, vp, i64, i64, vp, vp]
     L.qlora_rope_forward.argtypes = [vp, vp, vp, i64, ci, ci, ci, cf, vp]
     L.qlora_rope_backward.argtypes = [vp, vp, vp, i64, ci, ci, ci, cf, vp]
+    L.qlora_rope_table.argtypes = [ci, cf, i64, vp, vp]
+    L.qlora_forward_rope.argtypes = [LP, vp, i64, vp, vp, i64, ci, vp, vp, vp]
     L.qlora_lmhead_prepare.argtypes = [vp, i64, i64, vp, vp, vp]
     L.qlora_ce_workspace_size.argtypes = [i64, i64, i64]
     L.qlora_ce_workspace_size.restype = sz
@@ -107,8 +109,8 @@ def lib():
     L.qlora_last_error.restype = ctypes.c_char_p
     for f in ("qlora_quantize", "qlora_pack_codes", "qlora_dequantize", "qlora_forward", "qlora_backward", "qlora_backward_noalloc",
               "swiglu_mlp_forward", "swiglu_mlp_backward", "swiglu_mlp_forward_tiled", "swiglu_mlp_backward_tiled", "qlora_rmsnorm_forward",
-              "qlora_rmsnorm_backward", "qlora_rope_forward", "qlora_rope_backward", "qlora_lmhead_prepare",
-              "qlora_chunked_ce"):
+              "qlora_rmsnorm_backward", "qlora_rope_forward", "qlora_rope_backward", "qlora_rope_table",
+              "qlora_forward_rope", "qlora_lmhead_prepare", "qlora_chunked_ce"):
         getattr(L, f).restype = ctypes.c_int
     _lib = L
     return L

@@ -388,6 +388,30 @@ int qlora_forward(const qlora_layer* L, const uint16_t* X, int64_t M, uint16_t* 
   return QLORA_OK;
 }
 
+int qlora_rope_table(int d, float base, int64_t max_pos, float* table, void* stream) {
+  if (d < 16 || d > 1024 || d % 16 != 0 || !(base > 1.f) || max_pos < 0 || max_pos > kMaxDim) return QLORA_EINVAL;
+  if (max_pos == 0) return QLORA_OK;
+  if (!table || !aligned16(table)) return QLORA_EINVAL;
+  hipStream_t st = (hipStream_t)stream;
+  QL_LAUNCH("rope_table", st, launch_rope_table(d, (double)base, max_pos, table, st));
+  return QLORA_OK;
+}
+
+int qlora_forward_rope(const qlora_layer* L, const uint16_t* X, int64_t M, const int32_t* pos, const float* table,
+                       int64_t max_pos, int d, uint16_t* Y, uint16_t* Z_save, void* stream) {
+  if (!layer_ok(L) || M < 0 || d != 128 || L->N % d != 0 || max_pos < 1 || max_pos > kMaxDim) return QLORA_EINVAL;
+  if (M == 0) return QLORA_OK;
+  if (!X || !Y || !Z_save || !pos || !table || !aligned16(X) || !aligned16(Y) || !aligned16(Z_save) ||
+      !aligned16(table))
+    return QLORA_EINVAL;
+  hipStream_t st = (hipStream_t)stream;
+  const int r = (int)L->r;
+  QL_LAUNCH("skinny_nt", st, launch_skinny_nt(nt1(X, M, L->K, L->A, r, Z_save, r), st));
+  QL_LAUNCH("gemm_fwd_rope", st,
+            launch_gemm_fwd_rope(X, M, L->K, L->N, wsrc(L, L->B, Z_save), pos, table, max_pos, Y, st));
+  return QLORA_OK;
+}
+
 int qlora_backward(const qlora_layer* L, const uint16_t* dY, const uint16_t* X, const uint16_t* Z_save, int64_t M,
                    uint16_t* dX, void* dA, void* dB, void* ws, size_t ws_bytes, void* stream) {
   if (!layer_ok(L) || M < 0) return QLORA_EINVAL;

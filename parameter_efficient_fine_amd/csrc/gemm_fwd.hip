@@ -65,13 +65,18 @@ struct FwdArgs {
   uint16_t* out0;  // Y | g
   uint16_t* out1;  // u
   uint16_t* out2;  // h
+  const int32_t* pos;     // RoPE epilogue: token positions [M]
+  const float* rope_tab;  // [max_pos][64][2] fp32 (cos, sin)
+  int64_t max_pos;
 };
+
+constexpr int kRopeD = 128;  // head size of the RoPE epilogue (Llama-3)
 
 // The epilogue is branch-free: loads and stores go through buffer resources
 // (out-of-range lanes read zero or drop their store); divergent branches there
 // would push the 256 accumulators out of AGPRs and spill the main loop.
 
-template <int F, bool GATEUP, int RP, bool ALIGNED>
+template <int F, bool GATEUP, int RP, bool ALIGNED, bool ROPE>
 __global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_per_eu(1, 1)))
 void k_qgemm_fwd(FwdArgs p) {
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];  // [kNBuf][256 rows][128 B], swizzled
@@ -294,6 +299,90 @@ void k_qgemm_fwd(FwdArgs p) {
   if (s < nsteps) body(s, cs0, L0, cs1, as1, L1, cs2, as2);
   if (s + 1 < nsteps) body(s + 1, cs1, L1, cs2, as2, L2, cs0, as0);
 
+  // ---- RoPE epilogue ("Unsloth" wiki entry, Theory: fused RoPE kernel; rotate
+  // half, heads of 128 output columns, so the workgroup's 256 columns are two
+  // heads). The rotation pairs column i with i + 64 of the same head, which
+  // another wave holds; so, 32 tokens at a time, the four waves park their fp32
+  // results in LDS (free once the loop has ended) as a [32 token][256 column]
+  // tile, and each lane then takes one token and 8 frequencies
+  // (4g .. 4g+3 and 32+4g .. 32+4g+3) in both heads: it reads each (cos, sin)
+  // it needs once, rotates (first half v c - w s, second half w c + v s) and
+  // rounds once to bf16. Tile rows are 64 chunks of 16 bytes, chunk c of row t
+  // stored at c ^ (t & 7) (conflict-free writes and reads); the (cos, sin) rows
+  // come from the position table two fragments ahead.
+  if constexpr (ROPE) {
+    __builtin_amdgcn_s_waitcnt(0);  // this wave's trailing copies into the ring have landed
+    __builtin_amdgcn_s_barrier();   // and every wave is done reading the ring
+    // lane indices re-read through an empty asm: no prologue offsets stay alive
+    // across the main loop for this epilogue
+    int lne = lane, jle = jl, he = h;
+    asm volatile("" : "+v"(lne), "+v"(jle), "+v"(he));
+    float* const xb = reinterpret_cast<float*>(smem);  // [2 parity][32 rows][256 columns]
+    const int L = 64 * wave + lne, tt = L >> 3, g = L & 7;  // reader: token row tt, frequency group g
+    const int Ni = (int)N, rh = (int)rows_here, ci0 = (int)i0;
+    const __amdgpu_buffer_rsrc_t rPos = make_rsrc(p.pos + j0, rows_here * 4);
+    const __amdgpu_buffer_rsrc_t rTab = make_rsrc(p.rope_tab, p.max_pos * (kRopeD / 2) * 8);
+    const __amdgpu_buffer_rsrc_t rY = make_rsrc(p.out0 + j0 * N, rows_here * N * 2);
+    const int maxp = (int)p.max_pos;
+    // (cos, sin) of frequencies 4g .. 4g+3 and 32+4g .. +3 at the position of token
+    // row tt of fragment j (a position outside the table reads zeros)
+    u32x4 tb[3][4];
+    auto tload = [&](int j, u32x4 (&t)[4]) {
+      const int pj = (int)__builtin_amdgcn_raw_buffer_load_b32(rPos, (32 * j + tt) * 4, 0, 0);
+      const int base = (pj >= 0 && pj < maxp) ? (pj * (kRopeD / 2) + 4 * g) * 8 : kOff;
+      const int b2 = base == kOff ? kOff : base + 32 * 8;
+      t[0] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rTab, base, 0, 0));
+      t[1] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rTab, base, 16, 0));
+      t[2] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rTab, b2, 0, 0));
+      t[3] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rTab, b2, 16, 0));
+    };
+    tload(0, tb[0]);
+    tload(1, tb[1]);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      if (j + 2 < 8) tload(j + 2, tb[(j + 2) % 3]);
+      float* const tile = xb + (j & 1) * 32 * 256;
+      // writer: token row jle, chunk 16 wave + 8f + 2q + he holds columns 64 wave + 32f + 8q + 4he .. +3
+#pragma unroll
+      for (int f = 0; f < 2; ++f)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int c = (16 * wave + 8 * f + 2 * q + he) ^ (jle & 7);
+          *reinterpret_cast<f32x4*>(tile + jle * 256 + 4 * c) =
+              f32x4{acc[f][j][4 * q], acc[f][j][4 * q + 1], acc[f][j][4 * q + 2], acc[f][j][4 * q + 3]};
+        }
+      lds_barrier();
+      // reader: quarter k = head (k >> 1), half (k & 1); chunks 16k + g (frequencies 4g ..)
+      // and 16k + 8 + g (frequencies 32 + 4g ..)
+      f32x4 v[4][2];
+#pragma unroll
+      for (int k = 0; k < 4; ++k)
+#pragma unroll
+        for (int u = 0; u < 2; ++u)
+          v[k][u] = *reinterpret_cast<const f32x4*>(tile + tt * 256 + 4 * ((16 * k + 8 * u + g) ^ (tt & 7)));
+      const u32x4(&t)[4] = tb[j % 3];
+      const int mr = 32 * j + tt;
+#pragma unroll
+      for (int hd = 0; hd < 2; ++hd)
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+          const f32x4 t0 = __builtin_bit_cast(f32x4, t[2 * u]), t1 = __builtin_bit_cast(f32x4, t[2 * u + 1]);
+          const float c[4] = {t0[0], t0[2], t1[0], t1[2]}, sn[4] = {t0[1], t0[3], t1[1], t1[3]};
+          const f32x4 a = v[2 * hd][u], b = v[2 * hd + 1][u];  // first and second half of the head
+          float lo[4], hi[4];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            lo[e] = a[e] * c[e] - b[e] * sn[e];
+            hi[e] = b[e] * c[e] + a[e] * sn[e];
+          }
+          const int icl = ci0 + 128 * hd + 32 * u + 4 * g, ich = icl + 64;
+          store4(rY, (mr < rh && icl < Ni) ? (mr * Ni + icl) * 2 : kOff, lo);
+          store4(rY, (mr < rh && ich < Ni) ? (mr * Ni + ich) * 2 : kOff, hi);
+        }
+    }
+    return;
+  }
+
   // ---- epilogue (no control flow): SwiGLU gate for gate/up, bf16 stores
   const __amdgpu_buffer_rsrc_t rO0 = make_rsrc(p.out0 + j0 * N, rows_here * N * 2);
   const __amdgpu_buffer_rsrc_t rO1 = make_rsrc(GATEUP ? p.out1 + j0 * N : p.out0, GATEUP ? rows_here * N * 2 : 0);
@@ -335,34 +424,34 @@ void k_qgemm_fwd(FwdArgs p) {
   }
 }
 
-template <bool GATEUP, int RP, bool ALIGNED>
+template <bool GATEUP, int RP, bool ALIGNED, bool ROPE>
 hipError_t launch_rp(const FwdArgs& a, hipStream_t st) {
   // set once per kernel instance; a function-local static is initialised exactly
   // once even when several threads make their first call together
-  static const hipError_t attr = hipFuncSetAttribute((const void*)k_qgemm_fwd<kFmt, GATEUP, RP, ALIGNED>,
+  static const hipError_t attr = hipFuncSetAttribute((const void*)k_qgemm_fwd<kFmt, GATEUP, RP, ALIGNED, ROPE>,
                                                      hipFuncAttributeMaxDynamicSharedMemorySize, (int)kLds);
   if (attr != hipSuccess) return attr;
   const int64_t ipt = GATEUP ? 128 : 256;
   const int64_t nI = (a.N + ipt - 1) / ipt, nJ = (a.M + kTok - 1) / kTok;
   if (nI * nJ == 0) return hipSuccess;
-  k_qgemm_fwd<kFmt, GATEUP, RP, ALIGNED><<<(unsigned)(nI * nJ), 256, kLds, st>>>(a);
+  k_qgemm_fwd<kFmt, GATEUP, RP, ALIGNED, ROPE><<<(unsigned)(nI * nJ), 256, kLds, st>>>(a);
   return hipGetLastError();
 }
 
-template <bool GATEUP, int RP>
+template <bool GATEUP, int RP, bool ROPE>
 hipError_t launch_al(const FwdArgs& a, hipStream_t st) {
   const bool aligned = (a.w0.r % 8 == 0) && (a.w1.r % 8 == 0);
-  return aligned ? launch_rp<GATEUP, RP, true>(a, st) : launch_rp<GATEUP, RP, false>(a, st);
+  return aligned ? launch_rp<GATEUP, RP, true, ROPE>(a, st) : launch_rp<GATEUP, RP, false, ROPE>(a, st);
 }
 
-template <bool GATEUP>
+template <bool GATEUP, bool ROPE = false>
 hipError_t launch(const FwdArgs& a, hipStream_t st) {
   const int r = a.w0.r > a.w1.r ? a.w0.r : a.w1.r;
-  if (r <= 16) return launch_al<GATEUP, 16>(a, st);
-  if (r <= 32) return launch_al<GATEUP, 32>(a, st);
-  if (r <= 64) return launch_al<GATEUP, 64>(a, st);
-  if (r <= 128) return launch_al<GATEUP, 128>(a, st);
-  if (r <= 256) return launch_al<GATEUP, 256>(a, st);
+  if (r <= 16) return launch_al<GATEUP, 16, ROPE>(a, st);
+  if (r <= 32) return launch_al<GATEUP, 32, ROPE>(a, st);
+  if (r <= 64) return launch_al<GATEUP, 64, ROPE>(a, st);
+  if (r <= 128) return launch_al<GATEUP, 128, ROPE>(a, st);
+  if (r <= 256) return launch_al<GATEUP, 256, ROPE>(a, st);
   return hipErrorInvalidValue;
 }
 
@@ -377,6 +466,20 @@ hipError_t launch_gemm_fwd(const uint16_t* X, int64_t M, int64_t K, int64_t N, W
   a.M = M, a.K = K, a.N = N;
   a.out0 = Y;
   return launch<false>(a, st);
+}
+
+hipError_t launch_gemm_fwd_rope(const uint16_t* X, int64_t M, int64_t K, int64_t N, WSrc w, const int32_t* pos,
+                                const float* table, int64_t max_pos, uint16_t* Y, hipStream_t st) {
+  if (N % kRopeD != 0) return hipErrorInvalidValue;
+  FwdArgs a{};
+  a.X = X;
+  a.w0 = a.w1 = w;
+  a.M = M, a.K = K, a.N = N;
+  a.out0 = Y;
+  a.pos = pos;
+  a.rope_tab = table;
+  a.max_pos = max_pos;
+  return launch<false, true>(a, st);
 }
 
 hipError_t launch_gemm_fwd_gateup(const uint16_t* X, int64_t M, int64_t K, int64_t N, WSrc wg, WSrc wu, uint16_t* g,

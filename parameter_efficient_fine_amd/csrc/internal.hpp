@@ -127,6 +127,9 @@ struct WSrc {           // one frozen quantized weight [N, K] with its LoRA pair
   /* Y[M, N] = X . What^T + s . Z . B^T */                                                                         \
   hipError_t launch_gemm_fwd(const uint16_t* X, int64_t M, int64_t K, int64_t N, WSrc w, uint16_t* Y,              \
                              hipStream_t st);                                                                      \
+  /* the same with RoPE (heads of 128, rotate half) applied to the fp32 result before its bf16 rounding */          \
+  hipError_t launch_gemm_fwd_rope(const uint16_t* X, int64_t M, int64_t K, int64_t N, WSrc w, const int32_t* pos,  \
+                                  const float* table, int64_t max_pos, uint16_t* Y, hipStream_t st);               \
   /* gate/up of the SwiGLU block in one pass: g, u [M, N], h = silu(g) * u */                                      \
   hipError_t launch_gemm_fwd_gateup(const uint16_t* X, int64_t M, int64_t K, int64_t N, WSrc wg, WSrc wu,          \
                                     uint16_t* g, uint16_t* u, uint16_t* h, hipStream_t st);                        \
@@ -147,6 +150,10 @@ namespace f2 { QL_GEMM_LAUNCHERS }
 inline hipError_t launch_gemm_fwd(const uint16_t* X, int64_t M, int64_t K, int64_t N, WSrc w, uint16_t* Y,
                                   hipStream_t st) {
   return QL_BY_FMT(w.fmt, launch_gemm_fwd(X, M, K, N, w, Y, st));
+}
+inline hipError_t launch_gemm_fwd_rope(const uint16_t* X, int64_t M, int64_t K, int64_t N, WSrc w, const int32_t* pos,
+                                       const float* table, int64_t max_pos, uint16_t* Y, hipStream_t st) {
+  return QL_BY_FMT(w.fmt, launch_gemm_fwd_rope(X, M, K, N, w, pos, table, max_pos, Y, st));
 }
 inline hipError_t launch_gemm_fwd_gateup(const uint16_t* X, int64_t M, int64_t K, int64_t N, WSrc wg, WSrc wu,
                                          uint16_t* g, uint16_t* u, uint16_t* h, hipStream_t st) {
@@ -181,6 +188,8 @@ hipError_t launch_rmsnorm_fwd(const uint16_t* x, const uint16_t* w, int64_t M, i
                               float* rstd, hipStream_t st);
 hipError_t launch_rmsnorm_bwd(const uint16_t* dy, const uint16_t* x, const uint16_t* w, const float* rstd, int64_t M,
                               int64_t H, uint16_t* dx, hipStream_t st);
+// cos/sin table [max_pos][d/2][2] fp32 of the RoPE angles (fp64 angles and sin/cos)
+hipError_t launch_rope_table(int d, double base, int64_t max_pos, float* table, hipStream_t st);
 // In-place RoPE of q [M, hq*d] and k [M, hk*d] by pos [M]; inverse rotates back.
 hipError_t launch_rope(uint16_t* q, uint16_t* k, const int32_t* pos, int64_t M, int hq, int hk, int d, double base,
                        bool inverse, hipStream_t st);

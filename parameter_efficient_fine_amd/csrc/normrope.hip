@@ -263,6 +263,28 @@ hipError_t launch_rmsnorm_bwd(const uint16_t* dy, const uint16_t* x, const uint1
   });
 }
 
+// cos/sin of every (position, frequency), formed as k_rope forms them (angle and
+// sin/cos in fp64, rounded once to fp32): table[(p * d/2 + i) * 2 + 0 / 1] =
+// cos / sin of p * base^(-2i/d). Read by the q/k projection GEMM's RoPE epilogue.
+__global__ __launch_bounds__(256) void k_rope_table(int d, double base, int64_t n, float* __restrict__ table) {
+  const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (idx >= n) return;
+  const int half = d / 2;
+  const int64_t p = idx / half;
+  const int i = (int)(idx - p * half);
+  const double a = (double)p * pow(base, -2.0 * i / d);
+  double sv, cv;
+  sincos(a, &sv, &cv);
+  reinterpret_cast<f32x2*>(table)[idx] = f32x2{(float)cv, (float)sv};
+}
+
+hipError_t launch_rope_table(int d, double base, int64_t max_pos, float* table, hipStream_t st) {
+  const int64_t n = max_pos * (d / 2);
+  if (n == 0) return hipSuccess;
+  k_rope_table<<<(unsigned)((n + 255) / 256), 256, 0, st>>>(d, base, n, table);
+  return hipGetLastError();
+}
+
 hipError_t launch_rope(uint16_t* q, uint16_t* k, const int32_t* pos, int64_t M, int hq, int hk, int d, double base,
                        bool inverse, hipStream_t st) {
   if (M == 0 || hq + hk == 0) return hipSuccess;

@@ -338,6 +338,30 @@ def rope_backward(dq, dk, pos, d: int, base: float):
     return _rope("qlora_rope_backward", dq, dk, pos, d, base)
 
 
+def rope_table(d: int, base: float, max_pos: int, device="cuda"):
+    """fp32 cos/sin of the RoPE angles [max_pos, d/2, 2] (fp64 angles and sin/cos)."""
+    t = torch.empty((max_pos, d // 2, 2), dtype=torch.float32, device=device)
+    C.check("qlora_rope_table", C.lib().qlora_rope_table(d, float(base), max_pos, _ptr(t), _stream()))
+    return t
+
+
+def forward_rope(L: QLoraLayer, X: torch.Tensor, pos, table, d: int = 128, Y=None, Z=None):
+    """Y = rope(X.W^T + s.Z.B^T) [M,N] bf16 (RoPE in the GEMM epilogue) and Z = X.A^T [M,r]."""
+    M = X.shape[0]
+    _need(X, torch.bfloat16, (M, L.K), "X")
+    _need(pos, torch.int32, (M,), "pos")
+    max_pos = table.shape[0]
+    _need(table, torch.float32, (max_pos, d // 2, 2), "table")
+    Y = torch.empty((M, L.N), dtype=torch.bfloat16, device=X.device) if Y is None else Y
+    Z = torch.empty((M, L.r), dtype=torch.bfloat16, device=X.device) if Z is None else Z
+    _need(Y, torch.bfloat16, (M, L.N), "Y")
+    _need(Z, torch.bfloat16, (M, L.r), "Z")
+    lc = L.c()
+    C.check("qlora_forward_rope", C.lib().qlora_forward_rope(ctypes.byref(lc), _ptr(X), M, _ptr(pos), _ptr(table),
+                                                             max_pos, d, _ptr(Y), _ptr(Z), _stream()))
+    return Y, Z
+
+
 def lmhead_prepare(W):
     """The frozen LM head W [V, H] (bf16) laid out for chunked_ce's two products: (Wp, Wtp),
     each V*H bf16 values (tiled; see qlora_lmhead_prepare)."""

@@ -39,6 +39,7 @@ PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 MFMA (published)
 PEAK_HBM_GBS = 8000.0
 RIDGE_FLOP_PER_BYTE = PEAK_BF16_TFLOPS * 1e12 / (PEAK_HBM_GBS * 1e9)  # ~312: below it a step is HBM/latency-bound
 COLD_STEPS = 10
+SMALL_MAX_M, SMALL_MAX_R = 256, 32  # the library's small-batch path (one wave per 32 x 32 tile)
 WL_INDEX = {"tiny": 0, "attn": 1, "mlp": 2, "rsweep": 3, "layer": 4, "normrope": None, "lmhead": None,
             "qkrope": None}
 # cross-entropy over the Llama-3-8B LM head (vocabulary 128256, width 4096) for
@@ -80,6 +81,10 @@ def parse():
 # HBM traffic of the dominant kernel, from committed hardware-counter summaries
 
 KERNEL_SOURCES = {  # kernel class -> the sources its code is built from
+    "small_fwd": ["small.hip", "common.hpp"],
+    "small_bwd": ["small.hip", "common.hpp"],
+    "skinny_tn": ["skinny.hip", "common.hpp"],
+    "skinny_nt": ["skinny.hip", "common.hpp"],
     "gemm_bwd": ["gemm_bwd.hip", "common.hpp"],
     "gemm_bwd_swiglu": ["gemm_bwd.hip", "common.hpp"],
     "gemm_fwd": ["gemm_fwd.hip", "common.hpp"],
@@ -450,6 +455,8 @@ def gemm_flops(parts):
             M, K, N, r = p.M, p.K, p.N, p.r
             out.setdefault("gemm_fwd", []).append(2 * M * N * K + 2 * M * N * r)   # X.W^T + Z.B^T
             out.setdefault("gemm_fwd_rope", []).append(2 * M * N * K + 2 * M * N * r)
+            out.setdefault("small_fwd", []).append(2 * M * N * K + 2 * M * N * r + 2 * M * K * r)
+            out.setdefault("small_bwd", []).append(2 * M * N * K + 2 * M * K * r + 2 * M * N * r)
             out.setdefault("gemm_bwd", []).append(2 * M * N * K + 2 * M * K * r)   # dY.W + G.A
         else:
             H, I, r = p.H, p.I, p.r
@@ -480,7 +487,13 @@ def launch_bytes(parts, fmt=0):
         out.setdefault(k, []).append(float(v))
 
     for p in parts:
-        if isinstance(p, Proj):
+        if isinstance(p, Proj) and p.M <= SMALL_MAX_M and p.r <= SMALL_MAX_R:
+            # small-batch kernels: Y and Z in one launch, dX and G in one, then dB and dA
+            M, K, N, r = p.M, p.K, p.N, p.r
+            add("small_fwd", 2 * M * K + _wbytes(N, K, fmt) + 2 * r * K + 2 * N * r + 2 * M * N + 2 * M * r)
+            add("small_bwd", 2 * M * N + _wbytes(N, K, fmt) + 2 * r * K + 2 * N * r + 2 * M * K + 2 * M * r)
+            add("skinny_tn", 2 * M * N + 2 * M * r + 2 * M * K + 2 * M * r + 4 * r * (N + K))
+        elif isinstance(p, Proj):
             M, K, N, r = p.M, p.K, p.N, p.r
             add("gemm_fwd", 2 * M * K + _wbytes(N, K, fmt) + 2 * M * r + 2 * N * r + 2 * M * N)
             add("gemm_bwd", 2 * M * N + _wbytes(N, K, fmt) + 2 * M * r + 2 * r * K + 2 * M * K)

@@ -16,6 +16,7 @@ OBJDIR = os.path.join(HERE, "_build")
 # (source, object, extra flags): the fused GEMMs are built once per weight
 # format (QL_WFMT 0 NF4, 1 INT8, 2 FP8), each into its own namespace
 SOURCES = [("quant.hip", "quant.o", []), ("skinny.hip", "skinny.o", []), ("normrope.hip", "normrope.o", []),
+           ("small.hip", "small.o", []),
            ("lmhead.hip", "lmhead.o", []),
            ("api.cpp", "api.o", [])] + [
     (f"{g}.hip", f"{g}_f{fmt}.o", [f"-DQL_WFMT={fmt}"]) for g in ("gemm_bwd", "gemm_fwd") for fmt in (0, 1, 2)]

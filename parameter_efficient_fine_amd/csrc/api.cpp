@@ -196,6 +196,11 @@ size_t mlp_bwd_tiled_ws(int64_t M, int64_t H, int64_t I, int64_t r, int64_t tile
          2 * up256(r * I * 2) + up256(mlp_tiled_part_floats(M, H, I, r, tile) * 4) + mlp_grad_acc_bytes(H, I, r);
 }
 
+// Batches of at most kSmallMaxM tokens (ranks up to kSmallMaxR) take the
+// small-batch kernels: one wave per 32 x 32 output tile, the rank-r products
+// of the tile formed alongside, one-split reductions written out directly.
+bool small_batch(const qlora_layer* L, int64_t M) { return M <= kSmallMaxM && L->r <= kSmallMaxR; }
+
 WSrc wsrc(const qlora_layer* L, const uint16_t* lora_i, const uint16_t* lora_j, int64_t ldj = 0) {
   WSrc w;
   w.codes = L->codes;
@@ -289,8 +294,11 @@ struct TnCall {
   }
   int flush() {
     if (jobs.n == 0 || rc != QLORA_OK) return rc;
+    bool reduce = false;  // one-split jobs are written out by skinny_tn itself
+    for (int i = 0; i < jobs.n; ++i)
+      reduce = reduce || skinny_tn_plan(jobs.job[i].M, jobs.job[i].Kd, jobs.job[i].r1 + jobs.job[i].r2).splits > 1;
     hipError_t e = timed("skinny_tn", st, [&]() { return launch_skinny_tn(jobs, st); });
-    if (e == hipSuccess) e = timed("tn_reduce", st, [&]() { return launch_tn_reduce(jobs, st); });
+    if (e == hipSuccess && reduce) e = timed("tn_reduce", st, [&]() { return launch_tn_reduce(jobs, st); });
     if (e != hipSuccess) rc = hip_fail(e, "skinny_tn");
     jobs.n = 0;
     return rc;
@@ -383,6 +391,11 @@ int qlora_forward(const qlora_layer* L, const uint16_t* X, int64_t M, uint16_t* 
   if (!X || !Y || !Z_save || !aligned16(X) || !aligned16(Y) || !aligned16(Z_save)) return QLORA_EINVAL;
   hipStream_t st = (hipStream_t)stream;
   const int r = (int)L->r;
+  if (small_batch(L, M)) {
+    const SmallFwdArgs a{X, L->codes, L->absmax, L->A, L->B, M, L->K, L->N, r, L->s, Y, Z_save};
+    QL_LAUNCH("small_fwd", st, launch_small_fwd(a, L->format, st));
+    return QLORA_OK;
+  }
   QL_LAUNCH("skinny_nt", st, launch_skinny_nt(nt1(X, M, L->K, L->A, r, Z_save, r), st));
   QL_LAUNCH("gemm_fwd", st, launch_gemm_fwd(X, M, L->K, L->N, wsrc(L, L->B, Z_save), Y, st));
   return QLORA_OK;
@@ -436,6 +449,16 @@ int qlora_backward(const qlora_layer* L, const uint16_t* dY, const uint16_t* X, 
     QL_LAUNCH("fill_zero", st, zero_grad(dA, (int64_t)r * K, gb, st));
     QL_LAUNCH("fill_zero", st, zero_grad(dB, (int64_t)N * r, gb, st));
     return QLORA_OK;
+  }
+  if (small_batch(L, M) && dX) {
+    // dX and G in one launch, then dB and dA (one split each, written directly)
+    const SmallBwdArgs a{dY, L->codes, L->absmax, L->A, L->B, M, K, N, r, L->s, dX, G};
+    QL_LAUNCH("small_bwd", st, launch_small_bwd(a, L->format, st));
+    TnCall tn{part, part + lay.part, st};
+    tn.out_bf16 = gb;
+    tn.one(Z_save, r, r, L->s, dY, M, N, dB, true);
+    tn.one(G, r, r, L->s, X, M, K, dA, false);
+    return tn.flush();
   }
   if (!b_in_place(r)) {
     PrepJobs pj{};

@@ -170,6 +170,37 @@ inline hipError_t launch_gemm_bwd_swiglu(const uint16_t* dY, WSrc w, int64_t M, 
 }
 #undef QL_BY_FMT
 
+// Small-batch path (batches of at most kSmallMaxM tokens, ranks up to
+// kSmallMaxR): one wave per 32 x 32 output tile over the whole reduction.
+constexpr int64_t kSmallMaxM = 256;
+constexpr int kSmallMaxR = 32;
+struct SmallFwdArgs {       // Y = X . What^T + s . Z . B^T and Z = X . A^T
+  const uint16_t* X;        // [M, K]
+  const uint8_t* codes;     // frozen weight [N, K] (storage order of qlora.h)
+  const float* absmax;
+  const uint16_t* A;        // [r, K]
+  const uint16_t* B;        // [N, r]
+  int64_t M, K, N;
+  int r;
+  float s;
+  uint16_t* Y;              // [M, N]
+  uint16_t* Z;              // [M, r]
+};
+struct SmallBwdArgs {       // dX = dY . What + s . G . A and G = dY . B
+  const uint16_t* dY;       // [M, N]
+  const uint8_t* codes;
+  const float* absmax;
+  const uint16_t* A;
+  const uint16_t* B;
+  int64_t M, K, N;
+  int r;
+  float s;
+  uint16_t* dX;             // [M, K] (may be null: G only)
+  uint16_t* G;              // [M, r]
+};
+hipError_t launch_small_fwd(const SmallFwdArgs& a, int fmt, hipStream_t st);
+hipError_t launch_small_bwd(const SmallBwdArgs& a, int fmt, hipStream_t st);
+
 // LM head and chunked cross-entropy: Y [M, N] = X [M, K] . W [N, K]^T (bf16
 // operands, W in the tiled order of launch_tile_nt, fp32 or bf16 output); per-row statistics of a logits chunk; counts
 // and the final mean.

@@ -302,6 +302,7 @@ TnPlan skinny_tn_plan(int64_t M, int64_t Kd, int R) {
   const int64_t by_traffic = M / (8 * RR);                     // partials <= 1/4 of Q's bytes
   if (splits > by_traffic) splits = by_traffic;
   if (splits > 64) splits = 64;
+  if (M <= kSmallMaxM) splits = 1;  // short batches: one split, written out directly (no reduce launch)
   if (splits < 1) splits = 1;
   int64_t rows = (M + splits - 1) / splits;
   rows = (rows + kTnRows - 1) / kTnRows * kTnRows;
@@ -437,6 +438,33 @@ __global__ __launch_bounds__(256) void k_skinny_tn(TnJobs jobs) {
     lds_barrier();
   }
 
+  // One split: the result itself, as k_tn_reduce would write it from a single
+  // partial (one multiply by s, then fp32 (accumulated or not) or bf16).
+  if (p.splits == 1) {
+#pragma unroll
+    for (int a = 0; a < NJ; ++a)
+#pragma unroll
+      for (int b = 0; b < 2; ++b) {
+        const int64_t k = k0 + 32 * wave + 16 * b + sl;
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+          const int j = 16 * a + 4 * g + v;
+          if (j >= R || k >= Kd) continue;
+          const bool first = j < p.r1;
+          const float val = acc[a][b][v] * (first ? p.s1 : p.s2);
+          const int64_t jr = first ? j : j - p.r1, ldo = first ? p.ldo1 : p.ldo2;
+          const int64_t idx = p.transposed ? k * ldo + jr : jr * ldo + k;
+          void* out = first ? p.out1 : p.out2;
+          if (p.out_bf16) {
+            static_cast<uint16_t*>(out)[idx] = __builtin_bit_cast(uint16_t, (__bf16)val);
+          } else {
+            float* o = static_cast<float*>(out) + idx;
+            *o = p.accumulate ? *o + val : val;
+          }
+        }
+      }
+    return;
+  }
   // this split's partial. C layout: col (Q column) = lane%16, row (j) = 4*(lane/16) + v
   float* dst = p.part + (int64_t)blockIdx.y * R * Kd;
 #pragma unroll
@@ -555,13 +583,17 @@ hipError_t launch_skinny_tn(TnJobs jobs, hipStream_t st) {
 hipError_t launch_tn_reduce(TnJobs jobs, hipStream_t st) {
   if (jobs.n < 1 || jobs.n > kTnMaxJobs) return hipErrorInvalidValue;
   int64_t nmax = 0;
+  TnJobs multi{};  // the jobs with more than one split (one-split jobs wrote their result already)
   for (int i = 0; i < jobs.n; ++i) {
-    TnArgs& a = jobs.job[i];
+    TnArgs a = jobs.job[i];
     a.splits = skinny_tn_plan(a.M, a.Kd, a.r1 + a.r2).splits;
+    if (a.splits == 1) continue;
+    multi.job[multi.n++] = a;
     const int64_t n = (int64_t)(a.r1 + a.r2) * (a.Kd / 4);
     nmax = n > nmax ? n : nmax;
   }
-  if (nmax == 0) return hipSuccess;
+  jobs = multi;
+  if (nmax == 0 || jobs.n == 0) return hipSuccess;
   k_tn_reduce<<<dim3((unsigned)((nmax + 63) / 64), 1, (unsigned)jobs.n), 64, 0, st>>>(jobs);
   return hipGetLastError();
 }

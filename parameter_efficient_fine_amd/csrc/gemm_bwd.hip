@@ -699,22 +699,34 @@ void k_qgemm_bwd8(BwdArgs p) {
     swiglu_epilogue<4>(acc, rGs, rUs, rO0, rO1, 128 * th, rows_here, kc, K, jl, h);
     return;
   }
+  // dX through LDS (as in the forward GEMM): each wave parks its 128 tokens x 64
+  // columns as bf16 in its own 16 KB of the idle buffers, rows of 128 bytes with
+  // 16-byte chunk c of token row t at c ^ (t & 7), and stores 16-byte row pieces,
+  // so that one store instruction writes whole 128-byte pieces of 8 rows.
+  __builtin_amdgcn_s_waitcnt(0);  // this wave's trailing dY copies have landed
+  __builtin_amdgcn_s_barrier();   // and every wave is done with the buffers
+  int jle = jl, he = h, lne = lane;
+  asm volatile("" : "+v"(jle), "+v"(he), "+v"(lne));
+  uint8_t* const reg = smem + wave * (128 * 128);
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
-    const int64_t mr = 128 * th + 32 * j + jl;
-    const bool m_ok = mr < rows_here;
+    const int t = 32 * j + jle;
 #pragma unroll
-    for (int f = 0; f < 2; ++f) {
+    for (int f = 0; f < 2; ++f)
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const int64_t ic = kc + 32 * f + 8 * q + 4 * h;
-        const int off = (m_ok && ic < K) ? (int)((mr * K + ic) * 2) : kOff;
-        float v[4];
+      for (int q = 0; q < 4; ++q)
+        *reinterpret_cast<u32x2*>(reg + t * 128 + 16 * ((4 * f + q) ^ (t & 7)) + 8 * he) =
+            u32x2{pack_bf16x2(acc[f][j][4 * q], acc[f][j][4 * q + 1]),
+                  pack_bf16x2(acc[f][j][4 * q + 2], acc[f][j][4 * q + 3])};
+  }
+  lds_barrier();
+  const int c = lne & 7, tq = lne >> 3, rh = (int)rows_here;
+  const int64_t col = kc + 8 * c;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) v[e] = acc[f][j][4 * q + e];
-        store4(rO0, off, v);
-      }
-    }
+  for (int u = 0; u < 16; ++u) {
+    const int t = 8 * u + tq, mr = 128 * th + t;
+    const u32x4 v = *reinterpret_cast<const u32x4*>(reg + t * 128 + 16 * (c ^ (t & 7)));
+    __builtin_amdgcn_raw_buffer_store_b128(v, rO0, (mr < rh && col < K) ? (int)((mr * K + col) * 2) : kOff, 0, 0);
   }
 }
 

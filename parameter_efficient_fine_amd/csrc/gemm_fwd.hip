@@ -238,7 +238,6 @@ void k_qgemm_fwd(FwdArgs p) {
       __builtin_amdgcn_sched_group_barrier(0x002, decltype(nvalu)::value, 0);
     }
   };
-  using I0 = std::integral_constant<int, 0>;
   using I2 = std::integral_constant<int, 2>;
   using I4 = std::integral_constant<int, 4>;
   using I6 = std::integral_constant<int, 6>;
@@ -394,44 +393,97 @@ void k_qgemm_fwd(FwdArgs p) {
     return;
   }
 
-  // ---- epilogue (no control flow): SwiGLU gate for gate/up, bf16 stores
-  const __amdgpu_buffer_rsrc_t rO0 = make_rsrc(p.out0 + j0 * N, rows_here * N * 2);
-  const __amdgpu_buffer_rsrc_t rO1 = make_rsrc(GATEUP ? p.out1 + j0 * N : p.out0, GATEUP ? rows_here * N * 2 : 0);
-  const __amdgpu_buffer_rsrc_t rO2 = make_rsrc(GATEUP ? p.out2 + j0 * N : p.out0, GATEUP ? rows_here * N * 2 : 0);
+  // ---- epilogue through LDS. The accumulator layout gives a lane 4 columns of
+  // one token, so direct stores would write 8 bytes into each of 32 rows per
+  // instruction. Instead each wave parks its results as bf16 in its own 32 KB
+  // of the ring (idle once the loop has ended), token-major, and reads them
+  // back in 16-byte row pieces: a store instruction then covers whole 128-byte
+  // (plain: 64 columns) or 64-byte (gate/up: 32 columns) pieces of 8 or 16 rows.
+  // Plain: rows of 128 bytes, 16-byte chunk c of token row t at c ^ (t & 7).
+  // Gate/up: g and u, then h, as rows of 64 bytes, chunk c at c ^ ((t >> 2) & 3);
+  // h = silu(g) * u from the fp32 accumulators.
+  __builtin_amdgcn_s_waitcnt(0);  // this wave's trailing copies into the ring have landed
+  __builtin_amdgcn_s_barrier();   // and every wave is done reading the ring
+  int jle = jl, he = h, lne = lane;
+  asm volatile("" : "+v"(jle), "+v"(he), "+v"(lne));  // no prologue values kept alive for this
+  uint8_t* const reg = smem + wave * (kTok * 128);
+  const int rh = (int)rows_here;
+  if constexpr (!GATEUP) {
 #pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    const int64_t mr = 32 * j + jl;  // token row within the tile
-    const bool m_ok = mr < rows_here;
-    if (!GATEUP) {
+    for (int j = 0; j < 8; ++j) {
+      const int t = 32 * j + jle;
 #pragma unroll
-      for (int f = 0; f < 2; ++f) {
+      for (int f = 0; f < 2; ++f)
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const int64_t ic = nb[f] + 8 * q + 4 * h;
-          const int off = (m_ok && ic < N) ? (int)((mr * N + ic) * 2) : kOff;
-          float v[4];
+        for (int q = 0; q < 4; ++q)
+          *reinterpret_cast<u32x2*>(reg + t * 128 + 16 * ((4 * f + q) ^ (t & 7)) + 8 * he) =
+              u32x2{pack_bf16x2(acc[f][j][4 * q], acc[f][j][4 * q + 1]),
+                    pack_bf16x2(acc[f][j][4 * q + 2], acc[f][j][4 * q + 3])};
+    }
+    lds_barrier();
+    const __amdgpu_buffer_rsrc_t rY = make_rsrc(p.out0 + j0 * N, rows_here * N * 2);
+    const int c = lne & 7, tq = lne >> 3;
+    const int64_t col = i0 + 64 * wave + 8 * c;
 #pragma unroll
-          for (int e = 0; e < 4; ++e) v[e] = acc[f][j][4 * q + e];
-          store4(rO0, off, v);
-        }
+    for (int u = 0; u < 32; ++u) {
+      const int t = 8 * u + tq;
+      const u32x4 v = *reinterpret_cast<const u32x4*>(reg + t * 128 + 16 * (c ^ (t & 7)));
+      __builtin_amdgcn_raw_buffer_store_b128(v, rY, (t < rh && col < N) ? (int)((t * N + col) * 2) : kOff, 0, 0);
+    }
+  } else {
+    const __amdgpu_buffer_rsrc_t rO0 = make_rsrc(p.out0 + j0 * N, rows_here * N * 2);
+    const __amdgpu_buffer_rsrc_t rO1 = make_rsrc(p.out1 + j0 * N, rows_here * N * 2);
+    const __amdgpu_buffer_rsrc_t rO2 = make_rsrc(p.out2 + j0 * N, rows_here * N * 2);
+    const int c = lne & 3, tq = lne >> 2;
+    const int64_t col = i0 + 32 * wave + 8 * c;
+    auto put = [&](uint8_t* dst, int j, int q, const float (&v)[4]) {
+      const int t = 32 * j + jle;
+      *reinterpret_cast<u32x2*>(dst + t * 64 + 16 * (q ^ ((t >> 2) & 3)) + 8 * he) =
+          u32x2{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
+    };
+    auto drain = [&](const uint8_t* src, __amdgpu_buffer_rsrc_t rO) {
+#pragma unroll
+      for (int u = 0; u < 16; ++u) {
+        const int t = 16 * u + tq;
+        const u32x4 v = *reinterpret_cast<const u32x4*>(src + t * 64 + 16 * (c ^ ((t >> 2) & 3)));
+        __builtin_amdgcn_raw_buffer_store_b128(v, rO, (t < rh && col < N) ? (int)((t * N + col) * 2) : kOff, 0, 0);
       }
-    } else {
+    };
+    // g into the first half, u into the second, h into the first again; every
+    // wave touches only its own region, so the barriers only order its own LDS work
+    uint8_t* const reg2 = reg + kTok * 64;
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
-        const int64_t ic = nb[0] + 8 * q + 4 * h;
-        const int off = (m_ok && ic < N) ? (int)((mr * N + ic) * 2) : kOff;
-        float gv[4], uv[4], hv[4];
+        const float gv[4] = {acc[0][j][4 * q], acc[0][j][4 * q + 1], acc[0][j][4 * q + 2], acc[0][j][4 * q + 3]};
+        put(reg, j, q, gv);
+      }
+    lds_barrier();
+    drain(reg, rO0);
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const float uv[4] = {acc[1][j][4 * q], acc[1][j][4 * q + 1], acc[1][j][4 * q + 2], acc[1][j][4 * q + 3]};
+        put(reg2, j, q, uv);
+      }
+    lds_barrier();
+    drain(reg2, rO1);
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        float hv[4];
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          gv[e] = acc[0][j][4 * q + e];
-          uv[e] = acc[1][j][4 * q + e];
-          hv[e] = gv[e] * sigmoid_f(gv[e]) * uv[e];
+          const float g = acc[0][j][4 * q + e];
+          hv[e] = g * sigmoid_f(g) * acc[1][j][4 * q + e];
         }
-        store4(rO0, off, gv);
-        store4(rO1, off, uv);
-        store4(rO2, off, hv);
+        put(reg, j, q, hv);
       }
-    }
+    lds_barrier();
+    drain(reg, rO2);
   }
 }
 

@@ -696,7 +696,73 @@ void k_qgemm_bwd8(BwdArgs p) {
   const __amdgpu_buffer_rsrc_t rUs = make_rsrc(MODE == kSwiGLU ? p.u + j0 * K : p.out0,
                                                MODE == kSwiGLU ? rows_here * K * 2 : 0);
   if constexpr (MODE == kSwiGLU) {
-    swiglu_epilogue<4>(acc, rGs, rUs, rO0, rO1, 128 * th, rows_here, kc, K, jl, h);
+    // SwiGLU backward through LDS: dh (fp32) of 64 tokens x 64 columns per wave
+    // and half, token-major rows of 256 bytes (16-byte chunk c of row t at
+    // c ^ (t & 15)); each lane then takes 8 consecutive columns of one token:
+    // 16-byte loads of g and u, 16-byte stores of dg and du. The g, u loads of
+    // a half are issued before its dh is parked, so their latency is hidden.
+    __builtin_amdgcn_s_waitcnt(0);  // this wave's trailing dY copies have landed
+    __builtin_amdgcn_s_barrier();   // and every wave is done with the buffers
+    int jle = jl, he = h, lne = lane;
+    asm volatile("" : "+v"(jle), "+v"(he), "+v"(lne));
+    uint8_t* const reg = smem + wave * (64 * 256);
+    const int c8 = lne & 7, tq = lne >> 3, rh = (int)rows_here, Ki = (int)K;
+    const int col = (int)kc + 8 * c8;
+    u32x4 gq[8], uq[8];
+    auto off_of = [&](int hf, int u) {
+      const int mr = 128 * th + 64 * hf + 8 * u + tq;
+      return (mr < rh && col < Ki) ? (mr * Ki + col) * 2 : kOff;
+    };
+    auto load_gu = [&](int hf) {
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        gq[u] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rGs, off_of(hf, u), 0, 0));
+        uq[u] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rUs, off_of(hf, u), 0, 0));
+      }
+    };
+#pragma unroll
+    for (int hf = 0; hf < 2; ++hf) {
+      load_gu(hf);
+#pragma unroll
+      for (int jj = 0; jj < 2; ++jj) {
+        const int t = 32 * jj + jle;
+#pragma unroll
+        for (int f = 0; f < 2; ++f)
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const f32x16& a = acc[f][2 * hf + jj];
+            *reinterpret_cast<f32x4*>(reg + t * 256 + 16 * ((8 * f + 2 * q + he) ^ (t & 15))) =
+                f32x4{a[4 * q], a[4 * q + 1], a[4 * q + 2], a[4 * q + 3]};
+          }
+      }
+      lds_barrier();
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const int t = 8 * u + tq;
+        const f32x4 d0 = *reinterpret_cast<const f32x4*>(reg + t * 256 + 16 * ((2 * c8) ^ (t & 15)));
+        const f32x4 d1 = *reinterpret_cast<const f32x4*>(reg + t * 256 + 16 * ((2 * c8 + 1) ^ (t & 15)));
+        const float dh[8] = {d0[0], d0[1], d0[2], d0[3], d1[0], d1[1], d1[2], d1[3]};
+        float dg[8], du[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const float gv = (e & 1) ? bf16_hi(gq[u][e >> 1]) : bf16_lo(gq[u][e >> 1]);
+          const float uv = (e & 1) ? bf16_hi(uq[u][e >> 1]) : bf16_lo(uq[u][e >> 1]);
+          const float sg = sigmoid_f(gv);
+          dg[e] = dh[e] * uv * sg * (1.0f + gv * (1.0f - sg));
+          du[e] = dh[e] * gv * sg;
+        }
+        const int off = off_of(hf, u);
+        __builtin_amdgcn_raw_buffer_store_b128(
+            u32x4{pack_bf16x2(dg[0], dg[1]), pack_bf16x2(dg[2], dg[3]), pack_bf16x2(dg[4], dg[5]),
+                  pack_bf16x2(dg[6], dg[7])},
+            rO0, off, 0, 0);
+        __builtin_amdgcn_raw_buffer_store_b128(
+            u32x4{pack_bf16x2(du[0], du[1]), pack_bf16x2(du[2], du[3]), pack_bf16x2(du[4], du[5]),
+                  pack_bf16x2(du[6], du[7])},
+            rO1, off, 0, 0);
+      }
+      lds_barrier();  // the half's reads are done before the next half is parked
+    }
     return;
   }
   // dX through LDS (as in the forward GEMM): each wave parks its 128 tokens x 64

@@ -292,13 +292,20 @@ struct TnCall {
       jobs.job[jobs.n++] = a;
     });
   }
-  int flush() {
+  // defer != null: launch skinny_tn only and hand the reductions it leaves
+  // (one-split jobs are written out by skinny_tn itself) to the caller, which
+  // passes them to the backward GEMM it launches next on the same stream.
+  int flush(TnJobs* defer = nullptr) {
+    if (defer) defer->n = 0;
     if (jobs.n == 0 || rc != QLORA_OK) return rc;
-    bool reduce = false;  // one-split jobs are written out by skinny_tn itself
-    for (int i = 0; i < jobs.n; ++i)
-      reduce = reduce || skinny_tn_plan(jobs.job[i].M, jobs.job[i].Kd, jobs.job[i].r1 + jobs.job[i].r2).splits > 1;
+    const TnJobs red = tn_reduce_jobs(jobs);
     hipError_t e = timed("skinny_tn", st, [&]() { return launch_skinny_tn(jobs, st); });
-    if (e == hipSuccess && reduce) e = timed("tn_reduce", st, [&]() { return launch_tn_reduce(jobs, st); });
+    if (e == hipSuccess && red.n) {
+      if (defer)
+        *defer = red;
+      else
+        e = timed("tn_reduce", st, [&]() { return launch_tn_reduce(jobs, st); });
+    }
     if (e != hipSuccess) rc = hip_fail(e, "skinny_tn");
     jobs.n = 0;
     return rc;
@@ -472,8 +479,9 @@ int qlora_backward(const qlora_layer* L, const uint16_t* dY, const uint16_t* X, 
   tn.out_bf16 = gb;
   tn.one(Z_save, r, r, L->s, dY, M, N, dB, true);
   tn.one(G, r, r, L->s, X, M, K, dA, false);
-  if (int rc = tn.flush()) return rc;
-  if (dX) QL_LAUNCH("gemm_bwd", st, launch_gemm_bwd(dY, wsrc(L, L->A, G), nullptr, WSrc{}, M, K, N, dX, st));
+  TnJobs red{};  // reduced by the backward GEMM when there is one
+  if (int rc = tn.flush(dX ? &red : nullptr)) return rc;
+  if (dX) QL_LAUNCH("gemm_bwd", st, launch_gemm_bwd(dY, wsrc(L, L->A, G), nullptr, WSrc{}, M, K, N, dX, &red, st));
   return QLORA_OK;
 }
 
@@ -633,9 +641,10 @@ int mlp_bwd_body(const qlora_layer* gate, const qlora_layer* up, const qlora_lay
   QL_LAUNCH("skinny_nt", st, launch_skinny_nt(ntB(dY, M, H, down->B, w.Btd, r, w.Gd, r), st));
   tn.one(Zd, r, r, down->s, dY, M, H, dB[2], true);
   tn.one(w.Gd, r, r, down->s, h, M, I, dA[2], false);
-  if (int rc = tn.flush()) return rc;
+  TnJobs red{};  // reduced by the backward GEMM launched next
+  if (int rc = tn.flush(&red)) return rc;
   QL_LAUNCH("gemm_bwd_swiglu", st,
-            launch_gemm_bwd_swiglu(dY, wsrc(down, down->A, w.Gd), M, I, H, g, u, w.dg, w.du, st));
+            launch_gemm_bwd_swiglu(dY, wsrc(down, down->A, w.Gd), M, I, H, g, u, w.dg, w.du, &red, st));
   // gate and up: G = d(g|u).B ; dB = s.d(g|u)^T.Z ; dA_g = s_g.G_g^T.X and dA_u = s_u.G_u^T.X
   // (one pass over X when 2r fits a launch)
   QL_LAUNCH("skinny_nt", st, launch_skinny_nt(ntB(w.dg, M, I, gate->B, w.Btg, r, Gg, 2 * r), st));
@@ -643,12 +652,12 @@ int mlp_bwd_body(const qlora_layer* gate, const qlora_layer* up, const qlora_lay
   tn.one(Zg, r, r, gate->s, w.dg, M, I, dB[0], true);
   tn.one(Zu, r, r, up->s, w.du, M, I, dB[1], true);
   tn.two(w.Ggu, 2 * r, r, gate->s, dA[0], r, up->s, dA[1], X, M, H, false);
-  if (int rc = tn.flush()) return rc;
+  if (int rc = tn.flush(dX ? &red : nullptr)) return rc;
   // dX = dg.W_g + du.W_u + s.G_g.A_g + s.G_u.A_u : one GEMM over the concatenated reduction
   if (dX)
     QL_LAUNCH("gemm_bwd", st,
               launch_gemm_bwd(w.dg, wsrc(gate, gate->A, Gg, 2 * r), w.du, wsrc(up, up->A, Gu, 2 * r), M, H, I, dX,
-                              st));
+                              &red, st));
   return QLORA_OK;
 }
 

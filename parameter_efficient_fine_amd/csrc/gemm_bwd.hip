@@ -41,6 +41,7 @@
 
 #include "common.hpp"
 #include "internal.hpp"
+#include "reduce.hpp"
 
 // This source is compiled once per weight format (QL_WFMT: 0 NF4, 1 INT8,
 // 2 FP8); each object defines the launchers of its format's namespace.
@@ -82,6 +83,7 @@ struct BwdArgs {
   uint16_t* out1;         // du
   const uint16_t* g;      // SwiGLU: saved g, u [M, K]
   const uint16_t* u;
+  TnJobs red;             // partial sums of the preceding skinny_tn to reduce (n = 0: none)
 };
 
 // Weight tile swizzle: 16-byte chunk q of row j is stored at chunk q ^ wsw(j),
@@ -670,6 +672,9 @@ void k_qgemm_bwd8(BwdArgs p) {
   load_codes(nsteps > 1 ? 1 : 0, cB, aB);
   dma_y(0, 0);
   dma_y(nsteps > 1 ? 1 : 0, 1);
+  // the reductions of the preceding skinny_tn, one contiguous slice per
+  // workgroup, while this prologue's loads are in flight
+  if (p.red.n > 0) tn_reduce_slice(p.red, blockIdx.x, gridDim.x, threadIdx.x, 512);
   {
     const WPrep<F> lut0 = wprep<F>(aA);
     dequant_write(0, cA, lut0, 0, 4);
@@ -812,11 +817,15 @@ hipError_t launch_rp(const BwdArgs& a, hipStream_t st) {
   static const hipError_t attr = hipFuncSetAttribute(kfn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)kLds);
   if (attr != hipSuccess) return attr;
   const int64_t nI = (a.K + 255) / 256, nJ = (a.M + kTok - 1) / kTok;
-  if (nI * nJ == 0) return hipSuccess;
-  if constexpr (k8)
+  if (nI * nJ == 0) return a.red.n ? launch_tn_reduce(a.red, st) : hipSuccess;
+  if constexpr (k8) {
     k_qgemm_bwd8<kFmt, MODE, RP, ALIGNED><<<(unsigned)(nI * nJ), 512, kLds, st>>>(a);
-  else
+  } else {  // the 4-wave kernel leaves the reductions to their own launch
     k_qgemm_bwd<kFmt, MODE, RP, ALIGNED><<<(unsigned)(nI * nJ), 256, kLds, st>>>(a);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess || !a.red.n) return e;
+    return launch_tn_reduce(a.red, st);
+  }
   return hipGetLastError();
 }
 
@@ -846,8 +855,9 @@ hipError_t launch(const BwdArgs& a, hipStream_t st) {
 namespace QL_FMT_NS {
 
 hipError_t launch_gemm_bwd(const uint16_t* dY0, WSrc w0, const uint16_t* dY1, WSrc w1, int64_t M, int64_t K,
-                           int64_t N, uint16_t* dX, hipStream_t st) {
+                           int64_t N, uint16_t* dX, const TnJobs* red, hipStream_t st) {
   BwdArgs a{};
+  if (red) a.red = *red;
   a.dY[0] = dY0;
   a.dY[1] = dY1 ? dY1 : dY0;
   a.w[0] = w0;
@@ -858,8 +868,9 @@ hipError_t launch_gemm_bwd(const uint16_t* dY0, WSrc w0, const uint16_t* dY1, WS
 }
 
 hipError_t launch_gemm_bwd_swiglu(const uint16_t* dY, WSrc w, int64_t M, int64_t K, int64_t N, const uint16_t* g,
-                                  const uint16_t* u, uint16_t* dg, uint16_t* du, hipStream_t st) {
+                                  const uint16_t* u, uint16_t* dg, uint16_t* du, const TnJobs* red, hipStream_t st) {
   BwdArgs a{};
+  if (red) a.red = *red;
   a.dY[0] = a.dY[1] = dY;
   a.w[0] = a.w[1] = w;
   a.M = M, a.K = K, a.N = N;

@@ -78,6 +78,10 @@ struct TnJobs {
 };
 hipError_t launch_skinny_tn(TnJobs jobs, hipStream_t st);
 hipError_t launch_tn_reduce(TnJobs jobs, hipStream_t st);
+// The jobs of a skinny_tn launch that still need their partials reduced (more
+// than one split), with `splits` set; the backward GEMM takes such a set and
+// does the reduction itself (launch_gemm_bwd*, `red`).
+TnJobs tn_reduce_jobs(const TnJobs& jobs);
 
 // One launch before a backward: dst[C, R] = src[R, C]^T for each job (bf16).
 constexpr int kMaxPrepJobs = 3;
@@ -133,12 +137,14 @@ struct WSrc {           // one frozen quantized weight [N, K] with its LoRA pair
   /* gate/up of the SwiGLU block in one pass: g, u [M, N], h = silu(g) * u */                                      \
   hipError_t launch_gemm_fwd_gateup(const uint16_t* X, int64_t M, int64_t K, int64_t N, WSrc wg, WSrc wu,          \
                                     uint16_t* g, uint16_t* u, uint16_t* h, hipStream_t st);                        \
-  /* dX[M, K] = dY0 . What0 + s0 . G0 . A0 (+ dY1 . What1 + s1 . G1 . A1 when dY1 != null) */                       \
+  /* dX[M, K] = dY0 . What0 + s0 . G0 . A0 (+ dY1 . What1 + s1 . G1 . A1 when dY1 != null); red (may be null): */ \
+  /* reductions of the preceding skinny_tn (tn_reduce_jobs) done by the same launch */                              \
   hipError_t launch_gemm_bwd(const uint16_t* dY0, WSrc w0, const uint16_t* dY1, WSrc w1, int64_t M, int64_t K,     \
-                             int64_t N, uint16_t* dX, hipStream_t st);                                             \
+                             int64_t N, uint16_t* dX, const TnJobs* red, hipStream_t st);                          \
   /* dh = dY . What + s . G . A (never stored); dg = dh*u*sig(g)*(1+g*(1-sig(g))), du = dh*silu(g) */              \
   hipError_t launch_gemm_bwd_swiglu(const uint16_t* dY, WSrc w, int64_t M, int64_t K, int64_t N, const uint16_t* g, \
-                                    const uint16_t* u, uint16_t* dg, uint16_t* du, hipStream_t st);
+                                    const uint16_t* u, uint16_t* dg, uint16_t* du, const TnJobs* red,              \
+                                    hipStream_t st);
 namespace f0 { QL_GEMM_LAUNCHERS }
 namespace f1 { QL_GEMM_LAUNCHERS }
 namespace f2 { QL_GEMM_LAUNCHERS }
@@ -160,13 +166,13 @@ inline hipError_t launch_gemm_fwd_gateup(const uint16_t* X, int64_t M, int64_t K
   return QL_BY_FMT(wg.fmt, launch_gemm_fwd_gateup(X, M, K, N, wg, wu, g, u, h, st));
 }
 inline hipError_t launch_gemm_bwd(const uint16_t* dY0, WSrc w0, const uint16_t* dY1, WSrc w1, int64_t M, int64_t K,
-                                  int64_t N, uint16_t* dX, hipStream_t st) {
-  return QL_BY_FMT(w0.fmt, launch_gemm_bwd(dY0, w0, dY1, w1, M, K, N, dX, st));
+                                  int64_t N, uint16_t* dX, const TnJobs* red, hipStream_t st) {
+  return QL_BY_FMT(w0.fmt, launch_gemm_bwd(dY0, w0, dY1, w1, M, K, N, dX, red, st));
 }
 inline hipError_t launch_gemm_bwd_swiglu(const uint16_t* dY, WSrc w, int64_t M, int64_t K, int64_t N,
                                          const uint16_t* g, const uint16_t* u, uint16_t* dg, uint16_t* du,
-                                         hipStream_t st) {
-  return QL_BY_FMT(w.fmt, launch_gemm_bwd_swiglu(dY, w, M, K, N, g, u, dg, du, st));
+                                         const TnJobs* red, hipStream_t st) {
+  return QL_BY_FMT(w.fmt, launch_gemm_bwd_swiglu(dY, w, M, K, N, g, u, dg, du, red, st));
 }
 #undef QL_BY_FMT
 

@@ -11,6 +11,7 @@
 
 #include "common.hpp"
 #include "internal.hpp"
+#include "reduce.hpp"
 
 namespace qlora {
 
@@ -482,64 +483,17 @@ __global__ __launch_bounds__(256) void k_skinny_tn(TnJobs jobs) {
 }
 
 // out = s * (sum of the split partials, added in split order): one float4 of
-// outputs per thread with every split's load in flight at once. A kernel of
-// its own: the launch boundary makes the partials of all workgroups visible
-// (an in-kernel "last workgroup reduces" scheme needs device-scope release
-// fences, which write back the whole L2 of an XCD and cost far more here).
+// outputs per thread with every split's load in flight at once. Not in
+// skinny_tn itself: a launch boundary makes the partials of all workgroups
+// visible (an in-kernel "last workgroup reduces" scheme needs device-scope
+// release fences, which write back the whole L2 of an XCD and cost far more
+// here). When a backward GEMM follows, it does this work in its prologue
+// instead, and this kernel is launched only when none does.
 __global__ __launch_bounds__(64) void k_tn_reduce(TnJobs jobs) {
   const TnArgs& p = jobs.job[blockIdx.z];
-  const int64_t Kd = p.Kd, kq = Kd / 4;
-  const int R = p.r1 + p.r2;
   const int64_t idx = (int64_t)blockIdx.x * 64 + threadIdx.x;
-  if (idx >= R * kq) return;
-  const int j = (int)(idx / kq);
-  const int64_t k = 4 * (idx - j * kq);
-  const float* src = p.part + (int64_t)j * Kd + k;
-  const int64_t sstride = (int64_t)R * Kd;
-  f32x4 sum = *reinterpret_cast<const f32x4*>(src);
-  int sp = 1;
-  for (; sp + 16 <= p.splits; sp += 16) {
-    f32x4 v[16];
-#pragma unroll
-    for (int i = 0; i < 16; ++i) v[i] = *reinterpret_cast<const f32x4*>(src + (int64_t)(sp + i) * sstride);
-#pragma unroll
-    for (int i = 0; i < 16; ++i) sum += v[i];
-  }
-  for (; sp + 4 <= p.splits; sp += 4) {
-    f32x4 v[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) v[i] = *reinterpret_cast<const f32x4*>(src + (int64_t)(sp + i) * sstride);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) sum += v[i];
-  }
-  for (; sp < p.splits; ++sp) sum += *reinterpret_cast<const f32x4*>(src + (int64_t)sp * sstride);
-  const bool first = j < p.r1;
-  const float s = first ? p.s1 : p.s2;
-  void* out = first ? p.out1 : p.out2;
-  const int64_t jr = first ? j : j - p.r1;
-  const int64_t ldo = first ? p.ldo1 : p.ldo2;
-  sum *= s;
-  if (p.out_bf16) {  // one rounding of the fp32 sum (no accumulation in bf16)
-    uint16_t* ob = static_cast<uint16_t*>(out);
-    if (p.transposed) {
-#pragma unroll
-      for (int c = 0; c < 4; ++c) ob[(k + c) * ldo + jr] = __builtin_bit_cast(uint16_t, (__bf16)sum[c]);
-    } else {
-      *reinterpret_cast<u32x2*>(ob + jr * ldo + k) = u32x2{pack_bf16x2(sum[0], sum[1]), pack_bf16x2(sum[2], sum[3])};
-    }
-    return;
-  }
-  float* of = static_cast<float*>(out);
-  if (p.transposed) {
-#pragma unroll
-    for (int c = 0; c < 4; ++c) {
-      float* o = of + (k + c) * ldo + jr;
-      *o = p.accumulate ? *o + sum[c] : sum[c];
-    }
-  } else {
-    f32x4* o = reinterpret_cast<f32x4*>(of + jr * ldo + k);
-    *o = p.accumulate ? *o + sum : sum;
-  }
+  if (idx >= (int64_t)(p.r1 + p.r2) * (p.Kd / 4)) return;
+  tn_reduce_quad(p, idx);
 }
 
 hipError_t launch_skinny_tn(TnJobs jobs, hipStream_t st) {
@@ -580,20 +534,25 @@ hipError_t launch_skinny_tn(TnJobs jobs, hipStream_t st) {
   return hipGetLastError();
 }
 
-hipError_t launch_tn_reduce(TnJobs jobs, hipStream_t st) {
-  if (jobs.n < 1 || jobs.n > kTnMaxJobs) return hipErrorInvalidValue;
-  int64_t nmax = 0;
+TnJobs tn_reduce_jobs(const TnJobs& jobs) {
   TnJobs multi{};  // the jobs with more than one split (one-split jobs wrote their result already)
-  for (int i = 0; i < jobs.n; ++i) {
+  for (int i = 0; i < jobs.n && i < kTnMaxJobs; ++i) {
     TnArgs a = jobs.job[i];
     a.splits = skinny_tn_plan(a.M, a.Kd, a.r1 + a.r2).splits;
-    if (a.splits == 1) continue;
-    multi.job[multi.n++] = a;
-    const int64_t n = (int64_t)(a.r1 + a.r2) * (a.Kd / 4);
+    if (a.splits > 1) multi.job[multi.n++] = a;
+  }
+  return multi;
+}
+
+hipError_t launch_tn_reduce(TnJobs jobs, hipStream_t st) {
+  if (jobs.n < 1 || jobs.n > kTnMaxJobs) return hipErrorInvalidValue;
+  jobs = tn_reduce_jobs(jobs);
+  int64_t nmax = 0;
+  for (int i = 0; i < jobs.n; ++i) {
+    const int64_t n = (int64_t)(jobs.job[i].r1 + jobs.job[i].r2) * (jobs.job[i].Kd / 4);
     nmax = n > nmax ? n : nmax;
   }
-  jobs = multi;
-  if (nmax == 0 || jobs.n == 0) return hipSuccess;
+  if (nmax == 0) return hipSuccess;
   k_tn_reduce<<<dim3((unsigned)((nmax + 63) / 64), 1, (unsigned)jobs.n), 64, 0, st>>>(jobs);
   return hipGetLastError();
 }

@@ -83,10 +83,10 @@ def parse():
 KERNEL_SOURCES = {  # kernel class -> the sources its code is built from
     "small_fwd": ["small.hip", "common.hpp"],
     "small_bwd": ["small.hip", "common.hpp"],
-    "skinny_tn": ["skinny.hip", "common.hpp"],
-    "skinny_nt": ["skinny.hip", "common.hpp"],
-    "gemm_bwd": ["gemm_bwd.hip", "common.hpp"],
-    "gemm_bwd_swiglu": ["gemm_bwd.hip", "common.hpp"],
+    "skinny_tn": ["skinny.hip", "common.hpp", "reduce.hpp"],
+    "skinny_nt": ["skinny.hip", "common.hpp", "reduce.hpp"],
+    "gemm_bwd": ["gemm_bwd.hip", "common.hpp", "reduce.hpp"],
+    "gemm_bwd_swiglu": ["gemm_bwd.hip", "common.hpp", "reduce.hpp"],
     "gemm_fwd": ["gemm_fwd.hip", "common.hpp"],
     "gemm_fwd_gateup": ["gemm_fwd.hip", "common.hpp"],
     "rmsnorm_fwd": ["normrope.hip", "common.hpp"],

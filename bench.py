@@ -39,6 +39,11 @@ PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 MFMA (published)
 PEAK_HBM_GBS = 8000.0
 RIDGE_FLOP_PER_BYTE = PEAK_BF16_TFLOPS * 1e12 / (PEAK_HBM_GBS * 1e9)  # ~312: below it a step is HBM/latency-bound
 COLD_STEPS = 10
+# Untimed priming before the warm-up steps: back-to-back steps for this much
+# wall time. From idle the GPU needs some 30 ms of load before a step reaches
+# its steady time (attn: 306 us over the first 25 steps, 272 at 50-75, 266 from
+# 100 on, one box), longer than a few warm-up steps take.
+PRIME_S = 0.3
 SMALL_MAX_M, SMALL_MAX_R = 256, 32  # the library's small-batch path (one wave per 32 x 32 tile)
 WL_INDEX = {"tiny": 0, "attn": 1, "mlp": 2, "rsweep": 3, "layer": 4, "normrope": None, "lmhead": None,
             "qkrope": None}
@@ -68,6 +73,8 @@ def parse():
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--no-gpu-state", action="store_true",
                     help="skip reading clocks and power with rocm-smi while the step runs")
+    ap.add_argument("--prime-s", type=float, default=PRIME_S,
+                    help="seconds of untimed back-to-back steps before the warm-up steps (0: none)")
     ap.add_argument("--no-cold", action="store_true",
                     help="skip the 10 cache-cold steps (512 MiB written before each, untimed) timed after the warm ones")
     ap.add_argument("--graph", action="store_true",
@@ -691,6 +698,16 @@ def main():
         for p in parts:
             p.run(lib, st)
 
+    # priming (untimed): steps for args.prime_s seconds, the queue kept short so
+    # that the GPU is busy for that wall time
+    n_prime, t_prime = 0, time.perf_counter()
+    while time.perf_counter() - t_prime < args.prime_s:
+        step()
+        n_prime += 1
+        if n_prime % 4 == 0:
+            torch.cuda.synchronize()
+    torch.cuda.synchronize()
+    prime = dict(seconds=round(time.perf_counter() - t_prime, 3), steps=n_prime)
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
@@ -799,6 +816,7 @@ def main():
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
+        "prime": prime,
         "ms_per_step": ms,
         "higher_is_better": True,
         "scaling": "weak",

@@ -268,6 +268,10 @@ __device__ __forceinline__ f32x4 wdeq4_f32(uint32_t x, const WPrep<F>& p) {
 // store, which replaces data-dependent branches at tile edges.
 
 constexpr int kOff = (int)0x80000000u;  // an offset beyond every buffer's num_records
+// Cache policy of the GEMM epilogues' 16-byte result stores: non-temporal (the
+// lines go out of the L2 first; no workgroup of the launch reads them back).
+// Whole fwd+bwd steps measured 1% faster at the attention and decoder-layer shapes.
+constexpr int kStoreNT = 2;
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, int64_t bytes) {
   const int n = bytes > 0x7fffffff ? 0x7fffffff : (int)bytes;

@@ -760,11 +760,11 @@ void k_qgemm_bwd8(BwdArgs p) {
         __builtin_amdgcn_raw_buffer_store_b128(
             u32x4{pack_bf16x2(dg[0], dg[1]), pack_bf16x2(dg[2], dg[3]), pack_bf16x2(dg[4], dg[5]),
                   pack_bf16x2(dg[6], dg[7])},
-            rO0, off, 0, 0);
+            rO0, off, 0, kStoreNT);
         __builtin_amdgcn_raw_buffer_store_b128(
             u32x4{pack_bf16x2(du[0], du[1]), pack_bf16x2(du[2], du[3]), pack_bf16x2(du[4], du[5]),
                   pack_bf16x2(du[6], du[7])},
-            rO1, off, 0, 0);
+            rO1, off, 0, kStoreNT);
       }
       lds_barrier();  // the half's reads are done before the next half is parked
     }
@@ -797,7 +797,8 @@ void k_qgemm_bwd8(BwdArgs p) {
   for (int u = 0; u < 16; ++u) {
     const int t = 8 * u + tq, mr = 128 * th + t;
     const u32x4 v = *reinterpret_cast<const u32x4*>(reg + t * 128 + 16 * (c ^ (t & 7)));
-    __builtin_amdgcn_raw_buffer_store_b128(v, rO0, (mr < rh && col < K) ? (int)((mr * K + col) * 2) : kOff, 0, 0);
+    const int off = (mr < rh && col < K) ? (int)((mr * K + col) * 2) : kOff;
+    __builtin_amdgcn_raw_buffer_store_b128(v, rO0, off, 0, kStoreNT);
   }
 }
 

@@ -428,7 +428,8 @@ void k_qgemm_fwd(FwdArgs p) {
     for (int u = 0; u < 32; ++u) {
       const int t = 8 * u + tq;
       const u32x4 v = *reinterpret_cast<const u32x4*>(reg + t * 128 + 16 * (c ^ (t & 7)));
-      __builtin_amdgcn_raw_buffer_store_b128(v, rY, (t < rh && col < N) ? (int)((t * N + col) * 2) : kOff, 0, 0);
+      const int off = (t < rh && col < N) ? (int)((t * N + col) * 2) : kOff;
+      __builtin_amdgcn_raw_buffer_store_b128(v, rY, off, 0, kStoreNT);
     }
   } else {
     const __amdgpu_buffer_rsrc_t rO0 = make_rsrc(p.out0 + j0 * N, rows_here * N * 2);
@@ -446,7 +447,8 @@ void k_qgemm_fwd(FwdArgs p) {
       for (int u = 0; u < 16; ++u) {
         const int t = 16 * u + tq;
         const u32x4 v = *reinterpret_cast<const u32x4*>(src + t * 64 + 16 * (c ^ ((t >> 2) & 3)));
-        __builtin_amdgcn_raw_buffer_store_b128(v, rO, (t < rh && col < N) ? (int)((t * N + col) * 2) : kOff, 0, 0);
+        const int off = (t < rh && col < N) ? (int)((t * N + col) * 2) : kOff;
+        __builtin_amdgcn_raw_buffer_store_b128(v, rO, off, 0, kStoreNT);
       }
     };
     // g into the first half, u into the second, h into the first again; every

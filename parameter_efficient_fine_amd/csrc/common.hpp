@@ -326,6 +326,13 @@ __device__ __forceinline__ void split_scaled(const u32x4 v, float s, u32x4& hi, 
   }
 }
 
+// Whether any lane of the wave holds a nonzero low part (two fragments' worth):
+// the MFMAs of the low parts change nothing when every one is zero.
+__device__ __forceinline__ bool lo_any(const u32x4 a, const u32x4 b) {
+  const uint32_t v = a[0] | a[1] | a[2] | a[3] | b[0] | b[1] | b[2] | b[3];
+  return __builtin_amdgcn_ballot_w64(v != 0u) != 0;
+}
+
 __device__ __forceinline__ void store4(__amdgpu_buffer_rsrc_t rs, int off, const float (&v)[4]) {
   __builtin_amdgcn_raw_buffer_store_b64(u32x2{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])}, rs, off, 0, 0);
 }

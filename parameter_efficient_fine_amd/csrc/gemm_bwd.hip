@@ -549,15 +549,22 @@ void k_qgemm_bwd8(BwdArgs p) {
         }
         split_scaled(u32x4{wv[0], wv[1], wv[2], wv[3]}, w.s, ah[f], al[f]);
       }
+      u32x4 z[4];
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const int64_t mr = 128 * th + 32 * j + jl;
-        const u32x4 z = rank8<ALIGNED>(rG, mr < rows_here ? mr : -1, w.ldj, w.r, rr + c0);
+        z[j] = rank8<ALIGNED>(rG, mr < rows_here ? mr : -1, w.ldj, w.r, rr + c0);
+      }
 #pragma unroll
-        for (int f = 0; f < 2; ++f) {
-          acc[f][j] = mfma32(ah[f], z, acc[f][j]);
-          acc[f][j] = mfma32(al[f], z, acc[f][j]);
-        }
+      for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int f = 0; f < 2; ++f) acc[f][j] = mfma32(ah[f], z[j], acc[f][j]);
+      // the low parts only where some lane has one (none when s is a power of two)
+      if (lo_any(al[0], al[1])) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+#pragma unroll
+          for (int f = 0; f < 2; ++f) acc[f][j] = mfma32(al[f], z[j], acc[f][j]);
       }
     }
   }

@@ -177,16 +177,26 @@ void k_qgemm_fwd(FwdArgs p) {
         const u32x4 bv = rank8<ALIGNED>(second ? rB1 : rB0, ir < N ? ir : -1, rs, rs, rr + c0);
         split_scaled(bv, second ? p.w1.s : p.w0.s, bh[f], bl[f]);
       }
+      u32x4 z[8][2];
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
         const int64_t mr = 32 * j + jl;
         const int64_t zrow = mr < rows_here ? mr : -1;
-        const u32x4 z0 = rank8<ALIGNED>(rZ0, zrow, p.w0.r, p.w0.r, rr + c0);
-        const u32x4 z1 = GATEUP ? rank8<ALIGNED>(rZ1, zrow, p.w1.r, p.w1.r, rr + c0) : z0;
-        acc[0][j] = mfma32(bh[0], z0, acc[0][j]);
-        acc[0][j] = mfma32(bl[0], z0, acc[0][j]);
-        acc[1][j] = mfma32(bh[1], z1, acc[1][j]);
-        acc[1][j] = mfma32(bl[1], z1, acc[1][j]);
+        z[j][0] = rank8<ALIGNED>(rZ0, zrow, p.w0.r, p.w0.r, rr + c0);
+        z[j][1] = GATEUP ? rank8<ALIGNED>(rZ1, zrow, p.w1.r, p.w1.r, rr + c0) : z[j][0];
+      }
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        acc[0][j] = mfma32(bh[0], z[j][0], acc[0][j]);
+        acc[1][j] = mfma32(bh[1], z[j][1], acc[1][j]);
+      }
+      // the low parts only where some lane has one (none when s is a power of two)
+      if (lo_any(bl[0], bl[1])) {
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          acc[0][j] = mfma32(bl[0], z[j][0], acc[0][j]);
+          acc[1][j] = mfma32(bl[1], z[j][1], acc[1][j]);
+        }
       }
     }
   }

@@ -180,14 +180,15 @@ def random_linear(seed: int, M: int, K: int, N: int, r: int, alpha: float | None
                 order=["proj"], kind="linear")
 
 
-def random_mlp(seed: int, M: int, H: int, I: int, r: int):
+def random_mlp(seed: int, M: int, H: int, I: int, r: int, alpha: float | None = None):
     """A SwiGLU MLP of arbitrary shape with the same distributions (edge-case tests)."""
     rng = np.random.default_rng(seed)
     layers = {"gate": make_adapter_layer(rng, H, I, r), "up": make_adapter_layer(rng, H, I, r),
               "down": make_adapter_layer(rng, I, H, r)}
     X = bf16_bits(_normal(rng, (M, H)))
     dY = bf16_bits(_normal(rng, (M, H)))
-    return dict(layers=layers, X=X, dY=dY, M=M, r=r, alpha=2.0 * r, s=2.0,
+    alpha = 2.0 * r if alpha is None else alpha
+    return dict(layers=layers, X=X, dY=dY, M=M, r=r, alpha=alpha, s=float(alpha) / r,
                 order=["gate", "up", "down"], kind="mlp")
 
 

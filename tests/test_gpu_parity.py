@@ -142,6 +142,21 @@ def test_linear_ragged_shapes_full_oracle(M, K, N, r):
     assert max(errs.values()) <= TOL, errs
 
 
+@pytest.mark.parametrize("M,K,N,r,alpha", [
+    (300, 192, 264, 16, 24.0),    # s = 1.5: s.B and s.A^T split into two nonzero bf16 parts
+    (513, 640, 136, 24, 7.2),     # s = 0.3
+    (129, 320, 512, 128, 12.8),   # s = 0.1, the largest rank bucket of the fused GEMMs
+    (200, 256, 256, 8, 12.0),     # s = 1.5 on the small-batch path (M <= 256, r <= 32)
+])
+def test_linear_scale_not_a_power_of_two(M, K, N, r, alpha):
+    # With s a power of two the low parts of the split s-scaled adapter rows are
+    # zero and the GEMMs skip their MFMAs; these cases take the low parts.
+    _announce(f"linear s={alpha / r:g} M={M} K={K} N={N} r={r}")
+    d = random_linear(50_000 + M + K + N + r, M, K, N, r, alpha=alpha)
+    errs = _linear_case(d)
+    assert max(errs.values()) <= TOL, errs
+
+
 def test_linear_empty_batch_gives_zero_gradients():
     _announce("linear M=0")
     q = _q()
@@ -242,6 +257,12 @@ def test_mlp_high_rank_full_oracle(r):
     # splits the forward's paired Z = X.[A_g; A_u]^T (2r > 256)
     _announce(f"mlp high rank M=200 H=128 I=256 r={r}")
     errs = _mlp_case(random_mlp(90 + r, 200, 128, 256, r))
+    assert max(errs.values()) <= TOL, errs
+
+
+def test_mlp_scale_not_a_power_of_two():
+    _announce("mlp s=1.5 M=300 H=256 I=512 r=16")
+    errs = _mlp_case(random_mlp(81, 300, 256, 512, 16, alpha=24.0))
     assert max(errs.values()) <= TOL, errs
 
 

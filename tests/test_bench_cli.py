@@ -44,3 +44,12 @@ def test_counted_traffic_follows_the_source_hash(tmp_path, monkeypatch):
 def test_gpu_state_is_null_without_a_readable_rocm_smi(monkeypatch):
     monkeypatch.setenv("PATH", "/nonexistent")
     assert bench.gpu_state_under_load(lambda: None, lambda: None, cap_s=1) is None
+
+
+def test_priming_defaults_and_can_be_turned_off(monkeypatch):
+    # untimed back-to-back steps before the warm-up steps (the GPU ramps up from idle)
+    monkeypatch.setattr(sys, "argv", ["bench.py"])
+    assert bench.parse().prime_s == bench.PRIME_S > 0
+    monkeypatch.setattr(sys, "argv", ["bench.py", "--prime-s", "0", "--steps", "20", "--warmup", "5"])
+    a = bench.parse()
+    assert a.prime_s == 0 and a.steps == 20 and a.warmup == 5

@@ -241,8 +241,9 @@ NtArgs ntB(const uint16_t* in, int64_t M, int64_t Kd, const uint16_t* B, const u
 }
 
 // Collects independent reductions (out = s * P^T . Q) and issues them as one
-// skinny_tn launch and one tn_reduce launch per batch of kTnMaxJobs; each gets
-// its own slice of the partial buffer.
+// skinny_tn launch per batch of kTnMaxJobs, each job with its own slice of the
+// partial buffer; the split partials are then added by one tn_reduce launch,
+// or, for the last batch, by the backward GEMM launched next (flush(&red)).
 struct TnCall {
   float* part;
   const float* part_end;  // end of the partial region carved for this call

@@ -44,7 +44,8 @@ hipError_t launch_skinny_nt(const NtArgs& a, hipStream_t st);
 // out[k * ldo + j] when transposed; fp32, or bf16 (one rounding of the fp32
 // sum) when out_bf16. launch_skinny_tn splits the rows
 // over workgroups that write fp32 partials to `part`; launch_tn_reduce (next
-// on the same stream) adds them in split order and writes out1/out2.
+// on the same stream), or the prologue of a backward GEMM launched next with
+// them, adds them in split order and writes out1/out2.
 constexpr int kTnMaxR = 128;
 struct TnPlan {
   int splits;

@@ -106,3 +106,35 @@ def test_mlp_small_full_oracle(fmt):
     _announce(f"mlp fmt={fmt} M=300 H=256 I=512 r=16")
     errs = _mlp_case(random_mlp(177, 300, 256, 512, 16), fmt=fmt)
     assert max(errs.values()) <= TOL, errs
+
+
+@pytest.mark.parametrize("fmt", FMTS)
+def test_mlp_full_size(fmt):
+    # the SwiGLU block at the Llama-3.1-8B widths (M=4096, H=4096, I=14336, r=16) with
+    # 8-bit weights, on sampled rows (the upstream gradient zero elsewhere, so dA and
+    # dB are exact over the batch)
+    _announce(f"mlp fmt={fmt} M=4096 H=4096 I=14336 r=16")
+    d = make_workload(2)
+    rows = sample_rows(d["M"], np.random.default_rng(43), per_block=1)
+    errs = _mlp_case(d, rows, mask_dy=True, fmt=fmt)
+    assert max(errs.values()) <= TOL, errs
+
+
+@pytest.mark.parametrize("fmt", FMTS)
+def test_decoder_layer_full_size(fmt):
+    # the 7 projections of a Llama-3.1-8B decoder layer at M=16384 with 8-bit weights,
+    # on sampled rows (the SwiGLU block with its upstream gradient zero elsewhere)
+    _announce(f"decoder layer fmt={fmt} M=16384, 7 projections")
+    d = make_workload(4)
+    M = d["M"]
+    rows = sample_rows(M, np.random.default_rng(44), per_block=1, block=1024)
+    errs = {}
+    for nm, xk in (("q", "X_attn"), ("k", "X_attn"), ("v", "X_attn"), ("o", "X_o")):
+        sub = dict(layers={"proj": d["layers"][nm]}, X=d[xk], dY=d["dY_" + nm], s=d["s"], M=M)
+        for k, v in _linear_case(sub, rows, check_z=False, fmt=fmt).items():
+            errs[f"{nm}.{k}"] = v
+    mlp = dict(layers={k: d["layers"][k] for k in ("gate", "up", "down")}, X=d["X_mlp"], dY=d["dY_mlp"], M=M,
+               s=d["s"])
+    for k, v in _mlp_case(mlp, rows, mask_dy=True, fmt=fmt).items():
+        errs["mlp." + k] = v
+    assert max(errs.values()) <= TOL, errs

@@ -157,6 +157,27 @@ def test_linear_scale_not_a_power_of_two(M, K, N, r, alpha):
     assert max(errs.values()) <= TOL, errs
 
 
+@pytest.mark.parametrize("grad_bf16", [False, True])
+def test_linear_backward_without_dx_matches_the_one_with_dx(grad_bf16):
+    # Without dX the split partials of dA and dB are added by their own reduce
+    # launch; with dX, by the backward GEMM's prologue. Same partials, same split
+    # order: the gradients agree bit for bit, and with the oracle.
+    _announce(f"linear backward without dX M=2000 K=1024 N=384 r=16 bf16={grad_bf16}")
+    import torch
+    q = _q()
+    d = random_linear(4343, 2000, 1024, 384, 16)
+    P = Prepared(d["layers"]["proj"], d["s"], grad_dtype=torch.bfloat16 if grad_bf16 else torch.float32)
+    Xd, dYd = dev_bf16(d["X"]), dev_bf16(d["dY"])
+    _, Z = q.forward(P.dev, Xd)
+    _, dA1, dB1 = q.backward(P.dev, dYd, Xd, Z)
+    _, dA0, dB0 = q.backward(P.dev, dYd, Xd, Z, need_dX=False)
+    bits = (lambda t: t.contiguous().view(torch.int16 if grad_bf16 else torch.int32).cpu().numpy())
+    assert np.array_equal(bits(dA0), bits(dA1)) and np.array_equal(bits(dB0), bits(dB1))
+    dAr, dBr = ref.adapter_grads(ref.bf16_to_f64(d["dY"]), ref.bf16_to_f64(d["X"]), P.A, P.B, P.s)
+    errs = dict(dA=rel_err(host(dA0), dAr), dB=rel_err(host(dB0), dBr))
+    assert max(errs.values()) <= TOL, errs
+
+
 def test_linear_empty_batch_gives_zero_gradients():
     _announce("linear M=0")
     q = _q()

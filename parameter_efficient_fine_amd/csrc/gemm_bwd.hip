@@ -36,7 +36,7 @@
 //
 // k_qgemm_bwd8 below is the same pipeline with 8 waves (two per SIMD), each
 // holding 64 columns x 128 tokens; every product uses it except the
-// two-source one at rank 256.
+// two-source one at rank 256, the only one this 4-wave kernel runs.
 #include <type_traits>
 
 #include "common.hpp"
@@ -95,66 +95,12 @@ struct BwdArgs {
 // opposite halves of the row.
 __device__ __forceinline__ int wsw(int j) { return (j & 1) | (((j >> 1) & 1) << 2) | (((j >> 2) & 1) << 1); }
 
-// SwiGLU backward epilogue of a wave's accumulators (dh, never stored): with
-// the saved g, u of the same element, dg = dh.u.sig(g).(1 + g.(1 - sig(g))) and
-// du = dh.silu(g). Fragment row j of the wave covers tokens m0 + 32j + jl and
-// columns kc + 32f + 8q + 4h .. +3. The compiler must assume that the dg/du
-// stores may alias g and u, so it would keep every load after the previous
-// stores and wait for it right away; here the 16 loads of row j + 1 are issued
-// before the stores of row j, so one round trip covers a whole row.
-template <int NJ>
-__device__ __forceinline__ void swiglu_epilogue(const f32x16 (&acc)[2][NJ], __amdgpu_buffer_rsrc_t rG,
-                                                __amdgpu_buffer_rsrc_t rU, __amdgpu_buffer_rsrc_t rDg,
-                                                __amdgpu_buffer_rsrc_t rDu, int m0, int64_t rows_here,
-                                                int64_t kc, int64_t K, int jl, int h) {
-  // The lane's row and column are re-read through an empty asm statement, so the
-  // compiler cannot reuse row offsets of the prologue and keep them alive (in
-  // scratch) across the main loop. Offsets in 32 bits: at most 256 rows of at
-  // most 2^21 columns from the tile's first row.
-  int jle = jl, he = h;
-  asm volatile("" : "+v"(jle), "+v"(he));
-  const int rh = (int)rows_here, Ki = (int)K, c0 = (int)kc + 4 * he;
-  auto off_of = [&](int j, int i) -> int {
-    const int mr = m0 + 32 * j + jle;
-    const int ic = c0 + 32 * (i >> 2) + 8 * (i & 3);
-    return (mr < rh && ic < Ki) ? (mr * Ki + ic) * 2 : kOff;
-  };
-  u32x2 gw[2][8], uw[2][8];
-  auto load_row = [&](int j, int b) {
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int off = off_of(j, i);
-      gw[b][i] = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(rG, off, 0, 0));
-      uw[b][i] = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(rU, off, 0, 0));
-    }
-  };
-  load_row(0, 0);
-#pragma unroll
-  for (int j = 0; j < NJ; ++j) {
-    if (j + 1 < NJ) load_row(j + 1, (j + 1) & 1);
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const u32x2 g2 = gw[j & 1][i], u2 = uw[j & 1][i];
-      const float gv[4] = {bf16_lo(g2[0]), bf16_hi(g2[0]), bf16_lo(g2[1]), bf16_hi(g2[1])};
-      const float uv[4] = {bf16_lo(u2[0]), bf16_hi(u2[0]), bf16_lo(u2[1]), bf16_hi(u2[1])};
-      float dg[4], du[4];
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const float v = acc[i >> 2][j][4 * (i & 3) + e];
-        const float sg = sigmoid_f(gv[e]);
-        dg[e] = v * uv[e] * sg * (1.0f + gv[e] * (1.0f - sg));
-        du[e] = v * gv[e] * sg;
-      }
-      const int off = off_of(j, i);
-      store4(rDg, off, dg);
-      store4(rDu, off, du);
-    }
-  }
-}
-
 template <int F, int MODE, int RP, bool ALIGNED>
 __global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_per_eu(1, 1)))
 void k_qgemm_bwd(BwdArgs p) {
+  // launched only for the two-source product at rank 256, whose rank term does
+  // not fit the 8-wave kernel's 256 registers per lane (launch_rp)
+  static_assert(MODE != kSwiGLU, "the SwiGLU backward runs on the 8-wave kernel");
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];  // dY [2], then weight tiles [2][4 waves]
   constexpr int NSRC = MODE == kConcat ? 2 : 1;
   const int lane = threadIdx.x & 63;
@@ -414,18 +360,8 @@ void k_qgemm_bwd(BwdArgs p) {
     if (s + 1 < nsteps) body(s + 1, cA, aA, cB, aB);
   }
 
-  // ---- epilogue (no control flow): bf16 stores, or the SwiGLU backward
+  // ---- epilogue (no control flow): bf16 stores
   const __amdgpu_buffer_rsrc_t rO0 = make_rsrc(p.out0 + j0 * K, rows_here * K * 2);
-  const __amdgpu_buffer_rsrc_t rO1 = make_rsrc(MODE == kSwiGLU ? p.out1 + j0 * K : p.out0,
-                                               MODE == kSwiGLU ? rows_here * K * 2 : 0);
-  const __amdgpu_buffer_rsrc_t rGs = make_rsrc(MODE == kSwiGLU ? p.g + j0 * K : p.out0,
-                                               MODE == kSwiGLU ? rows_here * K * 2 : 0);
-  const __amdgpu_buffer_rsrc_t rUs = make_rsrc(MODE == kSwiGLU ? p.u + j0 * K : p.out0,
-                                               MODE == kSwiGLU ? rows_here * K * 2 : 0);
-  if constexpr (MODE == kSwiGLU) {
-    swiglu_epilogue<8>(acc, rGs, rUs, rO0, rO1, 0, rows_here, kc, K, jl, h);
-    return;
-  }
   int jle = jl, he = h;  // fresh copies: no prologue offsets kept alive across the loop
   asm volatile("" : "+v"(jle), "+v"(he));
 #pragma unroll

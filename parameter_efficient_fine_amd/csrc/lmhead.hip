@@ -175,30 +175,68 @@ void k_gemm_nt(NtGemmArgs p) {
   }
   if (s < nsteps) body(s, wa, wb);
 
-  // ---- epilogue: column ic = weight row, row mr = token (C layout of mfma32)
+  // ---- epilogue through LDS (the activation ring is idle now): each wave parks
+  // its 64 columns token-major, 16-byte chunk c of token row t at c ^ (t & 15)
+  // (fp32, 256-byte rows, two passes of 128 tokens) or c ^ (t & 7) (bf16,
+  // 128-byte rows, one pass), and every store then writes whole row pieces.
   constexpr int kOutB = OUT_F32 ? 4 : 2;
   const __amdgpu_buffer_rsrc_t rO = make_rsrc((uint8_t*)p.Y + j0 * N * kOutB, rows_here * N * kOutB);
+  __builtin_amdgcn_s_waitcnt(0);  // this wave's trailing copies into the ring have landed
+  __builtin_amdgcn_s_barrier();   // and every wave is done reading the ring
+  {
+    int jle = jl, he = h, lne = lane;
+    asm volatile("" : "+v"(jle), "+v"(he), "+v"(lne));
+    const int rh = (int)rows_here;
+    if constexpr (OUT_F32) {
+      uint8_t* const reg = smem + wave * (128 * 256);
+      const int c = lne & 15, tq = lne >> 4;
+      const int64_t col = i0 + 64 * wave + 4 * c;
 #pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    const int64_t mr = 32 * j + jl;
-    const bool m_ok = mr < rows_here;
+      for (int pass = 0; pass < 2; ++pass) {
 #pragma unroll
-    for (int f = 0; f < 2; ++f) {
+        for (int jj = 0; jj < 4; ++jj) {
+          const int t = 32 * jj + jle;
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const int64_t ic = i0 + 64 * wave + 32 * f + 8 * q + 4 * h;
-        const int off = (m_ok && ic < N) ? (int)((mr * N + ic) * kOutB) : kOff;
-        float v[4];
+          for (int f = 0; f < 2; ++f)
 #pragma unroll
-        for (int e = 0; e < 4; ++e) v[e] = acc[f][j][4 * q + e];
-        if constexpr (OUT_F32)
-          __builtin_amdgcn_raw_buffer_store_b128(u32x4{__builtin_bit_cast(uint32_t, v[0]),
-                                                       __builtin_bit_cast(uint32_t, v[1]),
-                                                       __builtin_bit_cast(uint32_t, v[2]),
-                                                       __builtin_bit_cast(uint32_t, v[3])},
-                                                 rO, off, 0, 0);
-        else
-          store4(rO, off, v);
+            for (int q = 0; q < 4; ++q) {
+              const f32x16& a = acc[f][4 * pass + jj];
+              *reinterpret_cast<f32x4*>(reg + t * 256 + 16 * ((8 * f + 2 * q + he) ^ (t & 15))) =
+                  f32x4{a[4 * q], a[4 * q + 1], a[4 * q + 2], a[4 * q + 3]};
+            }
+        }
+        lds_barrier();
+#pragma unroll
+        for (int u = 0; u < 32; ++u) {
+          const int t = 4 * u + tq, mr = 128 * pass + t;
+          const u32x4 v = *reinterpret_cast<const u32x4*>(reg + t * 256 + 16 * (c ^ (t & 15)));
+          const int off = (mr < rh && col < N) ? (int)((mr * N + col) * 4) : kOff;
+          __builtin_amdgcn_raw_buffer_store_b128(v, rO, off, 0, kStoreNT);
+        }
+        lds_barrier();
+      }
+    } else {
+      uint8_t* const reg = smem + wave * (256 * 128);
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const int t = 32 * j + jle;
+#pragma unroll
+        for (int f = 0; f < 2; ++f)
+#pragma unroll
+          for (int q = 0; q < 4; ++q)
+            *reinterpret_cast<u32x2*>(reg + t * 128 + 16 * ((4 * f + q) ^ (t & 7)) + 8 * he) =
+                u32x2{pack_bf16x2(acc[f][j][4 * q], acc[f][j][4 * q + 1]),
+                      pack_bf16x2(acc[f][j][4 * q + 2], acc[f][j][4 * q + 3])};
+      }
+      lds_barrier();
+      const int c = lne & 7, tq = lne >> 3;
+      const int64_t col = i0 + 64 * wave + 8 * c;
+#pragma unroll
+      for (int u = 0; u < 32; ++u) {
+        const int t = 8 * u + tq;
+        const u32x4 v = *reinterpret_cast<const u32x4*>(reg + t * 128 + 16 * (c ^ (t & 7)));
+        const int off = (t < rh && col < N) ? (int)((t * N + col) * 2) : kOff;
+        __builtin_amdgcn_raw_buffer_store_b128(v, rO, off, 0, kStoreNT);
       }
     }
   }

@@ -394,3 +394,25 @@ def test_calls_run_on_the_callers_stream():
     s.synchronize()
     for a, b in zip([Y0, Z0, *r0], [Y1, Z1, *r1]):
         assert np.array_equal(_bits(a), _bits(b))
+
+
+def _random_shapes(n, seed):
+    # seeded draws over both paths: M from 1 to ~2600 (the small-batch path up to
+    # 256 tokens at r <= 32), K a multiple of 64, N a multiple of 8, r from 1 to 160
+    rng = np.random.default_rng(seed)
+    out = []
+    for i in range(n):
+        M = int(rng.integers(1, 2600)) if i % 3 else int(rng.integers(1, 257))
+        K = 64 * int(rng.integers(1, 13))
+        N = 8 * int(rng.integers(1, 97))
+        r = int(rng.integers(1, 33)) if i % 2 else int(rng.integers(1, 161))
+        out.append((M, K, N, r, i % 3))
+    return out
+
+
+@pytest.mark.parametrize("M,K,N,r,fmt", _random_shapes(12, 2027))
+def test_linear_random_shapes_full_oracle(M, K, N, r, fmt):
+    _announce(f"linear random fmt={fmt} M={M} K={K} N={N} r={r}")
+    d = random_linear(60_000 + M + K + N + r, M, K, N, r)
+    errs = _linear_case(d, fmt=fmt)
+    assert max(errs.values()) <= TOL, errs

@@ -38,7 +38,7 @@ sys.path.insert(0, ROOT)
 PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 MFMA (published)
 PEAK_HBM_GBS = 8000.0
 RIDGE_FLOP_PER_BYTE = PEAK_BF16_TFLOPS * 1e12 / (PEAK_HBM_GBS * 1e9)  # ~312: below it a step is HBM/latency-bound
-COLD_STEPS = 10
+COLD_STEPS = 30  # the first ~25 cold steps of a run vary by up to ~10% (measured on the attn step)
 # Untimed priming before the warm-up steps: back-to-back steps for this much
 # wall time. From idle the GPU needs some 30 ms of load before a step reaches
 # its steady time (attn: 306 us over the first 25 steps, 272 at 50-75, 266 from
@@ -76,7 +76,7 @@ def parse():
     ap.add_argument("--prime-s", type=float, default=PRIME_S,
                     help="seconds of untimed back-to-back steps before the warm-up steps (0: none)")
     ap.add_argument("--no-cold", action="store_true",
-                    help="skip the 10 cache-cold steps (512 MiB written before each, untimed) timed after the warm ones")
+                    help=f"skip the {COLD_STEPS} cache-cold steps (512 MiB written before each, untimed) timed after the warm ones")
     ap.add_argument("--graph", action="store_true",
                     help="also time the step captured once in a HIP graph and replayed (reported under 'graph')")
     ap.add_argument("--copy-calibration", action="store_true",

@@ -30,10 +30,10 @@ def test_rope_table_matches_fp64_cos_sin():
     assert np.array_equal(t[0, :, 0], np.ones(D // 2)) and not t[0, :, 1].any()  # position 0: the identity
 
 
-def _case(d, pos, max_pos, rows=None, check_unfused=True):
+def _case(d, pos, max_pos, rows=None, check_unfused=True, fmt=0):
     import torch
     import parameter_efficient_fine_amd as q
-    P = Prepared(d["layers"]["proj"], d["s"])
+    P = Prepared(d["layers"]["proj"], d["s"], fmt=fmt)
     X = dev_bf16(d["X"])
     table = q.rope_table(D, BASE, max_pos)
     posd = torch.from_numpy(pos.astype(np.int32)).cuda()
@@ -64,6 +64,15 @@ def test_forward_rope_small_full_oracle(M, K, N, r):
     d = random_linear(30_000 + M + K + N + r, M, K, N, r)
     pos = packed_positions(np.random.default_rng(M + N), M, 1000)
     _case(d, pos, 1000)
+
+
+@pytest.mark.parametrize("fmt", [1, 2])
+def test_forward_rope_8bit_weights(fmt):
+    # the fused epilogue behind the INT8 and FP8 weight decoders, ragged token tile
+    _announce(f"forward_rope fmt={fmt} M=300 K=256 N=512 r=16")
+    d = random_linear(30_700 + fmt, 300, 256, 512, 16)
+    pos = packed_positions(np.random.default_rng(700 + fmt), 300, 1000)
+    _case(d, pos, 1000, fmt=fmt)
 
 
 def test_forward_rope_attn_q_projection_full_size():

@@ -30,9 +30,9 @@ def _bits(t):
     return t.detach().contiguous().view(torch.int32 if t.dtype == torch.float32 else torch.int16).cpu().numpy()
 
 
-def _run(d, tile):
+def _run(d, tile, fmt=0):
     import parameter_efficient_fine_amd as q
-    Ls = {nm: Prepared(d["layers"][nm], d["s"]) for nm in ("gate", "up", "down")}
+    Ls = {nm: Prepared(d["layers"][nm], d["s"], fmt=fmt) for nm in ("gate", "up", "down")}
     g, u, dn = Ls["gate"].dev, Ls["up"].dev, Ls["down"].dev
     X, dY = dev_bf16(d["X"]), dev_bf16(d["dY"])
     whole_f = q.mlp_forward(g, u, dn, X)
@@ -54,6 +54,18 @@ def _compare_to_whole(whole_f, whole_b, tf, tb, same_order):
                 assert rel_err(t, w) <= ORDER_TOL, (key, i, rel_err(t, w))
 
 
+def _oracle_errs(d, Ls, tf, tb):
+    X, dY = ref.bf16_to_f64(d["X"]), ref.bf16_to_f64(d["dY"])
+    trip = [Ls[nm].triple() for nm in ("gate", "up", "down")]
+    fr = ref.mlp_fwd(X, *trip, d["s"])
+    br = ref.mlp_bwd(dY, X, *trip, d["s"])
+    errs = dict(Y=rel_err(host(tf["Y"]), fr["Y"]), dX=rel_err(host(tb["dX"]), br["dX"]))
+    for i, nm in enumerate(("gate", "up", "down")):
+        errs["dA_" + nm] = rel_err(host(tb["dA"][i]), br["dA_" + nm])
+        errs["dB_" + nm] = rel_err(host(tb["dB"][i]), br["dB_" + nm])
+    return errs
+
+
 @pytest.mark.parametrize("M,tile", [
     (1000, 256),   # 3 full tiles and a ragged one
     (1000, 384),   # tile not a multiple of the GEMM's 256-token tile
@@ -66,14 +78,18 @@ def test_mlp_tiled_full_oracle(M, tile):
     d = random_mlp(500 + M + tile, M, 128, 256, 16)
     Ls, wf, wb, tf, tb = _run(d, tile)
     _compare_to_whole(wf, wb, tf, tb, same_order=tile >= M)
-    X, dY = ref.bf16_to_f64(d["X"]), ref.bf16_to_f64(d["dY"])
-    trip = [Ls[nm].triple() for nm in ("gate", "up", "down")]
-    fr = ref.mlp_fwd(X, *trip, d["s"])
-    br = ref.mlp_bwd(dY, X, *trip, d["s"])
-    errs = dict(Y=rel_err(host(tf["Y"]), fr["Y"]), dX=rel_err(host(tb["dX"]), br["dX"]))
-    for i, nm in enumerate(("gate", "up", "down")):
-        errs["dA_" + nm] = rel_err(host(tb["dA"][i]), br["dA_" + nm])
-        errs["dB_" + nm] = rel_err(host(tb["dB"][i]), br["dB_" + nm])
+    errs = _oracle_errs(d, Ls, tf, tb)
+    assert max(errs.values()) <= TOL, errs
+
+
+@pytest.mark.parametrize("fmt", [1, 2])
+def test_mlp_tiled_8bit_weights(fmt):
+    # INT8 and FP8 frozen weights through the tiled block: ragged last tile
+    _announce(f"tiled mlp fmt={fmt} M=1000 tile=384 H=128 I=256 r=16")
+    d = random_mlp(1_400 + fmt, 1000, 128, 256, 16)
+    Ls, wf, wb, tf, tb = _run(d, 384, fmt=fmt)
+    _compare_to_whole(wf, wb, tf, tb, same_order=False)
+    errs = _oracle_errs(d, Ls, tf, tb)
     assert max(errs.values()) <= TOL, errs
 
 

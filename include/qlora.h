@@ -205,7 +205,19 @@ int swiglu_mlp_backward(const qlora_layer* gate, const qlora_layer* up, const ql
  * are summed over the tiles in fp32 and rounded once at the end. The workspace
  * scales with min(tile, M), not M: size from
  * swiglu_mlp_tiled_workspace_size(backward = 0 or 1, M, H, I, r, tile).
- * tile >= 1 (a multiple of 256 keeps every GEMM tile full). */
+ * tile >= 1 (a multiple of 256 keeps every GEMM tile full).
+ * With more than one tile, when a tile's last GEMM would leave CUs idle
+ * (ceil(tile/256) * ceil(H/256) < 256 workgroups), the last part of each tile
+ * runs on a second stream beside the next tile's work on `stream`: the
+ * forward's down projection GEMM, and the backward's gate and up part (their
+ * G products, reductions and the dX GEMM). The second stream is kept by the library, one per device,
+ * created on first use. Events order it against `stream`, and every such part
+ * is done before work enqueued on `stream` after the call starts. Results are
+ * those of a single-stream run: the same kernels run on the same inputs, and
+ * each gradient adds its tiles in order on one stream. The buffers that the
+ * second stream reads (h; dg and du) are held twice in the workspace. Calls
+ * from several threads on one device share that stream, so their second-stream
+ * parts run one after another. */
 size_t swiglu_mlp_tiled_workspace_size(int backward, int64_t M, int64_t H, int64_t I, int64_t r, int64_t tile);
 int swiglu_mlp_forward_tiled(const qlora_layer* gate, const qlora_layer* up, const qlora_layer* down,
                              const uint16_t* X, int64_t M, int64_t tile, uint16_t* Y, uint16_t* Z_save, void* ws,

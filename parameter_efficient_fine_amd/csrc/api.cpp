@@ -148,13 +148,26 @@ size_t bwd_ws(int64_t M, int64_t K, int64_t N, int64_t r) {
   return up256(r * N * 2) + up256(M * r * 2) + up256(l.part * 4);
 }
 
-BwdLayout mlp_bwd_layout(int64_t M, int64_t H, int64_t I, int64_t r) {
+// The SwiGLU block's backward reductions, in launch order: the down projection's
+// part, then the gate and up projections' part.
+BwdLayout mlp_bwd_down_layout(int64_t M, int64_t H, int64_t I, int64_t r) {
   BwdLayout l;
   l.add(M, H, (int)r);            // dB_down
   l.add(M, I, (int)r);            // dA_down
+  return l;
+}
+
+BwdLayout mlp_bwd_gu_layout(int64_t M, int64_t H, int64_t I, int64_t r) {
+  BwdLayout l;
   l.add(M, I, (int)r);            // dB_gate
   l.add(M, I, (int)r);            // dB_up
   l.add(M, H, (int)r, (int)r);    // dA_gate, dA_up
+  return l;
+}
+
+BwdLayout mlp_bwd_layout(int64_t M, int64_t H, int64_t I, int64_t r) {
+  BwdLayout l;
+  l.part = mlp_bwd_down_layout(M, H, I, r).part + mlp_bwd_gu_layout(M, H, I, r).part;
   return l;
 }
 
@@ -165,22 +178,40 @@ size_t mlp_bwd_ws(int64_t M, int64_t H, int64_t I, int64_t r) {
 }
 
 // Token-tiled SwiGLU block: per-tile intermediates only (tile T = min(tile, M)).
-size_t mlp_fwd_tiled_ws(int64_t M, int64_t I, int64_t tile) {
-  const int64_t T = std::min(tile, M);
-  return 3 * up256((size_t)T * I * 2);  // g, u, h of one tile
+// A tile's last GEMM (the forward's down projection, the backward's dX: T
+// tokens by H columns in 256 x 256 tiles) runs on a second stream beside the
+// next tile's work when it launches fewer workgroups than the chip has CUs;
+// the buffers it reads then alternate between two copies.
+constexpr int64_t kChipCUs = 256;
+bool tiles_overlap(int64_t M, int64_t T, int64_t H) {
+  return M > T && ((T + 255) / 256) * ((H + 255) / 256) < kChipCUs;
 }
 
-// Reduction partials of the tiled backward: the split count of a reduction is
-// not monotone in its row count (rows per split are rounded to 64), so a ragged
-// last tile can need more partials than a full one; size for the larger.
-size_t mlp_tiled_part_floats(int64_t M, int64_t H, int64_t I, int64_t r, int64_t tile) {
+size_t mlp_fwd_tiled_ws(int64_t M, int64_t H, int64_t I, int64_t tile) {
   const int64_t T = std::min(tile, M);
-  size_t part = mlp_bwd_layout(T, H, I, r).part;
+  return (tiles_overlap(M, T, H) ? 4 : 3) * up256((size_t)T * I * 2);  // g, u, h of one tile (h twice)
+}
+
+// Reduction partials of the tiled backward: the down part's and the gate/up
+// part's in regions of their own (the two parts of a tile run on different
+// streams). The split count of a reduction is not monotone in its row count
+// (rows per split are rounded to 64), so a ragged last tile can need more
+// partials than a full one: each region is sized for the larger.
+struct TiledPart {
+  size_t down = 0, gu = 0;  // floats
+};
+
+TiledPart mlp_tiled_part(int64_t M, int64_t H, int64_t I, int64_t r, int64_t tile) {
+  const int64_t T = std::min(tile, M);
+  TiledPart p;
+  p.down = mlp_bwd_down_layout(T, H, I, r).part;
+  p.gu = mlp_bwd_gu_layout(T, H, I, r).part;
   if (T > 0) {
     const int64_t last = M - ((M - 1) / T) * T;
-    part = std::max(part, mlp_bwd_layout(last, H, I, r).part);
+    p.down = std::max(p.down, mlp_bwd_down_layout(last, H, I, r).part);
+    p.gu = std::max(p.gu, mlp_bwd_gu_layout(last, H, I, r).part);
   }
-  return part;
+  return p;
 }
 
 // fp32 sums of the six adapter gradients over the tiles (used for bf16 gradients,
@@ -192,8 +223,10 @@ size_t mlp_grad_acc_bytes(int64_t H, int64_t I, int64_t r) {
 
 size_t mlp_bwd_tiled_ws(int64_t M, int64_t H, int64_t I, int64_t r, int64_t tile) {
   const int64_t T = std::min(tile, M);
-  return 5 * up256((size_t)T * I * 2) + up256(T * r * 2) + up256(T * 2 * r * 2) + up256(r * H * 2) +
-         2 * up256(r * I * 2) + up256(mlp_tiled_part_floats(M, H, I, r, tile) * 4) + mlp_grad_acc_bytes(H, I, r);
+  const TiledPart tp = mlp_tiled_part(M, H, I, r, tile);
+  // g, u, h, dg, du of one tile (dg and du twice when the tiles overlap)
+  return (tiles_overlap(M, T, H) ? 7 : 5) * up256((size_t)T * I * 2) + up256(T * r * 2) + up256(T * 2 * r * 2) +
+         up256(r * H * 2) + 2 * up256(r * I * 2) + up256((tp.down + tp.gu) * 4) + mlp_grad_acc_bytes(H, I, r);
 }
 
 // Batches of at most kSmallMaxM tokens (ranks up to kSmallMaxR) take the
@@ -569,18 +602,31 @@ int mlp_zgu(const qlora_layer* gate, const qlora_layer* up, const uint16_t* X, i
   return QLORA_OK;
 }
 
-// SwiGLU block forward over M tokens: g, u, h, then Z_d and Y.
-int mlp_fwd_body(const qlora_layer* gate, const qlora_layer* up, const qlora_layer* down, const uint16_t* X,
-                 int64_t M, uint16_t* Y, uint16_t* g, uint16_t* u, uint16_t* h, uint16_t* Zg, uint16_t* Zu,
-                 uint16_t* Zd, hipStream_t st) {
+// SwiGLU block forward over M tokens, first part: Z_g, Z_u, then g, u, h and Z_d.
+int mlp_fwd_gu(const qlora_layer* gate, const qlora_layer* up, const qlora_layer* down, const uint16_t* X,
+               int64_t M, uint16_t* g, uint16_t* u, uint16_t* h, uint16_t* Zg, uint16_t* Zu, uint16_t* Zd,
+               hipStream_t st) {
   const int64_t H = gate->K, I = gate->N;
   const int r = (int)gate->r;
   if (int rc = mlp_zgu(gate, up, X, M, Zg, Zu, st)) return rc;
   QL_LAUNCH("gemm_fwd_gateup", st,
             launch_gemm_fwd_gateup(X, M, H, I, wsrc(gate, gate->B, Zg), wsrc(up, up->B, Zu), g, u, h, st));
   QL_LAUNCH("skinny_nt", st, launch_skinny_nt(nt1(h, M, I, down->A, r, Zd, r), st));
-  QL_LAUNCH("gemm_fwd", st, launch_gemm_fwd(h, M, I, H, wsrc(down, down->B, Zd), Y, st));
   return QLORA_OK;
+}
+
+// second part: Y = h.W_d^T + s.Z_d.B_d^T
+int mlp_fwd_down(const qlora_layer* down, const uint16_t* h, int64_t M, uint16_t* Y, const uint16_t* Zd,
+                 hipStream_t st) {
+  QL_LAUNCH("gemm_fwd", st, launch_gemm_fwd(h, M, down->K, down->N, wsrc(down, down->B, Zd), Y, st));
+  return QLORA_OK;
+}
+
+int mlp_fwd_body(const qlora_layer* gate, const qlora_layer* up, const qlora_layer* down, const uint16_t* X,
+                 int64_t M, uint16_t* Y, uint16_t* g, uint16_t* u, uint16_t* h, uint16_t* Zg, uint16_t* Zu,
+                 uint16_t* Zd, hipStream_t st) {
+  if (int rc = mlp_fwd_gu(gate, up, down, X, M, g, u, h, Zg, Zu, Zd, st)) return rc;
+  return mlp_fwd_down(down, h, M, Y, Zd, st);
 }
 
 struct MlpBwdWs {
@@ -626,41 +672,142 @@ int mlp_prep(const qlora_layer* gate, const qlora_layer* up, const qlora_layer* 
   return QLORA_OK;
 }
 
-// SwiGLU block backward over M tokens, after mlp_prep. accumulate = 1 adds
-// the adapter gradients to dA/dB (later tiles of a batch).
-int mlp_bwd_body(const qlora_layer* gate, const qlora_layer* up, const qlora_layer* down, const uint16_t* dY,
-                 const uint16_t* X, const uint16_t* g, const uint16_t* u, const uint16_t* h, const uint16_t* Zg,
-                 const uint16_t* Zu, const uint16_t* Zd, int64_t M, uint16_t* dX, void* const dA[3],
-                 void* const dB[3], const MlpBwdWs& w, int accumulate, bool out_bf16, hipStream_t st) {
-  const int64_t H = gate->K, I = gate->N;
-  const int r = (int)gate->r;
-  uint16_t* Gg = w.Ggu;
-  uint16_t* Gu = w.Ggu + r;
-  TnCall tn{w.part, w.part + w.part_floats, st, accumulate};
+// SwiGLU block backward over M tokens, after mlp_prep, in two parts. accumulate
+// = 1 adds the adapter gradients to dA/dB (later tiles of a batch); each part's
+// reduction partials go to [part, part_end).
+// Down projection: G_d = dY.B_d ; dB_d = s.dY^T.Z_d and dA_d = s.G_d^T.h ; dh -> (dg, du)
+// in the GEMM epilogue.
+int mlp_bwd_down(const qlora_layer* down, const uint16_t* dY, const uint16_t* g, const uint16_t* u,
+                 const uint16_t* h, const uint16_t* Zd, int64_t M, void* dA_d, void* dB_d, const MlpBwdWs& w,
+                 float* part, const float* part_end, int accumulate, bool out_bf16, hipStream_t st) {
+  const int64_t H = down->N, I = down->K;
+  const int r = (int)down->r;
+  TnCall tn{part, part_end, st, accumulate};
   tn.out_bf16 = out_bf16;
-  // down projection: G_d = dY.B_d ; dB_d = s.dY^T.Z_d and dA_d = s.G_d^T.h ; dh -> (dg, du) in the GEMM epilogue
   QL_LAUNCH("skinny_nt", st, launch_skinny_nt(ntB(dY, M, H, down->B, w.Btd, r, w.Gd, r), st));
-  tn.one(Zd, r, r, down->s, dY, M, H, dB[2], true);
-  tn.one(w.Gd, r, r, down->s, h, M, I, dA[2], false);
+  tn.one(Zd, r, r, down->s, dY, M, H, dB_d, true);
+  tn.one(w.Gd, r, r, down->s, h, M, I, dA_d, false);
   TnJobs red{};  // reduced by the backward GEMM launched next
   if (int rc = tn.flush(&red)) return rc;
   QL_LAUNCH("gemm_bwd_swiglu", st,
             launch_gemm_bwd_swiglu(dY, wsrc(down, down->A, w.Gd), M, I, H, g, u, w.dg, w.du, &red, st));
-  // gate and up: G = d(g|u).B ; dB = s.d(g|u)^T.Z ; dA_g = s_g.G_g^T.X and dA_u = s_u.G_u^T.X
-  // (one pass over X when 2r fits a launch)
+  return QLORA_OK;
+}
+
+// Gate and up, after the down part: G = d(g|u).B ; dB = s.d(g|u)^T.Z ;
+// dA_g = s_g.G_g^T.X and dA_u = s_u.G_u^T.X (one pass over X when 2r fits a
+// launch) ; dX = dg.W_g + du.W_u + s.G_g.A_g + s.G_u.A_u, one GEMM over the
+// concatenated reduction.
+int mlp_bwd_gu(const qlora_layer* gate, const qlora_layer* up, const uint16_t* X, const uint16_t* Zg,
+               const uint16_t* Zu, int64_t M, uint16_t* dX, void* const dA[3], void* const dB[3], const MlpBwdWs& w,
+               float* part, const float* part_end, int accumulate, bool out_bf16, hipStream_t st) {
+  const int64_t H = gate->K, I = gate->N;
+  const int r = (int)gate->r;
+  uint16_t* Gg = w.Ggu;
+  uint16_t* Gu = w.Ggu + r;
+  TnCall tn{part, part_end, st, accumulate};
+  tn.out_bf16 = out_bf16;
   QL_LAUNCH("skinny_nt", st, launch_skinny_nt(ntB(w.dg, M, I, gate->B, w.Btg, r, Gg, 2 * r), st));
   QL_LAUNCH("skinny_nt", st, launch_skinny_nt(ntB(w.du, M, I, up->B, w.Btu, r, Gu, 2 * r), st));
   tn.one(Zg, r, r, gate->s, w.dg, M, I, dB[0], true);
   tn.one(Zu, r, r, up->s, w.du, M, I, dB[1], true);
   tn.two(w.Ggu, 2 * r, r, gate->s, dA[0], r, up->s, dA[1], X, M, H, false);
+  TnJobs red{};
   if (int rc = tn.flush(dX ? &red : nullptr)) return rc;
-  // dX = dg.W_g + du.W_u + s.G_g.A_g + s.G_u.A_u : one GEMM over the concatenated reduction
   if (dX)
     QL_LAUNCH("gemm_bwd", st,
               launch_gemm_bwd(w.dg, wsrc(gate, gate->A, Gg, 2 * r), w.du, wsrc(up, up->A, Gu, 2 * r), M, H, I, dX,
                               &red, st));
   return QLORA_OK;
 }
+
+int mlp_bwd_body(const qlora_layer* gate, const qlora_layer* up, const qlora_layer* down, const uint16_t* dY,
+                 const uint16_t* X, const uint16_t* g, const uint16_t* u, const uint16_t* h, const uint16_t* Zg,
+                 const uint16_t* Zu, const uint16_t* Zd, int64_t M, uint16_t* dX, void* const dA[3],
+                 void* const dB[3], const MlpBwdWs& w, bool out_bf16, hipStream_t st) {
+  float* const mid = w.part + mlp_bwd_down_layout(M, gate->K, gate->N, gate->r).part;
+  if (int rc = mlp_bwd_down(down, dY, g, u, h, Zd, M, dA[2], dB[2], w, w.part, mid, 0, out_bf16, st)) return rc;
+  return mlp_bwd_gu(gate, up, X, Zg, Zu, M, dX, dA, dB, w, mid, w.part + w.part_floats, 0, out_bf16, st);
+}
+
+// ---- a second stream per device for the token-tiled SwiGLU block: a tile's
+// last GEMM (at 1024 tokens, 64 workgroups of 256 x 256 outputs) runs beside
+// the next tile's work instead of leaving most CUs idle. Created on first use
+// with the device current, at the default priority and non-blocking (no
+// implicit ordering with the null stream); kept until the process ends.
+std::mutex g_aux_mu;
+constexpr int kAuxDevices = 64;
+hipStream_t g_aux[kAuxDevices];
+
+int aux_stream_for_current_device(hipStream_t* out) {
+  int dev = 0;
+  QL_CHECK(hipGetDevice(&dev));
+  if (dev < 0 || dev >= kAuxDevices) {
+    snprintf(g_err, sizeof(g_err), "device %d: no second-stream slot", dev);
+    return QLORA_EUNSUPPORTED;
+  }
+  std::lock_guard<std::mutex> lock(g_aux_mu);
+  if (!g_aux[dev]) QL_CHECK(hipStreamCreateWithFlags(&g_aux[dev], hipStreamNonBlocking));
+  *out = g_aux[dev];
+  return QLORA_OK;
+}
+
+// Fork and join between the caller's stream and the second stream, for tiles
+// whose buffers alternate between two copies: tile t's work on the second
+// stream reads copy t % 2, and the caller's stream waits for that work to end
+// before it writes the copy again (tile t + 2). The destructor joins, so that no
+// return leaves work of the call behind on the second stream.
+struct TileOverlap {
+  hipStream_t st, aux = nullptr;
+  hipEvent_t ev = nullptr, done[2] = {nullptr, nullptr};
+  bool pending[2] = {false, false};
+  bool forked = false;
+  explicit TileOverlap(hipStream_t s) : st(s) {}
+  TileOverlap(const TileOverlap&) = delete;
+  TileOverlap& operator=(const TileOverlap&) = delete;
+  ~TileOverlap() {
+    (void)join();
+    for (hipEvent_t e : {ev, done[0], done[1]})
+      if (e) (void)hipEventDestroy(e);
+  }
+  int init() {
+    if (int rc = aux_stream_for_current_device(&aux)) return rc;
+    QL_CHECK(hipEventCreateWithFlags(&ev, hipEventDisableTiming));
+    QL_CHECK(hipEventCreateWithFlags(&done[0], hipEventDisableTiming));
+    QL_CHECK(hipEventCreateWithFlags(&done[1], hipEventDisableTiming));
+    return QLORA_OK;
+  }
+  // before the caller's stream writes copy b again
+  int reclaim(int b) {
+    if (pending[b]) {
+      QL_CHECK(hipStreamWaitEvent(st, done[b], 0));
+      pending[b] = false;
+    }
+    return QLORA_OK;
+  }
+  // what is enqueued next on the second stream starts after all that is enqueued on the caller's
+  int fork() {
+    QL_CHECK(hipEventRecord(ev, st));
+    QL_CHECK(hipStreamWaitEvent(aux, ev, 0));
+    forked = true;
+    return QLORA_OK;
+  }
+  // the second stream is done with copy b once what is enqueued on it so far has run
+  int release(int b) {
+    QL_CHECK(hipEventRecord(done[b], aux));
+    pending[b] = true;
+    return QLORA_OK;
+  }
+  // the caller's stream waits for all of the call's work on the second stream
+  int join() {
+    if (!forked) return QLORA_OK;
+    forked = false;
+    pending[0] = pending[1] = false;
+    QL_CHECK(hipEventRecord(ev, aux));
+    QL_CHECK(hipStreamWaitEvent(st, ev, 0));
+    return QLORA_OK;
+  }
+};
 
 bool mlp_grads_ok(void* const dA[3], void* const dB[3]) {
   if (!dA || !dB) return false;
@@ -710,12 +857,12 @@ int swiglu_mlp_backward(const qlora_layer* gate, const qlora_layer* up, const ql
   if (int rc = mlp_prep(gate, up, down, w, st)) return rc;
   const size_t Mr = (size_t)M * r;
   return mlp_bwd_body(gate, up, down, dY, X, g_save, u_save, h_save, Z_save, Z_save + Mr, Z_save + 2 * Mr, M, dX,
-                      dA, dB, w, 0, grads_bf16(gate), st);
+                      dA, dB, w, grads_bf16(gate), st);
 }
 
 size_t swiglu_mlp_tiled_workspace_size(int backward, int64_t M, int64_t H, int64_t I, int64_t r, int64_t tile) {
   if (M < 0 || H < 0 || I < 0 || r < 1 || tile < 1) return 0;
-  return backward ? mlp_bwd_tiled_ws(M, H, I, r, tile) : mlp_fwd_tiled_ws(M, I, tile);
+  return backward ? mlp_bwd_tiled_ws(M, H, I, r, tile) : mlp_fwd_tiled_ws(M, H, I, tile);
 }
 
 int swiglu_mlp_forward_tiled(const qlora_layer* gate, const qlora_layer* up, const qlora_layer* down,
@@ -726,21 +873,36 @@ int swiglu_mlp_forward_tiled(const qlora_layer* gate, const qlora_layer* up, con
   if (!X || !Y || !Z_save || !aligned16(X) || !aligned16(Y) || !aligned16(Z_save)) return QLORA_EINVAL;
   const int64_t H = gate->K, I = gate->N, r = gate->r;
   const int64_t T = std::min(tile, M);
-  if (!ws || ws_bytes < mlp_fwd_tiled_ws(M, I, tile)) return QLORA_EWORKSPACE;
+  if (!ws || ws_bytes < mlp_fwd_tiled_ws(M, H, I, tile)) return QLORA_EWORKSPACE;
   Carve c{(char*)ws, ws_bytes};
+  const bool two = tiles_overlap(M, T, H);  // the down projection's GEMM on the second stream
   uint16_t* g = c.take<uint16_t>((size_t)T * I);
   uint16_t* u = c.take<uint16_t>((size_t)T * I);
-  uint16_t* h = c.take<uint16_t>((size_t)T * I);
+  uint16_t* hb[2];
+  hb[0] = c.take<uint16_t>((size_t)T * I);
+  hb[1] = two ? c.take<uint16_t>((size_t)T * I) : hb[0];
   if (!c.ok) return QLORA_EWORKSPACE;
   hipStream_t st = (hipStream_t)stream;
+  TileOverlap ov(st);
+  if (two)
+    if (int rc = ov.init()) return rc;
   const size_t Mr = (size_t)M * r;
-  for (int64_t t0 = 0; t0 < M; t0 += T) {
+  for (int64_t t0 = 0, t = 0; t0 < M; t0 += T, ++t) {
     const int64_t Mt = std::min(T, M - t0);
+    const int b = (int)(t & 1);
     uint16_t* Zt = Z_save + (size_t)t0 * r;
-    if (int rc = mlp_fwd_body(gate, up, down, X + t0 * H, Mt, Y + t0 * H, g, u, h, Zt, Zt + Mr, Zt + 2 * Mr, st))
-      return rc;
+    if (int rc = ov.reclaim(b)) return rc;
+    if (int rc = mlp_fwd_gu(gate, up, down, X + t0 * H, Mt, g, u, hb[b], Zt, Zt + Mr, Zt + 2 * Mr, st)) return rc;
+    if (!two) {
+      if (int rc = mlp_fwd_down(down, hb[b], Mt, Y + t0 * H, Zt + 2 * Mr, st)) return rc;
+      continue;
+    }
+    // Y rows of this tile on the second stream, beside the next tile's Z, g, u, h
+    if (int rc = ov.fork()) return rc;
+    if (int rc = mlp_fwd_down(down, hb[b], Mt, Y + t0 * H, Zt + 2 * Mr, ov.aux)) return rc;
+    if (int rc = ov.release(b)) return rc;
   }
-  return QLORA_OK;
+  return ov.join();
 }
 
 int swiglu_mlp_backward_tiled(const qlora_layer* gate, const qlora_layer* up, const qlora_layer* down,
@@ -757,10 +919,20 @@ int swiglu_mlp_backward_tiled(const qlora_layer* gate, const qlora_layer* up, co
   const int64_t T = std::min(tile, M);
   if (!ws || ws_bytes < mlp_bwd_tiled_ws(M, H, I, r, tile)) return QLORA_EWORKSPACE;
   Carve c{(char*)ws, ws_bytes};
+  const bool two = tiles_overlap(M, T, H);  // each tile's gate/up part on the second stream
   uint16_t* g = c.take<uint16_t>((size_t)T * I);
   uint16_t* u = c.take<uint16_t>((size_t)T * I);
   uint16_t* h = c.take<uint16_t>((size_t)T * I);
-  const MlpBwdWs w = carve_mlp_bwd(c, T, H, I, r, mlp_tiled_part_floats(M, H, I, r, tile));
+  const TiledPart tp = mlp_tiled_part(M, H, I, r, tile);
+  MlpBwdWs wb[2];
+  wb[0] = carve_mlp_bwd(c, T, H, I, r, tp.down + tp.gu);
+  wb[1] = wb[0];
+  if (two) {  // a second dg, du: the gate/up part of tile t reads copy t % 2
+    wb[1].dg = c.take<uint16_t>((size_t)T * I);
+    wb[1].du = c.take<uint16_t>((size_t)T * I);
+  }
+  const MlpBwdWs& w = wb[0];
+  float* const part_gu = w.part + tp.down;  // the down part's region, then the gate/up part's
   // bf16 gradients: the tiles add into fp32 sums, rounded once at the end
   const bool gb = grads_bf16(gate);
   const qlora_layer* Ls[3] = {gate, up, down};
@@ -775,18 +947,38 @@ int swiglu_mlp_backward_tiled(const qlora_layer* gate, const qlora_layer* up, co
   if (int rc = mlp_prep(gate, up, down, w, st)) return rc;
   void* const* oA = gb ? accA : dA;
   void* const* oB = gb ? accB : dB;
+  TileOverlap ov(st);
+  if (two)
+    if (int rc = ov.init()) return rc;
   const size_t Mr = (size_t)M * r;
-  for (int64_t t0 = 0; t0 < M; t0 += T) {
+  for (int64_t t0 = 0, t = 0; t0 < M; t0 += T, ++t) {
     const int64_t Mt = std::min(T, M - t0);
+    const int b = (int)(t & 1);
+    const int acc = t0 > 0 ? 1 : 0;
     const uint16_t* Xt = X + t0 * H;
     const uint16_t* Zt = Z_save + (size_t)t0 * r;
+    if (int rc = ov.reclaim(b)) return rc;
     // recompute the tile's g, u, h (bitwise what the forward produced: same kernels, same inputs)
     QL_LAUNCH("gemm_fwd_gateup", st,
               launch_gemm_fwd_gateup(Xt, Mt, H, I, wsrc(gate, gate->B, Zt), wsrc(up, up->B, Zt + Mr), g, u, h, st));
-    if (int rc = mlp_bwd_body(gate, up, down, dY + t0 * H, Xt, g, u, h, Zt, Zt + Mr, Zt + 2 * Mr, Mt,
-                              dX ? dX + t0 * H : nullptr, oA, oB, w, t0 > 0 ? 1 : 0, false, st))
+    if (int rc = mlp_bwd_down(down, dY + t0 * H, g, u, h, Zt + 2 * Mr, Mt, oA[2], oB[2], wb[b], w.part, part_gu, acc,
+                              false, st))
       return rc;
+    // the gate and up projections' gradients and dX rows: on the second stream
+    // beside the next tile's recompute and down part (each gradient still adds
+    // its tiles in order, on one stream)
+    hipStream_t sg = st;
+    if (two) {
+      if (int rc = ov.fork()) return rc;
+      sg = ov.aux;
+    }
+    if (int rc = mlp_bwd_gu(gate, up, Xt, Zt, Zt + Mr, Mt, dX ? dX + t0 * H : nullptr, oA, oB, wb[b], part_gu,
+                            part_gu + tp.gu, acc, false, sg))
+      return rc;
+    if (two)
+      if (int rc = ov.release(b)) return rc;
   }
+  if (int rc = ov.join()) return rc;
   if (gb) {
     CastJobs cj{};
     for (int i = 0; i < 3; ++i) {

@@ -141,12 +141,20 @@ def test_tiled_mlp_workspace_scales_with_the_tile_not_the_batch():
     H, I = 4096, 14336
     for r in (1, 16, 129, 256):
         for bwd in (0, 1):
-            per_tile = lib.swiglu_mlp_tiled_workspace_size(bwd, 4096, H, I, r, 4096)
-            assert per_tile > 0 and per_tile % 256 == 0
-            # a longer batch with the same tile needs no more workspace
-            assert lib.swiglu_mlp_tiled_workspace_size(bwd, 1 << 20, H, I, r, 4096) == per_tile
-            # a tile longer than the batch is sized by the batch
-            assert lib.swiglu_mlp_tiled_workspace_size(bwd, 4096, H, I, r, 1 << 20) == per_tile
+            for tile in (1024, 4096):
+                one_tile = lib.swiglu_mlp_tiled_workspace_size(bwd, tile, H, I, r, tile)
+                assert one_tile > 0 and one_tile % 256 == 0
+                # from two tiles on, where a tile's last GEMM (tile x H outputs) has fewer
+                # 256 x 256 workgroups than the 256 CUs, one [tile, I] buffer more (h,
+                # forward) or two more (dg and du, backward): that GEMM runs beside the
+                # next tile's work, reading its own copy
+                extra = (2 if bwd else 1) * tile * I * 2 if (tile // 256) * (H // 256) < 256 else 0
+                two_tiles = lib.swiglu_mlp_tiled_workspace_size(bwd, 2 * tile, H, I, r, tile)
+                assert two_tiles == one_tile + extra, (bwd, tile, r)
+                # a longer batch with the same tile needs no more than two tiles do
+                assert lib.swiglu_mlp_tiled_workspace_size(bwd, 1 << 20, H, I, r, tile) == two_tiles
+                # a tile longer than the batch is sized by the batch
+                assert lib.swiglu_mlp_tiled_workspace_size(bwd, tile, H, I, r, 1 << 20) == one_tile
             assert lib.swiglu_mlp_tiled_workspace_size(bwd, 0, H, I, r, 4096) >= 0
         # the tiled backward's workspace holds g, u, h, dg, du of one tile; the whole-batch
         # backward holds dg, du of the batch (g, u, h are saved by its forward)
@@ -292,8 +300,9 @@ def test_tiled_mlp_workspace_covers_every_tile(H, I):
             for M in (tile + 64, 1088, 1920, 2 * tile - 128, 3 * tile + 896, 16384):
                 T = min(tile, M)
                 sizes = {T, M - ((M - 1) // T) * T}
-                fixed = (5 * _up256(T * I * 2) + _up256(T * r * 2) + _up256(T * 2 * r * 2) + _up256(r * H * 2)
-                         + 2 * _up256(r * I * 2))
+                overlap = M > T and -(-T // 256) * -(-H // 256) < 256
+                fixed = ((7 if overlap else 5) * _up256(T * I * 2) + _up256(T * r * 2) + _up256(T * 2 * r * 2)
+                         + _up256(r * H * 2) + 2 * _up256(r * I * 2))
                 need = fixed + max(_mlp_part_bytes(lib, m, H, I, r) for m in sizes)
                 got = lib.swiglu_mlp_tiled_workspace_size(1, M, H, I, r, tile)
                 assert got >= need, (M, tile, r, H, I, got, need)

@@ -128,6 +128,29 @@ def test_mlp_tiled_long_batch_full_size():
     assert not host(tb["dX"])[~keep].any()
 
 
+def test_mlp_tiled_second_stream_at_full_width():
+    # tiles of 1024 tokens (the last one ragged) at Llama-3.1-8B widths: each
+    # tile's down-projection GEMM (forward) and gate/up part (backward) run on
+    # the library's second stream beside the next tile's work. Rows must equal
+    # the whole-batch call's bit for bit and the gradients up to summation
+    # order, and repeated runs must give the first run's bits.
+    _announce("tiled mlp second stream M=3500 tile=1024 H=4096 I=14336 r=16")
+    import parameter_efficient_fine_amd as q
+    d = random_mlp(4100, 3500, 4096, 14336, 16)
+    Ls, wf, wb, tf, tb = _run(d, 1024)
+    _compare_to_whole(wf, wb, tf, tb, same_order=False)
+    g, u, dn = (Ls[nm].dev for nm in ("gate", "up", "down"))
+    X, dY = dev_bf16(d["X"]), dev_bf16(d["dY"])
+    for _ in range(2):
+        tf2 = q.mlp_forward_tiled(g, u, dn, X, 1024)
+        tb2 = q.mlp_backward_tiled(g, u, dn, dY, X, tf2["Z"], 1024)
+        for a, b in ((tf2["Y"], tf["Y"]), (tf2["Z"], tf["Z"]), (tb2["dX"], tb["dX"])):
+            assert np.array_equal(_bits(a), _bits(b))
+        for i in range(3):
+            for key in ("dA", "dB"):
+                assert np.array_equal(_bits(tb2[key][i]), _bits(tb[key][i])), (key, i)
+
+
 def test_mlp_tiled_backward_independent_of_workspace_and_output_contents():
     # the first tile overwrites dA/dB and later tiles add to them: outputs and a
     # workspace full of NaN bytes must not leak into the result

@@ -151,6 +151,32 @@ def test_mlp_tiled_second_stream_at_full_width():
                 assert np.array_equal(_bits(tb2[key][i]), _bits(tb[key][i])), (key, i)
 
 
+@pytest.mark.parametrize("tile", [0, 384])
+def test_mlp_backward_without_dx_matches_the_one_with_dx(tile):
+    # Without dX the gate/up reductions' split partials are added by a reduce
+    # launch of their own (on the second stream when the tiles overlap) instead
+    # of the dX GEMM's prologue. Same partials, same split order: the gradients
+    # agree bit for bit. tile = 0: the whole-batch call.
+    _announce(f"mlp backward without dX M=1000 H=128 I=256 r=16 tile={tile}")
+    import parameter_efficient_fine_amd as q
+    d = random_mlp(1_500 + tile, 1000, 128, 256, 16)
+    Ls = {nm: Prepared(d["layers"][nm], d["s"]) for nm in ("gate", "up", "down")}
+    g, u, dn = Ls["gate"].dev, Ls["up"].dev, Ls["down"].dev
+    X, dY = dev_bf16(d["X"]), dev_bf16(d["dY"])
+    if tile:
+        f = q.mlp_forward_tiled(g, u, dn, X, tile)
+        b1 = q.mlp_backward_tiled(g, u, dn, dY, X, f["Z"], tile)
+        b0 = q.mlp_backward_tiled(g, u, dn, dY, X, f["Z"], tile, need_dX=False)
+    else:
+        f = q.mlp_forward(g, u, dn, X)
+        b1 = q.mlp_backward(g, u, dn, dY, X, f)
+        b0 = q.mlp_backward(g, u, dn, dY, X, f, need_dX=False)
+    assert b0["dX"] is None and b1["dX"] is not None
+    for i in range(3):
+        for key in ("dA", "dB"):
+            assert np.array_equal(_bits(b0[key][i]), _bits(b1[key][i])), (key, i)
+
+
 def test_mlp_tiled_backward_independent_of_workspace_and_output_contents():
     # the first tile overwrites dA/dB and later tiles add to them: outputs and a
     # workspace full of NaN bytes must not leak into the result

@@ -93,6 +93,31 @@ def test_mlp_tiled_8bit_weights(fmt):
     assert max(errs.values()) <= TOL, errs
 
 
+def _random_tiled_shapes(n, seed):
+    rng = np.random.default_rng(seed)
+    out = []
+    for i in range(n):
+        M = int(rng.integers(1, 1500))
+        tile = int(rng.choice([64, 96, 128, 256, 320, 512, 700]))
+        H = 64 * int(rng.integers(1, 5))
+        I = 64 * int(rng.integers(1, 7))
+        r = int(rng.integers(1, 33)) if i % 3 else int(rng.integers(100, 161))
+        out.append((M, tile, H, I, r))
+    return out
+
+
+@pytest.mark.parametrize("M,tile,H,I,r", _random_tiled_shapes(8, 2028))
+def test_mlp_tiled_random_shapes(M, tile, H, I, r):
+    # seeded shapes: ragged last tiles, 1 to 20 tiles (two streams), ranks that
+    # need the B^T copies (r % 16 != 0) and reductions in several launches (2r > 256)
+    _announce(f"tiled mlp random M={M} tile={tile} H={H} I={I} r={r}")
+    d = random_mlp(2_000 + M + tile + H + I + r, M, H, I, r)
+    Ls, wf, wb, tf, tb = _run(d, tile)
+    _compare_to_whole(wf, wb, tf, tb, same_order=tile >= M)
+    errs = _oracle_errs(d, Ls, tf, tb)
+    assert max(errs.values()) <= TOL, errs
+
+
 def test_mlp_tiled_high_rank():
     # 2r > 256: the paired Z_g, Z_u product and the dA reductions split into several launches per tile
     _announce("tiled mlp M=600 tile=256 H=128 I=256 r=200")

@@ -230,7 +230,7 @@ size_t mlp_bwd_tiled_ws(int64_t M, int64_t H, int64_t I, int64_t r, int64_t tile
 }
 
 // Batches of at most kSmallMaxM tokens (ranks up to kSmallMaxR) take the
-// small-batch kernels: one wave per 32 x 32 output tile, the rank-r products
+// small-batch kernels: one workgroup per 32 x 32 output tile, the rank-r products
 // of the tile formed alongside, one-split reductions written out directly.
 bool small_batch(const qlora_layer* L, int64_t M) { return M <= kSmallMaxM && L->r <= kSmallMaxR; }
 

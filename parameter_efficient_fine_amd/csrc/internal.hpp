@@ -178,7 +178,8 @@ inline hipError_t launch_gemm_bwd_swiglu(const uint16_t* dY, WSrc w, int64_t M, 
 #undef QL_BY_FMT
 
 // Small-batch path (batches of at most kSmallMaxM tokens, ranks up to
-// kSmallMaxR): one wave per 32 x 32 output tile over the whole reduction.
+// kSmallMaxR): one workgroup per 32 x 32 output tile, its four waves splitting
+// the reduction.
 constexpr int64_t kSmallMaxM = 256;
 constexpr int kSmallMaxR = 32;
 struct SmallFwdArgs {       // Y = X . What^T + s . Z . B^T and Z = X . A^T

@@ -1,9 +1,14 @@
 // Small-batch path of the fused QLoRA layer (gfx950): batches of at most
 // kSmallMaxM tokens and ranks up to 32. The 256 x 256 tiles of the main GEMMs
 // give such a batch a handful of workgroups (two at 256 tokens x 512 outputs)
-// and the rank-r steps cost a launch each, so here one wave computes a 32 x 32
-// output tile over the whole reduction and does the rank-r products of its own
-// tile alongside, which leaves three launches per forward + backward:
+// and the rank-r steps cost a launch each, so here one workgroup computes a
+// 32 x 32 output tile and does the rank-r products of its own tile alongside,
+// which leaves three launches per forward + backward. The reduction is split
+// over the workgroup's kKS waves (wave w takes 64-deep blocks w, w + kKS, ..,
+// each wave prefetching its next block): a short reduction is then a few
+// load round trips deep instead of one per block. The waves' fp32 partial
+// products are added in wave order (fixed, so runs repeat bit for bit), and
+// wave 0 finishes the tile:
 //   forward  k_small_fwd: Y = X.What^T + s.Z.B^T and Z = X.A^T (Z formed by the
 //            wave from the X fragments it loads anyway; the workgroups of the
 //            first column tile write it out);
@@ -22,6 +27,26 @@ namespace {
 
 constexpr int kT = 32;   // tokens per workgroup, and output columns (fwd: weight rows; bwd: input features)
 constexpr int kRS = 32;  // rank slots (r <= 32, zero past r)
+constexpr int kKS = 4;   // waves per workgroup, splitting the reduction
+
+// wave 0's a and b += the partial products that waves 1 .. kKS-1 left in part,
+// in wave order. Every wave of the workgroup calls it; the other waves return
+// false and are done.
+__device__ __forceinline__ bool sum_waves(f32x16 (&part)[kKS - 1][2][64], int wave, int lane, f32x16& a,
+                                          f32x16& b) {
+  if (wave > 0) {
+    part[wave - 1][0][lane] = a;
+    part[wave - 1][1][lane] = b;
+  }
+  __syncthreads();
+  if (wave > 0) return false;
+#pragma unroll
+  for (int w = 0; w < kKS - 1; ++w) {
+    a += part[w][0][lane];
+    b += part[w][1][lane];
+  }
+  return true;
+}
 
 // ---------------------------------------------------------------------------
 // Forward. Lane l: weight row n0 + l%32 and input column half l/32 of each
@@ -30,9 +55,11 @@ constexpr int kRS = 32;  // rank slots (r <= 32, zero past r)
 // a workgroup lie in one 64-row group, whose block b holds its nr rows' codes
 // one after the other.
 template <int F, bool ALIGNED>
-__global__ __launch_bounds__(64) void k_small_fwd(SmallFwdArgs p) {
+__global__ __launch_bounds__(64 * kKS) void k_small_fwd(SmallFwdArgs p) {
   __shared__ __attribute__((aligned(16))) uint16_t zt[kT * kRS];  // Z tile [token][rank] bf16
-  const int lane = threadIdx.x, jl = lane & 31, h = lane >> 5;
+  __shared__ f32x16 part[kKS - 1][2][64];                          // partial Y and Z products of waves 1..
+  const int lane = threadIdx.x & 63, jl = lane & 31, h = lane >> 5;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int64_t M = p.M, K = p.K, N = p.N;
   const int64_t nJ = (M + kT - 1) / kT;
   const int64_t it = blockIdx.x / nJ, jt = blockIdx.x - it * nJ;
@@ -81,9 +108,9 @@ __global__ __launch_bounds__(64) void k_small_fwd(SmallFwdArgs p) {
 
   f32x16 acc = f32x16{}, accz = f32x16{};
   Blk cur, nxt;
-  load(0, cur);
-  for (int64_t b = 0; b < nblk; ++b) {
-    if (b + 1 < nblk) load(b + 1, nxt);
+  if (wave < nblk) load(wave, cur);
+  for (int64_t b = wave; b < nblk; b += kKS) {
+    if (b + kKS < nblk) load(b + kKS, nxt);
     const WPrep<F> prep = wprep<F>(cur.am);
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) {
@@ -93,14 +120,15 @@ __global__ __launch_bounds__(64) void k_small_fwd(SmallFwdArgs p) {
     }
     cur = nxt;
   }
+  if (!sum_waves(part, wave, lane, acc, accz)) return;
 
-  // Z in bf16 (lane: token jl, ranks 8q + 4h .. +3): the LDS tile for the rank
-  // term, and the saved Z from the first column tile
+  // wave 0 from here. Z in bf16 (lane: token jl, ranks 8q + 4h .. +3): the LDS
+  // tile for the rank term (written and read back by this wave alone), and the
+  // saved Z from the first column tile
 #pragma unroll
   for (int q = 0; q < 4; ++q)
     *reinterpret_cast<u32x2*>(&zt[jl * kRS + 8 * q + 4 * h]) =
         u32x2{pack_bf16x2(accz[4 * q], accz[4 * q + 1]), pack_bf16x2(accz[4 * q + 2], accz[4 * q + 3])};
-  __syncthreads();
   if (it == 0 && jl < rows_here) {
 #pragma unroll
     for (int q = 0; q < 4; ++q)
@@ -141,11 +169,15 @@ __global__ __launch_bounds__(64) void k_small_fwd(SmallFwdArgs p) {
 // the substep), which is the A operand of dX = What^T . dY^T and the B operand of
 // G = dY . B. The dY fragment (token l%32, 8 rows) serves both products.
 template <int F, bool ALIGNED>
-__global__ __launch_bounds__(64) void k_small_bwd(SmallBwdArgs p) {
-  __shared__ __attribute__((aligned(16))) uint16_t wt[64 * kT];   // weight rows x 32 columns
-  __shared__ __attribute__((aligned(16))) uint16_t bt[64 * kRS];  // B rows x 32 ranks
-  __shared__ __attribute__((aligned(16))) uint16_t gt[kT * kRS];  // G [token][rank] bf16
-  const int lane = threadIdx.x, jl = lane & 31, h = lane >> 5;
+__global__ __launch_bounds__(64 * kKS) void k_small_bwd(SmallBwdArgs p) {
+  __shared__ __attribute__((aligned(16))) uint16_t wts[kKS][64 * kT];   // per wave: weight rows x 32 columns
+  __shared__ __attribute__((aligned(16))) uint16_t bts[kKS][64 * kRS];  // per wave: B rows x 32 ranks
+  __shared__ __attribute__((aligned(16))) uint16_t gt[kT * kRS];        // G [token][rank] bf16
+  __shared__ f32x16 part[kKS - 1][2][64];                               // partial dX and G products of waves 1..
+  const int lane = threadIdx.x & 63, jl = lane & 31, h = lane >> 5;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  uint16_t* const wt = wts[wave];  // private to the wave: its own writes and reads, in order, need no barrier
+  uint16_t* const bt = bts[wave];
   const int64_t M = p.M, K = p.K, N = p.N;
   const int64_t nJ = (M + kT - 1) / kT;
   const int64_t ik = blockIdx.x / nJ, jt = blockIdx.x - ik * nJ;
@@ -192,16 +224,15 @@ __global__ __launch_bounds__(64) void k_small_bwd(SmallBwdArgs p) {
 
   f32x16 acc = f32x16{}, accg = f32x16{};
   Stp cur, nxt;
-  load(0, cur);
-  for (int st = 0; st < nsteps; ++st) {
-    if (st + 1 < nsteps) load(st + 1, nxt);
+  if (wave < nsteps) load(wave, cur);
+  for (int st = wave; st < nsteps; st += kKS) {
+    if (st + kKS < nsteps) load(st + kKS, nxt);
     const WPrep<F> prep = wprep<F>(cur.am);
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
       *reinterpret_cast<u32x4*>(&wt[lane * kT + 8 * c]) = wdeq8<F, kNVs>(cur.c, c, prep);
       *reinterpret_cast<u32x4*>(&bt[lane * kRS + 8 * c]) = cur.brow[c];
     }
-    __syncthreads();
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) {
       const int o0 = (16 * ks + trow) * kT + tcol, o1 = o0 + 4 * kT;
@@ -210,17 +241,17 @@ __global__ __launch_bounds__(64) void k_small_bwd(SmallBwdArgs p) {
       acc = mfma32(u32x4{w0[0], w0[1], w1[0], w1[1]}, cur.dy[ks], acc);   // D[input column][token]
       accg = mfma32(cur.dy[ks], u32x4{b0[0], b0[1], b1[0], b1[1]}, accg);  // D[token][rank]
     }
-    __syncthreads();  // the tiles are rewritten by the next step
     cur = nxt;
   }
+  if (!sum_waves(part, wave, lane, acc, accg)) return;
 
-  // G in bf16 (lane: rank jl, tokens 8q + 4h .. +3) into gt [token][rank]
+  // wave 0 from here. G in bf16 (lane: rank jl, tokens 8q + 4h .. +3) into gt
+  // [token][rank], written and read back by this wave alone
 #pragma unroll
   for (int q = 0; q < 4; ++q)
 #pragma unroll
     for (int e = 0; e < 4; ++e)
       gt[(8 * q + 4 * h + e) * kRS + jl] = __builtin_bit_cast(uint16_t, (__bf16)accg[4 * q + e]);
-  __syncthreads();
   if (ik == 0 && jl < rows_here) {  // G rows of this token tile: token jl, ranks 16h .. 16h+15
 #pragma unroll
     for (int e = 0; e < 16; ++e) {
@@ -269,9 +300,9 @@ hipError_t launch_small_fwd(const SmallFwdArgs& a, int fmt, hipStream_t st) {
 #define QL_SF(FM)                                               \
   do {                                                          \
     if (al)                                                     \
-      k_small_fwd<FM, true><<<grid, 64, 0, st>>>(a);            \
+      k_small_fwd<FM, true><<<grid, 64 * kKS, 0, st>>>(a);            \
     else                                                        \
-      k_small_fwd<FM, false><<<grid, 64, 0, st>>>(a);           \
+      k_small_fwd<FM, false><<<grid, 64 * kKS, 0, st>>>(a);           \
   } while (0)
   if (fmt == kNF4)
     QL_SF(kNF4);
@@ -290,9 +321,9 @@ hipError_t launch_small_bwd(const SmallBwdArgs& a, int fmt, hipStream_t st) {
 #define QL_SB(FM)                                               \
   do {                                                          \
     if (al)                                                     \
-      k_small_bwd<FM, true><<<grid, 64, 0, st>>>(a);            \
+      k_small_bwd<FM, true><<<grid, 64 * kKS, 0, st>>>(a);            \
     else                                                        \
-      k_small_bwd<FM, false><<<grid, 64, 0, st>>>(a);           \
+      k_small_bwd<FM, false><<<grid, 64 * kKS, 0, st>>>(a);           \
   } while (0)
   if (fmt == kNF4)
     QL_SB(kNF4);

@@ -1,8 +1,10 @@
 """GPU parity of the small-batch path (batches of at most 256 tokens, ranks up
-to 32: one wave per 32 x 32 output tile, the rank-r products of the tile formed
-in the same kernel, one-split reductions written directly) against the full
-oracle, over ragged batches, widths, ranks and the three weight formats; and
-at the boundary (256 and 257 tokens) where the main kernels take over."""
+to 32: one workgroup per 32 x 32 output tile, its four waves splitting the
+reduction and adding their partial products in wave order, the rank-r
+products of the tile formed in the same kernel, one-split reductions written
+directly) against the full oracle, over ragged batches, widths, ranks and the
+three weight formats; and at the boundary (256 and 257 tokens) where the main
+kernels take over."""
 import numpy as np
 import pytest
 

@@ -26,13 +26,15 @@
  * Conventions for every call:
  *   - Pointers are device pointers owned by the caller, row-major and
  *     contiguous, 16-byte aligned. bf16 tensors are passed as uint16_t bit
- *     patterns. The library allocates no memory; scratch space comes from the
- *     caller's workspace (size from qlora_workspace_size).
+ *     patterns. The library allocates no device memory; scratch space comes
+ *     from the caller's workspace (size from qlora_workspace_size).
  *   - Shapes: K % 64 == 0, N % 8 == 0, 1 <= r <= 256, K and N <= 2^21,
  *     N*K <= 2^31 (2^30 for the 8-bit formats), M >= 0 (M == 0 is a no-op; a backward then writes zero
  *     gradients). Anything else returns QLORA_EINVAL before any launch.
  *   - Every call enqueues its kernels on `stream` (a hipStream_t, 0 = the
- *     null stream) and returns without synchronising. Launch failures return
+ *     null stream) and returns without synchronising. (The token-tiled SwiGLU
+ *     calls also run part of their work on a second stream of the library's,
+ *     ordered against `stream` by events.) Launch failures return
  *     QLORA_EHIP; qlora_last_error() gives the HIP error text.
  *   - Calls are re-entrant; concurrent calls must not share output or
  *     workspace buffers.

@@ -263,9 +263,10 @@ NtArgs nt1(const uint16_t* in, int64_t M, int64_t Kd, const uint16_t* ad, int r,
   return a;
 }
 
-// G = in . B for B stored [Kd, r] (the layer's layout): read in place when r is a
-// multiple of 16, else from its transposed copy Bt [r, Kd] (made by the prep kernel).
-bool b_in_place(int64_t r) { return r % 16 == 0; }
+// G = in . B for B stored [Kd, r] (the layer's layout): read in place for the
+// ranks skinny_nt's [Kd, r] form is built for (16, 32, 64, 128, 256), else from
+// the transposed copy Bt [r, Kd] (made by the prep kernel).
+bool b_in_place(int64_t r) { return r == 16 || r == 32 || r == 64 || r == 128 || r == 256; }
 NtArgs ntB(const uint16_t* in, int64_t M, int64_t Kd, const uint16_t* B, const uint16_t* Bt, int r, uint16_t* out,
            int64_t ld) {
   NtArgs a = nt1(in, M, Kd, b_in_place(r) ? B : Bt, r, out, ld);

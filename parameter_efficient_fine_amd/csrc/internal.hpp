@@ -34,7 +34,7 @@ struct NtArgs {
   uint16_t* out1;
   uint16_t* out2;
   int64_t ld1, ld2;
-  int ad_kr;  // 1: a single adapter ad1 stored [Kd, r1] (r1 % 16 == 0, r2 == 0), e.g. B for G = dY.B
+  int ad_kr;  // 1: a single adapter ad1 stored [Kd, r1] (r1 = 16, 32, 64, 128 or 256, r2 == 0), e.g. B for G = dY.B
 };
 hipError_t launch_skinny_nt(const NtArgs& a, hipStream_t st);
 

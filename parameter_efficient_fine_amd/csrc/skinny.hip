@@ -255,7 +255,7 @@ hipError_t launch_skinny_nt(const NtArgs& a, hipStream_t st) {
   if (a.M == 0) return hipSuccess;
   const int R = a.r1 + a.r2;
   if (a.ad_kr) {  // a single adapter stored [Kd, R]
-    if (a.r2 != 0 || R % 16 != 0) return hipErrorInvalidValue;
+    if (a.r2 != 0) return hipErrorInvalidValue;  // R = 16, 32, 64, 128 or 256 below
     if (R == 16) return launch_nt_rf<16, true>(a, st);
     if (R == 32) return launch_nt_rf<32, true>(a, st);
     if (R == 64) return launch_nt_rf<64, true>(a, st);

@@ -131,13 +131,23 @@ def test_linear_tiny_workload_full_oracle():
     (8200, 128, 136, 24),   # two 16-row fragments per rank-product workgroup, ragged last group
     (16400, 64, 72, 40),    # four fragments per workgroup, ragged last group
     (8232, 64, 80, 200),    # rank 200 with two fragments per workgroup
-    (300, 192, 200, 16),    # B read in place (rank % 16 == 0) with a ragged last 32-row step of G = dY.B
+    (300, 192, 200, 16),    # B read in place (rank 16) with a ragged last 32-row step of G = dY.B
     (77, 256, 136, 32),     # the same at rank 32
     (520, 128, 8, 64),      # N = 8: one ragged step only
 ])
 def test_linear_ragged_shapes_full_oracle(M, K, N, r):
     _announce(f"linear ragged M={M} K={K} N={N} r={r}")
     d = random_linear(10_000 + M + K + N + r, M, K, N, r)
+    errs = _linear_case(d)
+    assert max(errs.values()) <= TOL, errs
+
+
+@pytest.mark.parametrize("r", [48, 80, 96, 112, 144, 160, 192, 240])
+def test_linear_ranks_multiple_of_16_not_a_power_of_two(r):
+    # B is read in place for G = dY.B only at ranks 16, 32, 64, 128 and 256 (the
+    # forms skinny_nt has); these ranks take the transposed copy of B instead
+    _announce(f"linear rank {r} M=700 K=256 N=200")
+    d = random_linear(61_000 + r, 700, 256, 200, r)
     errs = _linear_case(d)
     assert max(errs.values()) <= TOL, errs
 

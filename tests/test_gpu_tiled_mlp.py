@@ -109,11 +109,22 @@ def _random_tiled_shapes(n, seed):
 @pytest.mark.parametrize("M,tile,H,I,r", _random_tiled_shapes(8, 2028))
 def test_mlp_tiled_random_shapes(M, tile, H, I, r):
     # seeded shapes: ragged last tiles, 1 to 20 tiles (two streams), ranks that
-    # need the B^T copies (r % 16 != 0) and reductions in several launches (2r > 256)
+    # need the B^T copies (r not 16, 32, 64, 128, 256) and reductions in several launches (2r > 256)
     _announce(f"tiled mlp random M={M} tile={tile} H={H} I={I} r={r}")
     d = random_mlp(2_000 + M + tile + H + I + r, M, H, I, r)
     Ls, wf, wb, tf, tb = _run(d, tile)
     _compare_to_whole(wf, wb, tf, tb, same_order=tile >= M)
+    errs = _oracle_errs(d, Ls, tf, tb)
+    assert max(errs.values()) <= TOL, errs
+
+
+@pytest.mark.parametrize("r", [48, 96])
+def test_mlp_rank_multiple_of_16_not_a_power_of_two(r):
+    # the G products of such ranks read the transposed copies of B (whole and tiled)
+    _announce(f"mlp rank {r} M=600 tile=256 H=128 I=256")
+    d = random_mlp(620 + r, 600, 128, 256, r)
+    Ls, wf, wb, tf, tb = _run(d, 256)
+    _compare_to_whole(wf, wb, tf, tb, same_order=False)
     errs = _oracle_errs(d, Ls, tf, tb)
     assert max(errs.values()) <= TOL, errs
 

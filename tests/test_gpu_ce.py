@@ -45,6 +45,23 @@ def test_ce_full_oracle(M, H, V, chunk):
     assert not host(out["loss_rows"])[ign].any() and not host(out["dh"])[ign].any()
 
 
+def _random_ce_shapes(n, seed):
+    rng = np.random.default_rng(seed)
+    return [(int(rng.integers(1, 700)), 64 * int(rng.integers(1, 5)), 64 * int(rng.integers(1, 70)),
+             int(rng.integers(1, 900))) for _ in range(n)]
+
+
+@pytest.mark.parametrize("M,H,V,chunk", _random_ce_shapes(6, 9191))
+def test_ce_random_shapes(M, H, V, chunk):
+    _announce(f"ce random M={M} H={H} V={V} chunk={chunk}")
+    d = random_ce(700 + M + H + V + chunk, M, H, V)
+    out = _run(d, chunk)
+    loss, rows, dh = ce.ce_fwd_bwd(bf16_to_f64(d["h"]), bf16_to_f64(d["W"]), d["targets"])
+    assert abs(float(host(out["loss"])[0]) - loss) <= 1e-4 * max(abs(loss), 1e-12)
+    errs = dict(rows=rel_err(host(out["loss_rows"]), rows), dh=rel_err(host(out["dh"]), dh))
+    assert max(errs.values()) <= TOL, errs
+
+
 def test_ce_all_rows_ignored():
     _announce("ce all ignored")
     d = random_ce(5, 64, 64, 256)

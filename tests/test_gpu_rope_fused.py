@@ -75,6 +75,20 @@ def test_forward_rope_8bit_weights(fmt):
     _case(d, pos, 1000, fmt=fmt)
 
 
+def _random_rope_shapes(n, seed):
+    rng = np.random.default_rng(seed)
+    return [(int(rng.integers(16, 1500)), 64 * int(rng.integers(1, 9)), 128 * int(rng.integers(1, 9)),
+             int(rng.integers(1, 129)), int(rng.integers(0, 3)), int(rng.integers(64, 3000))) for _ in range(n)]
+
+
+@pytest.mark.parametrize("M,K,N,r,fmt,max_pos", _random_rope_shapes(6, 9292))
+def test_forward_rope_random_shapes(M, K, N, r, fmt, max_pos):
+    _announce(f"forward_rope random M={M} K={K} N={N} r={r} fmt={fmt} max_pos={max_pos}")
+    d = random_linear(31_000 + M + K + N + r, M, K, N, r)
+    pos = packed_positions(np.random.default_rng(M + max_pos), M, max_pos)
+    _case(d, pos, max_pos, fmt=fmt)
+
+
 def test_forward_rope_attn_q_projection_full_size():
     # the Llama-3-8B q projection (32 heads of 128), M=4096, packed sequences up to 4096
     _announce("forward_rope attn M=4096 K=N=4096 r=16")

@@ -219,7 +219,9 @@ int swiglu_mlp_backward(const qlora_layer* gate, const qlora_layer* up, const ql
  * each gradient adds its tiles in order on one stream. The buffers that the
  * second stream reads (h; dg and du) are held twice in the workspace. Calls
  * from several threads on one device share that stream, so their second-stream
- * parts run one after another. */
+ * parts run one after another. The calls can be captured in a HIP graph once
+ * that stream exists (after one such call on the device): it joins the
+ * capture through the events. */
 size_t swiglu_mlp_tiled_workspace_size(int backward, int64_t M, int64_t H, int64_t I, int64_t r, int64_t tile);
 int swiglu_mlp_forward_tiled(const qlora_layer* gate, const qlora_layer* up, const qlora_layer* down,
                              const uint16_t* X, int64_t M, int64_t tile, uint16_t* Y, uint16_t* Z_save, void* ws,

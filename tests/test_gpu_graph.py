@@ -1,7 +1,9 @@
 """The library's calls can be captured in a HIP graph: a captured fwd+bwd step,
 replayed several times with eager work and synchronisations in between, gives
-the eager result bit for bit on every replay (no memset nodes, no allocation,
-every launch on the caller's stream)."""
+the eager result bit for bit on every replay (no memset nodes, no allocation;
+every launch on the caller's stream, or, in the tiled SwiGLU calls, on the
+library's second stream, which joins the capture through the events that order
+it)."""
 import ctypes
 
 import numpy as np
@@ -84,3 +86,25 @@ def test_mlp_step_in_a_graph():
         q.mlp_forward(*Ls, X, out=f)
         q.mlp_backward(*Ls, dY, X, f, ws=ws, out=b)
     _check_graph(run, lambda: [f["Y"], f["h"], b["dX"]] + b["dA"] + b["dB"])
+
+
+@pytest.mark.parametrize("fmt", [0, 2])
+def test_tiled_mlp_step_in_a_graph(fmt):
+    # The tiled calls' second stream joins the capture through the events that
+    # fork and join it (the stream itself is created by the eager call made
+    # before the capture).
+    _announce(f"graph tiled mlp M=700 tile=256 H=128 I=256 r=16 fmt={fmt}")
+    import torch
+    import parameter_efficient_fine_amd as q
+    d = random_mlp(73 + fmt, 700, 128, 256, 16)
+    Ls = [Prepared(d["layers"][nm], d["s"], fmt=fmt).dev for nm in ("gate", "up", "down")]
+    X, dY = dev_bf16(d["X"]), dev_bf16(d["dY"])
+    f = q.mlp_forward_tiled(*Ls, X, 256)
+    b = q.mlp_backward_tiled(*Ls, dY, X, f["Z"], 256)
+    wsf = torch.empty((q.mlp_tiled_workspace_size(False, 700, 128, 256, 16, 256),), dtype=torch.uint8, device="cuda")
+    wsb = torch.empty((q.mlp_tiled_workspace_size(True, 700, 128, 256, 16, 256),), dtype=torch.uint8, device="cuda")
+
+    def run(st):
+        q.mlp_forward_tiled(*Ls, X, 256, ws=wsf, out=f)
+        q.mlp_backward_tiled(*Ls, dY, X, f["Z"], 256, ws=wsb, out=b)
+    _check_graph(run, lambda: [f["Y"], f["Z"], b["dX"]] + b["dA"] + b["dB"])

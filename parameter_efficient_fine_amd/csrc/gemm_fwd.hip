@@ -226,9 +226,15 @@ void k_qgemm_fwd(FwdArgs p) {
 #pragma unroll
     for (int f = 0; f < 2; ++f) dst[f] = wdeq8<F>(cr[f], ks, lut[f]);
   };
+  // NF4: lane half h builds the table of fragment h's row (lanes l and l+32 hold
+  // the same two rows) and the halves exchange them
   auto luts = [&](const float (&am)[2], WPrep<F> (&lut)[2]) {
+    if constexpr (F == kNF4) {
+      make_lut_pair(h ? am[1] : am[0], lut[0].lut, lut[1].lut);
+    } else {
 #pragma unroll
-    for (int f = 0; f < 2; ++f) lut[f] = wprep<F>(am[f]);
+      for (int f = 0; f < 2; ++f) lut[f] = wprep<F>(am[f]);
+    }
   };
   auto mfmas = [&](const u32x4 (&a)[2], const u32x4 (&b)[8]) {
 #pragma unroll

@@ -112,23 +112,6 @@ __device__ __forceinline__ Nf4Lut make_lut(float absmax) {
   return t;
 }
 
-// The tables of two weight rows held by the two halves of a wave (row 0 by
-// lanes 0-31, row 1 by lanes 32-63, lane l and l+32 on the same pair): each
-// lane builds the table of its own half's row, and v_permlane32_swap (the
-// upper 32 lanes of its first operand exchanged with the lower 32 lanes of its
-// second) hands every lane both: with both operands equal to the own table,
-// the first result carries row 0's table in all 64 lanes, the second row 1's.
-__device__ __forceinline__ void make_lut_pair(float absmax_own, Nf4Lut& t0, Nf4Lut& t1) {
-  const Nf4Lut own = make_lut(absmax_own);
-#pragma unroll
-  for (int q = 0; q < 4; ++q) {
-    const auto lo = __builtin_amdgcn_permlane32_swap(own.lo[q], own.lo[q], false, false);
-    const auto hi = __builtin_amdgcn_permlane32_swap(own.hi[q], own.hi[q], false, false);
-    t0.lo[q] = lo[0], t1.lo[q] = lo[1];
-    t0.hi[q] = hi[0], t1.hi[q] = hi[1];
-  }
-}
-
 // (a & m) | c as one v_and_or_b32. That instruction has three operands and,
 // on this architecture, no literal slot and a single scalar-register read, so
 // the two constants are pinned to vector registers (the empty asm only names

@@ -75,6 +75,23 @@ struct FwdArgs {
 
 constexpr int kRopeD = 128;  // head size of the RoPE epilogue (Llama-3)
 
+// The tables of two weight rows held by the two halves of a wave (row 0 by
+// lanes 0-31, row 1 by lanes 32-63, lane l and l+32 on the same pair): each
+// lane builds the table of its own half's row, and v_permlane32_swap (the
+// upper 32 lanes of its first operand exchanged with the lower 32 lanes of its
+// second) hands every lane both: with both operands equal to the own table,
+// the first result carries row 0's table in all 64 lanes, the second row 1's.
+__device__ __forceinline__ void make_lut_pair(float absmax_own, Nf4Lut& t0, Nf4Lut& t1) {
+  const Nf4Lut own = make_lut(absmax_own);
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const auto lo = __builtin_amdgcn_permlane32_swap(own.lo[q], own.lo[q], false, false);
+    const auto hi = __builtin_amdgcn_permlane32_swap(own.hi[q], own.hi[q], false, false);
+    t0.lo[q] = lo[0], t1.lo[q] = lo[1];
+    t0.hi[q] = hi[0], t1.hi[q] = hi[1];
+  }
+}
+
 // The epilogue is branch-free: loads and stores go through buffer resources
 // (out-of-range lanes read zero or drop their store); divergent branches there
 // would push the 256 accumulators out of AGPRs and spill the main loop.

@@ -305,7 +305,7 @@ void k_qgemm_fwd(FwdArgs p) {
     dequant_a(cc, 3, lc, av[1]);
     luts(an, ln);
     mfmas(av[0], bv[0]);
-    interleave(I8{}, I2{}, I8{});
+    interleave(I8{}, I2{}, I6{});
     __builtin_amdgcn_sched_barrier(0);
     // substep 3: substep 0 of step s+1 prepared from buffer (s+1)%4
     dma_x2(s3, b3, 6);

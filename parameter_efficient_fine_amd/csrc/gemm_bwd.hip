@@ -581,7 +581,7 @@ void k_qgemm_bwd8(BwdArgs p) {
     read_b(b0, 1, bv[1]);
     dequant_write(b1, cc, lut, 0, 2);
     mfmas(av[0], bv[0]);
-    interleave(I4{}, I2{}, I2{}, I6{});
+    interleave(I4{}, I2{}, I2{}, I8{});
     __builtin_amdgcn_sched_barrier(0);
     read_b(b0, 2, bv[0]);
     dequant_write(b1, cc, lut, 2, 3);

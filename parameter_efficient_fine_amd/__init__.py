@@ -7,12 +7,14 @@ the library; the first call does, and fails loudly if it is not built.
 from .ops import (  # noqa: F401
     KernelTimer,
     QLoraLayer,
+    QLoraLinear,
     backward,
     ce_chunk_for_budget,
     chunked_ce,
     dequantize,
     forward,
     forward_rope,
+    linear,
     lmhead_prepare,
     mlp_backward,
     mlp_backward_tiled,

@@ -176,6 +176,57 @@ def backward(L: QLoraLayer, dY, X, Z, need_dX=True, ws=None, out=None):
     return dX, dA, dB
 
 
+class _LinearFn(torch.autograd.Function):
+    """Autograd node of one projection: the library's forward, and its backward for
+    dX, dA and dB (the frozen weight gets no gradient)."""
+
+    @staticmethod
+    def forward(ctx, X, A, B, L):
+        Y, Z = forward(L, X)
+        ctx.save_for_backward(X, Z)
+        ctx.L = L
+        return Y
+
+    @staticmethod
+    def backward(ctx, dY):
+        X, Z = ctx.saved_tensors
+        dX, dA, dB = backward(ctx.L, dY.contiguous(), X, Z, need_dX=ctx.needs_input_grad[0])
+        return dX, dA, dB, None
+
+
+def linear(X: torch.Tensor, L: QLoraLayer) -> torch.Tensor:
+    """Y = X.What^T + s.(X.A^T).B^T for bf16 X [..., K] (leading dimensions are the
+    tokens), differentiable in X, L.A and L.B through the library's backward. The
+    adapters' gradients come in their own dtype, so L.grad_dtype must be bfloat16."""
+    if L.grad_dtype != L.A.dtype or L.grad_dtype != L.B.dtype:
+        raise ValueError("linear(): the layer's grad_dtype must be the adapters' dtype (torch.bfloat16)")
+    lead = X.shape[:-1]
+    Y = _LinearFn.apply(X.reshape(-1, L.K), L.A, L.B, L)
+    return Y.reshape(*lead, L.N)
+
+
+class QLoraLinear(torch.nn.Module):
+    """One projection for a PyTorch training loop: the frozen quantized weight (codes
+    and block values, as buffers) and the trainable bf16 adapters A [r, K], B [N, r]
+    (parameters); forward and backward run in the library."""
+
+    def __init__(self, codes: torch.Tensor, absmax: torch.Tensor, A: torch.Tensor, B: torch.Tensor, s: float,
+                 fmt: int = C.FMT_NF4):
+        super().__init__()
+        self.register_buffer("codes", codes)
+        self.register_buffer("absmax", absmax)
+        self.A = torch.nn.Parameter(A)
+        self.B = torch.nn.Parameter(B)
+        self.s = float(s)
+        self.fmt = int(fmt)
+
+    def layer(self) -> QLoraLayer:
+        return QLoraLayer(self.codes, self.absmax, self.A, self.B, self.s, self.fmt)
+
+    def forward(self, X: torch.Tensor) -> torch.Tensor:
+        return linear(X, self.layer())
+
+
 def mlp_forward(gate: QLoraLayer, up: QLoraLayer, down: QLoraLayer, X, out=None):
     """dict(Y, g, u, h, Z) for the SwiGLU block; Z is [3, M, r] (gate, up, down)."""
     M = X.shape[0]

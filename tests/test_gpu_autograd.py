@@ -1,0 +1,77 @@
+"""GPU: the autograd wrapper of one projection (`QLoraLinear`, `linear`) runs the
+library's forward and backward, so its output and gradients equal the explicit
+calls bit for bit (leading dimensions flattened to tokens), the backward without
+an input gradient skips dX, and an optimizer step on the adapters is seen by the
+next forward."""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+
+from synthetic import random_linear
+from tests._util import Prepared, dev_bf16
+
+pytestmark = pytest.mark.gpu
+
+
+def _bits(t):
+    import torch
+    t = t.detach().contiguous()
+    return t.view(torch.int16 if t.element_size() == 2 else torch.int32).cpu().numpy()
+
+
+def _module(seed, M, K, N, r):
+    import torch
+    import parameter_efficient_fine_amd as q
+    d = random_linear(seed, M, K, N, r)
+    P = Prepared(d["layers"]["proj"], d["s"], grad_dtype=torch.bfloat16)
+    L = P.dev
+    return d, L, q.QLoraLinear(L.codes, L.absmax, L.A.clone(), L.B.clone(), L.s)
+
+
+def test_autograd_linear_equals_the_explicit_calls():
+    print("[case] autograd linear M=600 K=512 N=384 r=16", flush=True)
+    import torch
+    import parameter_efficient_fine_amd as q
+    M, K, N = 600, 512, 384
+    d, L, mod = _module(91_001, M, K, N, 16)
+    X = dev_bf16(d["X"]).reshape(2, M // 2, K).requires_grad_(True)
+    dY = dev_bf16(d["dY"])
+    Y = mod(X)
+    Y.backward(dY.reshape(2, M // 2, N))
+    Xf = X.detach().reshape(M, K)
+    Ye, Ze = q.forward(L, Xf)
+    dXe, dAe, dBe = q.backward(L, dY, Xf, Ze)
+    torch.cuda.synchronize()
+    assert Y.shape == (2, M // 2, N) and X.grad.shape == X.shape
+    assert mod.codes.grad is None and not mod.codes.requires_grad
+    for got, want in ((Y.reshape(M, N), Ye), (X.grad.reshape(M, K), dXe), (mod.A.grad, dAe), (mod.B.grad, dBe)):
+        assert got.dtype == want.dtype and np.array_equal(_bits(got), _bits(want))
+    # an optimizer step changes A and B in place; the next forward reads them
+    torch.optim.SGD(mod.parameters(), lr=0.5).step()
+    with torch.no_grad():
+        Y2 = mod(Xf)
+    L2 = q.QLoraLayer(L.codes, L.absmax, mod.A.detach().clone(), mod.B.detach().clone(), L.s)
+    Y2e, _ = q.forward(L2, Xf)
+    torch.cuda.synchronize()
+    assert not np.array_equal(_bits(Y2), _bits(Ye))
+    assert np.array_equal(_bits(Y2), _bits(Y2e))
+
+
+def test_autograd_linear_without_an_input_gradient():
+    print("[case] autograd linear, no dX, M=300 K=256 N=200 r=8", flush=True)
+    import torch
+    import parameter_efficient_fine_amd as q
+    M, K, N = 300, 256, 200
+    d, L, mod = _module(91_002, M, K, N, 8)
+    X = dev_bf16(d["X"])
+    dY = dev_bf16(d["dY"])
+    mod(X).backward(dY)
+    _, Ze = q.forward(L, X)
+    _, dAe, dBe = q.backward(L, dY, X, Ze, need_dX=False)
+    torch.cuda.synchronize()
+    assert np.array_equal(_bits(mod.A.grad), _bits(dAe)) and np.array_equal(_bits(mod.B.grad), _bits(dBe))
+    # fp32 adapter gradients cannot be handed to bf16 parameters without a cast: refused
+    L32 = q.QLoraLayer(L.codes, L.absmax, L.A, L.B, L.s, grad_dtype=torch.float32)
+    with pytest.raises(ValueError):
+        q.linear(X, L32)

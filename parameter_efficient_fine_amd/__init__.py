@@ -29,5 +29,6 @@ from .ops import (  # noqa: F401
     rope_backward,
     rope_forward,
     rope_table,
+    swiglu_mlp,
     workspace_size,
 )

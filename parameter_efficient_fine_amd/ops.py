@@ -292,6 +292,37 @@ def mlp_backward(gate: QLoraLayer, up: QLoraLayer, down: QLoraLayer, dY, X, save
     return out
 
 
+class _SwiGLUFn(torch.autograd.Function):
+    """Autograd node of the SwiGLU block: the library's forward (saving g, u, h and
+    the three Z) and its backward for dX and the six adapter gradients."""
+
+    @staticmethod
+    def forward(ctx, X, Ag, Bg, Au, Bu, Ad, Bd, layers):
+        out = mlp_forward(*layers, X)
+        ctx.save_for_backward(X, out["g"], out["u"], out["h"], out["Z"])
+        ctx.layers = layers
+        return out["Y"]
+
+    @staticmethod
+    def backward(ctx, dY):
+        X, g, u, h, Z = ctx.saved_tensors
+        b = mlp_backward(*ctx.layers, dY.contiguous(), X, dict(g=g, u=u, h=h, Z=Z), need_dX=ctx.needs_input_grad[0])
+        (dAg, dAu, dAd), (dBg, dBu, dBd) = b["dA"], b["dB"]
+        return b["dX"], dAg, dBg, dAu, dBu, dAd, dBd, None
+
+
+def swiglu_mlp(X: torch.Tensor, gate: QLoraLayer, up: QLoraLayer, down: QLoraLayer) -> torch.Tensor:
+    """The SwiGLU block Y = down(silu(gate(X)) * up(X)) for bf16 X [..., H] (leading
+    dimensions are the tokens), differentiable in X and the six adapters through the
+    library's backward; the layers' grad_dtype must be the adapters' dtype (bfloat16)."""
+    layers = (gate, up, down)
+    if any(L.grad_dtype != L.A.dtype or L.grad_dtype != L.B.dtype for L in layers):
+        raise ValueError("swiglu_mlp(): the layers' grad_dtype must be the adapters' dtype (torch.bfloat16)")
+    lead = X.shape[:-1]
+    Y = _SwiGLUFn.apply(X.reshape(-1, gate.K), gate.A, gate.B, up.A, up.B, down.A, down.B, layers)
+    return Y.reshape(*lead, down.N)
+
+
 def mlp_tiled_workspace_size(backward: bool, M: int, H: int, I: int, r: int, tile: int) -> int:
     return int(C.lib().swiglu_mlp_tiled_workspace_size(1 if backward else 0, M, H, I, r, tile))
 

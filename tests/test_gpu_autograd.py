@@ -75,3 +75,29 @@ def test_autograd_linear_without_an_input_gradient():
     L32 = q.QLoraLayer(L.codes, L.absmax, L.A, L.B, L.s, grad_dtype=torch.float32)
     with pytest.raises(ValueError):
         q.linear(X, L32)
+
+
+def test_autograd_swiglu_block_equals_the_explicit_calls():
+    print("[case] autograd SwiGLU block M=300 H=256 I=512 r=16", flush=True)
+    import torch
+    import parameter_efficient_fine_amd as q
+    from synthetic import random_mlp
+    M, H, I = 300, 256, 512
+    d = random_mlp(91_003, M, H, I, 16)
+    Ls = [Prepared(d["layers"][nm], d["s"], grad_dtype=torch.bfloat16).dev for nm in ("gate", "up", "down")]
+    # the autograd path on parameter copies of the adapters, the explicit calls on the originals
+    P = [q.QLoraLayer(L.codes, L.absmax, torch.nn.Parameter(L.A.clone()), torch.nn.Parameter(L.B.clone()), L.s)
+         for L in Ls]
+    X = dev_bf16(d["X"]).reshape(3, M // 3, H).requires_grad_(True)
+    dY = dev_bf16(d["dY"])
+    Y = q.swiglu_mlp(X, *P)
+    Y.backward(dY.reshape(3, M // 3, H))
+    Xf = X.detach().reshape(M, H)
+    f = q.mlp_forward(*Ls, Xf)
+    b = q.mlp_backward(*Ls, dY, Xf, f)
+    torch.cuda.synchronize()
+    assert np.array_equal(_bits(Y.reshape(M, H)), _bits(f["Y"]))
+    assert np.array_equal(_bits(X.grad.reshape(M, H)), _bits(b["dX"]))
+    for i in range(3):
+        assert np.array_equal(_bits(P[i].A.grad), _bits(b["dA"][i]))
+        assert np.array_equal(_bits(P[i].B.grad), _bits(b["dB"][i]))

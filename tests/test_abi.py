@@ -352,3 +352,18 @@ def test_noalloc_backward_rejects_workspaces_beyond_its_scratch():
     # the header's limit and the binding's constant agree
     text = open(HEADER).read()
     assert "#define QLORA_NOALLOC_SCRATCH_BYTES (64u << 20)" in text and C.NOALLOC_SCRATCH_BYTES == 64 << 20
+
+
+def test_autograd_wrappers_refuse_gradients_of_another_dtype_than_the_adapters():
+    # checked on the host before any call into the library
+    import torch
+    import parameter_efficient_fine_amd as q
+    K, N, r = 128, 64, 8
+    L = q.QLoraLayer(torch.zeros((N, K // 2), dtype=torch.uint8), torch.zeros((N, K // 64)),
+                     torch.zeros((r, K), dtype=torch.bfloat16), torch.zeros((N, r), dtype=torch.bfloat16), 2.0,
+                     grad_dtype=torch.float32)
+    X = torch.zeros((4, K), dtype=torch.bfloat16)
+    with pytest.raises(ValueError):
+        q.linear(X, L)
+    with pytest.raises(ValueError):
+        q.swiglu_mlp(X, L, L, L)

@@ -55,6 +55,7 @@ constexpr int kNV = kFmt == kNF4 ? 1 : 2;   // 16-byte code loads per lane, row 
 constexpr int kCodeStepB = 16 * kNV;        // code bytes of a lane's 32 elements
 
 constexpr int kTok = 256;       // tokens per workgroup
+constexpr int64_t kCUs = 256;   // compute units of the chip (one workgroup each)
 constexpr int kStep = 64;       // reduction step (one absmax block)
 constexpr int kRowB = kStep * 2;           // bytes of one token row of the activation tile (dense)
 constexpr int kBufB = kTok * kRowB;        // 32 KB per buffer
@@ -96,20 +97,31 @@ __device__ __forceinline__ void make_lut_pair(float absmax_own, Nf4Lut& t0, Nf4L
 // (out-of-range lanes read zero or drop their store); divergent branches there
 // would push the 256 accumulators out of AGPRs and spill the main loop.
 
-template <int F, bool GATEUP, int RP, bool ALIGNED, bool ROPE>
-__global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_per_eu(1, 1)))
-void k_qgemm_fwd(FwdArgs p) {
-  extern __shared__ __attribute__((aligned(16))) uint8_t smem[];  // [kNBuf][256 rows][128 B], swizzled
+// EPI: 0 the plain product, 1 with the RoPE epilogue, 2 the plain product on
+// 128-token tiles (TK tokens per workgroup), taken where 256-token tiles would
+// leave CUs idle (launch_rp). Each output element sums the same products in the
+// same order on either tile, so both give the same bits.
+// (The body is a device function that the kernel below calls: with the tile
+// size a template parameter of a kernel itself, the host compilation emitted
+// no launch stubs for it.)
+template <int F, bool GATEUP, int RP, bool ALIGNED, int EPI>
+__device__ __forceinline__ void qgemm_fwd_body(FwdArgs p) {
+  constexpr bool ROPE = EPI == 1;
+  constexpr int TK = EPI == 2 ? 128 : kTok;
+  static_assert(EPI != 2 || !GATEUP, "128-token tiles: plain product only");
+  constexpr int NJ = TK / 32;          // token fragments per wave, activation copies per wave and step
+  constexpr int kBuf = TK * kRowB;     // bytes of one ring buffer
+  extern __shared__ __attribute__((aligned(16))) uint8_t smem[];  // [kNBuf][TK rows][128 B], swizzled
   const int t = threadIdx.x, lane = t & 63;
   const int wave = __builtin_amdgcn_readfirstlane(t >> 6);  // wave-uniform: LDS bases stay scalar
   const int h = lane >> 5, jl = lane & 31;
   const int64_t M = p.M, K = p.K, N = p.N;
   const int64_t ipt = GATEUP ? 128 : 256;  // output columns per workgroup
-  const int64_t nJ = (M + kTok - 1) / kTok;
+  const int64_t nJ = (M + TK - 1) / TK;
   const int64_t it = blockIdx.x / nJ, jt = blockIdx.x - it * nJ;
-  const int64_t i0 = it * ipt, j0 = jt * kTok;
+  const int64_t i0 = it * ipt, j0 = jt * TK;
   const int nsteps = (int)(K / kStep);
-  const int64_t rows_here = (M - j0) < kTok ? (M - j0) : kTok;  // tokens of this tile that exist
+  const int64_t rows_here = (M - j0) < TK ? (M - j0) : TK;  // tokens of this tile that exist
 
   // This lane's two weight rows: fragment f covers rows nb[f] .. nb[f]+31, lane row nb[f] + jl.
   int64_t nb[2];
@@ -136,26 +148,26 @@ void k_qgemm_fwd(FwdArgs p) {
     offA[f] = n < N ? (int)((grp * (K / kBlock) + (n - grp)) * 4) : kOff;
   }
   const int codes_per_step = (int)(nrw * kBB), values_per_step = (int)(nrw * 4);  // scalar strides
-  // activation copy: wave w, instruction i fills tile rows 64w+8i .. +7; lane l writes
-  // physical chunk l%8 of row 64w+8i+l/8, which holds logical chunk (l%8) ^ ((row>>1)&7)
-  int offX[8];
+  // activation copy: wave w, instruction i fills tile rows (TK/4)w+8i .. +7; lane l writes
+  // physical chunk l%8 of row (TK/4)w+8i+l/8, which holds logical chunk (l%8) ^ ((row>>1)&7)
+  int offX[NJ];
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const int row = 64 * wave + 8 * i + (lane >> 3);
+  for (int i = 0; i < NJ; ++i) {
+    const int row = (TK / 4) * wave + 8 * i + (lane >> 3);
     const int c = (lane & 7) ^ ((row >> 1) & 7);
     offX[i] = (int)((int64_t)row * K * 2 + 16 * c);
   }
-  auto dma_x2 = [&](int step, int buf, int i0) {  // copies i0, i0 + 1 of the 8
+  auto dma_q = [&](int step, int buf, int q) {  // quarter q of the NJ copies
     const int soff = step * kRowB;
-    uint8_t* base = smem + buf * kBufB + (64 * wave) * kRowB;
+    uint8_t* base = smem + buf * kBuf + ((TK / 4) * wave) * kRowB;
 #pragma unroll
-    for (int i = i0; i < i0 + 2; ++i)
+    for (int i = q * (NJ / 4); i < (q + 1) * (NJ / 4); ++i)
       __builtin_amdgcn_raw_ptr_buffer_load_lds(rX, (__attribute__((address_space(3))) void*)(base + 8 * i * kRowB),
                                                16, offX[i], soff, 0, 0);
   };
   auto dma_x = [&](int step, int buf) {
 #pragma unroll
-    for (int i = 0; i < 8; i += 2) dma_x2(step, buf, i);
+    for (int q = 0; q < 4; ++q) dma_q(step, buf, q);
   };
   auto load_codes = [&](int step, u32x4 (&cr)[2][kNV], float (&am)[2]) {
 #pragma unroll
@@ -169,11 +181,11 @@ void k_qgemm_fwd(FwdArgs p) {
       am[f] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rA[f], offA[f], step * values_per_step, 0));
   };
 
-  f32x16 acc[2][8];
+  f32x16 acc[2][NJ];
 #pragma unroll
   for (int f = 0; f < 2; ++f)
 #pragma unroll
-    for (int j = 0; j < 8; ++j) acc[f][j] = f32x16{};
+    for (int j = 0; j < NJ; ++j) acc[f][j] = f32x16{};
 
   // ---- the rank-r term, accumulated first by MFMA: acc = (s.B rows) . (Z rows)^T.
   // (Adding it here rather than in the epilogue keeps every accumulator in AGPRs.)
@@ -194,23 +206,23 @@ void k_qgemm_fwd(FwdArgs p) {
         const u32x4 bv = rank8<ALIGNED>(second ? rB1 : rB0, ir < N ? ir : -1, rs, rs, rr + c0);
         split_scaled(bv, second ? p.w1.s : p.w0.s, bh[f], bl[f]);
       }
-      u32x4 z[8][2];
+      u32x4 z[NJ][2];
 #pragma unroll
-      for (int j = 0; j < 8; ++j) {
+      for (int j = 0; j < NJ; ++j) {
         const int64_t mr = 32 * j + jl;
         const int64_t zrow = mr < rows_here ? mr : -1;
         z[j][0] = rank8<ALIGNED>(rZ0, zrow, p.w0.r, p.w0.r, rr + c0);
         z[j][1] = GATEUP ? rank8<ALIGNED>(rZ1, zrow, p.w1.r, p.w1.r, rr + c0) : z[j][0];
       }
 #pragma unroll
-      for (int j = 0; j < 8; ++j) {
+      for (int j = 0; j < NJ; ++j) {
         acc[0][j] = mfma32(bh[0], z[j][0], acc[0][j]);
         acc[1][j] = mfma32(bh[1], z[j][1], acc[1][j]);
       }
       // the low parts only where some lane has one (none when s is a power of two)
       if (lo_any(bl[0], bl[1])) {
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
+        for (int j = 0; j < NJ; ++j) {
           acc[0][j] = mfma32(bl[0], z[j][0], acc[0][j]);
           acc[1][j] = mfma32(bl[1], z[j][1], acc[1][j]);
         }
@@ -227,17 +239,17 @@ void k_qgemm_fwd(FwdArgs p) {
   u32x4 cs0[2][kNV], cs1[2][kNV], cs2[2][kNV];  // codes of steps s, s+1, s+2 (rotating)
   float as0[2], as1[2], as2[2];
   WPrep<F> L0[2], L1[2], L2[2];  // per-block tables / scales, rotating with the codes
-  u32x4 bv[2][8];                // activation fragments, alternating by substep
+  u32x4 bv[2][NJ];               // activation fragments, alternating by substep
   u32x4 av[2][2];                // weight fragments, alternating by substep
 
   // per-lane byte offset of activation fragment chunk for substep ks (swizzled)
   int offB[4];
 #pragma unroll
   for (int ks = 0; ks < 4; ++ks) offB[ks] = jl * kRowB + 16 * ((4 * h + ks) ^ ((jl >> 1) & 7));
-  auto read_b = [&](int buf, int ks, u32x4 (&dst)[8]) {
-    const uint8_t* bx = smem + buf * kBufB + offB[ks];
+  auto read_b = [&](int buf, int ks, u32x4 (&dst)[NJ]) {
+    const uint8_t* bx = smem + buf * kBuf + offB[ks];
 #pragma unroll
-    for (int j = 0; j < 8; ++j) dst[j] = *reinterpret_cast<const u32x4*>(bx + 32 * j * kRowB);
+    for (int j = 0; j < NJ; ++j) dst[j] = *reinterpret_cast<const u32x4*>(bx + 32 * j * kRowB);
   };
   auto dequant_a = [&](const u32x4 (&cr)[2][kNV], int ks, const WPrep<F> (&lut)[2], u32x4 (&dst)[2]) {
 #pragma unroll
@@ -253,32 +265,36 @@ void k_qgemm_fwd(FwdArgs p) {
       for (int f = 0; f < 2; ++f) lut[f] = wprep<F>(am[f]);
     }
   };
-  auto mfmas = [&](const u32x4 (&a)[2], const u32x4 (&b)[8]) {
+  auto mfmas = [&](const u32x4 (&a)[2], const u32x4 (&b)[NJ]) {
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
+    for (int j = 0; j < NJ; ++j) {
       acc[0][j] = mfma32(a[0], b[j], acc[0][j]);
       acc[1][j] = mfma32(a[1], b[j], acc[1][j]);
     }
   };
-  // issue order inside a substep: 16 MFMAs, each followed by a slice of the
-  // other work (LDS reads for the next substep, loads, dequant VALU)
-  auto interleave = [&](auto nds_read, auto nvmem, auto nvalu) {
+  // issue order inside a substep: its 2*NJ MFMAs, each followed by a slice of
+  // the other work (the NJ LDS reads of the next substep first, loads, and the
+  // dequant VALU spread at nvalu * 8/NJ ops per MFMA: the same per substep for
+  // either tile)
+  auto interleave = [&](auto nvmem, auto nvalu) {
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
+    for (int i = 0; i < 2 * NJ; ++i) {
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      if (i < decltype(nds_read)::value) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      if (i < NJ) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
       if (i < decltype(nvmem)::value) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(0x002, decltype(nvalu)::value, 0);
+      __builtin_amdgcn_sched_group_barrier(0x002, decltype(nvalu)::value * 8 / NJ, 0);
     }
   };
-  using I2 = std::integral_constant<int, 2>;
+  constexpr int kCL = 2 * kNV + 2;  // code and block-value loads of a step
+  using IC = std::integral_constant<int, kCL + NJ / 4>;
+  using IQ = std::integral_constant<int, NJ / 4>;
   using I4 = std::integral_constant<int, 4>;
   using I6 = std::integral_constant<int, 6>;
-  using I8 = std::integral_constant<int, 8>;
 
-  // Step s: VMEM issue order is fixed (4 code loads, then 8 activation copies)
-  // so the wait before the closing barrier can be counted: the copies of step
-  // s+2 (issued during step s-1) must have landed; 12 ops of step s may remain.
+  // Step s: VMEM issue order is fixed (the code loads, then NJ activation
+  // copies) so the wait before the closing barrier can be counted: the copies
+  // of step s+2 (issued during step s-1) must have landed; the kCL + NJ ops of
+  // step s may remain.
   auto body = [&](int s, const u32x4 (&cc)[2][kNV], const WPrep<F> (&lc)[2], const u32x4 (&cn)[2][kNV],
                   const float (&an)[2], WPrep<F> (&ln)[2], u32x4 (&cl)[2][kNV], float (&al)[2]) {
     const int b0 = s % kNBuf, b1 = (s + 1) % kNBuf, b3 = (s + 3) % kNBuf;
@@ -286,35 +302,35 @@ void k_qgemm_fwd(FwdArgs p) {
     const int s3 = s + 3 < nsteps ? s + 3 : nsteps - 1;
     // substep 0: codes of s+2 and two of the activation copies of s+3 requested
     load_codes(s2, cl, al);
-    dma_x2(s3, b3, 0);
+    dma_q(s3, b3, 0);
     read_b(b0, 1, bv[1]);
     dequant_a(cc, 1, lc, av[1]);
     mfmas(av[0], bv[0]);
-    interleave(I8{}, I6{}, I4{});
+    interleave(IC{}, I4{});
     __builtin_amdgcn_sched_barrier(0);
     // substep 1
-    dma_x2(s3, b3, 2);
+    dma_q(s3, b3, 1);
     read_b(b0, 2, bv[0]);
     dequant_a(cc, 2, lc, av[0]);
     mfmas(av[1], bv[1]);
-    interleave(I8{}, I2{}, I4{});
+    interleave(IQ{}, I4{});
     __builtin_amdgcn_sched_barrier(0);
     // substep 2: also the LUTs of step s+1
-    dma_x2(s3, b3, 4);
+    dma_q(s3, b3, 2);
     read_b(b0, 3, bv[1]);
     dequant_a(cc, 3, lc, av[1]);
     luts(an, ln);
     mfmas(av[0], bv[0]);
-    interleave(I8{}, I2{}, I6{});
+    interleave(IQ{}, I6{});
     __builtin_amdgcn_sched_barrier(0);
     // substep 3: substep 0 of step s+1 prepared from buffer (s+1)%4
-    dma_x2(s3, b3, 6);
+    dma_q(s3, b3, 3);
     read_b(b1, 0, bv[0]);
     dequant_a(cn, 0, ln, av[0]);
     mfmas(av[1], bv[1]);
-    interleave(I8{}, I2{}, I4{});
+    interleave(IQ{}, I4{});
     __builtin_amdgcn_sched_barrier(0);
-    __builtin_amdgcn_s_waitcnt(waitcnt_vm(12));  // activation copies of step s+2 done
+    __builtin_amdgcn_s_waitcnt(waitcnt_vm(kCL + NJ));  // activation copies of step s+2 done
     __builtin_amdgcn_s_waitcnt(0xC07F);           // and this wave's LDS reads
     __builtin_amdgcn_s_barrier();
   };
@@ -325,7 +341,7 @@ void k_qgemm_fwd(FwdArgs p) {
   dma_x(0, 0);
   dma_x(nsteps > 1 ? 1 : 0, 1);
   dma_x(nsteps > 2 ? 2 : nsteps - 1, 2);
-  __builtin_amdgcn_s_waitcnt(waitcnt_vm(8));
+  __builtin_amdgcn_s_waitcnt(waitcnt_vm(NJ));
   __builtin_amdgcn_s_barrier();
   luts(as0, L0);
   read_b(0, 0, bv[0]);
@@ -439,11 +455,11 @@ void k_qgemm_fwd(FwdArgs p) {
   __builtin_amdgcn_s_barrier();   // and every wave is done reading the ring
   int jle = jl, he = h, lne = lane;
   asm volatile("" : "+v"(jle), "+v"(he), "+v"(lne));  // no prologue values kept alive for this
-  uint8_t* const reg = smem + wave * (kTok * 128);
+  uint8_t* const reg = smem + wave * (TK * 128);
   const int rh = (int)rows_here;
   if constexpr (!GATEUP) {
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
+    for (int j = 0; j < NJ; ++j) {
       const int t = 32 * j + jle;
 #pragma unroll
       for (int f = 0; f < 2; ++f)
@@ -458,7 +474,7 @@ void k_qgemm_fwd(FwdArgs p) {
     const int c = lne & 7, tq = lne >> 3;
     const int64_t col = i0 + 64 * wave + 8 * c;
 #pragma unroll
-    for (int u = 0; u < 32; ++u) {
+    for (int u = 0; u < TK / 8; ++u) {
       const int t = 8 * u + tq;
       const u32x4 v = *reinterpret_cast<const u32x4*>(reg + t * 128 + 16 * (c ^ (t & 7)));
       const int off = (t < rh && col < N) ? (int)((t * N + col) * 2) : kOff;
@@ -522,17 +538,38 @@ void k_qgemm_fwd(FwdArgs p) {
   }
 }
 
+template <int F, bool GATEUP, int RP, bool ALIGNED, int EPI>
+__global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_per_eu(1, 1)))
+void k_qgemm_fwd(FwdArgs p) {
+  qgemm_fwd_body<F, GATEUP, RP, ALIGNED, EPI>(p);
+}
+
 template <bool GATEUP, int RP, bool ALIGNED, bool ROPE>
 hipError_t launch_rp(const FwdArgs& a, hipStream_t st) {
   // set once per kernel instance; a function-local static is initialised exactly
   // once even when several threads make their first call together
-  static const hipError_t attr = hipFuncSetAttribute((const void*)k_qgemm_fwd<kFmt, GATEUP, RP, ALIGNED, ROPE>,
+  static const hipError_t attr = hipFuncSetAttribute((const void*)k_qgemm_fwd<kFmt, GATEUP, RP, ALIGNED, ROPE ? 1 : 0>,
                                                      hipFuncAttributeMaxDynamicSharedMemorySize, (int)kLds);
   if (attr != hipSuccess) return attr;
   const int64_t ipt = GATEUP ? 128 : 256;
   const int64_t nI = (a.N + ipt - 1) / ipt, nJ = (a.M + kTok - 1) / kTok;
   if (nI * nJ == 0) return hipSuccess;
-  k_qgemm_fwd<kFmt, GATEUP, RP, ALIGNED, ROPE><<<(unsigned)(nI * nJ), 256, kLds, st>>>(a);
+  if constexpr (!GATEUP && !ROPE) {
+    // 128-token tiles where 256-token ones leave CUs idle and the 128-token
+    // grid still runs in one pass of one workgroup per CU (a decoded weight
+    // then feeds half as many MFMAs, which only pays where CUs would idle)
+    const int64_t nJ128 = (a.M + 127) / 128;
+    if (a.M > 256 && nI * nJ < kCUs && nI * nJ128 <= kCUs) {
+      constexpr size_t kLds128 = (size_t)kNBuf * 128 * kRowB;
+      static const hipError_t attr128 = hipFuncSetAttribute(
+          (const void*)k_qgemm_fwd<kFmt, false, RP, ALIGNED, 2>, hipFuncAttributeMaxDynamicSharedMemorySize,
+          (int)kLds128);
+      if (attr128 != hipSuccess) return attr128;
+      k_qgemm_fwd<kFmt, false, RP, ALIGNED, 2><<<(unsigned)(nI * nJ128), 256, kLds128, st>>>(a);
+      return hipGetLastError();
+    }
+  }
+  k_qgemm_fwd<kFmt, GATEUP, RP, ALIGNED, ROPE ? 1 : 0><<<(unsigned)(nI * nJ), 256, kLds, st>>>(a);
   return hipGetLastError();
 }
 

@@ -22,12 +22,19 @@ def _bits(t):
 
 # (M, K, N, r, alpha, fmt, slice): with N = 4096 a batch of M = 4096 tokens fills
 # the chip with 256-token tiles (16 x 16 workgroups); slices of 1000-1024 tokens
-# take 128-token tiles (16 x 8), the 1000-token ones with a ragged last tile.
+# take 128-token tiles (16 x 8), the 1000-token ones with a ragged last tile;
+# also a ragged column count (N = 4000), the rank buckets of 128 and 256 (r = 200
+# with its rank rows unaligned), and 300-token slices just above the small-batch
+# kernels' 256 tokens (3 tiles of 128, the last one ragged).
 CASES = [
     (4096, 512, 4096, 16, 32, 0, 1024),
     (4096, 256, 4096, 16, 24, 0, 1000),
     (4096, 256, 4096, 48, 96, 1, 1024),
     (4096, 256, 4096, 8, 16, 2, 1000),
+    (4096, 256, 4000, 16, 32, 0, 1000),
+    (4096, 256, 4096, 128, 128, 0, 1024),
+    (4096, 320, 4096, 200, 64, 1, 1000),
+    (4096, 256, 4096, 16, 32, 2, 300),
 ]
 
 
